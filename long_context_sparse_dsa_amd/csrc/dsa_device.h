@@ -1,0 +1,138 @@
+// dsa_device.h -- gfx950 device helpers shared by the DSA kernels.
+//
+// MFMA operand layouts used throughout (wave64, checked on gfx950):
+//   v_mfma_f32_32x32x16_bf16  A[i][k]: lane l holds row i = l%32, k = 8*(l/32)+0..7
+//                             B[k][j]: lane l holds col j = l%32, k = 8*(l/32)+0..7
+//                             C[i][j]: lane l, reg r holds i = 8*(r/4)+4*(l/32)+r%4, j = l%32
+// Because every contraction below sums over k, the kernels are free to assign
+// any fixed permutation of the contracted dimension to the k slots, as long
+// as both operands use the same one.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// float -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Order-preserving map of an fp32 score onto uint32: larger key <=> larger
+// value, with -0.0 mapped onto +0.0 so that the two compare equal.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t x = __float_as_uint(f);
+  if (x == 0x80000000u) x = 0u;
+  return (x & 0x80000000u) ? ~x : (x | 0x80000000u);
+}
+
+// 16 bytes holding 8 bf16 -> MFMA operand.
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+// 8 fp8 e4m3fn codes (two dwords) -> 8 bf16, exact (every e4m3fn value is a
+// bf16 value; the gfx950 conversion with scale 1.0 is exact).
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)lo, 1.0f, false);
+  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)lo, 1.0f, true);
+  bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)hi, 1.0f, false);
+  bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)hi, 1.0f, true);
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ u32x4 ld16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// Sum / max across the two 32-lane halves of a wave.
+__device__ __forceinline__ float xor32_add(float v) { return v + __shfl_xor(v, 32); }
+__device__ __forceinline__ float xor32_max(float v) { return fmaxf(v, __shfl_xor(v, 32)); }
+
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t t = __shfl_up(v, o);
+    if (l >= o) v += t;
+  }
+  return v;
+}
+
+// Exclusive block-wide prefix sum of one value per thread.  `scratch` holds
+// at least blockDim.x/64 + 1 uint32.  Returns the exclusive prefix; *total
+// receives the block total.  Contains barriers: call from every thread.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* scratch, uint32_t* total) {
+  const int w = wave_id(), nw = blockDim.x >> 6;
+  uint32_t inc = wave_incl_scan(v);
+  if (lane_id() == 63) scratch[w] = inc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t acc = 0;
+    for (int i = 0; i < nw; ++i) {
+      uint32_t t = scratch[i];
+      scratch[i] = acc;
+      acc += t;
+    }
+    scratch[nw] = acc;
+  }
+  __syncthreads();
+  uint32_t r = scratch[w] + inc - v;
+  *total = scratch[nw];
+  __syncthreads();
+  return r;
+}
+
+// Position of query row t: decode (cu_q == nullptr) has one query per
+// sequence at position ctx_len-1; otherwise query i of sequence b sits at
+// ctx_len[b] - n_q[b] + i.
+struct RowInfo {
+  int b;
+  int64_t p;
+};
+
+__device__ __forceinline__ RowInfo row_info(int t, const int32_t* cu_q, const int32_t* ctx_len,
+                                            int B) {
+  RowInfo r;
+  if (cu_q == nullptr) {
+    r.b = t;
+    r.p = (int64_t)ctx_len[t] - 1;
+    return r;
+  }
+  int lo = 0, hi = B - 1;  // last b with cu_q[b] <= t
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (cu_q[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  r.b = lo;
+  r.p = (int64_t)ctx_len[lo] - (cu_q[lo + 1] - cu_q[lo]) + (t - cu_q[lo]);
+  return r;
+}
+
+}  // namespace dsa

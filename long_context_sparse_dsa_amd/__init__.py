@@ -252,6 +252,40 @@ def dsa_layer_decode(q_idx, w, k_idx, k_scale, q, k_cache, v_cache, gate, K, ctx
     return out
 
 
+def prepare_layer_decode(q_idx, w, k_idx, k_scale, q, k_cache, v_cache, gate, K, ctx_len, cu_ctx,
+                         max_ctx, out, ws, sm_scale=0.0, idx_out=None, w_ld=None, stream=None):
+    """Marshal one dsa_layer_decode call once; returns a no-argument callable
+    that re-issues it (one ctypes call, no per-call argument checks).  The
+    tensors must stay alive and unchanged in shape while the callable is used."""
+    _check(q_idx, "q_idx", BF16, 3)
+    _check(w, "w", BF16)
+    _check(k_idx, "k_idx", KEYS, 2)
+    _check(k_scale, "k_scale", (torch.float32,), 1)
+    _check(q, "q", BF16, 3)
+    _check(k_cache, "k_cache", BF16, 2)
+    _check(v_cache, "v_cache", BF16, 2)
+    _check(gate, "gate", BF16, 3)
+    _check(ctx_len, "ctx_len", (torch.int32,), 1)
+    _check(cu_ctx, "cu_ctx", (torch.int64,), 1)
+    _check(out, "out", BF16, 3)
+    _check(idx_out, "idx_out", (torch.int32,), 2)
+    B, H_I, d_I = q_idx.shape
+    _, Hq, D = q.shape
+    if w_ld is None:
+        w_ld = 0 if w.dim() == 1 else w.shape[-1]
+    fn = load().dsa_layer_decode
+    args = (_p(q_idx), _p(w), w_ld, _p(k_idx), _key_dtype(k_idx), _p(k_scale), H_I, d_I, _p(q),
+            _p(k_cache), _p(v_cache), _p(gate), float(sm_scale), Hq, D, K, _p(ctx_len),
+            _p(cu_ctx), B, int(max_ctx), _p(out), _p(idx_out), _p(ws), ws.numel(),
+            _stream(stream))
+
+    def call():
+        st = fn(*args)
+        if st != 0:
+            raise DSAError("dsa_layer_decode", st, dsa_last_error())
+    return call
+
+
 def dsa_layer_prefill_workspace_size(B, T, max_ctx, K, Hq, D) -> int:
     return int(load().dsa_layer_prefill_workspace_size(B, T, max_ctx, K, Hq, D))
 

@@ -89,14 +89,14 @@ size_t decode_ws_layout(int B, int max_ctx, int K, int Hq, int D, char* base, De
   const int64_t ld = ws_ld(max_ctx);
   size_t off = 0;
   const size_t s_scores = align_up((size_t)B * ld * sizeof(float), 256);
-  const size_t s_rep = align_up(dsa::topk_report_bytes(B, max_ctx), 256);
+  const size_t s_rep = align_up(dsa::topk_report_bytes(B, max_ctx, K), 256);
   const size_t s_idx = align_up((size_t)B * K * sizeof(int32_t), 256);
   const dsa::AttnPlan plan = dsa::attn_plan(B, K, 0, Hq, D);
   const size_t s_attn = align_up(plan.ws_bytes, 256);
   if (out) {
     out->ld = ld;
     out->scores = reinterpret_cast<float*>(base + off);
-    out->topk = dsa::topk_ws_carve(base + off + s_scores, B, max_ctx);
+    out->topk = dsa::topk_ws_carve(base + off + s_scores, B, max_ctx, K);
     out->idx = reinterpret_cast<int32_t*>(base + off + s_scores + s_rep);
     out->attn = base + off + s_scores + s_rep + s_idx;
   }
@@ -106,14 +106,14 @@ size_t decode_ws_layout(int B, int max_ctx, int K, int Hq, int D, char* base, De
 size_t prefill_ws_layout(int T, int max_ctx, int K, int Hq, int D, char* base, DecodeWs* out) {
   const int64_t ld = ws_ld(max_ctx);
   const size_t s_scores = align_up((size_t)T * ld * sizeof(float), 256);
-  const size_t s_rep = align_up(dsa::topk_report_bytes(T, max_ctx), 256);
+  const size_t s_rep = align_up(dsa::topk_report_bytes(T, max_ctx, K), 256);
   const size_t s_idx = align_up((size_t)T * K * sizeof(int32_t), 256);
   const dsa::AttnPlan plan = dsa::attn_plan(T, K, 0, Hq, D);
   const size_t s_attn = align_up(plan.ws_bytes, 256);
   if (out) {
     out->ld = ld;
     out->scores = reinterpret_cast<float*>(base);
-    out->topk = dsa::topk_ws_carve(base + s_scores, T, max_ctx);
+    out->topk = dsa::topk_ws_carve(base + s_scores, T, max_ctx, K);
     out->idx = reinterpret_cast<int32_t*>(base + s_scores + s_rep);
     out->attn = base + s_scores + s_rep + s_idx;
   }
@@ -164,9 +164,8 @@ dsa_status_t dsa_index_scores(const void* q_idx, const void* w, int64_t w_ld, co
 
 size_t dsa_topk_workspace_size(int B, int T, int max_ctx, int K) {
   (void)B;
-  (void)K;
-  if (T < 1 || max_ctx < 1) return 0;
-  return dsa::topk_report_bytes(T, max_ctx);
+  if (T < 1 || max_ctx < 1 || K < 1) return 0;
+  return dsa::topk_report_bytes(T, max_ctx, K);
 }
 
 dsa_status_t dsa_topk(const float* scores, int64_t ld, const int32_t* cu_q,
@@ -184,7 +183,7 @@ dsa_status_t dsa_topk(const float* scores, int64_t ld, const int32_t* cu_q,
               ws_bytes, need);
   DSA_PTR(ws, "ws");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  dsa::TopkWs w = dsa::topk_ws_carve(ws, T, max_ctx);
+  dsa::TopkWs w = dsa::topk_ws_carve(ws, T, max_ctx, K);
   hipError_t e = dsa::launch_tile_reports(scores, ld, cu_q, ctx_len, B, T, max_ctx, w, s);
   if (e == hipSuccess) e = dsa::launch_topk_resolve(scores, ld, cu_q, ctx_len, B, T, K, w, idx,
                                                     nullptr, s);

@@ -66,11 +66,17 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
   const int head = 32 * hb + (l & 31);
   const bool head_ok = head < Hq;
   bf16x8 qb[KS];
+  {
+    // clamped address instead of a branch: every load is in flight at once
+    const int hc = min(head, Hq - 1);
+    u32x4 qv[KS];
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (head_ok) v = ld16(q + ((int64_t)t * Hq + head) * D + 16 * s + 8 * g);
-    qb[s] = as_bf16x8(v);
+    for (int s = 0; s < KS; ++s) qv[s] = ld16(q + ((int64_t)t * Hq + hc) * D + 16 * s + 8 * g);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      if (!head_ok) qv[s] = u32x4{0u, 0u, 0u, 0u};
+      qb[s] = as_bf16x8(qv[s]);
+    }
   }
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 o[DB];
@@ -95,7 +101,7 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
     for (int s = 0; s < KS; ++s) vf[s] = ld16(vc + row * D + 16 * s + 8 * g);
     const uint32_t vmask = (uint32_t)__ballot(valid);
     // V^T into this wave's LDS tile: element (d, r) at myvt[d*VTS + r]
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
 #pragma unroll
@@ -136,7 +142,7 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int e = 0; e < 8; ++e) pb[s2][e] = static_cast<__bf16>(sv[8 * s2 + e]);
-    __syncthreads();
+    lds_barrier();
     // O^T += V^T . P^T
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -151,7 +157,7 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
     }
   }
   // ---- merge the RB row-block waves of each head block ----
-  __syncthreads();
+  lds_barrier();
   if (rb > 0) {
     float* my = mo + ((rb - 1) * HB + hb) * 32 * (D + 2);
     const int hl = l & 31;
@@ -167,7 +173,7 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
       my[hl * (D + 2) + D + 1] = l_run;
     }
   }
-  __syncthreads();
+  lds_barrier();
   if (rb != 0) return;
   const int hl = l & 31;
   float M = m_run;
@@ -230,30 +236,53 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
   }
 }
 
-// Merge split partials: grid (T, Hq), D threads.
+// Merge split partials: grid (T, Hq), D threads.  All loads of a block are
+// independent: first every split's (m, l), then every split's O[d].
+constexpr int kMaxSplit = 64;
+
 template <int D>
 __global__ __launch_bounds__(D) void attn_combine_kernel(const float* __restrict__ part, int nsplit,
                                                          int Hq, const uint16_t* __restrict__ gate,
                                                          uint16_t* __restrict__ out,
                                                          float* __restrict__ lse) {
+  __shared__ float sm_m[kMaxSplit], sm_l[kMaxSplit], sm_w[kMaxSplit];
+  __shared__ float sm_ML[2];
   const int t = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
   const float* pp = part + ((int64_t)t * nsplit * Hq + h) * (D + 2);
   const int64_t stride = (int64_t)Hq * (D + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pp[s * stride + D]);
-  float L = 0.f, acc = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < nsplit; ++s) {
-      const float a = exp2f(pp[s * stride + D] - M);
-      L += a * pp[s * stride + D + 1];
-      acc += a * pp[s * stride + d];
+  for (int s = d; s < nsplit; s += D) {
+    sm_m[s] = pp[s * stride + D];
+    sm_l[s] = pp[s * stride + D + 1];
+  }
+  float g = 0.f;
+  const int64_t off = ((int64_t)t * Hq + h) * D + d;
+  if (gate) g = bf16_to_f32(gate[off]);
+  lds_barrier();
+  if (d < 64) {
+    float M = -INFINITY;
+    for (int s = d; s < nsplit; s += 64) M = fmaxf(M, sm_m[s]);
+    M = wave_max_f32(M);
+    float L = 0.f;
+    for (int s = d; s < nsplit; s += 64) {
+      const float a = (M == -INFINITY) ? 0.f : exp2f(sm_m[s] - M);
+      sm_w[s] = a;
+      L += a * sm_l[s];
+    }
+    L = wave_sum_f32(L);
+    if (d == 0) {
+      sm_ML[0] = M;
+      sm_ML[1] = L;
     }
   }
+  lds_barrier();
+  const float L = sm_ML[1];
+  float acc = 0.f;
+#pragma unroll 8
+  for (int s = 0; s < nsplit; ++s) acc += sm_w[s] * pp[s * stride + d];
   float v = L > 0.f ? acc / L : 0.f;
-  const int64_t off = ((int64_t)t * Hq + h) * D + d;
-  if (gate) v *= sigmoidf(bf16_to_f32(gate[off]));
+  if (gate) v *= sigmoidf(g);
   out[off] = f32_to_bf16(v);
-  if (lse && d == 0) lse[(int64_t)t * Hq + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+  if (lse && d == 0) lse[(int64_t)t * Hq + h] = L > 0.f ? (sm_ML[0] + log2f(L)) * kLn2 : -INFINITY;
 }
 
 AttnPlan attn_plan(int T, int K, int window, int Hq, int D) {
@@ -264,6 +293,7 @@ AttnPlan attn_plan(int T, int K, int window, int Hq, int D) {
   // a step per workgroup when few queries, otherwise whole rows
   int rows = step;
   if ((int64_t)T * ((nlist + step - 1) / step) > 2048) rows = nlist > 0 ? nlist : step;
+  while ((nlist + rows - 1) / rows > kMaxSplit) rows *= 2;
   p.rows_per_split = rows;
   p.nsplit = (nlist + rows - 1) / rows;
   if (p.nsplit < 1) p.nsplit = 1;

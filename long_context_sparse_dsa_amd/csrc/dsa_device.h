@@ -63,49 +63,134 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
 }
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Direct global->LDS loads (global_load_lds_dword{,x4}): lane l's bytes land
+// at lds + size * l, where `lds` must be the same for the whole wave.  The
+// load counts in vmcnt until its data is in LDS.  (Kept in plain functions:
+// the builtin used directly inside a kernel template stops the host pass
+// from emitting that kernel's launch stub.)
+__device__ __forceinline__ void lds_dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 4, 0, 0);
+}
 __device__ __forceinline__ u32x4 ld16_nt(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
-// Sum / max across the two 32-lane halves of a wave.
-__device__ __forceinline__ float xor32_add(float v) { return v + __shfl_xor(v, 32); }
-__device__ __forceinline__ float xor32_max(float v) { return fmaxf(v, __shfl_xor(v, 32)); }
-
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  const int l = lane_id();
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t t = __shfl_up(v, o);
-    if (l >= o) v += t;
-  }
+// ---------------------------------------------------------------------------
+// Cross-lane primitives.  A dependent ds_bpermute (__shfl_*) costs about 136
+// cycles on gfx950 and a ballot + popcount step about 72; DPP row moves and
+// v_permlane32_swap are VALU operations of a few cycles, so the wave-wide
+// scans and reductions below are built from them.
+// ---------------------------------------------------------------------------
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114,
+              kDppRowShr8 = 0x118, kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+template <int CTRL, int ROW_MASK, int BANK_MASK>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t src) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)src, CTRL, ROW_MASK, BANK_MASK,
+                                               false);
+}
+
+// The value of lane l^32 (the other half of the wave).
+__device__ __forceinline__ uint32_t xor32_u32(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return (lane_id() < 32) ? (uint32_t)r[1] : (uint32_t)r[0];
+}
+// Sum / max across the two 32-lane halves of a wave (same result in both).
+__device__ __forceinline__ float xor32_add(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float((uint32_t)r[0]) + __uint_as_float((uint32_t)r[1]);
+}
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float((uint32_t)r[0]), __uint_as_float((uint32_t)r[1]));
+}
+
+// Inclusive wave scan with an associative operator op and identity id:
+// row shifts 1, 2, 4, 8 build 16-lane row scans, two row broadcasts join
+// the rows.
+template <typename Op>
+__device__ __forceinline__ uint32_t dpp_wave_scan(uint32_t v, uint32_t id, Op op) {
+  v = op(v, dpp_u32<kDppRowShr1, 0xf, 0xf>(id, v));
+  v = op(v, dpp_u32<kDppRowShr2, 0xf, 0xf>(id, v));
+  v = op(v, dpp_u32<kDppRowShr4, 0xf, 0xf>(id, v));
+  v = op(v, dpp_u32<kDppRowShr8, 0xf, 0xf>(id, v));
+  v = op(v, dpp_u32<kDppRowBcast15, 0xa, 0xf>(id, v));
+  v = op(v, dpp_u32<kDppRowBcast31, 0xc, 0xf>(id, v));
   return v;
+}
+
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  return dpp_wave_scan(v, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(v), 63);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  const uint32_t s = dpp_wave_scan(v, 0u, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+  return (uint32_t)__builtin_amdgcn_readlane((int)s, 63);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  const uint32_t s =
+      dpp_wave_scan(v, 0xffffffffu, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+  return (uint32_t)__builtin_amdgcn_readlane((int)s, 63);
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  const uint32_t s = dpp_wave_scan(__float_as_uint(v), 0u, [](uint32_t a, uint32_t b) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  });
+  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)s, 63));
+}
+__device__ __forceinline__ int32_t wave_max_i32(int32_t v) {
+  // order-preserving bias so the unsigned maximum is the signed one
+  return (int32_t)(wave_max_u32((uint32_t)v ^ 0x80000000u) ^ 0x80000000u);
+}
+__device__ __forceinline__ float wave_max_f32(float v) {
+  // monotone map of fp32 onto uint32 (no NaN in use)
+  uint32_t x = __float_as_uint(v);
+  x = (x & 0x80000000u) ? ~x : (x | 0x80000000u);
+  x = wave_max_u32(x);
+  x = (x & 0x80000000u) ? (x & 0x7fffffffu) : ~x;
+  return __uint_as_float(x);
+}
+
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also
+// waits for every outstanding global load and store of the wave (vmcnt(0));
+// none of the barriers in these kernels protects global memory, so they use
+// this one and keep global traffic in flight across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Exclusive block-wide prefix sum of one value per thread.  `scratch` holds
 // at least blockDim.x/64 + 1 uint32.  Returns the exclusive prefix; *total
-// receives the block total.  Contains barriers: call from every thread.
+// receives the block total.  The cross-wave step runs in wave 0's registers
+// (no serial chain through LDS).  Contains barriers: call from every thread.
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* scratch, uint32_t* total) {
-  const int w = wave_id(), nw = blockDim.x >> 6;
-  uint32_t inc = wave_incl_scan(v);
-  if (lane_id() == 63) scratch[w] = inc;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t acc = 0;
-    for (int i = 0; i < nw; ++i) {
-      uint32_t t = scratch[i];
-      scratch[i] = acc;
-      acc += t;
-    }
-    scratch[nw] = acc;
+  const int w = wave_id(), nw = blockDim.x >> 6, l = lane_id();
+  const uint32_t inc = wave_incl_scan(v);
+  if (l == 63) scratch[w] = inc;
+  lds_barrier();
+  if (w == 0) {
+    const uint32_t x = l < nw ? scratch[l] : 0u;
+    const uint32_t xs = wave_incl_scan(x);
+    if (l < nw) scratch[l] = xs - x;
+    if (l == 63) scratch[nw] = xs;
   }
-  __syncthreads();
-  uint32_t r = scratch[w] + inc - v;
+  lds_barrier();
+  const uint32_t r = scratch[w] + inc - v;
   *total = scratch[nw];
-  __syncthreads();
+  lds_barrier();
   return r;
 }
 

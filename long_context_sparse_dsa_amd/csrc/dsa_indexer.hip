@@ -41,91 +41,232 @@ __device__ __forceinline__ int kslot_dim(int s, int g) {
 // ---------------------------------------------------------------------------
 // Decode
 // ---------------------------------------------------------------------------
+// One wave per tile of TILE keys.  The key rows are streamed through LDS
+// with global_load_lds_dwordx4: every load instruction reads 1 KiB of
+// consecutive rows (fully coalesced) and lands it in LDS, where a per-KiB pad
+// and a (row, chunk) lane permutation make the MFMA-operand reads free of
+// bank conflicts.  The tile is cut into stages of at most 16 KiB, three of
+// them in flight (a wave keeps under 64 loads outstanding, the limit of its
+// load counter): while stage s is consumed, stages s+1 and s+2 are loading.  Each
+// 32-key block is consumed as soon as its own loads have landed (vmcnt counts
+// completions in issue order).  Scores stay in registers until the end, and
+// with REPORT the wave writes the tile's Top-K candidate prefix
+// (dsa_topk_tile.h) without any cross-wave step.
+template <int ROWB, int TILE, bool FP8>
+struct KeyStage {
+  static constexpr int kTileBytes = TILE * ROWB;
+  // bytes per stage: at most 16 KiB, and (fp8) at most 128 keys, whose
+  // scales take two more load instructions
+  static constexpr int kCap = FP8 && 128 * ROWB < 16384 ? 128 * ROWB : 16384;
+  static constexpr int kBytes = kTileBytes < kCap ? kTileBytes : kCap;
+  static constexpr int kNum = kTileBytes / kBytes;       // stages per tile
+  static constexpr int kBufs = kNum < 3 ? kNum : 3;      // LDS stage buffers, all in flight
+  static constexpr int kRows = kBytes / ROWB;            // keys per stage
+  static constexpr int kRowsPerKiB = 1024 / ROWB;        // rows per load instruction
+  static constexpr int kPad = kRowsPerKiB >= 16 ? 0 : 256 / kRowsPerKiB;  // bytes per KiB
+  static constexpr int kStride = 1024 + kPad;            // LDS bytes per KiB of keys
+  static constexpr int kKeyBytes = (kBytes / 1024) * kStride;
+  static constexpr int kScaleLoads = FP8 ? kRows / 64 : 0;  // 4-byte scale loads per stage
+  static constexpr int kBufBytes = kKeyBytes + (FP8 ? 4 * kRows : 0);
+  static constexpr int kKeyLoads = kBytes / 1024;        // key load instructions per stage
+  static constexpr int kLoads = kKeyLoads + kScaleLoads; // load instructions per stage
+  // LDS byte offset of 16-byte chunk `ck` of stage row r
+  __device__ static int offset(int r, int ck) {
+    return (r / kRowsPerKiB) * kStride + (ck * kRowsPerKiB + r % kRowsPerKiB) * 16;
+  }
+};
+
+// s_waitcnt vmcnt(n) for an n that is a constant after unrolling (the
+// builtin needs an immediate; the switch folds away).
+// gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[15:14].
+#define DSA_WAITV(N) \
+  case N: __builtin_amdgcn_s_waitcnt(((N) & 15) | (7 << 4) | (15 << 8) | (((N) >> 4) << 14)); break;
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {
+    DSA_WAITV(0) DSA_WAITV(1) DSA_WAITV(2) DSA_WAITV(3) DSA_WAITV(4) DSA_WAITV(5) DSA_WAITV(6)
+    DSA_WAITV(7) DSA_WAITV(8) DSA_WAITV(9) DSA_WAITV(10) DSA_WAITV(11) DSA_WAITV(12)
+    DSA_WAITV(13) DSA_WAITV(14) DSA_WAITV(15) DSA_WAITV(16) DSA_WAITV(17) DSA_WAITV(18)
+    DSA_WAITV(19) DSA_WAITV(20) DSA_WAITV(21) DSA_WAITV(22) DSA_WAITV(23) DSA_WAITV(24)
+    DSA_WAITV(25) DSA_WAITV(26) DSA_WAITV(27) DSA_WAITV(28) DSA_WAITV(29) DSA_WAITV(30)
+    DSA_WAITV(31) DSA_WAITV(32) DSA_WAITV(33) DSA_WAITV(34) DSA_WAITV(35) DSA_WAITV(36)
+    DSA_WAITV(37) DSA_WAITV(38) DSA_WAITV(39) DSA_WAITV(40) DSA_WAITV(41) DSA_WAITV(42)
+    DSA_WAITV(43) DSA_WAITV(44) DSA_WAITV(45) DSA_WAITV(46) DSA_WAITV(47) DSA_WAITV(48)
+    DSA_WAITV(49) DSA_WAITV(50) DSA_WAITV(51) DSA_WAITV(52) DSA_WAITV(53) DSA_WAITV(54)
+    DSA_WAITV(55) DSA_WAITV(56) DSA_WAITV(57) DSA_WAITV(58) DSA_WAITV(59) DSA_WAITV(60)
+    DSA_WAITV(61) DSA_WAITV(62) DSA_WAITV(63)
+    default: __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); break;
+  }
+}
+#undef DSA_WAITV
+
 template <int DI, bool FP8, int TILE, bool REPORT>
-__global__ __launch_bounds__(256) void index_decode_kernel(
+__global__ __launch_bounds__(64) void index_decode_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ w, int64_t w_ld,
     const uint8_t* __restrict__ k_idx, const float* __restrict__ k_scale, int H_I,
     const int32_t* __restrict__ ctx_len, const int64_t* __restrict__ cu_ctx,
     float* __restrict__ scores, int64_t ld, RepHeader* hdr, uint32_t* rep_u, int32_t* rep_j,
     int ntiles_max) {
-  constexpr int KS = DI / 16;            // MFMA k-steps
-  constexpr int ROWB = FP8 ? DI : 2 * DI; // bytes per key row
-  constexpr int KPW = TILE / 4;          // keys per wave
-  constexpr int NB = KPW / 32;           // 32-key blocks per wave
-  constexpr int NLD = FP8 ? KS / 2 : KS; // 16-byte loads per lane per block
-  constexpr int PF = NB < 4 ? NB : 4;    // blocks loaded ahead together
+  constexpr int KS = DI / 16;                       // MFMA k-steps
+  constexpr int ROWB = FP8 ? DI : 2 * DI;           // bytes per key row
+  using St = KeyStage<ROWB, TILE, FP8>;
+  constexpr int NSTAGE = St::kNum;
+  constexpr int SROWS = St::kRows;
+  constexpr int SBLK = SROWS / 32;                  // 32-key blocks per stage
+  constexpr int NI = St::kKeyLoads;                 // key load instructions per stage
+  constexpr int NL = St::kLoads;                    // all load instructions per stage
+  constexpr int IPB = NI / SBLK;                    // key load instructions per block
+  constexpr int NLD = FP8 ? KS / 2 : KS;            // 16-byte operand chunks per lane per block
+  constexpr int V = TILE / 64;                      // report values per lane
+  static_assert(KS + 1 + St::kBufs * NL <= 63 && NI % SBLK == 0 && TILE % SROWS == 0,
+                "stage shape");
 
-  __shared__ uint32_t su[TILE];
-  __shared__ TileReportSmem sm;
+  // one LDS object: [query rows | head weights | stage buffers] (with
+  // several objects the compiler adds a wait for every load in flight
+  // before reading any of them)
+  __shared__ __attribute__((aligned(16))) uint8_t lds[1024 * KS + 256 + St::kBufs * St::kBufBytes];
+  uint8_t* const qw_lds = lds;
+  uint8_t* const stage = lds + 1024 * KS + 256;
 
   const int b = blockIdx.y, ti = blockIdx.x;
+  // both descriptor loads issued together (one round trip)
+  const int64_t row0 = cu_ctx[b];
   const int64_t p = (int64_t)ctx_len[b] - 1;
   const int64_t j0 = (int64_t)ti * TILE;
-  if (j0 > p) return;
+  // (testing row0 here keeps its load ahead of the branch, in the same round trip)
+  if (j0 > p || row0 < 0) return;
   const int n_valid = (int)min<int64_t>(TILE, p + 1 - j0);
-  const int l = lane_id(), g = l >> 5, wv = wave_id();
-  const int64_t row0 = cu_ctx[b];
+  const int l = lane_id(), g = l >> 5;
 
-  // A operand: query heads (rows), zero beyond H_I.
-  bf16x8 qa[KS];
+  // A operand: query heads (rows).  Rows past H_I repeat the last head and
+  // get head weight 0, so they add nothing.  The query rows and the head
+  // weights go through LDS too, issued ahead of the key stream: the first
+  // key block's wait then covers them, and every load in flight is of one
+  // kind, which lets the compiler count them in order.
+  //   q: instruction s (k-step), lane l -> head l % 32, dims kslot_dim(s, l / 32)
+  //   w: lane l -> the aligned dword holding head min(l, H_I - 1)
   {
-    const int head = l & 31;
+    const int hc = min(l & 31, H_I - 1);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (head < H_I) v = ld16(q_idx + ((int64_t)b * H_I + head) * DI + kslot_dim<FP8>(s, g));
-      qa[s] = as_bf16x8(v);
-    }
+    for (int s = 0; s < KS; ++s)
+      lds_dma16(q_idx + ((int64_t)b * H_I + hc) * DI + kslot_dim<FP8>(s, g),
+                                       qw_lds + 1024 * s);
+    const int64_t we = (int64_t)b * w_ld + min(l, H_I - 1);
+    lds_dma4(w + (we & ~(int64_t)1), qw_lds + 1024 * KS);
   }
-  // Head weights of the 16 accumulator rows this lane holds.
+  bf16x8 qa[KS];
   float wr[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int head = 8 * (r >> 2) + 4 * g + (r & 3);
-    wr[r] = head < H_I ? bf16_to_f32(w[(int64_t)b * w_ld + head]) : 0.f;
-  }
 
-#pragma unroll 1
-  for (int blk0 = 0; blk0 < NB; blk0 += PF) {
-    u32x4 kv[PF][NLD];
-    float sig[PF];
-    int jr[PF];
+  // lane permutation of a load instruction: row l % kRowsPerKiB, chunk l / kRowsPerKiB
+  const int lrow = l % St::kRowsPerKiB, lchunk = l / St::kRowsPerKiB;
+  // issue the loads of stage st into its buffer (fp8: the key scales first,
+  // then the rows); rows are clamped to the last visible position, so
+  // nothing past the context is ever read
+  auto issue = [&](int st) {
+    uint8_t* buf = stage + (st % St::kBufs) * St::kBufBytes;
+    if constexpr (FP8) {
 #pragma unroll
-    for (int u = 0; u < PF; ++u) {
-      jr[u] = wv * KPW + (blk0 + u) * 32 + (l & 31);
-      const int64_t jl = min<int64_t>(j0 + jr[u], p);  // clamp: never read past the context
-      const uint8_t* rowp = k_idx + (row0 + jl) * ROWB;
-#pragma unroll
-      for (int c = 0; c < NLD; ++c) kv[u][c] = ld16(rowp + 32 * c + 16 * g);
-      sig[u] = FP8 ? k_scale[row0 + jl] : 1.f;
+      for (int c = 0; c < St::kScaleLoads; ++c) {
+        const int64_t jl = min<int64_t>(j0 + st * SROWS + 64 * c + l, p);
+        lds_dma4(k_scale + row0 + jl, buf + St::kKeyBytes + 256 * c);
+      }
     }
 #pragma unroll
-    for (int u = 0; u < PF; ++u) {
+    for (int c = 0; c < NI; ++c) {
+      const int r = st * SROWS + c * St::kRowsPerKiB + lrow;  // tile row
+      const int64_t jl = min<int64_t>(j0 + r, p);
+      lds_dma16(k_idx + (row0 + jl) * ROWB + 16 * lchunk,
+                                       buf + c * St::kStride);
+    }
+  };
+  // Every stage of the tile is loaded and scored, also past the last valid
+  // key (those rows repeat it and their scores are dropped), so that the
+  // pipeline and its load counts are the same for every tile.
+#pragma unroll
+  for (int st = 0; st < St::kBufs; ++st) issue(st);
+
+  float sc_keep[NSTAGE][SBLK];
+#pragma unroll
+  for (int st = 0; st < NSTAGE; ++st) {
+    const uint8_t* buf = stage + (st % St::kBufs) * St::kBufBytes;
+    // stages issued after this one and still in flight
+    const int later = min(St::kBufs - 1, NSTAGE - 1 - st);
+#pragma unroll
+    for (int bl = 0; bl < SBLK; ++bl) {
+      // the scales and blocks 0..bl of this stage have landed once at most
+      // this many loads are outstanding
+      const int allow = NI - IPB * (bl + 1);
+      wait_vmcnt(allow + later * NL);
+      // keep the scheduler from hoisting consumers of loaded registers above
+      // the wait (the compiler would then wait for every load instead)
+      __builtin_amdgcn_sched_barrier(0);
+      if (st == 0 && bl == 0) {
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          qa[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qw_lds + 1024 * s + 16 * l));
+        const uint32_t* wl = reinterpret_cast<const uint32_t*>(qw_lds + 1024 * KS);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int hr = 8 * (r >> 2) + 4 * g + (r & 3);
+          const int64_t we = (int64_t)b * w_ld + min(hr, H_I - 1);
+          const uint32_t v = wl[min(hr, H_I - 1)] >> (16 * (int)(we & 1));
+          wr[r] = hr < H_I ? bf16_to_f32((uint16_t)v) : 0.f;
+        }
+      }
+      const int R = 32 * bl + (l & 31);  // stage row of this lane's key
+      u32x4 kv[NLD];
+#pragma unroll
+      for (int c = 0; c < NLD; ++c)
+        kv[c] = *reinterpret_cast<const u32x4*>(buf + St::offset(R, 2 * c + g));
+      const float sig = FP8 ? *reinterpret_cast<const float*>(buf + St::kKeyBytes + 4 * R) : 1.f;
       f32x16 acc = {};
       if constexpr (FP8) {
 #pragma unroll
         for (int c = 0; c < NLD; ++c) {
-          acc = mfma32(qa[2 * c], fp8x8_to_bf16x8(kv[u][c][0], kv[u][c][1]), acc);
-          acc = mfma32(qa[2 * c + 1], fp8x8_to_bf16x8(kv[u][c][2], kv[u][c][3]), acc);
+          acc = mfma32(qa[2 * c], fp8x8_to_bf16x8(kv[c][0], kv[c][1]), acc);
+          acc = mfma32(qa[2 * c + 1], fp8x8_to_bf16x8(kv[c][2], kv[c][3]), acc);
         }
       } else {
 #pragma unroll
-        for (int c = 0; c < NLD; ++c) acc = mfma32(qa[c], as_bf16x8(kv[u][c]), acc);
+        for (int c = 0; c < NLD; ++c) acc = mfma32(qa[c], as_bf16x8(kv[c]), acc);
       }
       float sl = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sl += wr[r] * fmaxf(sig[u] * acc[r], 0.f);
-      const float sc = xor32_add(sl);
-      if (g == 0 && jr[u] < n_valid) {
-        scores[(int64_t)b * ld + j0 + jr[u]] = sc;
-        su[jr[u]] = order_key(sc);
-      }
+      for (int r = 0; r < 16; ++r) sl += wr[r] * fmaxf(sig * acc[r], 0.f);
+      sc_keep[st][bl] = xor32_add(sl);
+    }
+    if (st + St::kBufs < NSTAGE) {
+      // every operand read of this buffer has returned (the MFMAs consumed
+      // them); refill it with stage st + kBufs
+      __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+      issue(st + St::kBufs);
     }
   }
-  if constexpr (!REPORT) return;
-  __syncthreads();
-  const int64_t slot = (int64_t)b * ntiles_max + ti;
-  tile_report(su, n_valid, j0, sm, hdr + slot, rep_u + slot * kRepMax, rep_j + slot * kRepMax);
+  // scores of 32-key block k (tile order) live in sc_keep, lanes 0..31 (and 32..63)
+#pragma unroll
+  for (int st = 0; st < NSTAGE; ++st)
+#pragma unroll
+    for (int bl = 0; bl < SBLK; ++bl) {
+      const int jr = st * SROWS + 32 * bl + (l & 31);
+      if (g == 0 && jr < n_valid) scores[(int64_t)b * ld + j0 + jr] = sc_keep[st][bl];
+    }
+  if constexpr (REPORT) {
+    // report value i of lane l is tile element 64i + l: block 2i (lanes < 32)
+    // or block 2i+1 (lanes >= 32), both already in this lane's registers
+    uint32_t uv[V];
+    int32_t jv[V];
+    bool vv[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const int k0 = 2 * i, k1 = 2 * i + 1;
+      const float s0 = sc_keep[k0 / SBLK][k0 % SBLK], s1 = sc_keep[k1 / SBLK][k1 % SBLK];
+      const int jl = 64 * i + l;
+      vv[i] = jl < n_valid;
+      uv[i] = order_key(g == 0 ? s0 : s1);
+      jv[i] = (int32_t)(j0 + jl);
+    }
+    const int64_t slot = (int64_t)b * ntiles_max + ti;
+    wave_tile_report<V>(uv, jv, vv, hdr + slot, rep_u + slot * kRep, rep_j + slot * kRep);
+  }
 }
 
 template <int DI, bool FP8, bool REPORT>
@@ -138,11 +279,13 @@ static hipError_t launch_decode_tiled(int tile, const uint16_t* q, const uint16_
   dim3 grid((max_ctx + tile - 1) / tile, B);
 #define DSA_DECODE_TILE(T_)                                                                    \
   case T_:                                                                                     \
-    hipLaunchKernelGGL((index_decode_kernel<DI, FP8, T_, REPORT>), grid, dim3(256), 0, st, q,  \
+    hipLaunchKernelGGL((index_decode_kernel<DI, FP8, T_, REPORT>), grid, dim3(64), 0, st, q,   \
                        w, w_ld, k, ks, H_I, ctx_len, cu_ctx, scores, ld, hdr, ru, rj,          \
                        ntiles_max);                                                            \
     break;
   switch (tile) {
+    DSA_DECODE_TILE(64)
+    DSA_DECODE_TILE(128)
     DSA_DECODE_TILE(256)
     DSA_DECODE_TILE(512)
     DSA_DECODE_TILE(1024)
@@ -173,7 +316,7 @@ hipError_t launch_index_decode(const void* q_idx, const void* w, int64_t w_ld, c
                                const int32_t* ctx_len, const int64_t* cu_ctx, int B, int max_ctx,
                                float* scores, int64_t ld, const TopkWs* reports,
                                hipStream_t stream) {
-  const int tile = reports ? reports->tile : topk_tile_for(max_ctx);
+  const int tile = reports ? reports->tile : 256;
   RepHeader* hdr = reports ? reports->hdr : nullptr;
   uint32_t* ru = reports ? reports->rep_u : nullptr;
   int32_t* rj = reports ? reports->rep_j : nullptr;
@@ -276,7 +419,7 @@ __global__ __launch_bounds__(256) void index_prefill_kernel(
   for (int64_t st = st_lo; st < st_hi; ++st) {
     const int64_t k0 = st * KT;
     // ---- stage key tile into LDS ----
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int c = 0; c < LDPT; ++c) {
       const int e = threadIdx.x + 256 * c;
@@ -286,7 +429,7 @@ __global__ __launch_bounds__(256) void index_prefill_kernel(
       *reinterpret_cast<u32x4*>(kt_lds + kr * LROW + 16 * kc) = v;
     }
     if (FP8 && threadIdx.x < KT) sig_lds[threadIdx.x] = k_scale[row0 + min<int64_t>(k0 + threadIdx.x, L - 1)];
-    __syncthreads();
+    lds_barrier();
     // ---- MFMA ----
     f32x16 acc[MB][NBK];
 #pragma unroll

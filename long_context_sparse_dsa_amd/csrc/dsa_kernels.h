@@ -21,9 +21,9 @@ struct TopkWs {
   int32_t* rep_j;
 };
 
-int topk_tile_for(int max_ctx);
-size_t topk_report_bytes(int T, int max_ctx);
-TopkWs topk_ws_carve(void* ws, int T, int max_ctx);
+int topk_tile_for(int max_ctx, int K);
+size_t topk_report_bytes(int T, int max_ctx, int K);
+TopkWs topk_ws_carve(void* ws, int T, int max_ctx, int K);
 
 hipError_t launch_tile_reports(const float* scores, int64_t ld, const int32_t* cu_q,
                                const int32_t* ctx_len, int B, int T, int max_ctx,

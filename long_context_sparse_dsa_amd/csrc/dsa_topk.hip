@@ -25,59 +25,78 @@
 namespace dsa {
 
 constexpr int kResolveThreads = 1024;
-constexpr int kResolveCap = 16384;  // candidates held in LDS
+constexpr int kResolveTiles = 1024;                         // tiles in the fast path
+constexpr int kSlots = kResolveTiles * kRep / kResolveThreads;  // report slots per thread (16)
+constexpr int kBruteMax = 64;   // boundary-bin elements ranked in wave 0's registers
 
-__global__ __launch_bounds__(256) void tile_report_kernel(const float* __restrict__ scores,
-                                                          int64_t ld, const int32_t* cu_q,
-                                                          const int32_t* ctx_len, int B, int tile,
-                                                          int ntiles_max, RepHeader* hdr,
-                                                          uint32_t* rep_u, int32_t* rep_j) {
-  __shared__ uint32_t su[kMaxTile];
-  __shared__ TileReportSmem sm;
+template <int TILE>
+__global__ __launch_bounds__(64) void tile_report_kernel(const float* __restrict__ scores,
+                                                         int64_t ld, const int32_t* cu_q,
+                                                         const int32_t* ctx_len, int B,
+                                                         int ntiles_max, RepHeader* hdr,
+                                                         uint32_t* rep_u, int32_t* rep_j) {
+  constexpr int V = TILE / 64;
   const int t = blockIdx.y, ti = blockIdx.x;
   const RowInfo ri = row_info(t, cu_q, ctx_len, B);
-  const int64_t j0 = (int64_t)ti * tile;
+  const int64_t j0 = (int64_t)ti * TILE;
   if (j0 > ri.p) return;
-  const int n = (int)min<int64_t>(tile, ri.p + 1 - j0);
+  const int n = (int)min<int64_t>(TILE, ri.p + 1 - j0);
   const float* row = scores + (int64_t)t * ld + j0;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) su[i] = order_key(row[i]);
-  __syncthreads();
+  const int l = lane_id();
+  uint32_t uv[V];
+  int32_t jv[V];
+  bool vv[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const int jl = 64 * i + l;
+    vv[i] = jl < n;
+    uv[i] = order_key(row[vv[i] ? jl : 0]);
+    jv[i] = (int32_t)(j0 + jl);
+  }
   const int64_t slot = (int64_t)t * ntiles_max + ti;
-  tile_report(su, n, j0, sm, hdr + slot, rep_u + slot * kRepMax, rep_j + slot * kRepMax);
+  wave_tile_report<V>(uv, jv, vv, hdr + slot, rep_u + slot * kRep, rep_j + slot * kRep);
 }
 
 // ---------------------------------------------------------------------------
 // Radix select helpers for the resolve kernel (1024 threads, 2048 bins).
 // ---------------------------------------------------------------------------
 struct ResolveSmem {
-  uint32_t cu[kResolveCap];
-  int32_t cj[kResolveCap];
+  int32_t stage[4096];  // selected positions before the coalesced store (K <= 4096)
   uint32_t hist[2048];
-  uint32_t toff[1025];
+  uint32_t bu[kBruteMax];
+  int32_t bj[kBruteMax];
+  uint32_t red[64];
   uint32_t scan[20];
   uint32_t st[8];
 };
 
 // Given hist[2048] of the current bucket and `above` elements strictly above
 // it, find digit d with above+gt(d) < k <= above+gt(d)+hist[d].  Writes
-// st[0] = d, st[1] = above + gt(d).  Every thread calls it.
+// st[0] = d, st[1] = above + gt(d).  Every thread calls it; ends with a
+// barrier.  Thread tid owns the 2048/blockDim.x consecutive digits from
+// tid*(2048/blockDim.x).
 __device__ void find_digit(ResolveSmem& sm, uint32_t above, uint32_t k) {
+  constexpr int PER = 2048 / kResolveThreads;
   const int tid = threadIdx.x;
-  // thread tid owns digits 2*tid, 2*tid+1
-  uint32_t h0 = sm.hist[2 * tid], h1 = sm.hist[2 * tid + 1];
+  uint32_t hv[PER];
+  uint32_t mine = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    hv[i] = sm.hist[PER * tid + i];
+    mine += hv[i];
+  }
   uint32_t tot;
-  uint32_t excl = block_excl_scan(h0 + h1, sm.scan, &tot);
-  uint32_t gt1 = tot - excl - h0 - h1;  // above digit 2*tid+1
-  uint32_t gt0 = gt1 + h1;              // above digit 2*tid
-  if (above + gt1 < k && above + gt1 + h1 >= k) {
-    sm.st[0] = 2 * tid + 1;
-    sm.st[1] = above + gt1;
+  const uint32_t excl = block_excl_scan(mine, sm.scan, &tot);
+  uint32_t gt = tot - excl - mine;  // above this thread's last digit
+#pragma unroll
+  for (int i = PER - 1; i >= 0; --i) {
+    if (above + gt < k && above + gt + hv[i] >= k) {
+      sm.st[0] = PER * tid + i;
+      sm.st[1] = above + gt;
+    }
+    gt += hv[i];
   }
-  if (above + gt0 < k && above + gt0 + h0 >= k) {
-    sm.st[0] = 2 * tid;
-    sm.st[1] = above + gt0;
-  }
-  __syncthreads();
+  lds_barrier();
 }
 
 // Exact threshold (tau_u, tau_j) over an array source; `get(i, &u, &j)`
@@ -91,7 +110,7 @@ __device__ void exact_threshold(ResolveSmem& sm, int64_t n, uint32_t k, Get get)
   for (int pass = 0; pass < 3; ++pass) {
     const int sh = shifts[pass];
     for (int i = tid; i < 2048; i += nt) sm.hist[i] = 0;
-    __syncthreads();
+    lds_barrier();
     for (int64_t i = tid; i < n; i += nt) {
       uint32_t u;
       int32_t j;
@@ -99,12 +118,12 @@ __device__ void exact_threshold(ResolveSmem& sm, int64_t n, uint32_t k, Get get)
       bool in = pass == 0 ? true : (pass == 1 ? (u >> 21) == prefix : (u >> 10) == prefix);
       if (in) atomicAdd(&sm.hist[(u >> sh) & masks[pass]], 1u);
     }
-    __syncthreads();
+    lds_barrier();
     find_digit(sm, above, k);
     const uint32_t d = sm.st[0];
     above = sm.st[1];
     prefix = pass == 0 ? d : (pass == 1 ? ((prefix << 11) | d) : ((prefix << 10) | d));
-    __syncthreads();
+    lds_barrier();
   }
   const uint32_t tau_u = prefix;
   const uint32_t need = k - above;  // >= 1 elements equal to tau_u, lowest positions
@@ -124,7 +143,184 @@ __device__ void exact_threshold(ResolveSmem& sm, int64_t n, uint32_t k, Get get)
     if (base >= need) break;  // uniform: tot is block-wide
   }
   if (tid == 0) sm.st[2] = tau_u;
-  __syncthreads();
+  lds_barrier();
+}
+
+// Fast path of the resolve.  The union of the row's tile reports (up to
+// 1024 tiles x kRep slots) is loaded with fully coalesced 16-byte loads:
+// wave w, load q, lane l holds slots s = 1024w + 256q + 4l + e (e < 4),
+// i.e. slot (4l+e) % kRep of tile s / kRep.  Slot order is position order, so a
+// position-ordered scan over the union is a per-q wave scan plus one
+// cross-wave prefix.  Per-slot validity is a bitmask (bit 4q+e) and the
+// per-element work is branch-free.
+constexpr int kQN = kSlots / 4;  // 16-byte loads per thread
+
+struct UnionRegs {
+  uint32_t u[kSlots];
+  int32_t j[kSlots];
+  uint32_t vmask;  // bit i: slot i holds a candidate
+};
+
+__device__ __forceinline__ int slot_index(int wv, int q, int l) { return 1024 * wv + 256 * q + 4 * l; }
+
+// Exclusive position-ordered prefix of per-slot flags (bitmask, bit 4q+e);
+// returns each slot's rank among flagged slots and the total.
+__device__ void ordered_ranks(ResolveSmem& sm, uint32_t fmask, uint32_t (&rank)[kSlots],
+                              uint32_t* total) {
+  const int l = lane_id(), wv = wave_id(), nw = blockDim.x >> 6;
+  uint32_t lane_ex[kQN], qoff[kQN];
+  uint32_t woff = 0;
+#pragma unroll
+  for (int q = 0; q < kQN; ++q) {
+    const uint32_t c = (uint32_t)__popc((fmask >> (4 * q)) & 15u);
+    const uint32_t inc = wave_incl_scan(c);
+    lane_ex[q] = inc - c;
+    qoff[q] = woff;
+    woff += (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+  }
+  if (l == 0) sm.red[wv] = woff;
+  lds_barrier();
+  const uint32_t wt = l < nw ? sm.red[l] : 0u;
+  const uint32_t wi = wave_incl_scan(wt);
+  const uint32_t wbase = (uint32_t)__builtin_amdgcn_readlane((int)(wi - wt), wv);
+  *total = (uint32_t)__builtin_amdgcn_readlane((int)wi, 63);
+#pragma unroll
+  for (int q = 0; q < kQN; ++q) {
+    const uint32_t r = wbase + qoff[q] + lane_ex[q];
+    const uint32_t m = (fmask >> (4 * q)) & 15u;
+    rank[4 * q + 0] = r;
+    rank[4 * q + 1] = r + (m & 1u);
+    rank[4 * q + 2] = r + __popc(m & 3u);
+    rank[4 * q + 3] = r + __popc(m & 7u);
+  }
+  lds_barrier();
+}
+
+// Exact K-th best candidate of the union: selected <=> key > tau_u, or
+// key == tau_u and position <= tau_j.  Radix digits are taken relative to
+// the union's key range, so the 2048 bins spread the candidates instead of
+// piling them onto the few bins the leading exponent bits would give;
+// refinement stops once the boundary bin holds at most kBruteMax elements,
+// which wave 0 then ranks in registers.
+__device__ void union_threshold(ResolveSmem& sm, const UnionRegs& R, uint32_t k, uint32_t* tau_u,
+                                int32_t* tau_j) {
+  const int tid = threadIdx.x, nt = blockDim.x, l = lane_id(), wv = wave_id();
+  uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+  for (int i = 0; i < kSlots; ++i) {
+    const bool vi = (R.vmask >> i) & 1u;
+    mn = min(mn, vi ? R.u[i] : 0xffffffffu);
+    mx = max(mx, vi ? R.u[i] : 0u);
+  }
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
+  if (l == 0) {
+    sm.red[wv] = mn;
+    sm.red[32 + wv] = mx;
+  }
+  for (int i = tid; i < 2048; i += nt) sm.hist[i] = 0;
+  lds_barrier();
+  {
+    const int nw = nt >> 6;
+    mn = wave_min_u32(l < nw ? sm.red[l] : 0xffffffffu);
+    mx = wave_max_u32(l < nw ? sm.red[32 + l] : 0u);
+  }
+  const uint32_t range = mx - mn;
+  // bucket = keys in [lo, lo + width); digits (key - lo) >> shift are < 2048
+  int shift = range == 0 ? 0 : max(0, 32 - __clz(range) - 11);
+  uint32_t lo = mn;
+  uint64_t width = (uint64_t)range + 1;
+  uint32_t above = 0;  // candidates strictly above the bucket
+  uint32_t h = 0;      // candidates in the bucket
+  uint32_t inb = 0;    // bucket membership bitmask
+  while (true) {
+    inb = 0;
+#pragma unroll
+    for (int i = 0; i < kSlots; ++i) {
+      const uint32_t x = R.u[i];
+      const bool in = ((R.vmask >> i) & 1u) && x >= lo && (uint64_t)(x - lo) < width;
+      inb |= (uint32_t)in << i;
+      if (in) atomicAdd(&sm.hist[(x - lo) >> shift], 1u);
+    }
+    lds_barrier();
+    find_digit(sm, above, k);  // ends with a barrier
+    const uint32_t d = sm.st[0];
+    above = sm.st[1];
+    h = sm.hist[d];
+    lds_barrier();
+    const uint64_t off = (uint64_t)d << shift;
+    lo += (uint32_t)off;
+    width = min<uint64_t>(width - off, 1ull << shift);
+    if (h <= (uint32_t)kBruteMax || shift == 0) break;
+    shift = max(0, shift - 11);
+    for (int i = tid; i < 2048; i += nt) sm.hist[i] = 0;
+    lds_barrier();
+  }
+  // final bucket membership
+  inb = 0;
+#pragma unroll
+  for (int i = 0; i < kSlots; ++i) {
+    const uint32_t x = R.u[i];
+    inb |= (uint32_t)(((R.vmask >> i) & 1u) && x >= lo && (uint64_t)(x - lo) < width) << i;
+  }
+  const uint32_t need = k - above;  // 1..h
+  if (h <= (uint32_t)kBruteMax) {
+    if (tid == 0) sm.st[4] = 0;
+    lds_barrier();
+    if (inb) {
+      uint32_t m = inb;
+      uint32_t slot = atomicAdd(&sm.st[4], (uint32_t)__popc(m));
+      while (m) {
+        const int i = __ffs(m) - 1;
+        m &= m - 1;
+        // dynamic index into registers is avoided by a select chain
+        uint32_t x = 0;
+        int32_t y = 0;
+#pragma unroll
+        for (int e = 0; e < kSlots; ++e)
+          if (e == i) {
+            x = R.u[e];
+            y = R.j[e];
+          }
+        sm.bu[slot] = x;
+        sm.bj[slot] = y;
+        ++slot;
+      }
+    }
+    lds_barrier();
+    if (wv == 0) {
+      const uint32_t ui = (uint32_t)l < h ? sm.bu[l] : 0u;
+      const int32_t ji = (uint32_t)l < h ? sm.bj[l] : 0;
+      uint32_t rank = 0;
+      for (uint32_t q = 0; q < h; ++q) {
+        const uint32_t uq = (uint32_t)__builtin_amdgcn_readlane((int)ui, (int)q);
+        const int32_t jq = __builtin_amdgcn_readlane(ji, (int)q);
+        rank += (uq > ui) || (uq == ui && jq < ji);
+      }
+      if ((uint32_t)l < h && rank == need - 1) {
+        sm.st[2] = ui;
+        sm.st[3] = (uint32_t)ji;
+      }
+    }
+    lds_barrier();
+  } else {
+    // one key shared by more than kBruteMax candidates: cut by position
+    uint32_t rk[kSlots], tot;
+    ordered_ranks(sm, inb, rk, &tot);
+    if (tid == 0) {
+      sm.st[2] = lo;
+      sm.st[3] = 0x7fffffffu;
+    }
+    lds_barrier();
+    if (need < tot) {
+#pragma unroll
+      for (int i = 0; i < kSlots; ++i)
+        if (((inb >> i) & 1u) && rk[i] == need - 1) sm.st[3] = (uint32_t)R.j[i];
+    }
+    lds_barrier();
+  }
+  *tau_u = sm.st[2];
+  *tau_j = (int32_t)sm.st[3];
 }
 
 __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(
@@ -133,7 +329,30 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(
     const uint32_t* __restrict__ rep_u, const int32_t* __restrict__ rep_j, int32_t* idx,
     uint32_t* stats) {
   __shared__ ResolveSmem sm;
-  const int t = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
+  const int t = blockIdx.x, tid = threadIdx.x, nt = blockDim.x, l = lane_id(), wv = wave_id();
+  const int64_t slot0 = (int64_t)t * ntiles_max;
+  const int nslots = ntiles_max * kRep;
+  // Issue the report loads together with the descriptor loads: one round trip.
+  UnionRegs R;
+  RepHeader hq[kQN];
+  {
+    u32x4 a[kQN], c[kQN];
+#pragma unroll
+    for (int q = 0; q < kQN; ++q) {
+      const int sidx = slot_index(wv, q, l);
+      const int sc = sidx < nslots ? sidx : 0;
+      a[q] = *reinterpret_cast<const u32x4*>(rep_u + slot0 * kRep + sc);
+      c[q] = *reinterpret_cast<const u32x4*>(rep_j + slot0 * kRep + sc);
+      hq[q] = hdr[slot0 + sc / kRep];
+    }
+#pragma unroll
+    for (int q = 0; q < kQN; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        R.u[4 * q + e] = a[q][e];
+        R.j[4 * q + e] = (int32_t)c[q][e];
+      }
+  }
   const RowInfo ri = row_info(t, cu_q, ctx_len, B);
   const int64_t n = ri.p + 1;
   int32_t* out = idx + (int64_t)t * K;
@@ -143,74 +362,73 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(
   }
   const uint32_t k = (uint32_t)K;
   const int ntiles = (int)((n + tile - 1) / tile);
-  const int64_t slot0 = (int64_t)t * ntiles_max;
-  // ---- tile offsets ----
-  bool fits = ntiles <= kResolveThreads;
-  uint32_t C = 0;
-  if (fits) {
-    uint32_t c = tid < ntiles ? hdr[slot0 + tid].count : 0u;
-    uint32_t tot;
-    uint32_t ex = block_excl_scan(c, sm.scan, &tot);
-    if (tid < ntiles) sm.toff[tid] = ex;
-    if (tid == 0) sm.toff[ntiles] = tot;
-    __syncthreads();
-    C = sm.toff[ntiles];
-    fits = C <= (uint32_t)kResolveCap && C >= k;
+  R.vmask = 0;
+#pragma unroll
+  for (int q = 0; q < kQN; ++q) {
+    const int sidx = slot_index(wv, q, l);
+    const bool tile_ok = sidx < nslots && sidx / kRep < ntiles;
+    const uint32_t sub = (uint32_t)(sidx % kRep);
+    const uint32_t cnt = hq[q].count;
+    // slots sub .. sub+3 of the tile are valid while below its count
+    const uint32_t nv = tile_ok ? (cnt > sub ? min(cnt - sub, 4u) : 0u) : 0u;
+    R.vmask |= ((1u << nv) - 1u) << (4 * q);
   }
   bool ok = false;
-  if (fits) {
-    // ---- gather the union into LDS in ascending position order ----
-    for (int64_t s = tid; s < (int64_t)ntiles * kRepMax; s += nt) {
-      int ti = (int)(s / kRepMax), e = (int)(s % kRepMax);
-      uint32_t off = sm.toff[ti], cnt = sm.toff[ti + 1] - off;
-      if ((uint32_t)e < cnt) {
-        sm.cu[off + e] = rep_u[(slot0 + ti) * kRepMax + e];
-        sm.cj[off + e] = rep_j[(slot0 + ti) * kRepMax + e];
-      }
+  if (ntiles <= kResolveTiles && ntiles <= ntiles_max) {
+    const uint32_t tot = wave_sum_u32((uint32_t)__popc(R.vmask));
+    if (l == 0) sm.red[wv] = tot;
+    lds_barrier();
+    uint32_t C = 0;
+    {
+      const int nw = nt >> 6;
+      C = wave_sum_u32(l < nw ? sm.red[l] : 0u);
     }
-    __syncthreads();
-    exact_threshold(sm, (int64_t)C, k, [&](int64_t i, uint32_t* u, int32_t* j) {
-      *u = sm.cu[i];
-      *j = sm.cj[i];
-    });
-    const uint32_t tau_u = sm.st[2];
-    const int32_t tau_j = (int32_t)sm.st[3];
-    // ---- certification ----
-    int bad = 0;
-    for (int ti = tid; ti < ntiles; ti += nt) {
-      RepHeader h = hdr[slot0 + ti];
-      if (!h.complete) {
-        bool fine = (h.worst_u < tau_u) || (h.worst_u == tau_u && h.worst_j >= tau_j);
-        bad |= !fine;
+    lds_barrier();
+    if (C >= k) {
+      uint32_t tau_u;
+      int32_t tau_j;
+      union_threshold(sm, R, k, &tau_u, &tau_j);
+      // ---- certification: every partly reported tile ends at or below theta ----
+      bool bad = false;
+#pragma unroll
+      for (int q = 0; q < kQN; ++q) {
+        const int sidx = slot_index(wv, q, l);
+        const RepHeader& h = hq[q];
+        if (sidx % kRep == 0 && sidx < nslots && sidx / kRep < ntiles && !h.complete &&
+            !((h.worst_u < tau_u) || (h.worst_u == tau_u && h.worst_j >= tau_j)))
+          bad = true;
       }
-    }
-    ok = !__syncthreads_or(bad);
-    if (ok) {
-      const int per = (int)((C + nt - 1) / nt);
-      const int lo = tid * per, hi = min((int)C, lo + per);
-      uint32_t cnt = 0;
-      for (int i = lo; i < hi; ++i) {
-        uint32_t u = sm.cu[i];
-        cnt += (u > tau_u) || (u == tau_u && sm.cj[i] <= tau_j);
-      }
-      uint32_t tot;
-      uint32_t pos = block_excl_scan(cnt, sm.scan, &tot);
-      for (int i = lo; i < hi; ++i) {
-        uint32_t u = sm.cu[i];
-        if ((u > tau_u) || (u == tau_u && sm.cj[i] <= tau_j)) {
-          if (pos < k) out[pos] = sm.cj[i];
-          ++pos;
+      if (tid == 0) sm.st[7] = 0;
+      lds_barrier();
+      if (bad) sm.st[7] = 1;
+      lds_barrier();
+      ok = sm.st[7] == 0;
+      if (ok) {
+        uint32_t smask = 0;
+#pragma unroll
+        for (int i = 0; i < kSlots; ++i) {
+          const bool si = ((R.vmask >> i) & 1u) &&
+                          ((R.u[i] > tau_u) || (R.u[i] == tau_u && R.j[i] <= tau_j));
+          smask |= (uint32_t)si << i;
         }
+        uint32_t rk[kSlots], total;
+        ordered_ranks(sm, smask, rk, &total);
+        // stage in LDS, then store coalesced
+#pragma unroll
+        for (int i = 0; i < kSlots; ++i)
+          if (((smask >> i) & 1u) && rk[i] < k) sm.stage[rk[i]] = R.j[i];
+        lds_barrier();
+        for (int i = tid; i < K; i += nt) out[i] = sm.stage[i];
+        if (stats && tid == 0) atomicAdd(&stats[0], 1u);
       }
-      if (stats && tid == 0) atomicAdd(&stats[0], 1u);
     }
   }
   if (!ok) {
     // ---- exact fallback straight from the score row ----
     const float* row = scores + (int64_t)t * ld;
-    auto get = [&](int64_t i, uint32_t* u, int32_t* j) {
-      *u = order_key(row[i]);
-      *j = (int32_t)i;
+    auto get = [&](int64_t i, uint32_t* uu, int32_t* jj) {
+      *uu = order_key(row[i]);
+      *jj = (int32_t)i;
     };
     exact_threshold(sm, n, k, get);
     const uint32_t tau_u = sm.st[2];
@@ -220,8 +438,8 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(
       int64_t i = r0 + tid;
       uint32_t f = 0;
       if (i < n) {
-        uint32_t u = order_key(row[i]);
-        f = (u > tau_u) || (u == tau_u && (int32_t)i <= tau_j);
+        uint32_t uu = order_key(row[i]);
+        f = (uu > tau_u) || (uu == tau_u && (int32_t)i <= tau_j);
       }
       uint32_t tot;
       uint32_t ex = block_excl_scan(f, sm.scan, &tot);
@@ -235,28 +453,36 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
-int topk_tile_for(int max_ctx) {
-  int tile = 256;
-  while (tile < kMaxTile && (int64_t)tile * 512 < (int64_t)max_ctx) tile <<= 1;
+// Tile size: a power of two in [64, 2048] with at most kResolveTiles tiles
+// per row and about four of the row's top K expected per tile, so that a
+// tile rarely holds more than kRep of them (which would send the row to
+// the exact fallback).
+int topk_tile_for(int max_ctx, int K) {
+  const int64_t k = K > 0 ? K : 1;
+  const int64_t per4 = (4LL * max_ctx) / k;  // about four winners per tile
+  const int64_t by_tiles = ((int64_t)max_ctx + kResolveTiles - 1) / kResolveTiles;
+  int tile = 64;
+  while (tile < kMaxTile && 2LL * tile <= per4) tile <<= 1;   // round down
+  while (tile < kMaxTile && tile < by_tiles) tile <<= 1;      // tile-count cap
   return tile;
 }
 
-size_t topk_report_bytes(int T, int max_ctx) {
-  const int tile = topk_tile_for(max_ctx);
+size_t topk_report_bytes(int T, int max_ctx, int K) {
+  const int tile = topk_tile_for(max_ctx, K);
   const int64_t ntiles = (max_ctx + tile - 1) / tile;
-  return (size_t)T * ntiles * (sizeof(RepHeader) + kRepMax * 8);
+  return (size_t)T * ntiles * (sizeof(RepHeader) + kRep * 8);
 }
 
-TopkWs topk_ws_carve(void* ws, int T, int max_ctx) {
+TopkWs topk_ws_carve(void* ws, int T, int max_ctx, int K) {
   TopkWs w;
-  w.tile = topk_tile_for(max_ctx);
+  w.tile = topk_tile_for(max_ctx, K);
   w.ntiles_max = (max_ctx + w.tile - 1) / w.tile;
   const size_t nslot = (size_t)T * w.ntiles_max;
   char* p = static_cast<char*>(ws);
   w.hdr = reinterpret_cast<RepHeader*>(p);
   p += nslot * sizeof(RepHeader);
   w.rep_u = reinterpret_cast<uint32_t*>(p);
-  p += nslot * kRepMax * sizeof(uint32_t);
+  p += nslot * kRep * sizeof(uint32_t);
   w.rep_j = reinterpret_cast<int32_t*>(p);
   return w;
 }
@@ -265,8 +491,22 @@ hipError_t launch_tile_reports(const float* scores, int64_t ld, const int32_t* c
                                const int32_t* ctx_len, int B, int T, int max_ctx,
                                const TopkWs& w, hipStream_t stream) {
   dim3 grid(w.ntiles_max, T);
-  hipLaunchKernelGGL(tile_report_kernel, grid, dim3(256), 0, stream, scores, ld, cu_q, ctx_len,
-                     B, w.tile, w.ntiles_max, w.hdr, w.rep_u, w.rep_j);
+  switch (w.tile) {
+#define DSA_TILE_CASE(T_)                                                                       \
+  case T_:                                                                                      \
+    hipLaunchKernelGGL(tile_report_kernel<T_>, grid, dim3(64), 0, stream, scores, ld, cu_q,    \
+                       ctx_len, B, w.ntiles_max, w.hdr, w.rep_u, w.rep_j);                     \
+    break;
+    DSA_TILE_CASE(64)
+    DSA_TILE_CASE(128)
+    DSA_TILE_CASE(256)
+    DSA_TILE_CASE(512)
+    DSA_TILE_CASE(1024)
+    DSA_TILE_CASE(2048)
+#undef DSA_TILE_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -10,19 +10,20 @@
 //
 // Kernel layout (gfx950, wave64, 4 waves per workgroup):
 //   - a workgroup takes `rows_per_split` consecutive entries of the query's
-//     index row; wave (hb, rb) handles head block hb (32 heads) and row block
-//     rb (32 rows) of each 32*RB-row step, keeping its own running softmax
-//     state (max, sum, O^T accumulators); the waves' states are merged at
-//     the end through LDS;
-//   - S^T = K_rows . q^T on MFMA: the gathered K rows are loaded straight
-//     into A-operand registers (16-byte chunks of each 256-byte row), q is
-//     the B operand held in registers for the whole kernel;
+//     index row in steps of 128; wave w takes rows 32w..32w+31 of a step,
+//     for every head (NHB blocks of 32 heads), and keeps its own running
+//     softmax state (max, sum, O^T accumulators); the four states are merged
+//     pairwise through LDS at the end;
+//   - S^T = K_rows . q^T on MFMA (v_mfma_f32_32x32x16_bf16): the gathered K
+//     rows are loaded straight into A-operand registers (16-byte chunks of
+//     each row), q is the B operand, held in registers for the whole kernel;
 //   - in the S^T accumulator layout each lane holds one head and 16 rows, so
 //     the per-head max / sum need one cross-half exchange, and P^T is
-//     already in B-operand layout (the k slots of the PV product are taken in
-//     the order the accumulator rows come in);
-//   - V rows are written transposed into a per-wave LDS tile so the A
-//     operand of O^T = V^T . P^T is two 8-byte LDS reads per k step;
+//     already a B operand once its k slots are taken in accumulator order;
+//   - the gathered V rows go to LDS with direct global-to-LDS loads, row
+//     major; the A operand of O^T = V^T . P^T (8 rows of one dim per lane)
+//     comes back with the LDS transpose read ds_read_b64_tr_b16, whose
+//     16-lane groups turn 4 rows x 16 dims into 16 dims x 4 rows;
 //   - with several splits per query the workgroups write partial (m, l, O)
 //     and a combine kernel merges them and applies the gate.
 #include "dsa_kernels.h"
@@ -35,6 +36,33 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float sigmoidf(float x) { return 1.f / (1.f + __expf(-x)); }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
+// (i % 4) of the 8 bytes addressed by lane 4e + i/4, for e = 0..3.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+  u32x2 r;
+  r[0] = (uint32_t)(uint16_t)v[0] | ((uint32_t)(uint16_t)v[1] << 16);
+  r[1] = (uint32_t)(uint16_t)v[2] | ((uint32_t)(uint16_t)v[3] << 16);
+  return r;
+}
+
+// Per-wave V tile in LDS: 32 rows of D bf16.  Direct load c (of D/8) puts
+// 16-byte chunk 2c + (l / 32) of row l % 32 at byte 16 l of block c.
+template <int D>
+struct VTile {
+  static constexpr int kBlocks = D / 16;       // direct loads per 32-row tile (chunk pairs)
+  static constexpr int kStride = 1024;         // bytes per block
+  static constexpr int kBytes = kBlocks * kStride;
+  // element (row r, dim d) of the tile
+  __device__ static int offset(int r, int d) {
+    const int ck = d >> 3;  // 16-byte chunk
+    return (ck >> 1) * kStride + (((ck & 1) << 5) + r) * 16 + (d & 7) * 2;
+  }
+};
+
 template <int D, int HB>
 __global__ __launch_bounds__(256) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
@@ -45,73 +73,70 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
   constexpr int KS = D / 16;   // k-steps of q . K
   constexpr int DB = D / 32;   // 32-wide blocks of the output dim
   constexpr int RB = 4 / HB;   // row-block waves per head block
-  constexpr int VTS = 32 + 4;  // padded row count of the transposed V tile (bf16)
-  constexpr int MO_FLOATS = (RB - 1) * HB * 32 * (D + 2);
-  constexpr int VT_HALFS = 4 * D * VTS;
-  constexpr int SMEM_BYTES = (MO_FLOATS * 4 > VT_HALFS * 2) ? MO_FLOATS * 4 : VT_HALFS * 2;
+  constexpr int STEP = 32 * RB;  // rows per workgroup step
+  using VT = VTile<D>;
+  // merge state of one wave: per lane (m, l) and DB x 16 O values
+  constexpr int ST_FLOATS = 2 + DB * 16;
+  constexpr int MERGE_BYTES = (RB / 2) * HB * 64 * ST_FLOATS * 4;
+  constexpr int VT_BYTES = 4 * VT::kBytes;
+  constexpr int SMEM_BYTES = MERGE_BYTES > VT_BYTES ? MERGE_BYTES : VT_BYTES;
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM_BYTES];
-  uint16_t* vt = reinterpret_cast<uint16_t*>(smem);
-  float* mo = reinterpret_cast<float*>(smem);
 
   const int t = blockIdx.y, split = blockIdx.x;
   const int l = lane_id(), g = l >> 5, wv = wave_id();
   const int hb = wv % HB, rb = wv / HB;
+  const int lo = split * rows_per_split;
+  // In index mode the first index load does not depend on the batch
+  // descriptor: issue it with the descriptor loads (one round trip).
+  int32_t j_first = -1;
+  if (idx) {
+    const int lp = lo + 32 * rb + (l & 31);
+    j_first = lp < K ? idx[(int64_t)t * K + lp] : -1;
+  }
   const RowInfo ri = row_info(t, cu_q, ctx_len, B);
   const int64_t row0 = cu_ctx[ri.b];
   const int nlist = idx ? K : (int)min<int64_t>(window, ri.p + 1);
   const int64_t jw0 = ri.p - nlist + 1;  // window mode: first position
-  const int lo = split * rows_per_split;
   const int hi = min(nlist, lo + rows_per_split);
 
-  const int head = 32 * hb + (l & 31);
-  const bool head_ok = head < Hq;
+  // q as the B operand of S^T: column = head 32 hb + l % 32, k = dims 16 s + 8 g + 0..7.
+  // Heads past Hq repeat the last head; their results are never written.
   bf16x8 qb[KS];
   {
-    // clamped address instead of a branch: every load is in flight at once
-    const int hc = min(head, Hq - 1);
-    u32x4 qv[KS];
+    const int hc = min(32 * hb + (l & 31), Hq - 1);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qv[s] = ld16(q + ((int64_t)t * Hq + hc) * D + 16 * s + 8 * g);
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      if (!head_ok) qv[s] = u32x4{0u, 0u, 0u, 0u};
-      qb[s] = as_bf16x8(qv[s]);
-    }
+    for (int s = 0; s < KS; ++s)
+      qb[s] = as_bf16x8(ld16(q + ((int64_t)t * Hq + hc) * D + 16 * s + 8 * g));
   }
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
 
-  uint16_t* myvt = vt + wv * (D * VTS);
+  uint8_t* vt = smem + wv * VT::kBytes;
+  const uint16_t* vt16 = reinterpret_cast<const uint16_t*>(vt);
+  const int G = l >> 4, jj = l & 15;
 #pragma unroll 1
-  for (int base = lo; base < hi; base += 32 * RB) {
-    const int lp = base + 32 * rb + (l & 31);
+  for (int base = lo + 32 * rb; base < hi; base += STEP) {
+    const int lp = base + (l & 31);
     bool valid = lp < hi;
     int64_t j = 0;
     if (valid) {
-      j = idx ? (int64_t)idx[(int64_t)t * K + lp] : jw0 + lp;
+      j = idx ? (int64_t)(base == lo + 32 * rb ? j_first : idx[(int64_t)t * K + lp]) : jw0 + lp;
       valid = j >= 0;
     }
     const int64_t row = row0 + (valid ? j : 0);
-    u32x4 kf[KS], vf[KS];
+    // K row chunks straight into A-operand registers, V rows into LDS; all
+    // issued before any is used
+    u32x4 kf[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) kf[s] = ld16(kc + row * D + 16 * s + 8 * g);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) vf[s] = ld16(vc + row * D + 16 * s + 8 * g);
+    for (int c = 0; c < VT::kBlocks; ++c)
+      lds_dma16(vc + row * D + 8 * (2 * c + g), vt + c * VT::kStride);
+    __builtin_amdgcn_sched_barrier(0);
     const uint32_t vmask = (uint32_t)__ballot(valid);
-    // V^T into this wave's LDS tile: element (d, r) at myvt[d*VTS + r]
-    lds_barrier();
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = 16 * s + 8 * g + e;
-        const uint32_t word = vf[s][e >> 1];
-        myvt[d * VTS + (l & 31)] = (uint16_t)((e & 1) ? (word >> 16) : (word & 0xffffu));
-      }
-    }
-    // S^T = K . q^T
+    // S^T = K . q^T, then the online softmax per head (exp2 domain)
     f32x16 sacc = {};
 #pragma unroll
     for (int s = 0; s < KS; ++s) sacc = mfma32(as_bf16x8(kf[s]), qb[s], sacc);
@@ -135,94 +160,115 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
     }
     l_run = l_run * alpha + xor32_add(psum);
     m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) o[db] *= alpha;
     bf16x8 pb[2];
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int e = 0; e < 8; ++e) pb[s2][e] = static_cast<__bf16>(sv[8 * s2 + e]);
-    lds_barrier();
-    // O^T += V^T . P^T
+    // V tile landed
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
+    __builtin_amdgcn_sched_barrier(0);
+    // O^T += V^T . P^T.  k slot e of step s2 is accumulator row
+    // 16 s2 + 8 (e / 4) + 4 g + e % 4, so the A operand's 8 rows for half g
+    // are two 4-row groups; each comes from one transpose read: lane jj of
+    // a 16-lane group addresses row k0 + jj / 4, dims n0 + 4 (jj % 4) .. + 3.
+    u32x2 av[DB][2][2];
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const uint16_t* vrow = myvt + (32 * db + (l & 31)) * VTS;
+      const int n0 = 32 * db + 16 * (G & 1) + 4 * (jj & 3);
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        const u32x2 a0 = *reinterpret_cast<const u32x2*>(vrow + 16 * s2 + 4 * g);
-        const u32x2 a1 = *reinterpret_cast<const u32x2*>(vrow + 16 * s2 + 8 + 4 * g);
-        const u32x4 av = {a0[0], a0[1], a1[0], a1[1]};
-        o[db] = mfma32(as_bf16x8(av), pb[s2], o[db]);
+        const int k0 = 16 * s2 + 4 * g + (jj >> 2);
+        av[db][s2][0] = lds_read_tr16(vt16 + VT::offset(k0, n0) / 2);
+        av[db][s2][1] = lds_read_tr16(vt16 + VT::offset(k0 + 8, n0) / 2);
       }
     }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      o[db] *= alpha;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+        o[db] = mfma32(as_bf16x8(u32x4{av[db][s2][0][0], av[db][s2][0][1], av[db][s2][1][0],
+                                       av[db][s2][1][1]}),
+                       pb[s2], o[db]);
+    }
   }
-  // ---- merge the RB row-block waves of each head block ----
-  lds_barrier();
-  if (rb > 0) {
-    float* my = mo + ((rb - 1) * HB + hb) * 32 * (D + 2);
-    const int hl = l & 31;
+
+  // ---- merge the RB row-block waves of each head block pairwise through LDS ----
+  float* ms = reinterpret_cast<float*>(smem);
+  auto put = [&](int slot) {
+    float* dst = ms + (slot * HB + hb) * 64 * ST_FLOATS;
+    dst[l] = m_run;
+    dst[64 + l] = l_run;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int d = 32 * db + 8 * (r >> 2) + 4 * g + (r & 3);
-        my[hl * (D + 2) + d] = o[db][r];
-      }
-    if (g == 0) {
-      my[hl * (D + 2) + D] = m_run;
-      my[hl * (D + 2) + D + 1] = l_run;
-    }
+      for (int r = 0; r < 16; ++r) dst[(2 + db * 16 + r) * 64 + l] = o[db][r];
+  };
+  auto take = [&](int slot) {
+    const float* src = ms + (slot * HB + hb) * 64 * ST_FLOATS;
+    const float mo = src[l], lo2 = src[64 + l];
+    const float M = fmaxf(m_run, mo);
+    const float a = (M == -INFINITY) ? 0.f : exp2f(m_run - M);
+    const float bb = (M == -INFINITY) ? 0.f : exp2f(mo - M);
+    l_run = l_run * a + lo2 * bb;
+    m_run = M;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * a + src[(2 + db * 16 + r) * 64 + l] * bb;
+  };
+  lds_barrier();  // every wave is done with its V tile
+  if constexpr (RB == 4) {
+    if (rb >= 2) put(rb - 2);
+    lds_barrier();
+    if (rb < 2) take(rb);
+    lds_barrier();
   }
+  if (rb == 1) put(0);
   lds_barrier();
   if (rb != 0) return;
-  const int hl = l & 31;
-  float M = m_run;
-#pragma unroll
-  for (int k = 1; k < RB; ++k) M = fmaxf(M, mo[((k - 1) * HB + hb) * 32 * (D + 2) + hl * (D + 2) + D]);
-  const float a_self = (M == -INFINITY) ? 0.f : exp2f(m_run - M);
-  float Lsum = l_run * a_self;
-  float ak[RB];
-  ak[0] = a_self;
-#pragma unroll
-  for (int k = 1; k < RB; ++k) {
-    const float* other = mo + ((k - 1) * HB + hb) * 32 * (D + 2) + hl * (D + 2);
-    ak[k] = (M == -INFINITY) ? 0.f : exp2f(other[D] - M);
-    Lsum += other[D + 1] * ak[k];
-  }
-  if (!head_ok) return;
+  take(0);
+
+  // ---- the row-block-0 wave of each head block writes the result ----
+  const int head = 32 * hb + (l & 31);
+  if (head >= Hq) return;
   const bool final_out = nsplit == 1;
+  const float Lsum = l_run, M = m_run;
   const float inv = (Lsum > 0.f) ? 1.f / Lsum : 0.f;
   float* pp = part + (((int64_t)t * nsplit + split) * Hq + head) * (D + 2);
+  // gate values of this lane's outputs, all loaded before any is used
+  u32x2 gw[DB][4];
+  if (final_out && gate) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        gw[db][r4] = *reinterpret_cast<const u32x2*>(gate + ((int64_t)t * Hq + head) * D +
+                                                     32 * db + 8 * r4 + 4 * g);
+  }
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
-      float vals[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * r4 + e;
-        const int d = 32 * db + 8 * r4 + 4 * g + e;
-        float acc = o[db][r] * ak[0];
-#pragma unroll
-        for (int k = 1; k < RB; ++k)
-          acc += mo[((k - 1) * HB + hb) * 32 * (D + 2) + hl * (D + 2) + d] * ak[k];
-        vals[e] = acc;
-      }
       const int d0 = 32 * db + 8 * r4 + 4 * g;
       if (final_out) {
-        const uint16_t* gp = gate ? gate + ((int64_t)t * Hq + head) * D + d0 : nullptr;
         uint16_t ob[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float v = vals[e] * inv;
-          if (gp) v *= sigmoidf(bf16_to_f32(gp[e]));
+          float v = o[db][4 * r4 + e] * inv;
+          if (gate) {
+            const uint32_t wd = gw[db][r4][e >> 1];
+            v *= sigmoidf(bf16_to_f32((uint16_t)((e & 1) ? (wd >> 16) : (wd & 0xffffu))));
+          }
           ob[e] = f32_to_bf16(v);
         }
         uint16_t* op = out + ((int64_t)t * Hq + head) * D + d0;
         *reinterpret_cast<u32x2*>(op) = u32x2{(uint32_t)ob[0] | ((uint32_t)ob[1] << 16),
                                              (uint32_t)ob[2] | ((uint32_t)ob[3] << 16)};
       } else {
-        *reinterpret_cast<f32x4*>(pp + d0) = f32x4{vals[0], vals[1], vals[2], vals[3]};
+        *reinterpret_cast<f32x4*>(pp + d0) =
+            f32x4{o[db][4 * r4], o[db][4 * r4 + 1], o[db][4 * r4 + 2], o[db][4 * r4 + 3]};
       }
     }
   }
@@ -236,60 +282,97 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
   }
 }
 
-// Merge split partials: grid (T, Hq), D threads.  All loads of a block are
-// independent: first every split's (m, l), then every split's O[d].
+// Merge split partials: grid (T, Hq), one wave; lane i owns dims
+// i*D/64 .. +D/64-1.  Every load is issued up front (one round trip): each
+// lane reads its dims of every split's O (NS >= nsplit loads, indices past
+// nsplit repeat the last split and get weight 0) and the (m, l) of split i;
+// the (m, l) go through LDS.
 constexpr int kMaxSplit = 64;
 
-template <int D>
-__global__ __launch_bounds__(D) void attn_combine_kernel(const float* __restrict__ part, int nsplit,
-                                                         int Hq, const uint16_t* __restrict__ gate,
-                                                         uint16_t* __restrict__ out,
-                                                         float* __restrict__ lse) {
-  __shared__ float sm_m[kMaxSplit], sm_l[kMaxSplit], sm_w[kMaxSplit];
-  __shared__ float sm_ML[2];
-  const int t = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+template <int D, int NS>
+__global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restrict__ part, int nsplit,
+                                                          int Hq, const uint16_t* __restrict__ gate,
+                                                          uint16_t* __restrict__ out,
+                                                          float* __restrict__ lse) {
+  constexpr int PL = D / 64;  // dims per lane (1 or 2)
+  static_assert(NS <= 64 && (PL == 1 || PL == 2), "combine shape");
+  __shared__ float sm_m[NS], sm_l[NS];
+  const int t = blockIdx.x, h = blockIdx.y, i = threadIdx.x;
   const float* pp = part + ((int64_t)t * nsplit * Hq + h) * (D + 2);
   const int64_t stride = (int64_t)Hq * (D + 2);
-  for (int s = d; s < nsplit; s += D) {
-    sm_m[s] = pp[s * stride + D];
-    sm_l[s] = pp[s * stride + D + 1];
-  }
-  float g = 0.f;
-  const int64_t off = ((int64_t)t * Hq + h) * D + d;
-  if (gate) g = bf16_to_f32(gate[off]);
-  lds_barrier();
-  if (d < 64) {
-    float M = -INFINITY;
-    for (int s = d; s < nsplit; s += 64) M = fmaxf(M, sm_m[s]);
-    M = wave_max_f32(M);
-    float L = 0.f;
-    for (int s = d; s < nsplit; s += 64) {
-      const float a = (M == -INFINITY) ? 0.f : exp2f(sm_m[s] - M);
-      sm_w[s] = a;
-      L += a * sm_l[s];
-    }
-    L = wave_sum_f32(L);
-    if (d == 0) {
-      sm_ML[0] = M;
-      sm_ML[1] = L;
+  const int64_t off = ((int64_t)t * Hq + h) * D + PL * i;
+  float ov[NS][PL];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const float* src = pp + min(s, nsplit - 1) * stride + PL * i;
+    if constexpr (PL == 2) {
+      const f32x2 v = *reinterpret_cast<const f32x2*>(src);
+      ov[s][0] = v[0];
+      ov[s][1] = v[1];
+    } else {
+      ov[s][0] = *src;
     }
   }
+  const int si = min(i, nsplit - 1);
+  const f32x2 ml = *reinterpret_cast<const f32x2*>(pp + si * stride + D);
+  uint32_t graw = 0;
+  if (gate) {
+    if constexpr (PL == 2) graw = *reinterpret_cast<const uint32_t*>(gate + off);
+    else graw = gate[off];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (i < NS) {
+    sm_m[i] = i < nsplit ? ml[0] : -INFINITY;
+    sm_l[i] = ml[1];
+  }
   lds_barrier();
-  const float L = sm_ML[1];
-  float acc = 0.f;
-#pragma unroll 8
-  for (int s = 0; s < nsplit; ++s) acc += sm_w[s] * pp[s * stride + d];
-  float v = L > 0.f ? acc / L : 0.f;
-  if (gate) v *= sigmoidf(g);
-  out[off] = f32_to_bf16(v);
-  if (lse && d == 0) lse[(int64_t)t * Hq + h] = L > 0.f ? (sm_ML[0] + log2f(L)) * kLn2 : -INFINITY;
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) M = fmaxf(M, sm_m[s]);
+  float L = 0.f, acc[PL] = {};
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const float wgt = (s < nsplit && M != -INFINITY) ? exp2f(sm_m[s] - M) : 0.f;
+    L += wgt * sm_l[s];
+#pragma unroll
+    for (int e = 0; e < PL; ++e) acc[e] += wgt * ov[s][e];
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  uint16_t ob[PL];
+#pragma unroll
+  for (int e = 0; e < PL; ++e) {
+    float v = acc[e] * inv;
+    if (gate) v *= sigmoidf(bf16_to_f32((uint16_t)(graw >> (16 * e))));
+    ob[e] = f32_to_bf16(v);
+  }
+  if constexpr (PL == 2) *reinterpret_cast<uint32_t*>(out + off) = (uint32_t)ob[0] | ((uint32_t)ob[1] << 16);
+  else out[off] = ob[0];
+  if (lse && i == 0) lse[(int64_t)t * Hq + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+}
+
+template <int D>
+static void launch_combine(int T, int Hq, const float* part, int nsplit, const uint16_t* gate,
+                           uint16_t* out, float* lse, hipStream_t stream) {
+  const dim3 grid(T, Hq);
+  if (nsplit <= 8)
+    hipLaunchKernelGGL((attn_combine_kernel<D, 8>), grid, dim3(64), 0, stream, part, nsplit, Hq,
+                       gate, out, lse);
+  else if (nsplit <= 16)
+    hipLaunchKernelGGL((attn_combine_kernel<D, 16>), grid, dim3(64), 0, stream, part, nsplit, Hq,
+                       gate, out, lse);
+  else if (nsplit <= 32)
+    hipLaunchKernelGGL((attn_combine_kernel<D, 32>), grid, dim3(64), 0, stream, part, nsplit, Hq,
+                       gate, out, lse);
+  else
+    hipLaunchKernelGGL((attn_combine_kernel<D, 64>), grid, dim3(64), 0, stream, part, nsplit, Hq,
+                       gate, out, lse);
 }
 
 AttnPlan attn_plan(int T, int K, int window, int Hq, int D) {
   AttnPlan p;
   const int nlist = K > 0 ? K : window;
   const int hb = (Hq + 31) / 32;
-  const int step = 32 * (4 / (hb > 2 ? 2 : hb));
+  const int step = 32 * (4 / (hb > 2 ? 2 : hb));  // rows per workgroup step
   // a step per workgroup when few queries, otherwise whole rows
   int rows = step;
   if ((int64_t)T * ((nlist + step - 1) / step) > 2048) rows = nlist > 0 ? nlist : step;
@@ -319,16 +402,12 @@ hipError_t launch_sparse_attn(const void* q, const void* k_cache, const void* v_
     hipLaunchKernelGGL((sparse_attn_kernel<128, 2>), grid, dim3(256), 0, stream, qp, kp, vp, idx,
                        K, window, gp, scale, Hq, cu_q, ctx_len, cu_ctx, B, plan.rows_per_split,
                        op, lse, part, plan.nsplit);
-    if (plan.nsplit > 1)
-      hipLaunchKernelGGL((attn_combine_kernel<128>), dim3(T, Hq), dim3(128), 0, stream, part,
-                         plan.nsplit, Hq, gp, op, lse);
+    if (plan.nsplit > 1) launch_combine<128>(T, Hq, part, plan.nsplit, gp, op, lse, stream);
   } else if (D == 64 && Hq == 8) {
     hipLaunchKernelGGL((sparse_attn_kernel<64, 1>), grid, dim3(256), 0, stream, qp, kp, vp, idx,
                        K, window, gp, scale, Hq, cu_q, ctx_len, cu_ctx, B, plan.rows_per_split,
                        op, lse, part, plan.nsplit);
-    if (plan.nsplit > 1)
-      hipLaunchKernelGGL((attn_combine_kernel<64>), dim3(T, Hq), dim3(64), 0, stream, part,
-                         plan.nsplit, Hq, gp, op, lse);
+    if (plan.nsplit > 1) launch_combine<64>(T, Hq, part, plan.nsplit, gp, op, lse, stream);
   } else {
     return hipErrorInvalidValue;
   }

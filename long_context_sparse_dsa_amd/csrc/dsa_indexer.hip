@@ -28,6 +28,8 @@
 #include "dsa_kernels.h"
 #include "dsa_topk_tile.h"
 
+#include <type_traits>
+
 namespace dsa {
 
 // Offset (in elements) of the 8 consecutive dims a lane of half `g` feeds
@@ -120,12 +122,16 @@ __global__ __launch_bounds__(64) void index_decode_kernel(
   static_assert(KS + 1 + St::kBufs * NL <= 63 && NI % SBLK == 0 && TILE % SROWS == 0,
                 "stage shape");
 
-  // one LDS object: [query rows | head weights | stage buffers] (with
-  // several objects the compiler adds a wait for every load in flight
-  // before reading any of them)
-  __shared__ __attribute__((aligned(16))) uint8_t lds[1024 * KS + 256 + St::kBufs * St::kBufBytes];
+  // One LDS object (with several objects the compiler adds a wait for every
+  // load in flight before reading any of them):
+  //   [query rows | head weights], later reused for the tile's scores
+  //   [stage buffers]
+  constexpr int kQwBytes = 1024 * KS + 256;
+  constexpr int kStageOff = kQwBytes > 4 * TILE ? kQwBytes : 4 * TILE;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kStageOff + St::kBufs * St::kBufBytes];
   uint8_t* const qw_lds = lds;
-  uint8_t* const stage = lds + 1024 * KS + 256;
+  uint8_t* const stage = lds + kStageOff;
+  float* const sc_lds = reinterpret_cast<float*>(lds);  // after the query rows are read
 
   const int b = blockIdx.y, ti = blockIdx.x;
   // both descriptor loads issued together (one round trip)
@@ -153,9 +159,6 @@ __global__ __launch_bounds__(64) void index_decode_kernel(
     const int64_t we = (int64_t)b * w_ld + min(l, H_I - 1);
     lds_dma4(w + (we & ~(int64_t)1), qw_lds + 1024 * KS);
   }
-  bf16x8 qa[KS];
-  float wr[16];
-
   // lane permutation of a load instruction: row l % kRowsPerKiB, chunk l / kRowsPerKiB
   const int lrow = l % St::kRowsPerKiB, lchunk = l / St::kRowsPerKiB;
   // issue the loads of stage st into its buffer (fp8: the key scales first,
@@ -184,34 +187,41 @@ __global__ __launch_bounds__(64) void index_decode_kernel(
 #pragma unroll
   for (int st = 0; st < St::kBufs; ++st) issue(st);
 
-  float sc_keep[NSTAGE][SBLK];
+  // Query rows and head weights: they were issued before every stage load,
+  // so they have landed once no more than the stage loads are outstanding.
+  wait_vmcnt(St::kBufs * NL);
+  __builtin_amdgcn_sched_barrier(0);
+  bf16x8 qa[KS];
+  float wr[16];
 #pragma unroll
-  for (int st = 0; st < NSTAGE; ++st) {
+  for (int s = 0; s < KS; ++s)
+    qa[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qw_lds + 1024 * s + 16 * l));
+  {
+    const uint32_t* wl = reinterpret_cast<const uint32_t*>(qw_lds + 1024 * KS);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int hr = 8 * (r >> 2) + 4 * g + (r & 3);
+      const int64_t we = (int64_t)b * w_ld + min(hr, H_I - 1);
+      const uint32_t v = wl[min(hr, H_I - 1)] >> (16 * (int)(we & 1));
+      wr[r] = hr < H_I ? bf16_to_f32((uint16_t)v) : 0.f;
+    }
+  }
+
+  float* const out_row = scores + (int64_t)b * ld + j0;
+  // Score one stage.  `later` (a compile-time constant) is the number of
+  // stages issued after this one that are still in flight.  Scores go to
+  // global memory and, for the report, to LDS.
+  auto do_stage = [&](int st, auto later_c) {
+    constexpr int later = decltype(later_c)::value;
     const uint8_t* buf = stage + (st % St::kBufs) * St::kBufBytes;
-    // stages issued after this one and still in flight
-    const int later = min(St::kBufs - 1, NSTAGE - 1 - st);
 #pragma unroll
     for (int bl = 0; bl < SBLK; ++bl) {
       // the scales and blocks 0..bl of this stage have landed once at most
       // this many loads are outstanding
-      const int allow = NI - IPB * (bl + 1);
-      wait_vmcnt(allow + later * NL);
+      wait_vmcnt(NI - IPB * (bl + 1) + later * NL);
       // keep the scheduler from hoisting consumers of loaded registers above
       // the wait (the compiler would then wait for every load instead)
       __builtin_amdgcn_sched_barrier(0);
-      if (st == 0 && bl == 0) {
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-          qa[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qw_lds + 1024 * s + 16 * l));
-        const uint32_t* wl = reinterpret_cast<const uint32_t*>(qw_lds + 1024 * KS);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int hr = 8 * (r >> 2) + 4 * g + (r & 3);
-          const int64_t we = (int64_t)b * w_ld + min(hr, H_I - 1);
-          const uint32_t v = wl[min(hr, H_I - 1)] >> (16 * (int)(we & 1));
-          wr[r] = hr < H_I ? bf16_to_f32((uint16_t)v) : 0.f;
-        }
-      }
       const int R = 32 * bl + (l & 31);  // stage row of this lane's key
       u32x4 kv[NLD];
 #pragma unroll
@@ -232,38 +242,45 @@ __global__ __launch_bounds__(64) void index_decode_kernel(
       float sl = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) sl += wr[r] * fmaxf(sig * acc[r], 0.f);
-      sc_keep[st][bl] = xor32_add(sl);
+      sl = xor32_add(sl);
+      // kept in LDS (the query rows there are in registers by now; LDS
+      // operations of one wave are processed in order).  Global stores wait
+      // for the end: a store in flight would count against the loads' waits.
+      if (g == 0) sc_lds[st * SROWS + R] = sl;
     }
-    if (st + St::kBufs < NSTAGE) {
+  };
+  // steady state: kBufs - 1 later stages in flight; the loop body is one
+  // stage, so code size does not grow with the tile
+  constexpr int NB = St::kBufs;
+#pragma unroll 1
+  for (int st = 0; st < NSTAGE - (NB - 1); ++st) {
+    do_stage(st, std::integral_constant<int, NB - 1>{});
+    if (st + NB < NSTAGE) {
       // every operand read of this buffer has returned (the MFMAs consumed
-      // them); refill it with stage st + kBufs
+      // them); refill it with stage st + NB
       __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
-      issue(st + St::kBufs);
+      issue(st + NB);
     }
   }
-  // scores of 32-key block k (tile order) live in sc_keep, lanes 0..31 (and 32..63)
+  // drain: the last NB - 1 stages, with fewer and fewer later stages
+  if constexpr (NB >= 4) do_stage(NSTAGE - 3, std::integral_constant<int, 2>{});
+  if constexpr (NB >= 3) do_stage(NSTAGE - 2, std::integral_constant<int, 1>{});
+  if constexpr (NB >= 2) do_stage(NSTAGE - 1, std::integral_constant<int, 0>{});
+  // value i of lane l is tile element 64i + l: coalesced stores, and the
+  // report's registers
+  uint32_t uv[V];
+  int32_t jv[V];
+  bool vv[V];
 #pragma unroll
-  for (int st = 0; st < NSTAGE; ++st)
-#pragma unroll
-    for (int bl = 0; bl < SBLK; ++bl) {
-      const int jr = st * SROWS + 32 * bl + (l & 31);
-      if (g == 0 && jr < n_valid) scores[(int64_t)b * ld + j0 + jr] = sc_keep[st][bl];
-    }
+  for (int i = 0; i < V; ++i) {
+    const int jl = 64 * i + l;
+    const float sc = sc_lds[jl];
+    vv[i] = jl < n_valid;
+    if (vv[i]) out_row[jl] = sc;
+    uv[i] = order_key(sc);
+    jv[i] = (int32_t)(j0 + jl);
+  }
   if constexpr (REPORT) {
-    // report value i of lane l is tile element 64i + l: block 2i (lanes < 32)
-    // or block 2i+1 (lanes >= 32), both already in this lane's registers
-    uint32_t uv[V];
-    int32_t jv[V];
-    bool vv[V];
-#pragma unroll
-    for (int i = 0; i < V; ++i) {
-      const int k0 = 2 * i, k1 = 2 * i + 1;
-      const float s0 = sc_keep[k0 / SBLK][k0 % SBLK], s1 = sc_keep[k1 / SBLK][k1 % SBLK];
-      const int jl = 64 * i + l;
-      vv[i] = jl < n_valid;
-      uv[i] = order_key(g == 0 ? s0 : s1);
-      jv[i] = (int32_t)(j0 + jl);
-    }
     const int64_t slot = (int64_t)b * ntiles_max + ti;
     wave_tile_report<V>(uv, jv, vv, hdr + slot, rep_u + slot * kRep, rep_j + slot * kRep);
   }

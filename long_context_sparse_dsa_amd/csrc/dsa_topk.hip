@@ -27,7 +27,6 @@ namespace dsa {
 constexpr int kResolveThreads = 1024;
 constexpr int kResolveTiles = 1024;                         // tiles in the fast path
 constexpr int kSlots = kResolveTiles * kRep / kResolveThreads;  // report slots per thread (16)
-constexpr int kBruteMax = 64;   // boundary-bin elements ranked in wave 0's registers
 
 template <int TILE>
 __global__ __launch_bounds__(64) void tile_report_kernel(const float* __restrict__ scores,
@@ -60,43 +59,55 @@ __global__ __launch_bounds__(64) void tile_report_kernel(const float* __restrict
 // ---------------------------------------------------------------------------
 // Radix select helpers for the resolve kernel (1024 threads, 2048 bins).
 // ---------------------------------------------------------------------------
+constexpr int kBucketMax = 64;  // boundary-bucket size ranked directly by wave 0
+
 struct ResolveSmem {
   int32_t stage[4096];  // selected positions before the coalesced store (K <= 4096)
   uint32_t hist[2048];
-  uint32_t bu[kBruteMax];
-  int32_t bj[kBruteMax];
+  uint32_t hist2[2048];  // the union select alternates between hist and hist2
+  uint32_t bu[kBucketMax];
+  int32_t bj[kBucketMax];
+  // per tile: worst reported (key, position | complete << 31), kept for the
+  // certification so the headers need not stay in registers
+  uint32_t wu[kResolveTiles];
+  uint32_t wj[kResolveTiles];
   uint32_t red[64];
   uint32_t scan[20];
   uint32_t st[8];
 };
 
-// Given hist[2048] of the current bucket and `above` elements strictly above
-// it, find digit d with above+gt(d) < k <= above+gt(d)+hist[d].  Writes
-// st[0] = d, st[1] = above + gt(d).  Every thread calls it; ends with a
-// barrier.  Thread tid owns the 2048/blockDim.x consecutive digits from
-// tid*(2048/blockDim.x).
-__device__ void find_digit(ResolveSmem& sm, uint32_t above, uint32_t k) {
-  constexpr int PER = 2048 / kResolveThreads;
-  const int tid = threadIdx.x;
-  uint32_t hv[PER];
+// Wave 0 of the block: given the 2048-bin histogram h of the current
+// bucket and `above` elements strictly above the bucket, find digit d with
+// above + gt(d) < k <= above + gt(d) + h[d] (gt(d): elements in digits > d).
+// Writes st[0] = d, st[1] = above + gt(d), st[5] = h[d].  Lane l owns bins
+// 32 l .. 32 l + 31: it sums them (chunk reads in a lane-rotated order, so
+// fewer lanes share a bank), one wave scan finds the lane holding d, and
+// that lane alone walks its bins.
+__device__ void wave_find_digit(ResolveSmem& sm, const uint32_t* h, uint32_t above, uint32_t k) {
+  const int l = lane_id();
   uint32_t mine = 0;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    hv[i] = sm.hist[PER * tid + i];
-    mine += hv[i];
+  for (int c = 0; c < 8; ++c) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(h + 32 * l + 4 * ((c + l) & 7));
+    mine += v[0] + v[1] + v[2] + v[3];
   }
-  uint32_t tot;
-  const uint32_t excl = block_excl_scan(mine, sm.scan, &tot);
-  uint32_t gt = tot - excl - mine;  // above this thread's last digit
+  const uint32_t incl = wave_incl_scan(mine);
+  const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+  uint32_t gt = total - incl;  // elements in the bins of higher lanes
+  if (above + gt < k && above + gt + mine >= k) {
+    for (int c = 7; c >= 0; --c) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(h + 32 * l + 4 * c);
 #pragma unroll
-  for (int i = PER - 1; i >= 0; --i) {
-    if (above + gt < k && above + gt + hv[i] >= k) {
-      sm.st[0] = PER * tid + i;
-      sm.st[1] = above + gt;
+      for (int i = 3; i >= 0; --i) {
+        if (above + gt < k && above + gt + v[i] >= k) {
+          sm.st[0] = 32 * l + 4 * c + i;
+          sm.st[1] = above + gt;
+          sm.st[5] = v[i];
+        }
+        gt += v[i];
+      }
     }
-    gt += hv[i];
   }
-  lds_barrier();
 }
 
 // Exact threshold (tau_u, tau_j) over an array source; `get(i, &u, &j)`
@@ -119,7 +130,8 @@ __device__ void exact_threshold(ResolveSmem& sm, int64_t n, uint32_t k, Get get)
       if (in) atomicAdd(&sm.hist[(u >> sh) & masks[pass]], 1u);
     }
     lds_barrier();
-    find_digit(sm, above, k);
+    if (wave_id() == 0) wave_find_digit(sm, sm.hist, above, k);
+    lds_barrier();
     const uint32_t d = sm.st[0];
     above = sm.st[1];
     prefix = pass == 0 ? d : (pass == 1 ? ((prefix << 11) | d) : ((prefix << 10) | d));
@@ -164,9 +176,10 @@ struct UnionRegs {
 __device__ __forceinline__ int slot_index(int wv, int q, int l) { return 1024 * wv + 256 * q + 4 * l; }
 
 // Exclusive position-ordered prefix of per-slot flags (bitmask, bit 4q+e);
-// returns each slot's rank among flagged slots and the total.
+// returns each slot's rank among flagged slots and the total.  Also ORs the
+// per-thread flag `bad` over the block into *any_bad (same exchange).
 __device__ void ordered_ranks(ResolveSmem& sm, uint32_t fmask, uint32_t (&rank)[kSlots],
-                              uint32_t* total) {
+                              uint32_t* total, bool bad = false, bool* any_bad = nullptr) {
   const int l = lane_id(), wv = wave_id(), nw = blockDim.x >> 6;
   uint32_t lane_ex[kQN], qoff[kQN];
   uint32_t woff = 0;
@@ -178,12 +191,17 @@ __device__ void ordered_ranks(ResolveSmem& sm, uint32_t fmask, uint32_t (&rank)[
     qoff[q] = woff;
     woff += (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
   }
-  if (l == 0) sm.red[wv] = woff;
+  const bool wbad = __ballot(bad) != 0;
+  if (l == 0) {
+    sm.red[wv] = woff;
+    sm.red[32 + wv] = wbad ? 1u : 0u;
+  }
   lds_barrier();
   const uint32_t wt = l < nw ? sm.red[l] : 0u;
   const uint32_t wi = wave_incl_scan(wt);
   const uint32_t wbase = (uint32_t)__builtin_amdgcn_readlane((int)(wi - wt), wv);
   *total = (uint32_t)__builtin_amdgcn_readlane((int)wi, 63);
+  if (any_bad) *any_bad = __ballot(l < nw && sm.red[32 + l] != 0u) != 0;
 #pragma unroll
   for (int q = 0; q < kQN; ++q) {
     const uint32_t r = wbase + qoff[q] + lane_ex[q];
@@ -197,34 +215,18 @@ __device__ void ordered_ranks(ResolveSmem& sm, uint32_t fmask, uint32_t (&rank)[
 }
 
 // Exact K-th best candidate of the union: selected <=> key > tau_u, or
-// key == tau_u and position <= tau_j.  Radix digits are taken relative to
-// the union's key range, so the 2048 bins spread the candidates instead of
-// piling them onto the few bins the leading exponent bits would give;
-// refinement stops once the boundary bin holds at most kBruteMax elements,
-// which wave 0 then ranks in registers.
-__device__ void union_threshold(ResolveSmem& sm, const UnionRegs& R, uint32_t k, uint32_t* tau_u,
-                                int32_t* tau_j) {
-  const int tid = threadIdx.x, nt = blockDim.x, l = lane_id(), wv = wave_id();
-  uint32_t mn = 0xffffffffu, mx = 0u;
-#pragma unroll
-  for (int i = 0; i < kSlots; ++i) {
-    const bool vi = (R.vmask >> i) & 1u;
-    mn = min(mn, vi ? R.u[i] : 0xffffffffu);
-    mx = max(mx, vi ? R.u[i] : 0u);
-  }
-  mn = wave_min_u32(mn);
-  mx = wave_max_u32(mx);
-  if (l == 0) {
-    sm.red[wv] = mn;
-    sm.red[32 + wv] = mx;
-  }
-  for (int i = tid; i < 2048; i += nt) sm.hist[i] = 0;
-  lds_barrier();
-  {
-    const int nw = nt >> 6;
-    mn = wave_min_u32(l < nw ? sm.red[l] : 0xffffffffu);
-    mx = wave_max_u32(l < nw ? sm.red[32 + l] : 0u);
-  }
+// key == tau_u and position <= tau_j.  Radix digits (11, 11, 10 bits) are
+// taken relative to the union's key range [mn, mx], so the first pass
+// spreads the candidates over the 2048 bins instead of piling them onto the
+// few bins the leading exponent bits would give.  Each pass is one LDS
+// histogram and one wave-0 digit search (the other waves clear the other
+// histogram meanwhile).  As soon as the boundary bucket holds at most
+// kBucketMax candidates they are gathered and wave 0 ranks them directly
+// under (key desc, position asc), which gives (tau_u, tau_j) at once.  Both
+// histograms are zero and st[4] is 0 on entry.
+__device__ void union_threshold(ResolveSmem& sm, const UnionRegs& R, uint32_t k, uint32_t mn,
+                                uint32_t mx, uint32_t* tau_u, int32_t* tau_j) {
+  const int tid = threadIdx.x, nt = blockDim.x, wv = wave_id(), l = lane_id();
   const uint32_t range = mx - mn;
   // bucket = keys in [lo, lo + width); digits (key - lo) >> shift are < 2048
   int shift = range == 0 ? 0 : max(0, 32 - __clz(range) - 11);
@@ -232,94 +234,100 @@ __device__ void union_threshold(ResolveSmem& sm, const UnionRegs& R, uint32_t k,
   uint64_t width = (uint64_t)range + 1;
   uint32_t above = 0;  // candidates strictly above the bucket
   uint32_t h = 0;      // candidates in the bucket
-  uint32_t inb = 0;    // bucket membership bitmask
+  int pass = 0;
   while (true) {
-    inb = 0;
+    uint32_t* hc = (pass & 1) ? sm.hist2 : sm.hist;
+    uint32_t* hn = (pass & 1) ? sm.hist : sm.hist2;
+#pragma unroll
+    for (int i = 0; i < kSlots; ++i) {
+      const uint32_t x = R.u[i];
+      const bool in = ((R.vmask >> i) & 1u) && x >= lo && (uint64_t)(x - lo) < width;
+      if (in) atomicAdd(&hc[(x - lo) >> shift], 1u);
+    }
+    lds_barrier();
+    if (wv == 0) {
+      wave_find_digit(sm, hc, above, k);
+    } else {
+      for (int i = tid - 64; i < 2048; i += nt - 64) hn[i] = 0;  // next pass's histogram
+    }
+    lds_barrier();
+    const uint32_t d = sm.st[0];
+    above = sm.st[1];
+    h = sm.st[5];
+    const uint64_t off = (uint64_t)d << shift;
+    lo += (uint32_t)off;
+    width = min<uint64_t>(width - off, 1ull << shift);
+    if (shift == 0 || h <= (uint32_t)kBucketMax) break;
+    shift = max(0, shift - 11);
+    ++pass;
+  }
+  const uint32_t need = k - above;  // 1..h: the need-th best of the bucket is theta
+  if (h <= (uint32_t)kBucketMax) {
+    // gather the bucket: per-wave ballot compaction at a base taken with
+    // one LDS atomic per wave
+    uint32_t inb = 0, cnt = 0;
 #pragma unroll
     for (int i = 0; i < kSlots; ++i) {
       const uint32_t x = R.u[i];
       const bool in = ((R.vmask >> i) & 1u) && x >= lo && (uint64_t)(x - lo) < width;
       inb |= (uint32_t)in << i;
-      if (in) atomicAdd(&sm.hist[(x - lo) >> shift], 1u);
+      cnt += popc64(__ballot(in));
     }
-    lds_barrier();
-    find_digit(sm, above, k);  // ends with a barrier
-    const uint32_t d = sm.st[0];
-    above = sm.st[1];
-    h = sm.hist[d];
-    lds_barrier();
-    const uint64_t off = (uint64_t)d << shift;
-    lo += (uint32_t)off;
-    width = min<uint64_t>(width - off, 1ull << shift);
-    if (h <= (uint32_t)kBruteMax || shift == 0) break;
-    shift = max(0, shift - 11);
-    for (int i = tid; i < 2048; i += nt) sm.hist[i] = 0;
-    lds_barrier();
-  }
-  // final bucket membership
-  inb = 0;
+    if (cnt) {
+      uint32_t base = 0;
+      if (l == 0) base = atomicAdd(&sm.st[4], cnt);
+      base = (uint32_t)__builtin_amdgcn_readlane((int)base, 0);
+      const uint64_t below = lanes_below();
 #pragma unroll
-  for (int i = 0; i < kSlots; ++i) {
-    const uint32_t x = R.u[i];
-    inb |= (uint32_t)(((R.vmask >> i) & 1u) && x >= lo && (uint64_t)(x - lo) < width) << i;
-  }
-  const uint32_t need = k - above;  // 1..h
-  if (h <= (uint32_t)kBruteMax) {
-    if (tid == 0) sm.st[4] = 0;
-    lds_barrier();
-    if (inb) {
-      uint32_t m = inb;
-      uint32_t slot = atomicAdd(&sm.st[4], (uint32_t)__popc(m));
-      while (m) {
-        const int i = __ffs(m) - 1;
-        m &= m - 1;
-        // dynamic index into registers is avoided by a select chain
-        uint32_t x = 0;
-        int32_t y = 0;
-#pragma unroll
-        for (int e = 0; e < kSlots; ++e)
-          if (e == i) {
-            x = R.u[e];
-            y = R.j[e];
-          }
-        sm.bu[slot] = x;
-        sm.bj[slot] = y;
-        ++slot;
+      for (int i = 0; i < kSlots; ++i) {
+        const bool in = (inb >> i) & 1u;
+        const uint64_t m = __ballot(in);
+        if (in) {
+          const uint32_t pos = base + popc64(m & below);
+          sm.bu[pos] = R.u[i];
+          sm.bj[pos] = R.j[i];
+        }
+        base += popc64(m);
       }
     }
     lds_barrier();
     if (wv == 0) {
-      const uint32_t ui = (uint32_t)l < h ? sm.bu[l] : 0u;
-      const int32_t ji = (uint32_t)l < h ? sm.bj[l] : 0;
+      const bool mine_ok = (uint32_t)l < h;
+      const uint32_t um = mine_ok ? sm.bu[l] : 0u;
+      const int32_t jm = mine_ok ? sm.bj[l] : 0;
       uint32_t rank = 0;
       for (uint32_t q = 0; q < h; ++q) {
-        const uint32_t uq = (uint32_t)__builtin_amdgcn_readlane((int)ui, (int)q);
-        const int32_t jq = __builtin_amdgcn_readlane(ji, (int)q);
-        rank += (uq > ui) || (uq == ui && jq < ji);
+        const uint32_t uq = sm.bu[q];
+        const int32_t jq = sm.bj[q];
+        rank += (uq > um) || (uq == um && jq < jm);
       }
-      if ((uint32_t)l < h && rank == need - 1) {
-        sm.st[2] = ui;
-        sm.st[3] = (uint32_t)ji;
+      if (mine_ok && rank == need - 1) {
+        sm.st[2] = um;
+        sm.st[3] = (uint32_t)jm;
       }
     }
     lds_barrier();
-  } else {
-    // one key shared by more than kBruteMax candidates: cut by position
-    uint32_t rk[kSlots], tot;
-    ordered_ranks(sm, inb, rk, &tot);
-    if (tid == 0) {
-      sm.st[2] = lo;
-      sm.st[3] = 0x7fffffffu;
-    }
-    lds_barrier();
-    if (need < tot) {
-#pragma unroll
-      for (int i = 0; i < kSlots; ++i)
-        if (((inb >> i) & 1u) && rk[i] == need - 1) sm.st[3] = (uint32_t)R.j[i];
-    }
-    lds_barrier();
+    *tau_u = sm.st[2];
+    *tau_j = (int32_t)sm.st[3];
+    return;
   }
-  *tau_u = sm.st[2];
+  // more than kBucketMax candidates share the single key lo: the need
+  // lowest positions among them are selected
+  *tau_u = lo;
+  uint32_t inb = 0;
+#pragma unroll
+  for (int i = 0; i < kSlots; ++i)
+    inb |= (uint32_t)(((R.vmask >> i) & 1u) && R.u[i] == lo) << i;
+  uint32_t rk[kSlots], tot;
+  ordered_ranks(sm, inb, rk, &tot);
+  if (tid == 0) sm.st[3] = 0x7fffffffu;
+  lds_barrier();
+  if (need < tot) {
+#pragma unroll
+    for (int i = 0; i < kSlots; ++i)
+      if (((inb >> i) & 1u) && rk[i] == need - 1) sm.st[3] = (uint32_t)R.j[i];
+  }
+  lds_barrier();
   *tau_j = (int32_t)sm.st[3];
 }
 
@@ -372,47 +380,69 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(
     // slots sub .. sub+3 of the tile are valid while below its count
     const uint32_t nv = tile_ok ? (cnt > sub ? min(cnt - sub, 4u) : 0u) : 0u;
     R.vmask |= ((1u << nv) - 1u) << (4 * q);
+    if (sub == 0 && sidx < nslots) {
+      sm.wu[sidx / kRep] = hq[q].worst_u;
+      sm.wj[sidx / kRep] = (uint32_t)hq[q].worst_j | (hq[q].complete ? 0x80000000u : 0u);
+    }
   }
   bool ok = false;
   if (ntiles <= kResolveTiles && ntiles <= ntiles_max) {
-    const uint32_t tot = wave_sum_u32((uint32_t)__popc(R.vmask));
-    if (l == 0) sm.red[wv] = tot;
+    // candidate count and key range of the union, in one block reduction;
+    // both histograms are cleared meanwhile
+    uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+    for (int i = 0; i < kSlots; ++i) {
+      const bool vi = (R.vmask >> i) & 1u;
+      mn = min(mn, vi ? R.u[i] : 0xffffffffu);
+      mx = max(mx, vi ? R.u[i] : 0u);
+    }
+    const uint32_t cw = wave_sum_u32((uint32_t)__popc(R.vmask));
+    mn = wave_min_u32(mn);
+    mx = wave_max_u32(mx);
+    if (l == 0) {
+      sm.red[wv] = cw;
+      sm.red[16 + wv] = mn;
+      sm.red[32 + wv] = mx;
+    }
+    for (int i = tid; i < 2048; i += nt) {
+      sm.hist[i] = 0;
+      sm.hist2[i] = 0;
+    }
+    if (tid == 0) sm.st[4] = 0;
     lds_barrier();
-    uint32_t C = 0;
+    uint32_t C;
     {
       const int nw = nt >> 6;
       C = wave_sum_u32(l < nw ? sm.red[l] : 0u);
+      mn = wave_min_u32(l < nw ? sm.red[16 + l] : 0xffffffffu);
+      mx = wave_max_u32(l < nw ? sm.red[32 + l] : 0u);
     }
-    lds_barrier();
+    lds_barrier();  // red[] is reused below
     if (C >= k) {
       uint32_t tau_u;
       int32_t tau_j;
-      union_threshold(sm, R, k, &tau_u, &tau_j);
-      // ---- certification: every partly reported tile ends at or below theta ----
+      union_threshold(sm, R, k, mn, mx, &tau_u, &tau_j);
+      // ---- certification: every partly reported tile ends at or below
+      // theta (checked in the same block exchange as the ranks) ----
       bool bad = false;
-#pragma unroll
-      for (int q = 0; q < kQN; ++q) {
-        const int sidx = slot_index(wv, q, l);
-        const RepHeader& h = hq[q];
-        if (sidx % kRep == 0 && sidx < nslots && sidx / kRep < ntiles && !h.complete &&
-            !((h.worst_u < tau_u) || (h.worst_u == tau_u && h.worst_j >= tau_j)))
-          bad = true;
+      if (tid < ntiles) {
+        const uint32_t wu = sm.wu[tid], wj = sm.wj[tid];
+        const bool complete = wj >> 31;
+        const int32_t wpos = (int32_t)(wj & 0x7fffffffu);
+        bad = !complete && !((wu < tau_u) || (wu == tau_u && wpos >= tau_j));
       }
-      if (tid == 0) sm.st[7] = 0;
-      lds_barrier();
-      if (bad) sm.st[7] = 1;
-      lds_barrier();
-      ok = sm.st[7] == 0;
-      if (ok) {
-        uint32_t smask = 0;
+      uint32_t smask = 0;
 #pragma unroll
-        for (int i = 0; i < kSlots; ++i) {
-          const bool si = ((R.vmask >> i) & 1u) &&
-                          ((R.u[i] > tau_u) || (R.u[i] == tau_u && R.j[i] <= tau_j));
-          smask |= (uint32_t)si << i;
-        }
-        uint32_t rk[kSlots], total;
-        ordered_ranks(sm, smask, rk, &total);
+      for (int i = 0; i < kSlots; ++i) {
+        const bool si = ((R.vmask >> i) & 1u) &&
+                        ((R.u[i] > tau_u) || (R.u[i] == tau_u && R.j[i] <= tau_j));
+        smask |= (uint32_t)si << i;
+      }
+      uint32_t rk[kSlots], total;
+      bool any_bad = false;
+      ordered_ranks(sm, smask, rk, &total, bad, &any_bad);
+      ok = !any_bad;
+      if (ok) {
         // stage in LDS, then store coalesced
 #pragma unroll
         for (int i = 0; i < kSlots; ++i)
@@ -513,7 +543,10 @@ hipError_t launch_tile_reports(const float* scores, int64_t ld, const int32_t* c
 hipError_t launch_topk_resolve(const float* scores, int64_t ld, const int32_t* cu_q,
                                const int32_t* ctx_len, int B, int T, int K, const TopkWs& w,
                                int32_t* idx, uint32_t* stats, hipStream_t stream) {
-  hipLaunchKernelGGL(topk_resolve_kernel, dim3(T), dim3(kResolveThreads), 0, stream, scores, ld,
+  // one thread per tile (16 report slots each), 64 .. 1024 threads
+  int nt = ((w.ntiles_max + 63) / 64) * 64;
+  nt = nt < 64 ? 64 : (nt > kResolveThreads ? kResolveThreads : nt);
+  hipLaunchKernelGGL(topk_resolve_kernel, dim3(T), dim3(nt), 0, stream, scores, ld,
                      cu_q, ctx_len, B, K, w.tile, w.ntiles_max, w.hdr, w.rep_u, w.rep_j, idx,
                      stats);
   return hipGetLastError();

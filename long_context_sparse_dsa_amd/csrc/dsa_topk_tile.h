@@ -60,14 +60,24 @@ __device__ void wave_tile_report(const uint32_t (&u)[V], const int32_t (&j)[V],
         mn = min(mn, u[i]);
         mx = max(mx, u[i]);
       }
-    // largest T with count(key >= T) >= kRep: the kRep-th best key
+    // largest T with count(key >= T) >= kRep: the kRep-th best key.  Every
+    // probe is >= 1, so invalid slots count as key 0 and drop out.  The
+    // search stops early once a probe has exactly kRep keys at or above it:
+    // that probe selects the same kRep elements.
+    uint32_t uz[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) uz[i] = valid[i] ? u[i] : 0u;
     uint32_t lo = wave_min_u32(mn), hi = wave_max_u32(mx);
     while (lo < hi) {
       const uint32_t mid = lo + ((hi - lo) >> 1) + 1;  // in (lo, hi]
       uint32_t c = 0;
 #pragma unroll
-      for (int i = 0; i < V; ++i) c += popc64(__ballot(valid[i] && u[i] >= mid));
-      if (c >= (uint32_t)kRep) lo = mid; else hi = mid - 1;
+      for (int i = 0; i < V; ++i) c += popc64(__ballot(uz[i] >= mid));
+      if (c == (uint32_t)kRep) {
+        lo = mid;
+        break;
+      }
+      if (c > (uint32_t)kRep) lo = mid; else hi = mid - 1;
     }
     const uint32_t T = lo;
     uint32_t gt = 0;

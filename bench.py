@@ -8,33 +8,105 @@ are resident in HBM before timing starts; the step rotates over
 `--rotate` distinct layer buffer sets so that every step streams its key
 cache from HBM rather than from the 256 MiB Infinity Cache.
 
-Prints one JSON line (rank 0) with the throughput, the roofline of the
-dominant kernel (the indexer's stream of the key cache, timed live with HIP
-events on the stream it runs on) and the CPU oracle's throughput on a
+Prints one JSON line with the throughput, the roofline of the dominant
+kernel (the indexer's stream of the key cache, timed live inside the timed
+steps with HIP events attached to that kernel's dispatch on the stream it
+runs on, see dsa_set_indexer_events) and the CPU oracle's throughput on a
 bounded sample of the same workload.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_decode_ctx131072_traffic.md")
+# sources of the timed indexer kernel: a traffic figure measured on other
+# sources is stale
+KERNEL_SOURCES = ["long_context_sparse_dsa_amd/csrc/dsa_indexer.hip",
+                  "long_context_sparse_dsa_amd/csrc/dsa_topk_tile.h",
+                  "long_context_sparse_dsa_amd/csrc/dsa_device.h"]
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--rotate", type=int, default=16, help="distinct layer buffer sets")
+    ap.add_argument("--workload", default="dec128k",
+                    choices=["dec128k", "dec1m_b32_fp8", "prefill8k"],
+                    help="dec128k (default, the headline metric); the others time the "
+                         "same path on the batched 1M-context fp8 decode and on the 8K "
+                         "prefill chunk")
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--rotate", type=int, default=None, help="distinct layer buffer sets")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-time budget of the CPU oracle sample (0: skip)")
-    ap.add_argument("--traffic-json", default=os.path.join(os.path.dirname(
-        os.path.abspath(__file__)), "profiles", "indexer_decode_ctx131072_traffic.json"))
-    return ap.parse_args()
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="before timing, copy a buffer of this many MiB once (a reference "
+                         "kernel of known traffic for hardware-counter runs)")
+    a = ap.parse_args()
+    dflt = {"dec128k": (200, 20, 16), "dec1m_b32_fp8": (20, 3, 1), "prefill8k": (5, 1, 1)}
+    st, wu, rot = dflt[a.workload]
+    a.steps = a.steps if a.steps is not None else st
+    a.warmup = a.warmup if a.warmup is not None else wu
+    a.rotate = a.rotate if a.rotate is not None else rot
+    return a
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """Bytes per indexer launch from the committed counter summary, if it was
+    taken on the current kernel sources (else None)."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    m = re.search(r"source_hash:\s*([0-9a-f]+)", text)
+    b = re.search(r"bytes_per_launch:\s*([0-9]+)", text)
+    if not m or not b or m.group(1) != kernel_source_hash():
+        return None
+    return int(b.group(1))
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return ev.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a),
+                                        ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, e):
+        self.hip.hipEventDestroy(ctypes.c_void_p(e))
 
 
 def main():
@@ -49,15 +121,30 @@ def main():
     from long_context_sparse_dsa_amd import workloads as W
 
     dsa.load()
-    dev = "cuda"
     torch.cuda.set_device(0)
-    wl = W.decode_128k()
-    L = wl.ctx_lens[0]
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    if args.workload == "prefill8k":
+        result = bench_prefill(args, torch, dsa, W)
+    else:
+        result = bench_decode(args, torch, dsa, W)
+    print(json.dumps(result), flush=True)
+
+
+def bench_decode(args, torch, dsa, W):
+    dev = "cuda"
+    wl = W.decode_128k() if args.workload == "dec128k" else W.decode_1m_b32_fp8()
+    L = max(wl.ctx_lens)
     sets = [W.make_inputs(wl, device=dev, seed_offset=i) for i in range(args.rotate)]
     ws = torch.empty(dsa.dsa_layer_decode_workspace_size(wl.B, L, wl.K, wl.Hq, wl.D),
                      dtype=torch.uint8, device=dev)
     outs = [torch.empty_like(s["q"]) for s in sets]
-    scores = torch.empty(wl.B, L, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
     # one marshalled C-ABI call per buffer set: the timed loop issues
@@ -66,48 +153,49 @@ def main():
                                       s["k_cache"], s["v_cache"], s["gate"], wl.K, s["ctx_len"],
                                       s["cu_ctx"], L, outs[i], ws)
              for i, s in enumerate(sets)]
+    hip = HipEvents()
+    ev = [(hip.create(), hip.create()) for _ in range(args.steps)]
+    set_events = dsa.load().dsa_set_indexer_events
+    rot = [args.rotate]
 
-    def step(i):
-        calls[i % args.rotate]()
-
-    def indexer(i):
-        s = sets[i % args.rotate]
-        dsa.dsa_index_scores(s["q_idx"], s["w"], s["k_idx"], s["k_scale"], s["ctx_len"],
-                             s["cu_ctx"], max_ctx=L, scores=scores)
-
-    def timed(fn, n, warm):
+    def timed(n, warm, with_events):
         for i in range(warm):
-            fn(i)
+            calls[i % rot[0]]()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
         for i in range(n):
-            fn(i)
+            if with_events:
+                set_events(ctypes.c_void_p(ev[i][0]), ctypes.c_void_p(ev[i][1]))
+            calls[i % rot[0]]()
         e1.record()
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n   # ms per call
+        set_events(None, None)
+        return e0.elapsed_time(e1) / n   # ms per step
 
     # ---- the timed region: K layer steps, inputs resident in HBM ----
-    ms = timed(step, args.steps, args.warmup)
+    ms = timed(args.steps, args.warmup, False)
     tok_s = wl.B / (ms * 1e-3)
+    # ---- the same K steps again, the indexer kernel of each step recording
+    # its own start / end events (attached to its dispatch); kept out of
+    # the headline figure, which the extra event packets would slow ----
+    timed(args.steps, 0, True)
+    idx_ms = [hip.elapsed_ms(a, b) for a, b in ev]
+    ms_idx = sum(idx_ms) / len(idx_ms)
+    for a, b in ev:
+        hip.destroy(a)
+        hip.destroy(b)
     # warm-cache figure (same buffer set every step), reported for context
-    rot = args.rotate
-    ms_warm = timed(lambda i: calls[0](), args.steps, args.warmup)
-    # ---- dominant kernel: indexer stream of the key cache, cold ----
-    ms_idx = timed(indexer, args.steps, args.warmup)
-    key_bytes = L * wl.d_I * 2
-    idx_bytes = key_bytes + wl.H_I * wl.d_I * 2 + wl.H_I * 2     # keys + query heads + weights
-    achieved = idx_bytes / (ms_idx * 1e-3) / 1e9
-    layer_bytes = key_bytes + wl.K * 2 * wl.D * 2 + (wl.H_I * wl.d_I + wl.H_I) * 2 + \
-        3 * wl.Hq * wl.D * 2
-    traffic = None
-    if os.path.exists(args.traffic_json):
-        try:
-            traffic = json.load(open(args.traffic_json)).get("bytes_per_launch")
-        except Exception:
-            traffic = None
+    rot[0] = 1
+    ms_warm = timed(args.steps, args.warmup, False)
 
+    fp8 = wl.key_dtype == "fp8"
+    key_bytes = sum(wl.ctx_lens) * (wl.d_I + 4 if fp8 else 2 * wl.d_I)   # keys (+ fp8 scales)
+    idx_bytes = key_bytes + wl.B * (wl.H_I * wl.d_I * 2 + wl.H_I * 2)   # + query heads, weights
+    achieved = idx_bytes / (ms_idx * 1e-3) / 1e9
+    layer_bytes = key_bytes + wl.B * (wl.K * 2 * wl.D * 2 + (wl.H_I * wl.d_I + wl.H_I) * 2 +
+                                      3 * wl.Hq * wl.D * 2)
     result = {
         "metric": "DSA layer decode tokens/s @128K ctx (indexer HBM GB/s, % roofline)",
         "value": round(tok_s, 1),
@@ -123,42 +211,148 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.B, "ctx": L, "indexer": f"{wl.H_I}x{wl.d_I}",
                    "topk": wl.K, "q_heads": wl.Hq, "kv_heads": 1, "head_dim": wl.D,
-                   "key_cache": "bf16", "planted_frac": wl.plant_frac,
-                   "rotated_buffer_sets": rot},
+                   "key_cache": wl.key_dtype, "planted_frac": wl.plant_frac,
+                   "rotated_buffer_sets": args.rotate},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "index_decode_kernel (key-cache stream)",
+                     "traffic": read_traffic() if args.workload == "dec128k" else None,
+                     "kernel": "index_decode_kernel (key-cache stream + Top-K tile reports)",
                      "kernel_us": round(ms_idx * 1e3, 3),
                      "algorithmic_bytes_per_launch": idx_bytes},
-        "layer_roofline": {"algorithmic_bytes_per_token": layer_bytes,
+        "layer_roofline": {"algorithmic_bytes_per_step": layer_bytes,
                            "frac_of_hbm_peak": round(layer_bytes / (ms * 1e-3) / 1e9 /
                                                      HBM_PEAK_GBS, 4)},
         "warm_cache": {"ms_per_step": round(ms_warm, 5),
                        "tokens_per_s": round(wl.B / (ms_warm * 1e-3), 1)},
     }
+    if args.workload != "dec128k":
+        result["metric"] = "DSA layer decode tokens/s (batched 1M-context fp8 decode)"
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(sets[0], wl, args.cpu_seconds)
-    print(json.dumps(result), flush=True)
+    return result
+
+
+def bench_prefill(args, torch, dsa, W):
+    """The 8K prefill chunk: tokens/s of dsa_layer_prefill, and the MFMA
+    roofline of its indexer (timed with HIP events around back-to-back
+    dsa_index_scores launches on the same stream)."""
+    wl = W.prefill_8k()
+    s = W.make_inputs(wl, device="cuda")
+    L = wl.ctx_lens[0]
+    ws = torch.empty(dsa.dsa_layer_prefill_workspace_size(wl.B, wl.T, L, wl.K, wl.Hq, wl.D),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(s["q"])
+
+    def layer():
+        dsa.dsa_layer_prefill(s["q_idx"], s["w"], s["k_idx"], s["k_scale"], s["q"], s["k_cache"],
+                              s["v_cache"], s["gate"], wl.K, s["cu_q"], s["ctx_len"], s["cu_ctx"],
+                              max_q=wl.T, max_ctx=L, out=out, ws=ws)
+
+    def timed(fn, n, warm):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    ms = timed(layer, args.steps, args.warmup)
+    del ws
+    torch.cuda.empty_cache()
+    scores = torch.empty(wl.T, L, dtype=torch.float32, device="cuda")
+
+    def indexer():
+        dsa.dsa_index_scores(s["q_idx"], s["w"], s["k_idx"], s["k_scale"], s["ctx_len"],
+                             s["cu_ctx"], cu_q=s["cu_q"], max_q=wl.T, max_ctx=L, scores=scores)
+
+    ms_idx = timed(indexer, args.steps, args.warmup)
+    p0 = L - wl.T
+    visible = sum(p0 + i + 1 for i in range(wl.T))
+    flops = visible * 2 * wl.H_I * wl.d_I
+    achieved = flops / (ms_idx * 1e-3) / 1e12
+    result = {
+        "metric": "DSA layer prefill tokens/s (8K chunk at 131K context; indexer MFMA TFLOP/s)",
+        "value": round(wl.T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "queries": wl.T, "ctx": L,
+                   "indexer": f"{wl.H_I}x{wl.d_I}", "topk": wl.K, "q_heads": wl.Hq,
+                   "head_dim": wl.D},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": 2500.0,
+                     "unit": "TFLOP/s", "frac": round(achieved / 2500.0, 4), "traffic": None,
+                     "kernel": "index_prefill_kernel", "kernel_us": round(ms_idx * 1e3, 1),
+                     "algorithmic_flops_per_launch": flops},
+    }
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline_prefill(s, wl, args.cpu_seconds)
+    return result
+
+
+def _host(s):
+    return {k: (v.cpu() if hasattr(v, "cpu") else v) for k, v in s.items()}
 
 
 def cpu_baseline(s, wl, budget):
-    """The fp64 oracle, untuned, on host cores: whole decode layer, repeated."""
+    """The fp64 oracle, untuned, on host cores: whole decode steps of the
+    first sequence of the batch, repeated for about `budget` seconds."""
+    import numpy as np
     import oracle
-    c = {k: (v.cpu() if hasattr(v, "cpu") else v) for k, v in s.items()}
+    c = _host(s)
+    L = wl.ctx_lens[0]
+    one = {"q_idx": c["q_idx"][:1], "w": c["w"][:1], "k_idx": c["k_idx"][:L],
+           "k_scale": None if c["k_scale"] is None else c["k_scale"][:L], "q": c["q"][:1],
+           "k_cache": c["k_cache"][:L], "v_cache": c["v_cache"][:L], "gate": c["gate"][:1]}
     n = oracle.default_threads()
     t0 = time.perf_counter()
     runs = 0
     while True:
-        oracle.layer(c["q_idx"], c["w"], c["k_idx"], c["k_scale"], c["q"], c["k_cache"],
-                     c["v_cache"], c["gate"], wl.K, c["ctx_len"].numpy(), nthreads=n)
+        oracle.layer(one["q_idx"], one["w"], one["k_idx"], one["k_scale"], one["q"],
+                     one["k_cache"], one["v_cache"], one["gate"], wl.K,
+                     np.array([L], dtype=np.int32), nthreads=n)
         runs += 1
         el = time.perf_counter() - t0
         if el >= budget or runs >= 200:
             break
-    return {"value": round(runs * wl.B / el, 3), "unit": "tokens/s", "cores": n,
-            "kind": "oracle",
-            "sample": f"{runs} full decode-layer steps of the same workload (ctx 131072) "
-                      f"in {el:.1f} s, fp64, {n} threads"}
+    return {"value": round(runs / el, 3), "unit": "tokens/s", "cores": n, "kind": "oracle",
+            "sample": f"{runs} whole decode-layer steps of one sequence (ctx {L}) in {el:.1f} s, "
+                      f"fp64, {n} threads"}
+
+
+def cpu_baseline_prefill(s, wl, budget):
+    """The oracle on the last queries of the chunk (the costliest), for about
+    `budget` seconds; tokens/s over the queries it finished."""
+    import numpy as np
+    import oracle
+    c = _host(s)
+    L = wl.ctx_lens[0]
+    n = oracle.default_threads()
+    t0 = time.perf_counter()
+    done = 0
+    while True:
+        i = wl.T - 1 - done
+        oracle.layer(c["q_idx"][i:i + 1], c["w"][i:i + 1], c["k_idx"], c["k_scale"],
+                     c["q"][i:i + 1], c["k_cache"], c["v_cache"], c["gate"][i:i + 1], wl.K,
+                     np.array([L - wl.T + i + 1], dtype=np.int32), nthreads=n)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= budget or done >= wl.T:
+            break
+    return {"value": round(done / el, 3), "unit": "tokens/s", "cores": n, "kind": "oracle",
+            "sample": f"the last {done} queries of the chunk, one decode-shaped oracle call each "
+                      f"(context up to {L}) in {el:.1f} s, fp64, {n} threads"}
 
 
 if __name__ == "__main__":

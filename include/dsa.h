@@ -158,8 +158,8 @@ dsa_status_t dsa_sparse_attn(const void* q, const void* k_cache, const void* v_c
 /* Steps 1 -> 2 -> 3 above on the caller's stream, with the step-1 kernel   */
 /* also emitting the per-tile candidate lists that step 2 certifies (the     */
 /* selection is still exact).  Arguments are those of the three steps;       */
-/* idx_out (int32 [B, K]) and scores_out (fp32 [B, ld]) are optional copies */
-/* of the intermediate results (NULL: kept in the workspace only).          */
+/* idx_out (int32 [B, K], or NULL) receives the selected positions, which   */
+/* otherwise stay in the workspace.                                          */
 /* ------------------------------------------------------------------------ */
 size_t dsa_layer_decode_workspace_size(int B, int max_ctx, int K, int Hq, int D);
 dsa_status_t dsa_layer_decode(const void* q_idx, const void* w, int64_t w_ld, const void* k_idx,
@@ -168,6 +168,15 @@ dsa_status_t dsa_layer_decode(const void* q_idx, const void* w, int64_t w_ld, co
                               float sm_scale, int Hq, int D, int K, const int32_t* ctx_len,
                               const int64_t* cu_ctx, int B, int max_ctx, void* out,
                               int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Measurement hook: on the calling thread, every later dsa_layer_decode    */
+/* call launches its step-1 indexer kernel with `start` and `stop` (both    */
+/* hipEvent_t) attached to the dispatch, which records them when that       */
+/* kernel starts and ends, so the caller can time it inside a running       */
+/* sequence of layer calls.  The events stay owned by the caller and must   */
+/* outlive their use; pass NULL, NULL to stop.                              */
+/* Returns DSA_ERR_INVALID_ARG if exactly one of them is NULL.               */
+dsa_status_t dsa_set_indexer_events(void* start, void* stop);
 
 /* ------------------------------------------------------------------------ */
 /* Whole layer, prefill: a chunk of new queries per sequence (cu_q given).   */

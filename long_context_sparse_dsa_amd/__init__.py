@@ -27,7 +27,7 @@ EXPORTS = [
     "dsa_index_scores",
     "dsa_topk_workspace_size", "dsa_topk",
     "dsa_sparse_attn_workspace_size", "dsa_sparse_attn",
-    "dsa_layer_decode_workspace_size", "dsa_layer_decode",
+    "dsa_layer_decode_workspace_size", "dsa_layer_decode", "dsa_set_indexer_events",
     "dsa_layer_prefill_workspace_size", "dsa_layer_prefill",
 ]
 
@@ -70,8 +70,9 @@ def load(path: str | None = None):
     lib.dsa_layer_prefill_workspace_size.restype = S
     lib.dsa_layer_prefill.argtypes = [P, P, L, P, I, P, I, I, P, P, P, P, F, I, I, I, P, P, P,
                                       I, I, I, I, P, P, P, S, P]
+    lib.dsa_set_indexer_events.argtypes = [P, P]
     for fn in ("dsa_index_scores", "dsa_topk", "dsa_sparse_attn", "dsa_layer_decode",
-               "dsa_layer_prefill"):
+               "dsa_layer_prefill", "dsa_set_indexer_events"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -284,6 +285,13 @@ def prepare_layer_decode(q_idx, w, k_idx, k_scale, q, k_cache, v_cache, gate, K,
         if st != 0:
             raise DSAError("dsa_layer_decode", st, dsa_last_error())
     return call
+
+
+def dsa_set_indexer_events(start, stop):
+    """Record the caller's HIP events (raw hipEvent_t handles as ints, or
+    None, None) around the indexer launch of later dsa_layer_decode calls
+    on this thread."""
+    _call("dsa_set_indexer_events", start, stop)
 
 
 def dsa_layer_prefill_workspace_size(B, T, max_ctx, K, Hq, D) -> int:

@@ -235,6 +235,17 @@ size_t dsa_layer_decode_workspace_size(int B, int max_ctx, int K, int Hq, int D)
   return decode_ws_layout(B, max_ctx, K, Hq, D, nullptr, nullptr);
 }
 
+// Caller-owned events recorded around the indexer launch (this thread).
+thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
+
+dsa_status_t dsa_set_indexer_events(void* start, void* stop) {
+  DSA_REQUIRE((start == nullptr) == (stop == nullptr), DSA_ERR_INVALID_ARG,
+              "start and stop events must both be set or both be NULL");
+  t_ev_start = static_cast<hipEvent_t>(start);
+  t_ev_stop = static_cast<hipEvent_t>(stop);
+  return DSA_OK;
+}
+
 dsa_status_t dsa_layer_decode(const void* q_idx, const void* w, int64_t w_ld, const void* k_idx,
                               int k_dtype, const float* k_scale, int H_I, int d_I, const void* q,
                               const void* k_cache, const void* v_cache, const void* gate,
@@ -275,7 +286,8 @@ dsa_status_t dsa_layer_decode(const void* q_idx, const void* w, int64_t w_ld, co
   int32_t* idx = idx_out ? idx_out : L.idx;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = dsa::launch_index_decode(q_idx, w, w_ld, k_idx, k_dtype, k_scale, H_I, d_I,
-                                          ctx_len, cu_ctx, B, max_ctx, L.scores, L.ld, &L.topk, s);
+                                          ctx_len, cu_ctx, B, max_ctx, L.scores, L.ld, &L.topk, s,
+                                          t_ev_start, t_ev_stop);
   if (e == hipSuccess)
     e = dsa::launch_topk_resolve(L.scores, L.ld, nullptr, ctx_len, B, B, K, L.topk, idx, nullptr,
                                  s);

@@ -25,6 +25,8 @@
 //   accumulator rows are whole queries, keeping the head sum in registers.
 //   Key tiles past the last visible position of the workgroup's queries are
 //   skipped; the diagonal tile is masked.
+#include <hip/hip_ext.h>
+
 #include "dsa_kernels.h"
 #include "dsa_topk_tile.h"
 
@@ -54,15 +56,19 @@ __device__ __forceinline__ int kslot_dim(int s, int g) {
 // completions in issue order).  Scores stay in registers until the end, and
 // with REPORT the wave writes the tile's Top-K candidate prefix
 // (dsa_topk_tile.h) without any cross-wave step.
-template <int ROWB, int TILE, bool FP8>
+template <int ROWB, int TILE, bool FP8, bool DEEP>
 struct KeyStage {
   static constexpr int kTileBytes = TILE * ROWB;
-  // bytes per stage: at most 16 KiB, and (fp8) at most 128 keys, whose
-  // scales take two more load instructions
-  static constexpr int kCap = FP8 && 128 * ROWB < 16384 ? 128 * ROWB : 16384;
+  // Two shapes: DEEP (few tiles per CU): stages of at most 16 KiB, three in
+  // flight, so each wave keeps up to 48 KiB of loads outstanding; otherwise
+  // stages of at most 8 KiB, two in flight, and more waves fit in LDS.
+  // (fp8: at most 128 keys per stage, whose scales take two more loads.)
+  static constexpr int kMax = DEEP ? 16384 : 8192;
+  static constexpr int kCap = FP8 && 128 * ROWB < kMax ? 128 * ROWB : kMax;
   static constexpr int kBytes = kTileBytes < kCap ? kTileBytes : kCap;
   static constexpr int kNum = kTileBytes / kBytes;       // stages per tile
-  static constexpr int kBufs = kNum < 3 ? kNum : 3;      // LDS stage buffers, all in flight
+  static constexpr int kDepth = DEEP ? 3 : 2;
+  static constexpr int kBufs = kNum < kDepth ? kNum : kDepth;  // LDS stage buffers, all in flight
   static constexpr int kRows = kBytes / ROWB;            // keys per stage
   static constexpr int kRowsPerKiB = 1024 / ROWB;        // rows per load instruction
   static constexpr int kPad = kRowsPerKiB >= 16 ? 0 : 256 / kRowsPerKiB;  // bytes per KiB
@@ -101,7 +107,7 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 }
 #undef DSA_WAITV
 
-template <int DI, bool FP8, int TILE, bool REPORT>
+template <int DI, bool FP8, int TILE, bool REPORT, bool DEEP>
 __global__ __launch_bounds__(64) void index_decode_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ w, int64_t w_ld,
     const uint8_t* __restrict__ k_idx, const float* __restrict__ k_scale, int H_I,
@@ -110,7 +116,7 @@ __global__ __launch_bounds__(64) void index_decode_kernel(
     int ntiles_max) {
   constexpr int KS = DI / 16;                       // MFMA k-steps
   constexpr int ROWB = FP8 ? DI : 2 * DI;           // bytes per key row
-  using St = KeyStage<ROWB, TILE, FP8>;
+  using St = KeyStage<ROWB, TILE, FP8, DEEP>;
   constexpr int NSTAGE = St::kNum;
   constexpr int SROWS = St::kRows;
   constexpr int SBLK = SROWS / 32;                  // 32-key blocks per stage
@@ -292,13 +298,25 @@ static hipError_t launch_decode_tiled(int tile, const uint16_t* q, const uint16_
                                       const int32_t* ctx_len, const int64_t* cu_ctx, int B,
                                       int max_ctx, float* scores, int64_t ld, RepHeader* hdr,
                                       uint32_t* ru, int32_t* rj, int ntiles_max,
-                                      hipStream_t st) {
+                                      hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   dim3 grid((max_ctx + tile - 1) / tile, B);
+  // deep pipelines when there are few waves per CU (256 CUs)
+  const bool deep = (int64_t)grid.x * B <= 1024;
+  // with events: the dispatch itself records them at the kernel's start and end
+#define DSA_DECODE_LAUNCH(KER)                                                                 \
+  if (ev0)                                                                                     \
+    hipExtLaunchKernelGGL(KER, grid, dim3(64), 0, st, ev0, ev1, 0, q, w, w_ld, k, ks, H_I,     \
+                          ctx_len, cu_ctx, scores, ld, hdr, ru, rj, ntiles_max);               \
+  else                                                                                         \
+    hipLaunchKernelGGL(KER, grid, dim3(64), 0, st, q, w, w_ld, k, ks, H_I, ctx_len, cu_ctx,    \
+                       scores, ld, hdr, ru, rj, ntiles_max);
 #define DSA_DECODE_TILE(T_)                                                                    \
   case T_:                                                                                     \
-    hipLaunchKernelGGL((index_decode_kernel<DI, FP8, T_, REPORT>), grid, dim3(64), 0, st, q,   \
-                       w, w_ld, k, ks, H_I, ctx_len, cu_ctx, scores, ld, hdr, ru, rj,          \
-                       ntiles_max);                                                            \
+    if (deep) {                                                                                \
+      DSA_DECODE_LAUNCH((index_decode_kernel<DI, FP8, T_, REPORT, true>))                      \
+    } else {                                                                                   \
+      DSA_DECODE_LAUNCH((index_decode_kernel<DI, FP8, T_, REPORT, false>))                     \
+    }                                                                                          \
     break;
   switch (tile) {
     DSA_DECODE_TILE(64)
@@ -311,6 +329,7 @@ static hipError_t launch_decode_tiled(int tile, const uint16_t* q, const uint16_
       return hipErrorInvalidValue;
   }
 #undef DSA_DECODE_TILE
+#undef DSA_DECODE_LAUNCH
   return hipGetLastError();
 }
 
@@ -319,20 +338,21 @@ static hipError_t launch_decode_any(bool report, int tile, const uint16_t* q, co
                                     int64_t w_ld, const uint8_t* k, const float* ks, int H_I,
                                     const int32_t* ctx_len, const int64_t* cu_ctx, int B,
                                     int max_ctx, float* scores, int64_t ld, RepHeader* hdr,
-                                    uint32_t* ru, int32_t* rj, int ntiles_max, hipStream_t st) {
+                                    uint32_t* ru, int32_t* rj, int ntiles_max, hipStream_t st,
+                                    hipEvent_t ev0, hipEvent_t ev1) {
   return report ? launch_decode_tiled<DI, FP8, true>(tile, q, w, w_ld, k, ks, H_I, ctx_len,
                                                      cu_ctx, B, max_ctx, scores, ld, hdr, ru, rj,
-                                                     ntiles_max, st)
+                                                     ntiles_max, st, ev0, ev1)
                 : launch_decode_tiled<DI, FP8, false>(tile, q, w, w_ld, k, ks, H_I, ctx_len,
                                                       cu_ctx, B, max_ctx, scores, ld, hdr, ru,
-                                                      rj, ntiles_max, st);
+                                                      rj, ntiles_max, st, ev0, ev1);
 }
 
 hipError_t launch_index_decode(const void* q_idx, const void* w, int64_t w_ld, const void* k_idx,
                                int k_dtype, const float* k_scale, int H_I, int d_I,
                                const int32_t* ctx_len, const int64_t* cu_ctx, int B, int max_ctx,
                                float* scores, int64_t ld, const TopkWs* reports,
-                               hipStream_t stream) {
+                               hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   const int tile = reports ? reports->tile : 256;
   RepHeader* hdr = reports ? reports->hdr : nullptr;
   uint32_t* ru = reports ? reports->rep_u : nullptr;
@@ -345,16 +365,16 @@ hipError_t launch_index_decode(const void* q_idx, const void* w, int64_t w_ld, c
   const bool rep = reports != nullptr;
   if (d_I == 128 && !fp8)
     return launch_decode_any<128, false>(rep, tile, q, wp, w_ld, k, k_scale, H_I, ctx_len,
-                                         cu_ctx, B, max_ctx, scores, ld, hdr, ru, rj, ntm, stream);
+                                         cu_ctx, B, max_ctx, scores, ld, hdr, ru, rj, ntm, stream, ev0, ev1);
   if (d_I == 128 && fp8)
     return launch_decode_any<128, true>(rep, tile, q, wp, w_ld, k, k_scale, H_I, ctx_len, cu_ctx,
-                                        B, max_ctx, scores, ld, hdr, ru, rj, ntm, stream);
+                                        B, max_ctx, scores, ld, hdr, ru, rj, ntm, stream, ev0, ev1);
   if (d_I == 64 && !fp8)
     return launch_decode_any<64, false>(rep, tile, q, wp, w_ld, k, k_scale, H_I, ctx_len, cu_ctx,
-                                        B, max_ctx, scores, ld, hdr, ru, rj, ntm, stream);
+                                        B, max_ctx, scores, ld, hdr, ru, rj, ntm, stream, ev0, ev1);
   if (d_I == 64 && fp8)
     return launch_decode_any<64, true>(rep, tile, q, wp, w_ld, k, k_scale, H_I, ctx_len, cu_ctx,
-                                       B, max_ctx, scores, ld, hdr, ru, rj, ntm, stream);
+                                       B, max_ctx, scores, ld, hdr, ru, rj, ntm, stream, ev0, ev1);
   return hipErrorInvalidValue;
 }
 

@@ -34,11 +34,13 @@ hipError_t launch_topk_resolve(const float* scores, int64_t ld, const int32_t* c
 
 // Indexer, one query per sequence.  When `reports` is non-null the kernel
 // also writes the Top-K candidate reports of its tiles (tile = reports->tile).
+// With events, the dispatch records ev0 / ev1 at the kernel's start / end.
 hipError_t launch_index_decode(const void* q_idx, const void* w, int64_t w_ld, const void* k_idx,
                                int k_dtype, const float* k_scale, int H_I, int d_I,
                                const int32_t* ctx_len, const int64_t* cu_ctx, int B, int max_ctx,
                                float* scores, int64_t ld, const TopkWs* reports,
-                               hipStream_t stream);
+                               hipStream_t stream, hipEvent_t ev0 = nullptr,
+                               hipEvent_t ev1 = nullptr);
 
 // Indexer, a chunk of queries per sequence (dense MFMA contraction).
 hipError_t launch_index_prefill(const void* q_idx, const void* w, int64_t w_ld, const void* k_idx,

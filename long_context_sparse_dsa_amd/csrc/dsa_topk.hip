@@ -65,8 +65,8 @@ struct ResolveSmem {
   int32_t stage[4096];  // selected positions before the coalesced store (K <= 4096)
   uint32_t hist[2048];
   uint32_t hist2[2048];  // the union select alternates between hist and hist2
-  uint32_t bu[kBucketMax];
-  int32_t bj[kBucketMax];
+  alignas(16) uint32_t bu[kBucketMax];
+  alignas(16) int32_t bj[kBucketMax];
   // per tile: worst reported (key, position | complete << 31), kept for the
   // certification so the headers need not stay in registers
   uint32_t wu[kResolveTiles];
@@ -95,16 +95,19 @@ __device__ void wave_find_digit(ResolveSmem& sm, const uint32_t* h, uint32_t abo
   const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
   uint32_t gt = total - incl;  // elements in the bins of higher lanes
   if (above + gt < k && above + gt + mine >= k) {
-    for (int c = 7; c >= 0; --c) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(h + 32 * l + 4 * c);
+#pragma unroll 1
+    for (int c2 = 3; c2 >= 0; --c2) {  // two chunks per step
+      const u32x4 v1 = *reinterpret_cast<const u32x4*>(h + 32 * l + 8 * c2 + 4);
+      const u32x4 v0 = *reinterpret_cast<const u32x4*>(h + 32 * l + 8 * c2);
+      const uint32_t vv[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
 #pragma unroll
-      for (int i = 3; i >= 0; --i) {
-        if (above + gt < k && above + gt + v[i] >= k) {
-          sm.st[0] = 32 * l + 4 * c + i;
+      for (int i = 7; i >= 0; --i) {
+        if (above + gt < k && above + gt + vv[i] >= k) {
+          sm.st[0] = 32 * l + 8 * c2 + i;
           sm.st[1] = above + gt;
-          sm.st[5] = v[i];
+          sm.st[5] = vv[i];
         }
-        gt += v[i];
+        gt += vv[i];
       }
     }
   }
@@ -295,11 +298,22 @@ __device__ void union_threshold(ResolveSmem& sm, const UnionRegs& R, uint32_t k,
       const bool mine_ok = (uint32_t)l < h;
       const uint32_t um = mine_ok ? sm.bu[l] : 0u;
       const int32_t jm = mine_ok ? sm.bj[l] : 0;
+      // every lane reads the whole bucket (broadcast reads, all issued at once)
       uint32_t rank = 0;
-      for (uint32_t q = 0; q < h; ++q) {
-        const uint32_t uq = sm.bu[q];
-        const int32_t jq = sm.bj[q];
-        rank += (uq > um) || (uq == um && jq < jm);
+#pragma unroll 1
+      for (int q0 = 0; q0 < (int)h; q0 += 16) {
+        u32x4 uq[4], jq[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          uq[c] = *reinterpret_cast<const u32x4*>(sm.bu + q0 + 4 * c);
+          jq[c] = *reinterpret_cast<const u32x4*>(sm.bj + q0 + 4 * c);
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            rank += (uint32_t)(q0 + 4 * c + e) < h &&
+                    ((uq[c][e] > um) || (uq[c][e] == um && (int32_t)jq[c][e] < jm));
       }
       if (mine_ok && rank == need - 1) {
         sm.st[2] = um;

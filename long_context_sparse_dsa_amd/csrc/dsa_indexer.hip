@@ -394,25 +394,55 @@ struct RowMap {
   }
 };
 
-template <int DI, int HI, bool FP8, int MB>
-__global__ __launch_bounds__(256) void index_prefill_kernel(
+// Prefill workgroup = NCW compute waves + one loader wave + one storer wave.
+//   - the loader streams the key range in 64-key stages into a ring of
+//     NBUF LDS buffers with direct global-to-LDS loads; its load counter
+//     tracks nothing else, so its waits are exact;
+//   - the compute waves hold their query heads (A operand, MB blocks of 32
+//     (query, head) rows) in registers, run the MFMAs on the stage's keys,
+//     apply ReLU / head weights / head sum in registers and write the
+//     stage's scores into an LDS double buffer; they never touch global
+//     memory inside the loop;
+//   - the storer writes the previous stage's scores to global memory
+//     (causal positions only) and never waits on its stores.
+// One workgroup barrier per stage orders the three roles.
+template <int DI, int HI, bool FP8>
+struct PrefillShape {
+  static constexpr int KT = 64;                          // keys per stage
+  static constexpr int ROWB = FP8 ? DI : 2 * DI;         // bytes per key row
+  static constexpr int SB = KT * ROWB;                   // key bytes per stage
+  static constexpr int RPK = 1024 / ROWB;                // rows per 1 KiB load
+  static constexpr int PAD = RPK >= 16 ? 0 : 256 / RPK;  // LDS pad per KiB
+  static constexpr int STRIDE = 1024 + PAD;
+  static constexpr int NI = SB / 1024;                   // key loads per stage
+  static constexpr int NL = NI + (FP8 ? 1 : 0);          // all loads per stage
+  static constexpr int KEYB = NI * STRIDE;
+  static constexpr int BUFB = KEYB + (FP8 ? 4 * KT : 0); // LDS bytes per stage buffer
+  static constexpr int SCW = KT + 32;                    // score row stride (floats)
+  __device__ static int offset(int r, int ck) {
+    return (r / RPK) * STRIDE + (ck * RPK + r % RPK) * 16;
+  }
+};
+
+template <int DI, int HI, bool FP8, int MB, int NCW, int NBUF>
+__global__ __launch_bounds__(64 * (NCW + 2)) void index_prefill_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ w, int64_t w_ld,
     const uint8_t* __restrict__ k_idx, const float* __restrict__ k_scale,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ ctx_len,
     const int64_t* __restrict__ cu_ctx, float* __restrict__ scores, int64_t ld, int nsplit) {
+  using PS = PrefillShape<DI, HI, FP8>;
+  constexpr int KT = PS::KT;
   constexpr int KS = DI / 16;
-  constexpr int ROWB = FP8 ? DI : 2 * DI;
-  constexpr int NBK = 2;                     // 32-key blocks per stage
-  constexpr int KT = 32 * NBK;               // keys per stage
-  constexpr int LROW = ROWB + 16;            // padded LDS row (bytes)
+  constexpr int ROWB = PS::ROWB;
   constexpr int QPB = RowMap<HI>::QPB;
-  constexpr int QW = MB * QPB;               // queries per wave
-  constexpr int QWG = 4 * QW;                // queries per workgroup
-  constexpr int CH = ROWB / 16;              // 16-byte chunks per key row
-  constexpr int LDPT = KT * CH / 256;        // chunks per thread per stage
+  constexpr int QW = MB * QPB;               // queries per compute wave
+  constexpr int QWG = NCW * QW;              // queries per workgroup
+  constexpr int NLD = FP8 ? KS / 2 : KS;     // 16-byte operand chunks per lane per key block
+  static_assert(PS::NL * (NBUF - 1) <= 63, "loads in flight");
 
-  __shared__ __attribute__((aligned(16))) uint8_t kt_lds[KT * LROW];
-  __shared__ float sig_lds[KT];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NBUF * PS::BUFB + 2 * QWG * PS::SCW * 4];
+  uint8_t* const ring = lds;
+  float* const sc = reinterpret_cast<float*>(lds + NBUF * PS::BUFB);
 
   const int b = blockIdx.z, qt = blockIdx.y, split = blockIdx.x;
   const int nq = cu_q[b + 1] - cu_q[b];
@@ -423,111 +453,170 @@ __global__ __launch_bounds__(256) void index_prefill_kernel(
   const int64_t row0 = cu_ctx[b];
   const int64_t t0 = cu_q[b];
   const int l = lane_id(), g = l >> 5, wv = wave_id();
+  // visible key range of this workgroup: [0, last position of its queries]
+  const int qlast = min(nq, qbase + QWG) - 1;
+  const int64_t kend = pos0 + qlast + 1;
+  const int64_t nst_all = (kend + KT - 1) / KT;
+  const int64_t st_lo = nst_all * split / nsplit;
+  const int nst = (int)(nst_all * (split + 1) / nsplit - st_lo);
+  if (nst <= 0) return;
 
-  // Query tile of this wave and its A fragments.
+  if (wv == NCW) {
+    // ---------------- loader ----------------
+    const int lrow = l % PS::RPK, lchunk = l / PS::RPK;
+    auto issue = [&](int k) {
+      uint8_t* buf = ring + (k % NBUF) * PS::BUFB;
+      const int64_t kb = (st_lo + k) * KT;
+      if constexpr (FP8)
+        lds_dma4(k_scale + row0 + min<int64_t>(kb + l, L - 1), buf + PS::KEYB);
+#pragma unroll
+      for (int c = 0; c < PS::NI; ++c)
+        lds_dma16(k_idx + (row0 + min<int64_t>(kb + c * PS::RPK + lrow, L - 1)) * ROWB +
+                      16 * lchunk,
+                  buf + c * PS::STRIDE);
+    };
+#pragma unroll
+    for (int k = 0; k < NBUF - 1; ++k)
+      if (k < nst) issue(k);
+#pragma unroll 1
+    for (int i = 0; i < nst; ++i) {
+      // stage i has landed once only the stages issued after it are in flight
+      const int later = min(NBUF - 2, nst - 1 - i);
+      wait_vmcnt(later * PS::NL);
+      lds_barrier();
+      if (i + NBUF - 1 < nst) issue(i + NBUF - 1);  // into the buffer of stage i - 1
+    }
+    lds_barrier();
+    return;
+  }
+  if (wv == NCW + 1) {
+    // ---------------- storer ----------------
+    const bool vec = (ld & 3) == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
+    auto store_stage = [&](int k) {
+      const float* src = sc + (k & 1) * QWG * PS::SCW;
+      const int64_t kb = (st_lo + k) * KT;
+#pragma unroll
+      for (int q4 = 0; q4 < (QWG + 3) / 4; ++q4) {
+        const int q = 4 * q4 + (l >> 4);          // query row of the workgroup
+        const int kk = 4 * (l & 15);              // first of 4 keys
+        const int qq = qbase + q;
+        if (q >= QWG || qq >= nq) continue;
+        const int64_t jmax = pos0 + qq;           // last visible key
+        const int64_t j = kb + kk;
+        if (j > jmax) continue;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(src + q * PS::SCW + kk);
+        float* dst = scores + (t0 + qq) * ld + j;
+        if (vec && j + 3 <= jmax) {
+          *reinterpret_cast<f32x4*>(dst) = v;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (j + e <= jmax) dst[e] = v[e];
+        }
+      }
+    };
+#pragma unroll 1
+    for (int i = 0; i < nst; ++i) {
+      lds_barrier();
+      if (i > 0) store_stage(i - 1);
+    }
+    lds_barrier();
+    store_stage(nst - 1);
+    return;
+  }
+
+  // ---------------- compute waves ----------------
   const int wq0 = qbase + wv * QW;
   bf16x8 qa[MB][KS];
   float wr[MB][16];
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
     const int i = l & 31;
-    const int qq = wq0 + m * QPB + RowMap<HI>::query_of_row(i);
+    const int qq = min(wq0 + m * QPB + RowMap<HI>::query_of_row(i), nq - 1);
     const int hh = RowMap<HI>::head_of_row(i);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (qq < nq) v = ld16(q_idx + ((t0 + qq) * HI + hh) * DI + kslot_dim<FP8>(s, g));
-      qa[m][s] = as_bf16x8(v);
-    }
+    for (int s = 0; s < KS; ++s)
+      qa[m][s] = as_bf16x8(ld16(q_idx + ((t0 + qq) * HI + hh) * DI + kslot_dim<FP8>(s, g)));
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int ir = 8 * (r >> 2) + 4 * g + (r & 3);
       const int q2 = wq0 + m * QPB + RowMap<HI>::query_of_row(ir);
-      wr[m][r] = q2 < nq ? bf16_to_f32(w[(t0 + q2) * w_ld + RowMap<HI>::head_of_row(ir)]) : 0.f;
+      const float wv2 = bf16_to_f32(w[(t0 + min(q2, nq - 1)) * w_ld + RowMap<HI>::head_of_row(ir)]);
+      wr[m][r] = q2 < nq ? wv2 : 0.f;
     }
   }
-  // Visible key range of this workgroup: [0, last position of its queries].
-  const int qlast = min(nq, qbase + QWG) - 1;
-  const int64_t kend = pos0 + qlast + 1;
-  const int64_t nst = (kend + KT - 1) / KT;
-  const int64_t st_lo = nst * split / nsplit, st_hi = nst * (split + 1) / nsplit;
-
 #pragma unroll 1
-  for (int64_t st = st_lo; st < st_hi; ++st) {
-    const int64_t k0 = st * KT;
-    // ---- stage key tile into LDS ----
+  for (int i = 0; i < nst; ++i) {
     lds_barrier();
+    const uint8_t* buf = ring + (i % NBUF) * PS::BUFB;
+    float* dst = sc + (i & 1) * QWG * PS::SCW;
+    // both 32-key blocks of the stage at once: 2 * MB independent
+    // accumulator chains interleave on the MFMA pipe
+    constexpr int NB = KT / 32;
+    u32x4 kv[NB][NLD];
+    float sg[NB];
 #pragma unroll
-    for (int c = 0; c < LDPT; ++c) {
-      const int e = threadIdx.x + 256 * c;
-      const int kr = e / CH, kc = e % CH;
-      const int64_t j = min<int64_t>(k0 + kr, L - 1);
-      u32x4 v = ld16(k_idx + (row0 + j) * ROWB + 16 * kc);
-      *reinterpret_cast<u32x4*>(kt_lds + kr * LROW + 16 * kc) = v;
+    for (int n = 0; n < NB; ++n) {
+      const int R = 32 * n + (l & 31);
+#pragma unroll
+      for (int c = 0; c < NLD; ++c)
+        kv[n][c] = *reinterpret_cast<const u32x4*>(buf + PS::offset(R, 2 * c + g));
+      sg[n] = FP8 ? reinterpret_cast<const float*>(buf + PS::KEYB)[R] : 1.f;
     }
-    if (FP8 && threadIdx.x < KT) sig_lds[threadIdx.x] = k_scale[row0 + min<int64_t>(k0 + threadIdx.x, L - 1)];
-    lds_barrier();
-    // ---- MFMA ----
-    f32x16 acc[MB][NBK];
+    f32x16 acc[MB][NB];
 #pragma unroll
     for (int m = 0; m < MB; ++m)
 #pragma unroll
-      for (int n = 0; n < NBK; ++n) acc[m][n] = f32x16{};
+      for (int n = 0; n < NB; ++n) acc[m][n] = f32x16{};
 #pragma unroll
-    for (int n = 0; n < NBK; ++n) {
-      const uint8_t* kr = kt_lds + (32 * n + (l & 31)) * LROW;
-      if constexpr (FP8) {
+    for (int c = 0; c < NLD; ++c) {
 #pragma unroll
-        for (int c = 0; c < KS / 2; ++c) {
-          u32x4 v = *reinterpret_cast<const u32x4*>(kr + 32 * c + 16 * g);
-          bf16x8 b0 = fp8x8_to_bf16x8(v[0], v[1]), b1 = fp8x8_to_bf16x8(v[2], v[3]);
+      for (int n = 0; n < NB; ++n) {
+        if constexpr (FP8) {
+          const bf16x8 b0 = fp8x8_to_bf16x8(kv[n][c][0], kv[n][c][1]);
+          const bf16x8 b1 = fp8x8_to_bf16x8(kv[n][c][2], kv[n][c][3]);
 #pragma unroll
           for (int m = 0; m < MB; ++m) {
             acc[m][n] = mfma32(qa[m][2 * c], b0, acc[m][n]);
             acc[m][n] = mfma32(qa[m][2 * c + 1], b1, acc[m][n]);
           }
-        }
-      } else {
+        } else {
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          bf16x8 bb = as_bf16x8(*reinterpret_cast<const u32x4*>(kr + 32 * s + 16 * g));
-#pragma unroll
-          for (int m = 0; m < MB; ++m) acc[m][n] = mfma32(qa[m][s], bb, acc[m][n]);
+          for (int m = 0; m < MB; ++m) acc[m][n] = mfma32(qa[m][c], as_bf16x8(kv[n][c]), acc[m][n]);
         }
       }
     }
-    // ---- epilogue: ReLU, head weights, head sum, causal mask, store ----
+    // epilogue: ReLU, head weights, head sum -> LDS scores
 #pragma unroll
-    for (int n = 0; n < NBK; ++n) {
-      const int64_t j = k0 + 32 * n + (l & 31);
-      const float sg = FP8 ? sig_lds[32 * n + (l & 31)] : 1.f;
+    for (int n = 0; n < NB; ++n) {
+      const int R = 32 * n + (l & 31);
 #pragma unroll
       for (int m = 0; m < MB; ++m) {
+        const int q0 = wv * QW + m * QPB;  // workgroup-local query of block m
         if constexpr (HI == 4) {
 #pragma unroll
           for (int c4 = 0; c4 < 4; ++c4) {
-            float s = 0.f;
+            float sum = 0.f;
 #pragma unroll
-            for (int r = 4 * c4; r < 4 * c4 + 4; ++r) s += wr[m][r] * fmaxf(sg * acc[m][n][r], 0.f);
-            const int qq = wq0 + m * QPB + 2 * c4 + g;
-            if (qq < nq && j <= pos0 + qq) scores[(t0 + qq) * ld + j] = s;
+            for (int r = 4 * c4; r < 4 * c4 + 4; ++r)
+              sum += wr[m][r] * fmaxf(sg[n] * acc[m][n][r], 0.f);
+            dst[(q0 + 2 * c4 + g) * PS::SCW + R] = sum;
           }
         } else {
-          float s = 0.f;
+          float sum = 0.f;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s += wr[m][r] * fmaxf(sg * acc[m][n][r], 0.f);
-          int qq;
+          for (int r = 0; r < 16; ++r) sum += wr[m][r] * fmaxf(sg[n] * acc[m][n][r], 0.f);
           if constexpr (HI == 32) {
-            s = xor32_add(s);
-            qq = (g == 0) ? wq0 + m : nq;  // one half writes
+            sum = xor32_add(sum);
+            if (g == 0) dst[q0 * PS::SCW + R] = sum;
           } else {
-            qq = wq0 + m * QPB + g;
+            dst[(q0 + g) * PS::SCW + R] = sum;
           }
-          if (qq < nq && j <= pos0 + qq) scores[(t0 + qq) * ld + j] = s;
         }
       }
     }
   }
+  lds_barrier();
 }
 
 template <int DI, int HI, bool FP8>
@@ -536,8 +625,10 @@ static hipError_t launch_prefill_t(const uint16_t* q, const uint16_t* w, int64_t
                                    const int32_t* ctx_len, const int64_t* cu_ctx, int B,
                                    int max_q, int max_ctx, float* scores, int64_t ld,
                                    hipStream_t st) {
-  constexpr int MB = 2;
-  constexpr int QWG = 4 * MB * (32 / HI);
+  // 6 compute waves (+ loader + storer); two 32-row query blocks per compute
+  // wave where the registers allow it (8 queries of 4 heads fill a block)
+  constexpr int MB = HI == 4 ? 1 : 2, NCW = 6, NBUF = 3;
+  constexpr int QWG = NCW * MB * (32 / HI);
   const int qtiles = (max_q + QWG - 1) / QWG;
   // enough workgroups to fill the chip: split the key range when needed
   int nsplit = 1;
@@ -545,8 +636,9 @@ static hipError_t launch_prefill_t(const uint16_t* q, const uint16_t* w, int64_t
          (int64_t)max_ctx / (nsplit * 2) >= 1024)
     nsplit *= 2;
   dim3 grid(nsplit, qtiles, B);
-  hipLaunchKernelGGL((index_prefill_kernel<DI, HI, FP8, MB>), grid, dim3(256), 0, st, q, w, w_ld,
-                     k, ks, cu_q, ctx_len, cu_ctx, scores, ld, nsplit);
+  hipLaunchKernelGGL((index_prefill_kernel<DI, HI, FP8, MB, NCW, NBUF>), grid,
+                     dim3(64 * (NCW + 2)), 0, st, q, w, w_ld, k, ks, cu_q, ctx_len, cu_ctx,
+                     scores, ld, nsplit);
   return hipGetLastError();
 }
 

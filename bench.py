@@ -39,10 +39,11 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--workload", default="dec128k",
-                    choices=["dec128k", "dec1m_b32_fp8", "prefill8k"],
+                    choices=["dec128k", "dec1m_b32_fp8", "prefill8k", "hybrid51"],
                     help="dec128k (default, the headline metric); the others time the "
-                         "same path on the batched 1M-context fp8 decode and on the 8K "
-                         "prefill chunk")
+                         "same path on the batched 1M-context fp8 decode, on the 8K "
+                         "prefill chunk, and on one 5:1 SWA/DSA hybrid decode step of a "
+                         "ragged batch of 8")
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--rotate", type=int, default=None, help="distinct layer buffer sets")
@@ -52,7 +53,8 @@ def parse():
                     help="before timing, copy a buffer of this many MiB once (a reference "
                          "kernel of known traffic for hardware-counter runs)")
     a = ap.parse_args()
-    dflt = {"dec128k": (200, 20, 16), "dec1m_b32_fp8": (20, 3, 1), "prefill8k": (5, 1, 1)}
+    dflt = {"dec128k": (200, 20, 16), "dec1m_b32_fp8": (20, 3, 1), "prefill8k": (5, 1, 1),
+            "hybrid51": (50, 5, 1)}
     st, wu, rot = dflt[a.workload]
     a.steps = a.steps if a.steps is not None else st
     a.warmup = a.warmup if a.warmup is not None else wu
@@ -132,6 +134,8 @@ def main():
         del src, dst
     if args.workload == "prefill8k":
         result = bench_prefill(args, torch, dsa, W)
+    elif args.workload == "hybrid51":
+        result = bench_hybrid(args, torch, dsa, W)
     else:
         result = bench_decode(args, torch, dsa, W)
     print(json.dumps(result), flush=True)
@@ -229,6 +233,96 @@ def bench_decode(args, torch, dsa, W):
         result["metric"] = "DSA layer decode tokens/s (batched 1M-context fp8 decode)"
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(sets[0], wl, args.cpu_seconds)
+    return result
+
+
+def bench_hybrid(args, torch, dsa, W):
+    """One decode step of the 5:1 hybrid: five sliding-window (128) attention
+    layers, ungated, each with its own K/V cache, then one Gated DSA layer;
+    ragged batch of 8 sequences."""
+    dev = "cuda"
+    wl = W.hybrid_5to1()
+    nswa, window = wl.extra["swa_layers"], wl.extra["window"]
+    L = max(wl.ctx_lens)
+    ntot = sum(wl.ctx_lens)
+    s = W.make_inputs(wl, device=dev)
+    swa = []
+    for i in range(nswa):
+        swa.append({"q": W.randn_bf16((wl.B, wl.Hq, wl.D), wl.seed, f"swa{i}_q", dev),
+                    "k": W.randn_bf16((ntot, wl.D), wl.seed, f"swa{i}_k", dev),
+                    "v": W.randn_bf16((ntot, wl.D), wl.seed, f"swa{i}_v", dev),
+                    "out": torch.empty(wl.B, wl.Hq, wl.D, dtype=torch.bfloat16, device=dev)})
+    swa_calls = [dsa.prepare_sparse_attn(x["q"], x["k"], x["v"], None, s["ctx_len"], s["cu_ctx"],
+                                         L, x["out"], window=window) for x in swa]
+    ws = torch.empty(dsa.dsa_layer_decode_workspace_size(wl.B, L, wl.K, wl.Hq, wl.D),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty_like(s["q"])
+    dsa_call = dsa.prepare_layer_decode(s["q_idx"], s["w"], s["k_idx"], s["k_scale"], s["q"],
+                                        s["k_cache"], s["v_cache"], s["gate"], wl.K, s["ctx_len"],
+                                        s["cu_ctx"], L, out, ws)
+    hip = HipEvents()
+    ev = [(hip.create(), hip.create()) for _ in range(args.steps)]
+    set_events = dsa.load().dsa_set_indexer_events
+
+    def step():
+        for c in swa_calls:
+            c()
+        dsa_call()
+
+    def timed(n, warm, with_events):
+        for _ in range(warm):
+            step()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n):
+            if with_events:
+                set_events(ctypes.c_void_p(ev[i][0]), ctypes.c_void_p(ev[i][1]))
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        set_events(None, None)
+        return e0.elapsed_time(e1) / n
+
+    ms = timed(args.steps, args.warmup, False)
+    timed(args.steps, 0, True)
+    ms_idx = sum(hip.elapsed_ms(a, b) for a, b in ev) / len(ev)
+    for a, b in ev:
+        hip.destroy(a)
+        hip.destroy(b)
+    idx_bytes = ntot * 2 * wl.d_I + wl.B * (wl.H_I * wl.d_I * 2 + wl.H_I * 2)
+    dsa_bytes = idx_bytes + wl.B * (wl.K * 2 * wl.D * 2 + 3 * wl.Hq * wl.D * 2)
+    swa_bytes = nswa * wl.B * (window * 2 * wl.D * 2 + 2 * wl.Hq * wl.D * 2)
+    achieved = idx_bytes / (ms_idx * 1e-3) / 1e9
+    result = {
+        "metric": "5:1 SWA/DSA hybrid decode step tokens/s (ragged batch of 8)",
+        "value": round(wl.B / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.B, "ctx_lens": wl.ctx_lens,
+                   "swa_layers": nswa, "window": window, "dsa_layers": 1,
+                   "indexer": f"{wl.H_I}x{wl.d_I}", "topk": wl.K, "q_heads": wl.Hq,
+                   "head_dim": wl.D},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "index_decode_kernel (DSA layer)",
+                     "kernel_us": round(ms_idx * 1e3, 3),
+                     "algorithmic_bytes_per_launch": idx_bytes},
+        "layer_roofline": {"algorithmic_bytes_per_step": dsa_bytes + swa_bytes,
+                           "frac_of_hbm_peak": round((dsa_bytes + swa_bytes) / (ms * 1e-3) /
+                                                     1e9 / HBM_PEAK_GBS, 4)},
+    }
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline_hybrid(s, swa, wl, args.cpu_seconds)
     return result
 
 
@@ -353,6 +447,37 @@ def cpu_baseline_prefill(s, wl, budget):
     return {"value": round(done / el, 3), "unit": "tokens/s", "cores": n, "kind": "oracle",
             "sample": f"the last {done} queries of the chunk, one decode-shaped oracle call each "
                       f"(context up to {L}) in {el:.1f} s, fp64, {n} threads"}
+
+
+def cpu_baseline_hybrid(s, swa, wl, budget):
+    """The oracle on whole hybrid steps (five windowed attention layers and
+    one DSA layer) of the batch's shortest sequence, for about `budget` s."""
+    import numpy as np
+    import oracle
+    c = _host(s)
+    b = int(np.argmin(wl.ctx_lens))
+    L = wl.ctx_lens[b]
+    r0 = int(sum(wl.ctx_lens[:b]))
+    sw = [{k: v[b:b + 1].cpu() if k in ("q", "out") else v[r0:r0 + L].cpu()
+           for k, v in x.items()} for x in swa]
+    ctx = np.array([L], dtype=np.int32)
+    n = oracle.default_threads()
+    t0 = time.perf_counter()
+    runs = 0
+    while True:
+        for x in sw:
+            oracle.sparse_attn(x["q"], x["k"], x["v"], window=wl.extra["window"], ctx_len=ctx,
+                               nthreads=n)
+        oracle.layer(c["q_idx"][b:b + 1], c["w"][b:b + 1], c["k_idx"][r0:r0 + L], None,
+                     c["q"][b:b + 1], c["k_cache"][r0:r0 + L], c["v_cache"][r0:r0 + L],
+                     c["gate"][b:b + 1], wl.K, ctx, nthreads=n)
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= budget or runs >= 200:
+            break
+    return {"value": round(runs / el, 3), "unit": "tokens/s", "cores": n, "kind": "oracle",
+            "sample": f"{runs} whole hybrid steps (5 SWA + 1 DSA layers) of one sequence "
+                      f"(ctx {L}) in {el:.1f} s, fp64, {n} threads"}
 
 
 if __name__ == "__main__":

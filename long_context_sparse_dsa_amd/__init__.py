@@ -217,6 +217,38 @@ def dsa_sparse_attn(q, k_cache, v_cache, idx, ctx_len, cu_ctx, window=0, gate=No
     return out
 
 
+def prepare_sparse_attn(q, k_cache, v_cache, idx, ctx_len, cu_ctx, max_ctx, out, window=0,
+                        gate=None, sm_scale=0.0, ws=None, stream=None):
+    """Marshal one dsa_sparse_attn call (one new query per sequence) once;
+    returns a no-argument callable that re-issues it (one ctypes call).  The
+    tensors must stay alive and unchanged in shape while the callable is used."""
+    _check(q, "q", BF16, 3)
+    _check(k_cache, "k_cache", BF16, 2)
+    _check(v_cache, "v_cache", BF16, 2)
+    _check(idx, "idx", (torch.int32,), 2)
+    _check(gate, "gate", BF16, 3)
+    _check(ctx_len, "ctx_len", (torch.int32,), 1)
+    _check(cu_ctx, "cu_ctx", (torch.int64,), 1)
+    _check(out, "out", BF16, 3)
+    T, Hq, D = q.shape
+    B = ctx_len.shape[0]
+    K = 0 if idx is None else idx.shape[1]
+    nbytes = load().dsa_sparse_attn_workspace_size(B, T, K, window, Hq, D)
+    if ws is None:
+        ws = _workspace(nbytes, q.device)
+    fn = load().dsa_sparse_attn
+    args = (_p(q), _p(k_cache), _p(v_cache), _p(idx), K, window, _p(gate), float(sm_scale), Hq,
+            D, None, _p(ctx_len), _p(cu_ctx), B, T, 1, int(max_ctx), _p(out), None, _p(ws),
+            ws.numel(), _stream(stream))
+
+    def call():
+        st = fn(*args)
+        if st != 0:
+            raise DSAError("dsa_sparse_attn", st, dsa_last_error())
+    call.workspace = ws
+    return call
+
+
 def dsa_layer_decode_workspace_size(B, max_ctx, K, Hq, D) -> int:
     return int(load().dsa_layer_decode_workspace_size(B, max_ctx, K, Hq, D))
 

@@ -34,7 +34,11 @@ namespace dsa {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-__device__ __forceinline__ float sigmoidf(float x) { return 1.f / (1.f + __expf(-x)); }
+// Hardware exp2 and reciprocal (v_exp_f32, v_rcp_f32: about 1 ulp), which
+// keep the latency-bound epilogues short; the outputs are bf16.
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float frcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float sigmoidf(float x) { return frcp(1.f + fexp2(-x * kLog2e)); }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -63,7 +67,7 @@ struct VTile {
   }
 };
 
-template <int D, int HB>
+template <int D, int HB, bool FINAL>
 __global__ __launch_bounds__(256) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ idx, int K, int window,
@@ -151,11 +155,11 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
     }
     mx = xor32_max(mx);
     const float m_new = fmaxf(m_run, mx);
-    const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
+    const float alpha = (m_new == -INFINITY) ? 1.f : fexp2(m_run - m_new);
     float psum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      sv[r] = (sv[r] == -INFINITY) ? 0.f : exp2f(sv[r] - m_new);
+      sv[r] = (sv[r] == -INFINITY) ? 0.f : fexp2(sv[r] - m_new);
       psum += sv[r];
     }
     l_run = l_run * alpha + xor32_add(psum);
@@ -209,8 +213,8 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
     const float* src = ms + (slot * HB + hb) * 64 * ST_FLOATS;
     const float mo = src[l], lo2 = src[64 + l];
     const float M = fmaxf(m_run, mo);
-    const float a = (M == -INFINITY) ? 0.f : exp2f(m_run - M);
-    const float bb = (M == -INFINITY) ? 0.f : exp2f(mo - M);
+    const float a = (M == -INFINITY) ? 0.f : fexp2(m_run - M);
+    const float bb = (M == -INFINITY) ? 0.f : fexp2(mo - M);
     l_run = l_run * a + lo2 * bb;
     m_run = M;
 #pragma unroll
@@ -233,9 +237,9 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
   // ---- the row-block-0 wave of each head block writes the result ----
   const int head = 32 * hb + (l & 31);
   if (head >= Hq) return;
-  const bool final_out = nsplit == 1;
+  constexpr bool final_out = FINAL;  // one split: gated bf16 output, else partials
   const float Lsum = l_run, M = m_run;
-  const float inv = (Lsum > 0.f) ? 1.f / Lsum : 0.f;
+  const float inv = (Lsum > 0.f) ? frcp(Lsum) : 0.f;
   float* pp = part + (((int64_t)t * nsplit + split) * Hq + head) * (D + 2);
   // gate values of this lane's outputs, all loaded before any is used
   u32x2 gw[DB][4];
@@ -252,7 +256,7 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int d0 = 32 * db + 8 * r4 + 4 * g;
-      if (final_out) {
+      if constexpr (final_out) {
         uint16_t ob[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -332,12 +336,12 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restric
   float L = 0.f, acc[PL] = {};
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    const float wgt = (s < nsplit && M != -INFINITY) ? exp2f(sm_m[s] - M) : 0.f;
+    const float wgt = (s < nsplit && M != -INFINITY) ? fexp2(sm_m[s] - M) : 0.f;
     L += wgt * sm_l[s];
 #pragma unroll
     for (int e = 0; e < PL; ++e) acc[e] += wgt * ov[s][e];
   }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
+  const float inv = L > 0.f ? frcp(L) : 0.f;
   uint16_t ob[PL];
 #pragma unroll
   for (int e = 0; e < PL; ++e) {
@@ -398,19 +402,26 @@ hipError_t launch_sparse_attn(const void* q, const void* k_cache, const void* v_
   auto op = static_cast<uint16_t*>(out);
   float* part = static_cast<float*>(ws);
   dim3 grid(plan.nsplit, T);
+  const bool final_out = plan.nsplit == 1;
+#define DSA_ATTN_LAUNCH(D_, HB_)                                                               \
+  if (final_out)                                                                               \
+    hipLaunchKernelGGL((sparse_attn_kernel<D_, HB_, true>), grid, dim3(256), 0, stream, qp, kp, \
+                       vp, idx, K, window, gp, scale, Hq, cu_q, ctx_len, cu_ctx, B,            \
+                       plan.rows_per_split, op, lse, part, plan.nsplit);                       \
+  else                                                                                         \
+    hipLaunchKernelGGL((sparse_attn_kernel<D_, HB_, false>), grid, dim3(256), 0, stream, qp,   \
+                       kp, vp, idx, K, window, gp, scale, Hq, cu_q, ctx_len, cu_ctx, B,        \
+                       plan.rows_per_split, op, lse, part, plan.nsplit);
   if (D == 128 && Hq == 64) {
-    hipLaunchKernelGGL((sparse_attn_kernel<128, 2>), grid, dim3(256), 0, stream, qp, kp, vp, idx,
-                       K, window, gp, scale, Hq, cu_q, ctx_len, cu_ctx, B, plan.rows_per_split,
-                       op, lse, part, plan.nsplit);
-    if (plan.nsplit > 1) launch_combine<128>(T, Hq, part, plan.nsplit, gp, op, lse, stream);
+    DSA_ATTN_LAUNCH(128, 2)
+    if (!final_out) launch_combine<128>(T, Hq, part, plan.nsplit, gp, op, lse, stream);
   } else if (D == 64 && Hq == 8) {
-    hipLaunchKernelGGL((sparse_attn_kernel<64, 1>), grid, dim3(256), 0, stream, qp, kp, vp, idx,
-                       K, window, gp, scale, Hq, cu_q, ctx_len, cu_ctx, B, plan.rows_per_split,
-                       op, lse, part, plan.nsplit);
-    if (plan.nsplit > 1) launch_combine<64>(T, Hq, part, plan.nsplit, gp, op, lse, stream);
+    DSA_ATTN_LAUNCH(64, 1)
+    if (!final_out) launch_combine<64>(T, Hq, part, plan.nsplit, gp, op, lse, stream);
   } else {
     return hipErrorInvalidValue;
   }
+#undef DSA_ATTN_LAUNCH
   return hipGetLastError();
 }
 

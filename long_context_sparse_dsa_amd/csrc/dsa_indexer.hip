@@ -107,8 +107,8 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 }
 #undef DSA_WAITV
 
-template <int DI, bool FP8, int TILE, bool REPORT, bool DEEP>
-__global__ __launch_bounds__(64) void index_decode_kernel(
+template <int DI, bool FP8, int TILE, bool REPORT, bool DEEP, int WPT>
+__global__ __launch_bounds__(64 * WPT) void index_decode_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ w, int64_t w_ld,
     const uint8_t* __restrict__ k_idx, const float* __restrict__ k_scale, int H_I,
     const int32_t* __restrict__ ctx_len, const int64_t* __restrict__ cu_ctx,
@@ -116,7 +116,8 @@ __global__ __launch_bounds__(64) void index_decode_kernel(
     int ntiles_max) {
   constexpr int KS = DI / 16;                       // MFMA k-steps
   constexpr int ROWB = FP8 ? DI : 2 * DI;           // bytes per key row
-  using St = KeyStage<ROWB, TILE, FP8, DEEP>;
+  constexpr int TW = TILE / WPT;                    // keys per wave
+  using St = KeyStage<ROWB, TW, FP8, DEEP>;
   constexpr int NSTAGE = St::kNum;
   constexpr int SROWS = St::kRows;
   constexpr int SBLK = SROWS / 32;                  // 32-key blocks per stage
@@ -125,19 +126,21 @@ __global__ __launch_bounds__(64) void index_decode_kernel(
   constexpr int IPB = NI / SBLK;                    // key load instructions per block
   constexpr int NLD = FP8 ? KS / 2 : KS;            // 16-byte operand chunks per lane per block
   constexpr int V = TILE / 64;                      // report values per lane
-  static_assert(KS + 1 + St::kBufs * NL <= 63 && NI % SBLK == 0 && TILE % SROWS == 0,
+  constexpr int VW = TW / 64;                       // stored values per lane and wave
+  static_assert(KS + 1 + St::kBufs * NL <= 63 && NI % SBLK == 0 && TW % SROWS == 0,
                 "stage shape");
+  static_assert(KS % WPT == 0, "query rows split over the waves");
 
   // One LDS object (with several objects the compiler adds a wait for every
   // load in flight before reading any of them):
-  //   [query rows | head weights], later reused for the tile's scores
-  //   [stage buffers]
+  //   [query rows | head weights] [tile scores] [stage buffers of wave 0 | 1 ..]
   constexpr int kQwBytes = 1024 * KS + 256;
-  constexpr int kStageOff = kQwBytes > 4 * TILE ? kQwBytes : 4 * TILE;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kStageOff + St::kBufs * St::kBufBytes];
+  constexpr int kScOff = kQwBytes;
+  constexpr int kStageOff = kScOff + 4 * TILE;
+  constexpr int kWaveStage = St::kBufs * St::kBufBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kStageOff + WPT * kWaveStage];
   uint8_t* const qw_lds = lds;
-  uint8_t* const stage = lds + kStageOff;
-  float* const sc_lds = reinterpret_cast<float*>(lds);  // after the query rows are read
+  float* const sc_lds = reinterpret_cast<float*>(lds + kScOff);
 
   const int b = blockIdx.y, ti = blockIdx.x;
   // both descriptor loads issued together (one round trip)
@@ -147,24 +150,29 @@ __global__ __launch_bounds__(64) void index_decode_kernel(
   // (testing row0 here keeps its load ahead of the branch, in the same round trip)
   if (j0 > p || row0 < 0) return;
   const int n_valid = (int)min<int64_t>(TILE, p + 1 - j0);
-  const int l = lane_id(), g = l >> 5;
+  const int l = lane_id(), g = l >> 5, wv = WPT > 1 ? wave_id() : 0;
+  const int64_t jw0 = j0 + wv * TW;               // first key of this wave
+  uint8_t* const stage = lds + kStageOff + wv * kWaveStage;
 
   // A operand: query heads (rows).  Rows past H_I repeat the last head and
   // get head weight 0, so they add nothing.  The query rows and the head
-  // weights go through LDS too, issued ahead of the key stream: the first
-  // key block's wait then covers them, and every load in flight is of one
-  // kind, which lets the compiler count them in order.
+  // weights go through LDS too, issued ahead of the key stream (the waves
+  // share them, each loading its part): the first key block's wait then
+  // covers them, and every load in flight is of one kind, which lets the
+  // compiler count them in order.
   //   q: instruction s (k-step), lane l -> head l % 32, dims kslot_dim(s, l / 32)
   //   w: lane l -> the aligned dword holding head min(l, H_I - 1)
   {
     const int hc = min(l & 31, H_I - 1);
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
-      lds_dma16(q_idx + ((int64_t)b * H_I + hc) * DI + kslot_dim<FP8>(s, g),
-                                       qw_lds + 1024 * s);
-    const int64_t we = (int64_t)b * w_ld + min(l, H_I - 1);
-    lds_dma4(w + (we & ~(int64_t)1), qw_lds + 1024 * KS);
+    for (int s = wv * (KS / WPT); s < (wv + 1) * (KS / WPT); ++s)
+      lds_dma16(q_idx + ((int64_t)b * H_I + hc) * DI + kslot_dim<FP8>(s, g), qw_lds + 1024 * s);
+    if (wv == 0) {
+      const int64_t we = (int64_t)b * w_ld + min(l, H_I - 1);
+      lds_dma4(w + (we & ~(int64_t)1), qw_lds + 1024 * KS);
+    }
   }
+
   // lane permutation of a load instruction: row l % kRowsPerKiB, chunk l / kRowsPerKiB
   const int lrow = l % St::kRowsPerKiB, lchunk = l / St::kRowsPerKiB;
   // issue the loads of stage st into its buffer (fp8: the key scales first,
@@ -175,16 +183,15 @@ __global__ __launch_bounds__(64) void index_decode_kernel(
     if constexpr (FP8) {
 #pragma unroll
       for (int c = 0; c < St::kScaleLoads; ++c) {
-        const int64_t jl = min<int64_t>(j0 + st * SROWS + 64 * c + l, p);
+        const int64_t jl = min<int64_t>(jw0 + st * SROWS + 64 * c + l, p);
         lds_dma4(k_scale + row0 + jl, buf + St::kKeyBytes + 256 * c);
       }
     }
 #pragma unroll
     for (int c = 0; c < NI; ++c) {
-      const int r = st * SROWS + c * St::kRowsPerKiB + lrow;  // tile row
-      const int64_t jl = min<int64_t>(j0 + r, p);
-      lds_dma16(k_idx + (row0 + jl) * ROWB + 16 * lchunk,
-                                       buf + c * St::kStride);
+      const int r = st * SROWS + c * St::kRowsPerKiB + lrow;  // row of this wave's range
+      const int64_t jl = min<int64_t>(jw0 + r, p);
+      lds_dma16(k_idx + (row0 + jl) * ROWB + 16 * lchunk, buf + c * St::kStride);
     }
   };
   // Every stage of the tile is loaded and scored, also past the last valid
@@ -194,8 +201,10 @@ __global__ __launch_bounds__(64) void index_decode_kernel(
   for (int st = 0; st < St::kBufs; ++st) issue(st);
 
   // Query rows and head weights: they were issued before every stage load,
-  // so they have landed once no more than the stage loads are outstanding.
+  // so they have landed once no more than the stage loads are outstanding
+  // (and, with several waves, once every wave got there).
   wait_vmcnt(St::kBufs * NL);
+  if constexpr (WPT > 1) lds_barrier();
   __builtin_amdgcn_sched_barrier(0);
   bf16x8 qa[KS];
   float wr[16];
@@ -213,10 +222,9 @@ __global__ __launch_bounds__(64) void index_decode_kernel(
     }
   }
 
-  float* const out_row = scores + (int64_t)b * ld + j0;
   // Score one stage.  `later` (a compile-time constant) is the number of
   // stages issued after this one that are still in flight.  Scores go to
-  // global memory and, for the report, to LDS.
+  // the tile's LDS score buffer.
   auto do_stage = [&](int st, auto later_c) {
     constexpr int later = decltype(later_c)::value;
     const uint8_t* buf = stage + (st % St::kBufs) * St::kBufBytes;
@@ -249,10 +257,9 @@ __global__ __launch_bounds__(64) void index_decode_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) sl += wr[r] * fmaxf(sig * acc[r], 0.f);
       sl = xor32_add(sl);
-      // kept in LDS (the query rows there are in registers by now; LDS
-      // operations of one wave are processed in order).  Global stores wait
-      // for the end: a store in flight would count against the loads' waits.
-      if (g == 0) sc_lds[st * SROWS + R] = sl;
+      // kept in LDS; global stores wait for the end: a store in flight would
+      // count against the loads' waits
+      if (g == 0) sc_lds[wv * TW + st * SROWS + R] = sl;
     }
   };
   // steady state: kBufs - 1 later stages in flight; the loop body is one
@@ -272,21 +279,31 @@ __global__ __launch_bounds__(64) void index_decode_kernel(
   if constexpr (NB >= 4) do_stage(NSTAGE - 3, std::integral_constant<int, 2>{});
   if constexpr (NB >= 3) do_stage(NSTAGE - 2, std::integral_constant<int, 1>{});
   if constexpr (NB >= 2) do_stage(NSTAGE - 1, std::integral_constant<int, 0>{});
-  // value i of lane l is tile element 64i + l: coalesced stores, and the
-  // report's registers
-  uint32_t uv[V];
-  int32_t jv[V];
-  bool vv[V];
+
+  // this wave's scores: coalesced stores (value i of lane l is element
+  // 64 i + l of the wave's range; LDS operations of one wave run in order)
+  float* const out_row = scores + (int64_t)b * ld + j0;
 #pragma unroll
-  for (int i = 0; i < V; ++i) {
-    const int jl = 64 * i + l;
-    const float sc = sc_lds[jl];
-    vv[i] = jl < n_valid;
-    if (vv[i]) out_row[jl] = sc;
-    uv[i] = order_key(sc);
-    jv[i] = (int32_t)(j0 + jl);
+  for (int i = 0; i < VW; ++i) {
+    const int jl = wv * TW + 64 * i + l;
+    if (jl < n_valid) out_row[jl] = sc_lds[jl];
   }
   if constexpr (REPORT) {
+    if constexpr (WPT > 1) {
+      lds_barrier();  // every wave's scores are in LDS
+      if (wv != 0) return;
+    }
+    // report value i of lane l is tile element 64 i + l
+    uint32_t uv[V];
+    int32_t jv[V];
+    bool vv[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const int jl = 64 * i + l;
+      vv[i] = jl < n_valid;
+      uv[i] = order_key(sc_lds[jl]);
+      jv[i] = (int32_t)(j0 + jl);
+    }
     const int64_t slot = (int64_t)b * ntiles_max + ti;
     wave_tile_report<V>(uv, jv, vv, hdr + slot, rep_u + slot * kRep, rep_j + slot * kRep);
   }
@@ -300,22 +317,25 @@ static hipError_t launch_decode_tiled(int tile, const uint16_t* q, const uint16_
                                       uint32_t* ru, int32_t* rj, int ntiles_max,
                                       hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   dim3 grid((max_ctx + tile - 1) / tile, B);
-  // deep pipelines when there are few waves per CU (256 CUs)
+  // Few tiles per CU (256 CUs): two waves per tile, each with a deep
+  // pipeline, so more loads are in flight per CU; many tiles: one wave per
+  // tile with a shallow pipeline, so more waves fit in LDS.
   const bool deep = (int64_t)grid.x * B <= 1024;
   // with events: the dispatch itself records them at the kernel's start and end
-#define DSA_DECODE_LAUNCH(KER)                                                                 \
+#define DSA_DECODE_LAUNCH(KER, NT)                                                             \
   if (ev0)                                                                                     \
-    hipExtLaunchKernelGGL(KER, grid, dim3(64), 0, st, ev0, ev1, 0, q, w, w_ld, k, ks, H_I,     \
+    hipExtLaunchKernelGGL(KER, grid, dim3(NT), 0, st, ev0, ev1, 0, q, w, w_ld, k, ks, H_I,     \
                           ctx_len, cu_ctx, scores, ld, hdr, ru, rj, ntiles_max);               \
   else                                                                                         \
-    hipLaunchKernelGGL(KER, grid, dim3(64), 0, st, q, w, w_ld, k, ks, H_I, ctx_len, cu_ctx,    \
+    hipLaunchKernelGGL(KER, grid, dim3(NT), 0, st, q, w, w_ld, k, ks, H_I, ctx_len, cu_ctx,    \
                        scores, ld, hdr, ru, rj, ntiles_max);
 #define DSA_DECODE_TILE(T_)                                                                    \
   case T_:                                                                                     \
     if (deep) {                                                                                \
-      DSA_DECODE_LAUNCH((index_decode_kernel<DI, FP8, T_, REPORT, true>))                      \
+      DSA_DECODE_LAUNCH((index_decode_kernel<DI, FP8, T_, REPORT, true, (T_ >= 128 ? 2 : 1)>), \
+                        64 * (T_ >= 128 ? 2 : 1))                                              \
     } else {                                                                                   \
-      DSA_DECODE_LAUNCH((index_decode_kernel<DI, FP8, T_, REPORT, false>))                     \
+      DSA_DECODE_LAUNCH((index_decode_kernel<DI, FP8, T_, REPORT, false, 1>), 64)              \
     }                                                                                          \
     break;
   switch (tile) {

@@ -223,6 +223,32 @@ def test_sparse_attn_window(dsa, lens, window):
     check_out(out, ref, ATOL_BF16)
 
 
+def test_hybrid_step_swa_layers_then_dsa_layer(dsa):
+    """One decode step of the 5:1 hybrid at a small ragged shape: two
+    sliding-window layers (own K/V caches, ungated, through the prepared-call
+    path the bench uses) and one Gated DSA layer, each against the oracle."""
+    say("hybrid step: 2 SWA layers (window 128) + 1 DSA layer, ragged batch")
+    lens = [130, 5000, 777]
+    w = wl("t", lens, [1] * 3, 16, 128, 64, 128, 256, seed=41)
+    inp = W.make_inputs(w)
+    d = to_dev(inp)
+    ntot = sum(lens)
+    for i in range(2):
+        q = W.randn_bf16((3, 64, 128), 41, f"swa{i}_q")
+        k = W.randn_bf16((ntot, 128), 41, f"swa{i}_k")
+        v = W.randn_bf16((ntot, 128), 41, f"swa{i}_v")
+        out = torch.empty(3, 64, 128, dtype=torch.bfloat16, device=DEV)
+        call = dsa.prepare_sparse_attn(q.to(DEV), k.to(DEV), v.to(DEV), None, d["ctx_len"],
+                                       d["cu_ctx"], max(lens), out, window=128)
+        call()
+        call()  # re-issued: same result
+        torch.cuda.synchronize()
+        ref, _ = oracle.sparse_attn(q, k, v, window=128, ctx_len=inp["ctx_len"],
+                                    cu_ctx=inp["cu_ctx"])
+        check_out(out, ref, ATOL_BF16)
+    _layer_decode_check(dsa, w, inp, d)
+
+
 # --------------------------------------------------------------------------
 # Whole layer
 # --------------------------------------------------------------------------

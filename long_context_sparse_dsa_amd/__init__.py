@@ -28,6 +28,7 @@ EXPORTS = [
     "dsa_topk_workspace_size", "dsa_topk",
     "dsa_sparse_attn_workspace_size", "dsa_sparse_attn",
     "dsa_layer_decode_workspace_size", "dsa_layer_decode", "dsa_set_indexer_events",
+    "dsa_set_topk_counters",
     "dsa_layer_prefill_workspace_size", "dsa_layer_prefill",
 ]
 
@@ -71,8 +72,9 @@ def load(path: str | None = None):
     lib.dsa_layer_prefill.argtypes = [P, P, L, P, I, P, I, I, P, P, P, P, F, I, I, I, P, P, P,
                                       I, I, I, I, P, P, P, S, P]
     lib.dsa_set_indexer_events.argtypes = [P, P]
+    lib.dsa_set_topk_counters.argtypes = [P]
     for fn in ("dsa_index_scores", "dsa_topk", "dsa_sparse_attn", "dsa_layer_decode",
-               "dsa_layer_prefill", "dsa_set_indexer_events"):
+               "dsa_layer_prefill", "dsa_set_indexer_events", "dsa_set_topk_counters"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -324,6 +326,16 @@ def dsa_set_indexer_events(start, stop):
     None, None) around the indexer launch of later dsa_layer_decode calls
     on this thread."""
     _call("dsa_set_indexer_events", start, stop)
+
+
+def dsa_set_topk_counters(counters):
+    """Count, per Top-K row on this thread, the path that produced it into a
+    caller-owned uint32 [3] device tensor (certified union, exact fallback,
+    direct); None stops counting."""
+    if counters is not None:
+        assert counters.dtype == torch.int32
+        assert counters.is_cuda and counters.numel() >= 3 and counters.is_contiguous()
+    _call("dsa_set_topk_counters", None if counters is None else counters.data_ptr())
 
 
 def dsa_layer_prefill_workspace_size(B, T, max_ctx, K, Hq, D) -> int:

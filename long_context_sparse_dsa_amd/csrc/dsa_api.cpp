@@ -122,6 +122,9 @@ size_t prefill_ws_layout(int T, int max_ctx, int K, int Hq, int D, char* base, D
 
 }  // namespace
 
+// Caller-owned Top-K path counters (this thread), or null.
+thread_local uint32_t* t_topk_counters = nullptr;
+
 extern "C" {
 
 const char* dsa_version(void) { return "dsa-mi355x 0.1.0 gfx950"; }
@@ -184,9 +187,9 @@ dsa_status_t dsa_topk(const float* scores, int64_t ld, const int32_t* cu_q,
   DSA_PTR(ws, "ws");
   hipStream_t s = static_cast<hipStream_t>(stream);
   dsa::TopkWs w = dsa::topk_ws_carve(ws, T, max_ctx, K);
-  hipError_t e = dsa::launch_tile_reports(scores, ld, cu_q, ctx_len, B, T, max_ctx, w, s);
+  hipError_t e = dsa::launch_tile_reports(scores, ld, cu_q, ctx_len, B, T, K, w, s);
   if (e == hipSuccess) e = dsa::launch_topk_resolve(scores, ld, cu_q, ctx_len, B, T, K, w, idx,
-                                                    nullptr, s);
+                                                    t_topk_counters, s);
   return hip_status(e, "dsa_topk");
 }
 
@@ -237,6 +240,11 @@ size_t dsa_layer_decode_workspace_size(int B, int max_ctx, int K, int Hq, int D)
 
 // Caller-owned events recorded around the indexer launch (this thread).
 thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
+
+dsa_status_t dsa_set_topk_counters(uint32_t* counters) {
+  t_topk_counters = counters;
+  return DSA_OK;
+}
 
 dsa_status_t dsa_set_indexer_events(void* start, void* stop) {
   DSA_REQUIRE((start == nullptr) == (stop == nullptr), DSA_ERR_INVALID_ARG,
@@ -289,8 +297,8 @@ dsa_status_t dsa_layer_decode(const void* q_idx, const void* w, int64_t w_ld, co
                                           ctx_len, cu_ctx, B, max_ctx, L.scores, L.ld, &L.topk, s,
                                           t_ev_start, t_ev_stop);
   if (e == hipSuccess)
-    e = dsa::launch_topk_resolve(L.scores, L.ld, nullptr, ctx_len, B, B, K, L.topk, idx, nullptr,
-                                 s);
+    e = dsa::launch_topk_resolve(L.scores, L.ld, nullptr, ctx_len, B, B, K, L.topk, idx,
+                                 t_topk_counters, s);
   if (e == hipSuccess) {
     const dsa::AttnPlan plan = dsa::attn_plan(B, K, 0, Hq, D);
     e = dsa::launch_sparse_attn(q, k_cache, v_cache, idx, K, 0, gate, sm_scale, Hq, D, nullptr,
@@ -351,10 +359,10 @@ dsa_status_t dsa_layer_prefill(const void* q_idx, const void* w, int64_t w_ld, c
                                            cu_q, ctx_len, cu_ctx, B, max_q, max_ctx, L.scores,
                                            L.ld, s);
   if (e == hipSuccess)
-    e = dsa::launch_tile_reports(L.scores, L.ld, cu_q, ctx_len, B, T, max_ctx, L.topk, s);
+    e = dsa::launch_tile_reports(L.scores, L.ld, cu_q, ctx_len, B, T, K, L.topk, s);
   if (e == hipSuccess)
-    e = dsa::launch_topk_resolve(L.scores, L.ld, cu_q, ctx_len, B, T, K, L.topk, idx, nullptr,
-                                 s);
+    e = dsa::launch_topk_resolve(L.scores, L.ld, cu_q, ctx_len, B, T, K, L.topk, idx,
+                                 t_topk_counters, s);
   if (e == hipSuccess) {
     const dsa::AttnPlan plan = dsa::attn_plan(T, K, 0, Hq, D);
     e = dsa::launch_sparse_attn(q, k_cache, v_cache, idx, K, 0, gate, sm_scale, Hq, D, cu_q,

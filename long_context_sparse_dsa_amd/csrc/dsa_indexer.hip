@@ -113,7 +113,7 @@ __global__ __launch_bounds__(64 * WPT) void index_decode_kernel(
     const uint8_t* __restrict__ k_idx, const float* __restrict__ k_scale, int H_I,
     const int32_t* __restrict__ ctx_len, const int64_t* __restrict__ cu_ctx,
     float* __restrict__ scores, int64_t ld, RepHeader* hdr, uint32_t* rep_u, int32_t* rep_j,
-    int ntiles_max) {
+    int stride, int topk) {
   constexpr int KS = DI / 16;                       // MFMA k-steps
   constexpr int ROWB = FP8 ? DI : 2 * DI;           // bytes per key row
   constexpr int TW = TILE / WPT;                    // keys per wave
@@ -289,9 +289,18 @@ __global__ __launch_bounds__(64 * WPT) void index_decode_kernel(
     if (jl < n_valid) out_row[jl] = sc_lds[jl];
   }
   if constexpr (REPORT) {
+    const int64_t nrow = p + 1;
+    if (nrow <= kDirectMax) return;  // selected straight from its scores
     if constexpr (WPT > 1) {
       lds_barrier();  // every wave's scores are in LDS
       if (wv != 0) return;
+    }
+    const int S = topk_subtile(nrow, topk);  // divides TILE
+    const int64_t slot = (int64_t)b * stride + (int64_t)ti * (TILE / S);
+    if (S < TILE) {
+      wave_subtile_reports<V>([&](int e) { return sc_lds[e]; }, n_valid, j0, S, hdr + slot,
+                              rep_u + slot * kRep, rep_j + slot * kRep);
+      return;
     }
     // report value i of lane l is tile element 64 i + l
     uint32_t uv[V];
@@ -304,7 +313,6 @@ __global__ __launch_bounds__(64 * WPT) void index_decode_kernel(
       uv[i] = order_key(sc_lds[jl]);
       jv[i] = (int32_t)(j0 + jl);
     }
-    const int64_t slot = (int64_t)b * ntiles_max + ti;
     wave_tile_report<V>(uv, jv, vv, hdr + slot, rep_u + slot * kRep, rep_j + slot * kRep);
   }
 }
@@ -314,7 +322,7 @@ static hipError_t launch_decode_tiled(int tile, const uint16_t* q, const uint16_
                                       int64_t w_ld, const uint8_t* k, const float* ks, int H_I,
                                       const int32_t* ctx_len, const int64_t* cu_ctx, int B,
                                       int max_ctx, float* scores, int64_t ld, RepHeader* hdr,
-                                      uint32_t* ru, int32_t* rj, int ntiles_max,
+                                      uint32_t* ru, int32_t* rj, int stride, int topk,
                                       hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   dim3 grid((max_ctx + tile - 1) / tile, B);
   // Few tiles per CU (256 CUs): two waves per tile, each with a deep
@@ -325,10 +333,10 @@ static hipError_t launch_decode_tiled(int tile, const uint16_t* q, const uint16_
 #define DSA_DECODE_LAUNCH(KER, NT)                                                             \
   if (ev0)                                                                                     \
     hipExtLaunchKernelGGL(KER, grid, dim3(NT), 0, st, ev0, ev1, 0, q, w, w_ld, k, ks, H_I,     \
-                          ctx_len, cu_ctx, scores, ld, hdr, ru, rj, ntiles_max);               \
+                          ctx_len, cu_ctx, scores, ld, hdr, ru, rj, stride, topk);             \
   else                                                                                         \
     hipLaunchKernelGGL(KER, grid, dim3(NT), 0, st, q, w, w_ld, k, ks, H_I, ctx_len, cu_ctx,    \
-                       scores, ld, hdr, ru, rj, ntiles_max);
+                       scores, ld, hdr, ru, rj, stride, topk);
 #define DSA_DECODE_TILE(T_)                                                                    \
   case T_:                                                                                     \
     if (deep) {                                                                                \
@@ -358,14 +366,14 @@ static hipError_t launch_decode_any(bool report, int tile, const uint16_t* q, co
                                     int64_t w_ld, const uint8_t* k, const float* ks, int H_I,
                                     const int32_t* ctx_len, const int64_t* cu_ctx, int B,
                                     int max_ctx, float* scores, int64_t ld, RepHeader* hdr,
-                                    uint32_t* ru, int32_t* rj, int ntiles_max, hipStream_t st,
+                                    uint32_t* ru, int32_t* rj, int stride, int topk, hipStream_t st,
                                     hipEvent_t ev0, hipEvent_t ev1) {
   return report ? launch_decode_tiled<DI, FP8, true>(tile, q, w, w_ld, k, ks, H_I, ctx_len,
                                                      cu_ctx, B, max_ctx, scores, ld, hdr, ru, rj,
-                                                     ntiles_max, st, ev0, ev1)
+                                                     stride, topk, st, ev0, ev1)
                 : launch_decode_tiled<DI, FP8, false>(tile, q, w, w_ld, k, ks, H_I, ctx_len,
                                                       cu_ctx, B, max_ctx, scores, ld, hdr, ru,
-                                                      rj, ntiles_max, st, ev0, ev1);
+                                                      rj, stride, topk, st, ev0, ev1);
 }
 
 hipError_t launch_index_decode(const void* q_idx, const void* w, int64_t w_ld, const void* k_idx,
@@ -377,7 +385,8 @@ hipError_t launch_index_decode(const void* q_idx, const void* w, int64_t w_ld, c
   RepHeader* hdr = reports ? reports->hdr : nullptr;
   uint32_t* ru = reports ? reports->rep_u : nullptr;
   int32_t* rj = reports ? reports->rep_j : nullptr;
-  const int ntm = reports ? reports->ntiles_max : 0;
+  const int ntm = reports ? reports->stride : 0;
+  const int topk = reports ? reports->K : 0;
   auto q = static_cast<const uint16_t*>(q_idx);
   auto wp = static_cast<const uint16_t*>(w);
   auto k = static_cast<const uint8_t*>(k_idx);
@@ -385,16 +394,16 @@ hipError_t launch_index_decode(const void* q_idx, const void* w, int64_t w_ld, c
   const bool rep = reports != nullptr;
   if (d_I == 128 && !fp8)
     return launch_decode_any<128, false>(rep, tile, q, wp, w_ld, k, k_scale, H_I, ctx_len,
-                                         cu_ctx, B, max_ctx, scores, ld, hdr, ru, rj, ntm, stream, ev0, ev1);
+                                         cu_ctx, B, max_ctx, scores, ld, hdr, ru, rj, ntm, topk, stream, ev0, ev1);
   if (d_I == 128 && fp8)
     return launch_decode_any<128, true>(rep, tile, q, wp, w_ld, k, k_scale, H_I, ctx_len, cu_ctx,
-                                        B, max_ctx, scores, ld, hdr, ru, rj, ntm, stream, ev0, ev1);
+                                        B, max_ctx, scores, ld, hdr, ru, rj, ntm, topk, stream, ev0, ev1);
   if (d_I == 64 && !fp8)
     return launch_decode_any<64, false>(rep, tile, q, wp, w_ld, k, k_scale, H_I, ctx_len, cu_ctx,
-                                        B, max_ctx, scores, ld, hdr, ru, rj, ntm, stream, ev0, ev1);
+                                        B, max_ctx, scores, ld, hdr, ru, rj, ntm, topk, stream, ev0, ev1);
   if (d_I == 64 && fp8)
     return launch_decode_any<64, true>(rep, tile, q, wp, w_ld, k, k_scale, H_I, ctx_len, cu_ctx,
-                                       B, max_ctx, scores, ld, hdr, ru, rj, ntm, stream, ev0, ev1);
+                                       B, max_ctx, scores, ld, hdr, ru, rj, ntm, topk, stream, ev0, ev1);
   return hipErrorInvalidValue;
 }
 

@@ -14,20 +14,24 @@ constexpr int kMaxTile = 2048;
 
 // Workspace of the Top-K candidate reports.
 struct TopkWs {
-  int tile;
-  int ntiles_max;
+  int tile;     // positions per report-writing workgroup
+  int ntiles;   // such tiles per row of max_ctx positions
+  int stride;   // report entries (sub-tiles) per row
+  int max_ctx;
+  int K;
   RepHeader* hdr;
   uint32_t* rep_u;
   int32_t* rep_j;
 };
 
 int topk_tile_for(int max_ctx, int K);
+int topk_report_stride(int max_ctx, int K);
 size_t topk_report_bytes(int T, int max_ctx, int K);
 TopkWs topk_ws_carve(void* ws, int T, int max_ctx, int K);
 
 hipError_t launch_tile_reports(const float* scores, int64_t ld, const int32_t* cu_q,
-                               const int32_t* ctx_len, int B, int T, int max_ctx,
-                               const TopkWs& w, hipStream_t stream);
+                               const int32_t* ctx_len, int B, int T, int K, const TopkWs& w,
+                               hipStream_t stream);
 hipError_t launch_topk_resolve(const float* scores, int64_t ld, const int32_t* cu_q,
                                const int32_t* ctx_len, int B, int T, int K, const TopkWs& w,
                                int32_t* idx, uint32_t* stats, hipStream_t stream);

@@ -19,28 +19,37 @@
 //                       If certification fails, or the union does not fit
 //                       LDS, it runs the same exact radix select over the
 //                       whole score row from global memory instead.
+#include <algorithm>
+
 #include "dsa_kernels.h"
 #include "dsa_topk_tile.h"
 
 namespace dsa {
 
-constexpr int kResolveThreads = 1024;
 constexpr int kResolveTiles = 1024;                         // tiles in the fast path
-constexpr int kSlots = kResolveTiles * kRep / kResolveThreads;  // report slots per thread (16)
+constexpr int kResolveSlots = kResolveTiles * kRep;         // union capacity (16384)
 
 template <int TILE>
 __global__ __launch_bounds__(64) void tile_report_kernel(const float* __restrict__ scores,
                                                          int64_t ld, const int32_t* cu_q,
-                                                         const int32_t* ctx_len, int B,
-                                                         int ntiles_max, RepHeader* hdr,
+                                                         const int32_t* ctx_len, int B, int K,
+                                                         int stride, RepHeader* hdr,
                                                          uint32_t* rep_u, int32_t* rep_j) {
   constexpr int V = TILE / 64;
   const int t = blockIdx.y, ti = blockIdx.x;
   const RowInfo ri = row_info(t, cu_q, ctx_len, B);
   const int64_t j0 = (int64_t)ti * TILE;
-  if (j0 > ri.p) return;
-  const int n = (int)min<int64_t>(TILE, ri.p + 1 - j0);
+  const int64_t nrow = ri.p + 1;
+  if (j0 > ri.p || nrow <= kDirectMax) return;  // short rows are selected directly
+  const int n = (int)min<int64_t>(TILE, nrow - j0);
   const float* row = scores + (int64_t)t * ld + j0;
+  const int S = topk_subtile(nrow, K);  // <= TILE
+  const int64_t slot = (int64_t)t * stride + (int64_t)ti * (TILE / S);
+  if (S < TILE) {
+    wave_subtile_reports<V>([&](int e) { return row[e]; }, n, j0, S, hdr + slot,
+                            rep_u + slot * kRep, rep_j + slot * kRep);
+    return;
+  }
   const int l = lane_id();
   uint32_t uv[V];
   int32_t jv[V];
@@ -52,7 +61,6 @@ __global__ __launch_bounds__(64) void tile_report_kernel(const float* __restrict
     uv[i] = order_key(row[vv[i] ? jl : 0]);
     jv[i] = (int32_t)(j0 + jl);
   }
-  const int64_t slot = (int64_t)t * ntiles_max + ti;
   wave_tile_report<V>(uv, jv, vv, hdr + slot, rep_u + slot * kRep, rep_j + slot * kRep);
 }
 
@@ -72,6 +80,7 @@ struct ResolveSmem {
   uint32_t wu[kResolveTiles];
   uint32_t wj[kResolveTiles];
   uint32_t red[64];
+  uint32_t flag[16];
   uint32_t scan[20];
   uint32_t st[8];
 };
@@ -79,12 +88,13 @@ struct ResolveSmem {
 // Wave 0 of the block: given the 2048-bin histogram h of the current
 // bucket and `above` elements strictly above the bucket, find digit d with
 // above + gt(d) < k <= above + gt(d) + h[d] (gt(d): elements in digits > d).
-// Writes st[0] = d, st[1] = above + gt(d), st[5] = h[d].  Lane l owns bins
-// 32 l .. 32 l + 31: it sums them (chunk reads in a lane-rotated order, so
-// fewer lanes share a bank), one wave scan finds the lane holding d, and
-// that lane alone walks its bins.
+// Writes st[0] = d, st[1] = above + gt(d), st[5] = h[d].  Two levels of one
+// wave scan each: the 64 chunks of 32 bins, then the 32 bins of the chunk
+// that holds d.
 __device__ void wave_find_digit(ResolveSmem& sm, const uint32_t* h, uint32_t above, uint32_t k) {
   const int l = lane_id();
+  // level 1: lane l sums bins 32 l .. 32 l + 31 (chunk reads in a
+  // lane-rotated order, so fewer lanes share a bank)
   uint32_t mine = 0;
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
@@ -93,121 +103,75 @@ __device__ void wave_find_digit(ResolveSmem& sm, const uint32_t* h, uint32_t abo
   }
   const uint32_t incl = wave_incl_scan(mine);
   const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
-  uint32_t gt = total - incl;  // elements in the bins of higher lanes
-  if (above + gt < k && above + gt + mine >= k) {
-#pragma unroll 1
-    for (int c2 = 3; c2 >= 0; --c2) {  // two chunks per step
-      const u32x4 v1 = *reinterpret_cast<const u32x4*>(h + 32 * l + 8 * c2 + 4);
-      const u32x4 v0 = *reinterpret_cast<const u32x4*>(h + 32 * l + 8 * c2);
-      const uint32_t vv[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-#pragma unroll
-      for (int i = 7; i >= 0; --i) {
-        if (above + gt < k && above + gt + vv[i] >= k) {
-          sm.st[0] = 32 * l + 8 * c2 + i;
-          sm.st[1] = above + gt;
-          sm.st[5] = vv[i];
-        }
-        gt += vv[i];
-      }
-    }
+  const uint32_t gt = total - incl;  // elements in the bins of higher lanes
+  const uint64_t m1 = __ballot(above + gt < k && above + gt + mine >= k);
+  const int L = m1 ? __ffsll((long long)m1) - 1 : 0;  // the chunk holding the k-th
+  const uint32_t base = above + (uint32_t)__builtin_amdgcn_readlane((int)gt, L);
+  // level 2: lane i < 32 takes bin 32 L + i; elements in the chunk's higher
+  // bins come from one more scan
+  const uint32_t x = l < 32 ? h[32 * L + l] : 0u;
+  const uint32_t incl2 = wave_incl_scan(x);
+  const uint32_t gt2 = base + (uint32_t)__builtin_amdgcn_readlane((int)incl2, 31) - incl2;
+  const bool hit = l < 32 && gt2 < k && gt2 + x >= k;
+  if (hit) {
+    sm.st[0] = 32 * L + l;
+    sm.st[1] = gt2;
+    sm.st[5] = x;
   }
 }
 
-// Exact threshold (tau_u, tau_j) over an array source; `get(i, &u, &j)`
-// returns element i (in ascending position order).  Result in st[2], st[3].
-template <typename Get>
-__device__ void exact_threshold(ResolveSmem& sm, int64_t n, uint32_t k, Get get) {
-  const int tid = threadIdx.x, nt = blockDim.x;
-  uint32_t prefix = 0, above = 0;
-  const int shifts[3] = {21, 10, 0};
-  const uint32_t masks[3] = {0x7ffu, 0x7ffu, 0x3ffu};
-  for (int pass = 0; pass < 3; ++pass) {
-    const int sh = shifts[pass];
-    for (int i = tid; i < 2048; i += nt) sm.hist[i] = 0;
-    lds_barrier();
-    for (int64_t i = tid; i < n; i += nt) {
-      uint32_t u;
-      int32_t j;
-      get(i, &u, &j);
-      bool in = pass == 0 ? true : (pass == 1 ? (u >> 21) == prefix : (u >> 10) == prefix);
-      if (in) atomicAdd(&sm.hist[(u >> sh) & masks[pass]], 1u);
-    }
-    lds_barrier();
-    if (wave_id() == 0) wave_find_digit(sm, sm.hist, above, k);
-    lds_barrier();
-    const uint32_t d = sm.st[0];
-    above = sm.st[1];
-    prefix = pass == 0 ? d : (pass == 1 ? ((prefix << 11) | d) : ((prefix << 10) | d));
-    lds_barrier();
-  }
-  const uint32_t tau_u = prefix;
-  const uint32_t need = k - above;  // >= 1 elements equal to tau_u, lowest positions
-  // tie rank in position order, processed in rounds of nt elements
-  if (tid == 0) sm.st[3] = 0xffffffffu;
-  uint32_t base = 0;
-  for (int64_t r0 = 0; r0 < n; r0 += nt) {
-    int64_t i = r0 + tid;
-    uint32_t u = 0;
-    int32_t j = -1;
-    if (i < n) get(i, &u, &j);
-    uint32_t f = (i < n && u == tau_u) ? 1u : 0u;
-    uint32_t tot;
-    uint32_t ex = block_excl_scan(f, sm.scan, &tot);
-    if (f && base + ex == need - 1) sm.st[3] = (uint32_t)j;
-    base += tot;
-    if (base >= need) break;  // uniform: tot is block-wide
-  }
-  if (tid == 0) sm.st[2] = tau_u;
-  lds_barrier();
-}
-
-// Fast path of the resolve.  The union of the row's tile reports (up to
-// 1024 tiles x kRep slots) is loaded with fully coalesced 16-byte loads:
-// wave w, load q, lane l holds slots s = 1024w + 256q + 4l + e (e < 4),
-// i.e. slot (4l+e) % kRep of tile s / kRep.  Slot order is position order, so a
-// position-ordered scan over the union is a per-q wave scan plus one
-// cross-wave prefix.  Per-slot validity is a bitmask (bit 4q+e) and the
-// per-element work is branch-free.
-constexpr int kQN = kSlots / 4;  // 16-byte loads per thread
-
+// Register path of the resolve.  A candidate set in position order (the
+// union of a row's sub-tile reports: slot s is slot s % kRep of sub-tile
+// s / kRep; or, for a direct row, slot s is position s) is held q-major:
+// group q of thread tid holds slots 4 nt q + 4 tid + e (e < 4, nt threads).
+// The first qn groups of all threads therefore hold the first 4 nt qn slots,
+// and every loop skips the groups at or beyond qn (block-uniform), so a short
+// set costs no more than its size.  Loads are coalesced 16-byte loads;
+// per-slot validity is a bitmask (bit 4q+e).
+template <int NSL>
 struct UnionRegs {
-  uint32_t u[kSlots];
-  int32_t j[kSlots];
+  uint32_t u[NSL];
+  int32_t j[NSL];
   uint32_t vmask;  // bit i: slot i holds a candidate
+  int qn;          // live groups
 };
 
-__device__ __forceinline__ int slot_index(int wv, int q, int l) { return 1024 * wv + 256 * q + 4 * l; }
+__device__ __forceinline__ int slot_of(int q, int tid, int nt) { return 4 * nt * q + 4 * tid; }
 
-// Exclusive position-ordered prefix of per-slot flags (bitmask, bit 4q+e);
-// returns each slot's rank among flagged slots and the total.  Also ORs the
-// per-thread flag `bad` over the block into *any_bad (same exchange).
-__device__ void ordered_ranks(ResolveSmem& sm, uint32_t fmask, uint32_t (&rank)[kSlots],
-                              uint32_t* total, bool bad = false, bool* any_bad = nullptr) {
-  const int l = lane_id(), wv = wave_id(), nw = blockDim.x >> 6;
-  uint32_t lane_ex[kQN], qoff[kQN];
-  uint32_t woff = 0;
+// Exclusive position-ordered prefix of per-slot flags (bitmask, bit 4q+e)
+// over the live groups; returns each slot's rank among flagged slots and the
+// total.  Also ORs the per-thread flag `bad` over the block into *any_bad
+// (same exchange).  One cross-wave exchange of the per-(group, wave) counts
+// (at most 64 of them: NSL/4 groups x nt/64 waves).  nt: active threads.
+template <int NSL>
+__device__ __forceinline__ void ordered_ranks(ResolveSmem& sm, uint32_t fmask, int qn, int nt,
+                                              uint32_t (&rank)[NSL], uint32_t* total,
+                                              bool bad = false, bool* any_bad = nullptr) {
+  static_assert((NSL / 4) * (kResolveSlots / NSL / 64) <= 64, "exchange size");
+  const int l = lane_id(), wv = wave_id(), nw = nt >> 6;
+  uint32_t lane_ex[NSL / 4];
 #pragma unroll
-  for (int q = 0; q < kQN; ++q) {
-    const uint32_t c = (uint32_t)__popc((fmask >> (4 * q)) & 15u);
-    const uint32_t inc = wave_incl_scan(c);
-    lane_ex[q] = inc - c;
-    qoff[q] = woff;
-    woff += (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+  for (int q = 0; q < NSL / 4; ++q) {
+    lane_ex[q] = 0;
+    if (q < qn) {
+      const uint32_t c = (uint32_t)__popc((fmask >> (4 * q)) & 15u);
+      const uint32_t inc = wave_incl_scan(c);
+      lane_ex[q] = inc - c;
+      if (l == 63) sm.red[q * nw + wv] = inc;
+    }
   }
   const bool wbad = __ballot(bad) != 0;
-  if (l == 0) {
-    sm.red[wv] = woff;
-    sm.red[32 + wv] = wbad ? 1u : 0u;
-  }
+  if (l == 0) sm.flag[wv] = wbad ? 1u : 0u;
   lds_barrier();
-  const uint32_t wt = l < nw ? sm.red[l] : 0u;
-  const uint32_t wi = wave_incl_scan(wt);
-  const uint32_t wbase = (uint32_t)__builtin_amdgcn_readlane((int)(wi - wt), wv);
-  *total = (uint32_t)__builtin_amdgcn_readlane((int)wi, 63);
-  if (any_bad) *any_bad = __ballot(l < nw && sm.red[32 + l] != 0u) != 0;
+  const uint32_t x = l < qn * nw ? sm.red[l] : 0u;
+  const uint32_t xi = wave_incl_scan(x);
+  const uint32_t xe = xi - x;
+  *total = (uint32_t)__builtin_amdgcn_readlane((int)xi, 63);
+  if (any_bad) *any_bad = __ballot(l < nw && sm.flag[l] != 0u) != 0;
 #pragma unroll
-  for (int q = 0; q < kQN; ++q) {
-    const uint32_t r = wbase + qoff[q] + lane_ex[q];
+  for (int q = 0; q < NSL / 4; ++q) {
+    uint32_t r = 0;
+    if (q < qn) r = (uint32_t)__builtin_amdgcn_readlane((int)xe, q * nw + wv) + lane_ex[q];
     const uint32_t m = (fmask >> (4 * q)) & 15u;
     rank[4 * q + 0] = r;
     rank[4 * q + 1] = r + (m & 1u);
@@ -217,19 +181,92 @@ __device__ void ordered_ranks(ResolveSmem& sm, uint32_t fmask, uint32_t (&rank)[
   lds_barrier();
 }
 
-// Exact K-th best candidate of the union: selected <=> key > tau_u, or
+// Appends the candidates with keys in [lo, lo + width) to sm.bu / sm.bj:
+// per-wave ballot compaction at a base taken with one LDS atomic per wave
+// (sm.st[4] counts the bucket; the caller guarantees at most kBucketMax).
+template <int NSL>
+__device__ __forceinline__ void gather_bucket(ResolveSmem& sm, const UnionRegs<NSL>& R,
+                                              uint32_t lo, uint64_t width) {
+  const int l = lane_id();
+  uint32_t inb = 0, cnt = 0;
+#pragma unroll
+  for (int i = 0; i < NSL; ++i) {
+    if (i / 4 < R.qn) {
+      const uint32_t x = R.u[i];
+      const bool in = ((R.vmask >> i) & 1u) && x >= lo && (uint64_t)(x - lo) < width;
+      inb |= (uint32_t)in << i;
+      cnt += popc64(__ballot(in));
+    }
+  }
+  if (cnt == 0) return;
+  uint32_t base = 0;
+  if (l == 0) base = atomicAdd(&sm.st[4], cnt);
+  base = (uint32_t)__builtin_amdgcn_readlane((int)base, 0);
+  const uint64_t below = lanes_below();
+#pragma unroll
+  for (int i = 0; i < NSL; ++i) {
+    if (i / 4 < R.qn) {
+      const bool in = (inb >> i) & 1u;
+      const uint64_t m = __ballot(in);
+      if (in) {
+        const uint32_t pos = base + popc64(m & below);
+        sm.bu[pos] = R.u[i];
+        sm.bj[pos] = R.j[i];
+      }
+      base += popc64(m);
+    }
+  }
+}
+
+// Wave 0 ranks the h <= kBucketMax gathered candidates under (key desc,
+// position asc) and writes the need-th one to st[2] (key), st[3] (position).
+// Every lane reads the whole bucket (broadcast reads, all issued at once).
+// Called by the whole block; ends with a barrier.
+__device__ __forceinline__ void rank_bucket(ResolveSmem& sm, uint32_t h, uint32_t need) {
+  const int l = lane_id();
+  if (wave_id() == 0) {
+    const bool mine_ok = (uint32_t)l < h;
+    const uint32_t um = mine_ok ? sm.bu[l] : 0u;
+    const int32_t jm = mine_ok ? sm.bj[l] : 0;
+    uint32_t rank = 0;
+#pragma unroll 1
+    for (int q0 = 0; q0 < (int)h; q0 += 16) {
+      u32x4 uq[4], jq[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        uq[c] = *reinterpret_cast<const u32x4*>(sm.bu + q0 + 4 * c);
+        jq[c] = *reinterpret_cast<const u32x4*>(sm.bj + q0 + 4 * c);
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          rank += (uint32_t)(q0 + 4 * c + e) < h &&
+                  ((uq[c][e] > um) || (uq[c][e] == um && (int32_t)jq[c][e] < jm));
+    }
+    if (mine_ok && rank == need - 1) {
+      sm.st[2] = um;
+      sm.st[3] = (uint32_t)jm;
+    }
+  }
+  lds_barrier();
+}
+
+// Exact K-th best candidate of the set: selected <=> key > tau_u, or
 // key == tau_u and position <= tau_j.  Radix digits (11, 11, 10 bits) are
-// taken relative to the union's key range [mn, mx], so the first pass
+// taken relative to the set's key range [mn, mx], so the first pass
 // spreads the candidates over the 2048 bins instead of piling them onto the
 // few bins the leading exponent bits would give.  Each pass is one LDS
 // histogram and one wave-0 digit search (the other waves clear the other
 // histogram meanwhile).  As soon as the boundary bucket holds at most
 // kBucketMax candidates they are gathered and wave 0 ranks them directly
 // under (key desc, position asc), which gives (tau_u, tau_j) at once.  Both
-// histograms are zero and st[4] is 0 on entry.
-__device__ void union_threshold(ResolveSmem& sm, const UnionRegs& R, uint32_t k, uint32_t mn,
-                                uint32_t mx, uint32_t* tau_u, int32_t* tau_j) {
-  const int tid = threadIdx.x, nt = blockDim.x, wv = wave_id(), l = lane_id();
+// histograms are zero and st[4] is 0 on entry.  nt: active threads.
+template <int NSL>
+__device__ __forceinline__ void union_threshold(ResolveSmem& sm, const UnionRegs<NSL>& R,
+                                                uint32_t k, uint32_t mn, uint32_t mx, int nt,
+                                                uint32_t* tau_u, int32_t* tau_j) {
+  const int tid = threadIdx.x, wv = wave_id();
   const uint32_t range = mx - mn;
   // bucket = keys in [lo, lo + width); digits (key - lo) >> shift are < 2048
   int shift = range == 0 ? 0 : max(0, 32 - __clz(range) - 11);
@@ -242,14 +279,18 @@ __device__ void union_threshold(ResolveSmem& sm, const UnionRegs& R, uint32_t k,
     uint32_t* hc = (pass & 1) ? sm.hist2 : sm.hist;
     uint32_t* hn = (pass & 1) ? sm.hist : sm.hist2;
 #pragma unroll
-    for (int i = 0; i < kSlots; ++i) {
-      const uint32_t x = R.u[i];
-      const bool in = ((R.vmask >> i) & 1u) && x >= lo && (uint64_t)(x - lo) < width;
-      if (in) atomicAdd(&hc[(x - lo) >> shift], 1u);
+    for (int i = 0; i < NSL; ++i) {
+      if (i / 4 < R.qn) {
+        const uint32_t x = R.u[i];
+        const bool in = ((R.vmask >> i) & 1u) && x >= lo && (uint64_t)(x - lo) < width;
+        if (in) atomicAdd(&hc[(x - lo) >> shift], 1u);
+      }
     }
     lds_barrier();
     if (wv == 0) {
       wave_find_digit(sm, hc, above, k);
+      if (nt == 64)  // a single wave clears the next pass's histogram itself
+        for (int i = tid; i < 2048; i += 64) hn[i] = 0;
     } else {
       for (int i = tid - 64; i < 2048; i += nt - 64) hn[i] = 0;  // next pass's histogram
     }
@@ -266,61 +307,9 @@ __device__ void union_threshold(ResolveSmem& sm, const UnionRegs& R, uint32_t k,
   }
   const uint32_t need = k - above;  // 1..h: the need-th best of the bucket is theta
   if (h <= (uint32_t)kBucketMax) {
-    // gather the bucket: per-wave ballot compaction at a base taken with
-    // one LDS atomic per wave
-    uint32_t inb = 0, cnt = 0;
-#pragma unroll
-    for (int i = 0; i < kSlots; ++i) {
-      const uint32_t x = R.u[i];
-      const bool in = ((R.vmask >> i) & 1u) && x >= lo && (uint64_t)(x - lo) < width;
-      inb |= (uint32_t)in << i;
-      cnt += popc64(__ballot(in));
-    }
-    if (cnt) {
-      uint32_t base = 0;
-      if (l == 0) base = atomicAdd(&sm.st[4], cnt);
-      base = (uint32_t)__builtin_amdgcn_readlane((int)base, 0);
-      const uint64_t below = lanes_below();
-#pragma unroll
-      for (int i = 0; i < kSlots; ++i) {
-        const bool in = (inb >> i) & 1u;
-        const uint64_t m = __ballot(in);
-        if (in) {
-          const uint32_t pos = base + popc64(m & below);
-          sm.bu[pos] = R.u[i];
-          sm.bj[pos] = R.j[i];
-        }
-        base += popc64(m);
-      }
-    }
+    gather_bucket(sm, R, lo, width);
     lds_barrier();
-    if (wv == 0) {
-      const bool mine_ok = (uint32_t)l < h;
-      const uint32_t um = mine_ok ? sm.bu[l] : 0u;
-      const int32_t jm = mine_ok ? sm.bj[l] : 0;
-      // every lane reads the whole bucket (broadcast reads, all issued at once)
-      uint32_t rank = 0;
-#pragma unroll 1
-      for (int q0 = 0; q0 < (int)h; q0 += 16) {
-        u32x4 uq[4], jq[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          uq[c] = *reinterpret_cast<const u32x4*>(sm.bu + q0 + 4 * c);
-          jq[c] = *reinterpret_cast<const u32x4*>(sm.bj + q0 + 4 * c);
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            rank += (uint32_t)(q0 + 4 * c + e) < h &&
-                    ((uq[c][e] > um) || (uq[c][e] == um && (int32_t)jq[c][e] < jm));
-      }
-      if (mine_ok && rank == need - 1) {
-        sm.st[2] = um;
-        sm.st[3] = (uint32_t)jm;
-      }
-    }
-    lds_barrier();
+    rank_bucket(sm, h, need);
     *tau_u = sm.st[2];
     *tau_j = (int32_t)sm.st[3];
     return;
@@ -330,166 +319,409 @@ __device__ void union_threshold(ResolveSmem& sm, const UnionRegs& R, uint32_t k,
   *tau_u = lo;
   uint32_t inb = 0;
 #pragma unroll
-  for (int i = 0; i < kSlots; ++i)
+  for (int i = 0; i < NSL; ++i)
     inb |= (uint32_t)(((R.vmask >> i) & 1u) && R.u[i] == lo) << i;
-  uint32_t rk[kSlots], tot;
-  ordered_ranks(sm, inb, rk, &tot);
+  uint32_t rk[NSL], tot;
+  ordered_ranks<NSL>(sm, inb, R.qn, nt, rk, &tot);
   if (tid == 0) sm.st[3] = 0x7fffffffu;
   lds_barrier();
   if (need < tot) {
 #pragma unroll
-    for (int i = 0; i < kSlots; ++i)
+    for (int i = 0; i < NSL; ++i)
       if (((inb >> i) & 1u) && rk[i] == need - 1) sm.st[3] = (uint32_t)R.j[i];
   }
   lds_barrier();
   *tau_j = (int32_t)sm.st[3];
 }
 
-__global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(
-    const float* __restrict__ scores, int64_t ld, const int32_t* cu_q, const int32_t* ctx_len,
-    int B, int K, int tile, int ntiles_max, const RepHeader* __restrict__ hdr,
-    const uint32_t* __restrict__ rep_u, const int32_t* __restrict__ rep_j, int32_t* idx,
-    uint32_t* stats) {
-  __shared__ ResolveSmem sm;
-  const int t = blockIdx.x, tid = threadIdx.x, nt = blockDim.x, l = lane_id(), wv = wave_id();
-  const int64_t slot0 = (int64_t)t * ntiles_max;
-  const int nslots = ntiles_max * kRep;
-  // Issue the report loads together with the descriptor loads: one round trip.
-  UnionRegs R;
-  RepHeader hq[kQN];
-  {
-    u32x4 a[kQN], c[kQN];
+// Threshold, selection and coalesced store for a candidate set held in
+// registers.  With ntiles > 0 the set is a report union and is certified
+// against the sub-tile headers kept in sm.wu / sm.wj.  Returns false,
+// leaving `out` untouched, when the set has fewer than k candidates or the
+// certification fails.  nt: active threads.
+template <int NSL>
+__device__ __forceinline__ bool select_from_regs(ResolveSmem& sm, const UnionRegs<NSL>& R,
+                                                 uint32_t k, int K, int ntiles, int nt,
+                                                 int32_t* out) {
+  const int tid = threadIdx.x, l = lane_id(), wv = wave_id();
+  // candidate count and key range, in one block reduction; both histograms
+  // are cleared meanwhile
+  uint32_t mn = 0xffffffffu, mx = 0u;
 #pragma unroll
-    for (int q = 0; q < kQN; ++q) {
-      const int sidx = slot_index(wv, q, l);
-      const int sc = sidx < nslots ? sidx : 0;
-      a[q] = *reinterpret_cast<const u32x4*>(rep_u + slot0 * kRep + sc);
-      c[q] = *reinterpret_cast<const u32x4*>(rep_j + slot0 * kRep + sc);
-      hq[q] = hdr[slot0 + sc / kRep];
-    }
-#pragma unroll
-    for (int q = 0; q < kQN; ++q)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        R.u[4 * q + e] = a[q][e];
-        R.j[4 * q + e] = (int32_t)c[q][e];
-      }
-  }
-  const RowInfo ri = row_info(t, cu_q, ctx_len, B);
-  const int64_t n = ri.p + 1;
-  int32_t* out = idx + (int64_t)t * K;
-  if (n <= K) {
-    for (int i = tid; i < K; i += nt) out[i] = i < n ? i : -1;
-    return;
-  }
-  const uint32_t k = (uint32_t)K;
-  const int ntiles = (int)((n + tile - 1) / tile);
-  R.vmask = 0;
-#pragma unroll
-  for (int q = 0; q < kQN; ++q) {
-    const int sidx = slot_index(wv, q, l);
-    const bool tile_ok = sidx < nslots && sidx / kRep < ntiles;
-    const uint32_t sub = (uint32_t)(sidx % kRep);
-    const uint32_t cnt = hq[q].count;
-    // slots sub .. sub+3 of the tile are valid while below its count
-    const uint32_t nv = tile_ok ? (cnt > sub ? min(cnt - sub, 4u) : 0u) : 0u;
-    R.vmask |= ((1u << nv) - 1u) << (4 * q);
-    if (sub == 0 && sidx < nslots) {
-      sm.wu[sidx / kRep] = hq[q].worst_u;
-      sm.wj[sidx / kRep] = (uint32_t)hq[q].worst_j | (hq[q].complete ? 0x80000000u : 0u);
-    }
-  }
-  bool ok = false;
-  if (ntiles <= kResolveTiles && ntiles <= ntiles_max) {
-    // candidate count and key range of the union, in one block reduction;
-    // both histograms are cleared meanwhile
-    uint32_t mn = 0xffffffffu, mx = 0u;
-#pragma unroll
-    for (int i = 0; i < kSlots; ++i) {
+  for (int i = 0; i < NSL; ++i) {
+    if (i / 4 < R.qn) {
       const bool vi = (R.vmask >> i) & 1u;
       mn = min(mn, vi ? R.u[i] : 0xffffffffu);
       mx = max(mx, vi ? R.u[i] : 0u);
     }
-    const uint32_t cw = wave_sum_u32((uint32_t)__popc(R.vmask));
-    mn = wave_min_u32(mn);
-    mx = wave_max_u32(mx);
-    if (l == 0) {
-      sm.red[wv] = cw;
-      sm.red[16 + wv] = mn;
-      sm.red[32 + wv] = mx;
-    }
-    for (int i = tid; i < 2048; i += nt) {
-      sm.hist[i] = 0;
-      sm.hist2[i] = 0;
-    }
-    if (tid == 0) sm.st[4] = 0;
-    lds_barrier();
-    uint32_t C;
-    {
-      const int nw = nt >> 6;
-      C = wave_sum_u32(l < nw ? sm.red[l] : 0u);
-      mn = wave_min_u32(l < nw ? sm.red[16 + l] : 0xffffffffu);
-      mx = wave_max_u32(l < nw ? sm.red[32 + l] : 0u);
-    }
-    lds_barrier();  // red[] is reused below
-    if (C >= k) {
-      uint32_t tau_u;
-      int32_t tau_j;
-      union_threshold(sm, R, k, mn, mx, &tau_u, &tau_j);
-      // ---- certification: every partly reported tile ends at or below
-      // theta (checked in the same block exchange as the ranks) ----
-      bool bad = false;
-      if (tid < ntiles) {
-        const uint32_t wu = sm.wu[tid], wj = sm.wj[tid];
-        const bool complete = wj >> 31;
-        const int32_t wpos = (int32_t)(wj & 0x7fffffffu);
-        bad = !complete && !((wu < tau_u) || (wu == tau_u && wpos >= tau_j));
-      }
-      uint32_t smask = 0;
+  }
+  const uint32_t cw = wave_sum_u32((uint32_t)__popc(R.vmask));
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
+  if (l == 0) {
+    sm.red[wv] = cw;
+    sm.red[16 + wv] = mn;
+    sm.red[32 + wv] = mx;
+  }
+  for (int i = tid; i < 2048; i += nt) {
+    sm.hist[i] = 0;
+    sm.hist2[i] = 0;
+  }
+  if (tid == 0) sm.st[4] = 0;
+  lds_barrier();
+  uint32_t C;
+  {
+    const int nw = nt >> 6;
+    C = wave_sum_u32(l < nw ? sm.red[l] : 0u);
+    mn = wave_min_u32(l < nw ? sm.red[16 + l] : 0xffffffffu);
+    mx = wave_max_u32(l < nw ? sm.red[32 + l] : 0u);
+  }
+  lds_barrier();  // red[] is reused below
+  if (C < k) return false;
+  uint32_t tau_u;
+  int32_t tau_j;
+  union_threshold(sm, R, k, mn, mx, nt, &tau_u, &tau_j);
+  // certification: every partly reported sub-tile ends at or below theta
+  // (checked in the same block exchange as the ranks)
+  bool bad = false;
+  for (int ti = tid; ti < ntiles; ti += nt) {
+    const uint32_t wu = sm.wu[ti], wj = sm.wj[ti];
+    const bool complete = wj >> 31;
+    const int32_t wpos = (int32_t)(wj & 0x7fffffffu);
+    bad |= !complete && !((wu < tau_u) || (wu == tau_u && wpos >= tau_j));
+  }
+  uint32_t smask = 0;
 #pragma unroll
-      for (int i = 0; i < kSlots; ++i) {
-        const bool si = ((R.vmask >> i) & 1u) &&
-                        ((R.u[i] > tau_u) || (R.u[i] == tau_u && R.j[i] <= tau_j));
-        smask |= (uint32_t)si << i;
-      }
-      uint32_t rk[kSlots], total;
-      bool any_bad = false;
-      ordered_ranks(sm, smask, rk, &total, bad, &any_bad);
-      ok = !any_bad;
-      if (ok) {
-        // stage in LDS, then store coalesced
+  for (int i = 0; i < NSL; ++i) {
+    const bool si = ((R.vmask >> i) & 1u) &&
+                    ((R.u[i] > tau_u) || (R.u[i] == tau_u && R.j[i] <= tau_j));
+    smask |= (uint32_t)si << i;
+  }
+  uint32_t rk[NSL], total;
+  bool any_bad = false;
+  ordered_ranks<NSL>(sm, smask, R.qn, nt, rk, &total, bad, &any_bad);
+  if (any_bad) return false;
+  // stage in LDS, then store coalesced
 #pragma unroll
-        for (int i = 0; i < kSlots; ++i)
-          if (((smask >> i) & 1u) && rk[i] < k) sm.stage[rk[i]] = R.j[i];
-        lds_barrier();
-        for (int i = tid; i < K; i += nt) out[i] = sm.stage[i];
-        if (stats && tid == 0) atomicAdd(&stats[0], 1u);
-      }
+  for (int i = 0; i < NSL; ++i)
+    if (((smask >> i) & 1u) && rk[i] < k) sm.stage[rk[i]] = R.j[i];
+  lds_barrier();
+  for (int i = tid; i < K; i += nt) out[i] = sm.stage[i];
+  return true;
+}
+
+// Exclusive prefix sum of one value per thread over the nw active waves;
+// *total receives the sum.  Contains barriers.
+__device__ __forceinline__ uint32_t excl_scan_active(ResolveSmem& sm, uint32_t v, int nw,
+                                                     uint32_t* total) {
+  const int l = lane_id(), wv = wave_id();
+  const uint32_t inc = wave_incl_scan(v);
+  if (l == 63) sm.scan[wv] = inc;
+  lds_barrier();
+  const uint32_t x = l < nw ? sm.scan[l] : 0u;
+  const uint32_t xi = wave_incl_scan(x);
+  const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)(xi - x), wv);
+  *total = (uint32_t)__builtin_amdgcn_readlane((int)xi, 63);
+  lds_barrier();
+  return base + inc - v;
+}
+
+// Sixteen consecutive keys of a row from position p0 (a multiple of 16);
+// returns the validity mask.  `vec`: the row is 16-byte aligned and its
+// stride a multiple of four, so 16-byte loads below n stay inside it.
+__device__ __forceinline__ uint32_t load_keys16(const float* row, int64_t n, int64_t p0, bool vec,
+                                                uint32_t (&u)[16]) {
+  uint32_t vm = 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int64_t p = p0 + 4 * c;
+    float f[4];
+    if (vec) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(row + (p < n ? p : 0));
+      f[0] = v[0];
+      f[1] = v[1];
+      f[2] = v[2];
+      f[3] = v[3];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f[e] = row[p + e < n ? p + e : 0];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool v = p + e < n;
+      u[4 * c + e] = v ? order_key(f[e]) : 0u;
+      vm |= (uint32_t)v << (4 * c + e);
     }
   }
-  if (!ok) {
-    // ---- exact fallback straight from the score row ----
-    const float* row = scores + (int64_t)t * ld;
-    auto get = [&](int64_t i, uint32_t* uu, int32_t* jj) {
-      *uu = order_key(row[i]);
-      *jj = (int32_t)i;
-    };
-    exact_threshold(sm, n, k, get);
-    const uint32_t tau_u = sm.st[2];
-    const int32_t tau_j = (int32_t)sm.st[3];
-    uint32_t base = 0;
-    for (int64_t r0 = 0; r0 < n; r0 += nt) {
-      int64_t i = r0 + tid;
-      uint32_t f = 0;
-      if (i < n) {
-        uint32_t uu = order_key(row[i]);
-        f = (uu > tau_u) || (uu == tau_u && (int32_t)i <= tau_j);
-      }
-      uint32_t tot;
-      uint32_t ex = block_excl_scan(f, sm.scan, &tot);
-      if (f && base + ex < k) out[base + ex] = (int32_t)i;
-      base += tot;
+  return vm;
+}
+
+// Exact Top-k of a whole score row from global memory, for rows the
+// register paths cannot take (a failed certification, too many sub-tiles).
+// Compact code: each sweep is a rolled loop over chunks of 16 consecutive
+// positions per thread.  One sweep for the key range, range-relative radix
+// histograms (11 bits per sweep) until the boundary bucket holds at most
+// kBucketMax keys or a single key; the bucket is gathered and ranked
+// directly (or, for one key shared by many positions, its need lowest
+// positions are found with ordered block scans); a last ordered sweep
+// writes the selected positions in ascending order.
+__device__ __forceinline__ void exact_select_row(ResolveSmem& sm, const float* row, int64_t n,
+                                                 uint32_t k, bool vec, int nt, int32_t* out) {
+  const int tid = threadIdx.x, l = lane_id(), wv = wave_id(), nw = nt >> 6;
+  const int64_t step = 16 * (int64_t)nt;
+  uint32_t u[16];
+  uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll 1
+  for (int64_t b0 = 0; b0 < n; b0 += step) {
+    const uint32_t vm = load_keys16(row, n, b0 + 16 * tid, vec, u);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const bool v = (vm >> i) & 1u;
+      mn = min(mn, v ? u[i] : 0xffffffffu);
+      mx = max(mx, v ? u[i] : 0u);
     }
+  }
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
+  if (l == 0) {
+    sm.red[16 + wv] = mn;
+    sm.red[32 + wv] = mx;
+  }
+  for (int i = tid; i < 2048; i += nt) sm.hist[i] = 0;
+  if (tid == 0) sm.st[4] = 0;
+  lds_barrier();
+  mn = wave_min_u32(l < nw ? sm.red[16 + l] : 0xffffffffu);
+  mx = wave_max_u32(l < nw ? sm.red[32 + l] : 0u);
+  const uint32_t range = mx - mn;
+  int shift = range == 0 ? 0 : max(0, 32 - __clz(range) - 11);
+  uint32_t lo = mn;
+  uint64_t width = (uint64_t)range + 1;
+  uint32_t above = 0, h = 0;
+#pragma unroll 1
+  while (true) {
+#pragma unroll 1
+    for (int64_t b0 = 0; b0 < n; b0 += step) {
+      const uint32_t vm = load_keys16(row, n, b0 + 16 * tid, vec, u);
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (((vm >> i) & 1u) && u[i] >= lo && (uint64_t)(u[i] - lo) < width)
+          atomicAdd(&sm.hist[(u[i] - lo) >> shift], 1u);
+    }
+    lds_barrier();
+    if (wv == 0) wave_find_digit(sm, sm.hist, above, k);
+    lds_barrier();
+    const uint32_t d = sm.st[0];
+    above = sm.st[1];
+    h = sm.st[5];
+    const uint64_t off = (uint64_t)d << shift;
+    lo += (uint32_t)off;
+    width = min<uint64_t>(width - off, 1ull << shift);
+    if (shift == 0 || h <= (uint32_t)kBucketMax) break;
+    shift = max(0, shift - 11);
+    for (int i = tid; i < 2048; i += nt) sm.hist[i] = 0;
+    lds_barrier();
+  }
+  const uint32_t need = k - above;  // 1..h
+  uint32_t tau_u;
+  int32_t tau_j;
+  if (h <= (uint32_t)kBucketMax) {
+#pragma unroll 1
+    for (int64_t b0 = 0; b0 < n; b0 += step) {
+      const int64_t p0 = b0 + 16 * tid;
+      const uint32_t vm = load_keys16(row, n, p0, vec, u);
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (((vm >> i) & 1u) && u[i] >= lo && (uint64_t)(u[i] - lo) < width) {
+          const uint32_t pos = atomicAdd(&sm.st[4], 1u);
+          sm.bu[pos] = u[i];
+          sm.bj[pos] = (int32_t)(p0 + i);
+        }
+    }
+    lds_barrier();
+    rank_bucket(sm, h, need);
+    tau_u = sm.st[2];
+    tau_j = (int32_t)sm.st[3];
+  } else {
+    // one key shared by more than kBucketMax positions: its need lowest
+    tau_u = lo;
+    if (tid == 0) sm.st[3] = 0x7fffffffu;
+    uint32_t cum = 0;
+#pragma unroll 1
+    for (int64_t b0 = 0; b0 < n && cum < need; b0 += step) {
+      const int64_t p0 = b0 + 16 * tid;
+      const uint32_t vm = load_keys16(row, n, p0, vec, u);
+      uint32_t f = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) f |= (uint32_t)(((vm >> i) & 1u) && u[i] == lo) << i;
+      uint32_t tot;
+      uint32_t r = cum + excl_scan_active(sm, (uint32_t)__popc(f), nw, &tot);
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if ((f >> i) & 1u) {
+          if (r == need - 1) sm.st[3] = (uint32_t)(p0 + i);
+          ++r;
+        }
+      cum += tot;
+    }
+    lds_barrier();
+    tau_j = (int32_t)sm.st[3];
+  }
+  uint32_t cum = 0;
+#pragma unroll 1
+  for (int64_t b0 = 0; b0 < n && cum < k; b0 += step) {
+    const int64_t p0 = b0 + 16 * tid;
+    const uint32_t vm = load_keys16(row, n, p0, vec, u);
+    uint32_t f = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      f |= (uint32_t)(((vm >> i) & 1u) &&
+                      ((u[i] > tau_u) || (u[i] == tau_u && (int32_t)(p0 + i) <= tau_j)))
+           << i;
+    uint32_t tot;
+    uint32_t r = cum + excl_scan_active(sm, (uint32_t)__popc(f), nw, &tot);
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if ((f >> i) & 1u) {
+        if (r < k) out[r] = (int32_t)(p0 + i);
+        ++r;
+      }
+    cum += tot;
+  }
+}
+
+// One workgroup per row.  Rows of at most kDirectMax positions are selected
+// from their scores directly; longer rows from the union of their sub-tile
+// reports, certified; anything else (a failed certification, more
+// sub-tiles than the block holds) by the exact select over the row.
+//
+// The block is sized for the most slots any row may need; a row that needs
+// fewer threads lets the surplus waves exit before the first barrier (a
+// barrier waits only for the waves still running), so it pays for the
+// threads it uses.  The first eager_q groups of report loads, laid out for
+// eager_nt threads (the layout a row of max_ctx positions uses), are issued
+// before the row's length is known: one round trip for the common case at
+// small batch.  A row that needs another layout or more groups loads them
+// after.
+template <int NSL>
+__global__ __launch_bounds__(kResolveSlots / NSL) void topk_resolve_kernel(
+    const float* __restrict__ scores, int64_t ld, const int32_t* cu_q, const int32_t* ctx_len,
+    int B, int K, int stride, int eager_nt, int eager_q, const RepHeader* __restrict__ hdr,
+    const uint32_t* __restrict__ rep_u, const int32_t* __restrict__ rep_j, int32_t* idx,
+    uint32_t* stats) {
+  constexpr int QN = NSL / 4;
+  __shared__ ResolveSmem sm;
+  const int t = blockIdx.x, tid = threadIdx.x, nb = blockDim.x;
+  const int64_t slot0 = (int64_t)t * stride;
+  const int nslots = min(stride, kResolveTiles) * kRep;  // a row's slots in the workspace
+  UnionRegs<NSL> R;
+  RepHeader hq[QN];
+  // report loads of groups [q0, q1) in the layout of nt threads: slots,
+  // positions and sub-tile headers
+  auto load_reports = [&](int q0, int q1, int nt) {
+#pragma unroll
+    for (int q = 0; q < QN; ++q) {
+      if (q >= q0 && q < q1) {
+        const int sidx = slot_of(q, tid, nt);
+        const int sc = sidx < nslots ? sidx : 0;
+        const u32x4 a = *reinterpret_cast<const u32x4*>(rep_u + slot0 * kRep + sc);
+        const u32x4 c = *reinterpret_cast<const u32x4*>(rep_j + slot0 * kRep + sc);
+        hq[q] = hdr[slot0 + sc / kRep];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          R.u[4 * q + e] = a[e];
+          R.j[4 * q + e] = (int32_t)c[e];
+        }
+      }
+    }
+  };
+  if (tid < eager_nt) load_reports(0, eager_q, eager_nt);
+  const RowInfo ri = row_info(t, cu_q, ctx_len, B);
+  const int64_t n = ri.p + 1;
+  int32_t* out = idx + (int64_t)t * K;
+  if (n <= K) {
+    for (int i = tid; i < K; i += nb) out[i] = i < n ? i : -1;
+    return;
+  }
+  const uint32_t k = (uint32_t)K;
+  const float* row = scores + (int64_t)t * ld;
+  const bool vec = ((ld & 3) == 0) && ((reinterpret_cast<uintptr_t>(scores) & 15) == 0);
+  // threads (whole waves) for a set of `slots` candidates
+  auto threads_for = [&](int64_t slots) {
+    const int64_t w = (slots + 64 * NSL - 1) / (64 * NSL);
+    return (int)min<int64_t>(nb, 64 * max<int64_t>(w, 1));
+  };
+  int path = -1;   // counter index of the register path taken: 0 union, 2 direct
+  int ntiles = 0;  // sub-tiles to certify (union path)
+  int nt = nb;     // active threads
+  R.vmask = 0;
+  if (n <= kDirectMax && n <= (int64_t)nb * NSL) {
+    // ---- direct: slot s holds position s ----
+    nt = threads_for(n);
+    if (tid >= nt) return;
+    R.qn = (int)((n + 4 * nt - 1) / (4 * nt));
+#pragma unroll
+    for (int q = 0; q < QN; ++q) {
+      if (q < R.qn) {
+        const int p = slot_of(q, tid, nt);
+        float f[4];
+        if (vec) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(row + (p < n ? p : 0));
+          f[0] = v[0];
+          f[1] = v[1];
+          f[2] = v[2];
+          f[3] = v[3];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) f[e] = row[p + e < n ? p + e : 0];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool v = p + e < n;
+          R.u[4 * q + e] = v ? order_key(f[e]) : 0u;
+          R.j[4 * q + e] = p + e;
+          R.vmask |= (uint32_t)v << (4 * q + e);
+        }
+      }
+    }
+    path = 2;
+  } else {
+    const int S = topk_subtile(n, K);
+    const int nt_row = (int)((n + S - 1) / S);
+    if (nt_row <= kResolveTiles && nt_row <= stride && nt_row * kRep <= nb * NSL) {
+      nt = max(threads_for((int64_t)nt_row * kRep), eager_nt);
+      if (tid >= nt) return;
+      R.qn = (nt_row * kRep + 4 * nt - 1) / (4 * nt);
+      if (nt != eager_nt)
+        load_reports(0, R.qn, nt);  // another layout: load every group
+      else if (R.qn > eager_q)
+        load_reports(eager_q, R.qn, nt);
+#pragma unroll
+      for (int q = 0; q < QN; ++q) {
+        if (q < R.qn) {
+          const int sidx = slot_of(q, tid, nt);
+          const bool tile_ok = sidx / kRep < nt_row;
+          const uint32_t sub = (uint32_t)(sidx % kRep);
+          const uint32_t cnt = hq[q].count;
+          // slots sub .. sub+3 of the sub-tile are valid while below its count
+          const uint32_t nv = tile_ok ? (cnt > sub ? min(cnt - sub, 4u) : 0u) : 0u;
+          R.vmask |= ((1u << nv) - 1u) << (4 * q);
+          if (sub == 0 && tile_ok) {
+            sm.wu[sidx / kRep] = hq[q].worst_u;
+            sm.wj[sidx / kRep] = (uint32_t)hq[q].worst_j | (hq[q].complete ? 0x80000000u : 0u);
+          }
+        }
+      }
+      path = 0;
+      ntiles = nt_row;
+    }
+  }
+  bool ok = false;
+  if (path >= 0) {
+    ok = select_from_regs(sm, R, k, K, ntiles, nt, out);
+    if (ok && stats && tid == 0) atomicAdd(&stats[path], 1u);
+  }
+  if (!ok) {
+    exact_select_row(sm, row, n, k, vec, nt, out);
     if (stats && tid == 0) atomicAdd(&stats[1], 1u);
   }
 }
@@ -497,31 +729,47 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
-// Tile size: a power of two in [64, 2048] with at most kResolveTiles tiles
-// per row and about four of the row's top K expected per tile, so that a
-// tile rarely holds more than kRep of them (which would send the row to
-// the exact fallback).
+// Tile of the report-writing kernels (the indexer epilogue and
+// tile_report_kernel): the sub-tile size of the longest row, at least one
+// wave of positions.  Sub-tile sizes never decrease with the row length, so
+// every row's sub-tiles divide this tile.
+static_assert(kSubMax == kMaxTile, "report tile range");
 int topk_tile_for(int max_ctx, int K) {
-  const int64_t k = K > 0 ? K : 1;
-  const int64_t per4 = (4LL * max_ctx) / k;  // about four winners per tile
-  const int64_t by_tiles = ((int64_t)max_ctx + kResolveTiles - 1) / kResolveTiles;
-  int tile = 64;
-  while (tile < kMaxTile && 2LL * tile <= per4) tile <<= 1;   // round down
-  while (tile < kMaxTile && tile < by_tiles) tile <<= 1;      // tile-count cap
-  return tile;
+  const int s = topk_subtile(max_ctx, K);
+  return s < 64 ? 64 : s;
+}
+
+// Report entries per row: the most sub-tiles any row of kDirectMax < n <=
+// max_ctx positions has.  Over each range of n with one sub-tile size the
+// longest row has the most, so only the top of each range is checked.
+int topk_report_stride(int max_ctx, int K) {
+  int64_t best = 1;
+  int64_t n = max_ctx;
+  while (n > kDirectMax) {
+    const int s = topk_subtile(n, K);
+    best = std::max<int64_t>(best, (n + s - 1) / s);
+    int64_t lo = kDirectMax + 1, hi = n;  // smallest m with topk_subtile(m) == s
+    while (lo < hi) {
+      const int64_t mid = lo + (hi - lo) / 2;
+      if (topk_subtile(mid, K) >= s) hi = mid; else lo = mid + 1;
+    }
+    n = lo - 1;
+  }
+  return (int)best;
 }
 
 size_t topk_report_bytes(int T, int max_ctx, int K) {
-  const int tile = topk_tile_for(max_ctx, K);
-  const int64_t ntiles = (max_ctx + tile - 1) / tile;
-  return (size_t)T * ntiles * (sizeof(RepHeader) + kRep * 8);
+  return (size_t)T * topk_report_stride(max_ctx, K) * (sizeof(RepHeader) + kRep * 8);
 }
 
 TopkWs topk_ws_carve(void* ws, int T, int max_ctx, int K) {
   TopkWs w;
   w.tile = topk_tile_for(max_ctx, K);
-  w.ntiles_max = (max_ctx + w.tile - 1) / w.tile;
-  const size_t nslot = (size_t)T * w.ntiles_max;
+  w.ntiles = (max_ctx + w.tile - 1) / w.tile;
+  w.stride = topk_report_stride(max_ctx, K);
+  w.max_ctx = max_ctx;
+  w.K = K;
+  const size_t nslot = (size_t)T * w.stride;
   char* p = static_cast<char*>(ws);
   w.hdr = reinterpret_cast<RepHeader*>(p);
   p += nslot * sizeof(RepHeader);
@@ -532,14 +780,15 @@ TopkWs topk_ws_carve(void* ws, int T, int max_ctx, int K) {
 }
 
 hipError_t launch_tile_reports(const float* scores, int64_t ld, const int32_t* cu_q,
-                               const int32_t* ctx_len, int B, int T, int max_ctx,
-                               const TopkWs& w, hipStream_t stream) {
-  dim3 grid(w.ntiles_max, T);
+                               const int32_t* ctx_len, int B, int T, int K, const TopkWs& w,
+                               hipStream_t stream) {
+  if (w.max_ctx <= kDirectMax) return hipSuccess;  // every row is selected directly
+  dim3 grid(w.ntiles, T);
   switch (w.tile) {
 #define DSA_TILE_CASE(T_)                                                                       \
   case T_:                                                                                      \
     hipLaunchKernelGGL(tile_report_kernel<T_>, grid, dim3(64), 0, stream, scores, ld, cu_q,    \
-                       ctx_len, B, w.ntiles_max, w.hdr, w.rep_u, w.rep_j);                     \
+                       ctx_len, B, K, w.stride, w.hdr, w.rep_u, w.rep_j);                      \
     break;
     DSA_TILE_CASE(64)
     DSA_TILE_CASE(128)
@@ -557,11 +806,31 @@ hipError_t launch_tile_reports(const float* scores, int64_t ld, const int32_t* c
 hipError_t launch_topk_resolve(const float* scores, int64_t ld, const int32_t* cu_q,
                                const int32_t* ctx_len, int B, int T, int K, const TopkWs& w,
                                int32_t* idx, uint32_t* stats, hipStream_t stream) {
-  // one thread per tile (16 report slots each), 64 .. 1024 threads
-  int nt = ((w.ntiles_max + 63) / 64) * 64;
-  nt = nt < 64 ? 64 : (nt > kResolveThreads ? kResolveThreads : nt);
-  hipLaunchKernelGGL(topk_resolve_kernel, dim3(T), dim3(nt), 0, stream, scores, ld,
-                     cu_q, ctx_len, B, K, w.tile, w.ntiles_max, w.hdr, w.rep_u, w.rep_j, idx,
+  // Register slots the longest need: kRep per sub-tile, or one per position
+  // of a direct row; 16 per thread (at most 1024 threads).  Rows needing
+  // fewer run with fewer waves.
+  constexpr int NSL = 16;
+  const int direct = std::min(w.max_ctx, kDirectMax);
+  const int64_t cap = std::min<int64_t>(kResolveSlots,
+                                        std::max<int64_t>((int64_t)w.stride * kRep, direct));
+  auto threads = [](int64_t slots) {
+    const int64_t wv = (slots + 64 * NSL - 1) / (64 * NSL);
+    return (int)(64 * std::max<int64_t>(wv, 1));
+  };
+  const int nt = threads(cap);
+  // Few rows: the report groups a row of max_ctx positions uses are loaded
+  // before the row length is known (latency), spread over the whole block
+  // (fewer slots per thread is faster than fewer waves); many rows: after
+  // (traffic).
+  int eager_nt = 0, eager_q = 0;
+  if (T <= 256 && w.max_ctx > kDirectMax) {
+    const int s = topk_subtile(w.max_ctx, K);
+    const int64_t slots = std::min<int64_t>(cap, (int64_t)((w.max_ctx + s - 1) / s) * kRep);
+    eager_nt = nt;
+    eager_q = (int)((slots + 4 * eager_nt - 1) / (4 * eager_nt));
+  }
+  hipLaunchKernelGGL(topk_resolve_kernel<NSL>, dim3(T), dim3(nt), 0, stream, scores, ld, cu_q,
+                     ctx_len, B, K, w.stride, eager_nt, eager_q, w.hdr, w.rep_u, w.rep_j, idx,
                      stats);
   return hipGetLastError();
 }

@@ -23,6 +23,28 @@ namespace dsa {
 
 constexpr int kRep = 16;  // candidates reported per tile
 
+// Rows of at most kDirectMax positions are selected straight from their
+// scores (the whole row fits the resolve block's registers); longer rows
+// are reported in sub-tiles of topk_subtile(n, K) positions.
+constexpr int kDirectMax = 16384;
+constexpr int kSubMin = 32;
+constexpr int kSubMax = 2048;
+constexpr int kSubTiles = 1024;  // most sub-tiles a row may have on the fast path
+
+// Sub-tile size for a row of n positions: the largest power of two S in
+// [kSubMin, kSubMax] with S <= 4 n / K (about four of the row's top K per
+// sub-tile, so one rarely holds more than kRep of them), raised until the row
+// has at most kSubTiles sub-tiles.  Non-decreasing in n.
+__host__ __device__ inline int topk_subtile(int64_t n, int K) {
+  const int64_t k = K > 0 ? K : 1;
+  const int64_t per4 = 4 * n / k;
+  const int64_t by_tiles = (n + kSubTiles - 1) / kSubTiles;
+  int s = kSubMin;
+  while (s < kSubMax && 2 * (int64_t)s <= per4) s <<= 1;
+  while (s < kSubMax && s < by_tiles) s <<= 1;
+  return s;
+}
+
 struct RepHeader {
   uint32_t count;     // reported elements
   uint32_t complete;  // 1: every element of the tile is reported
@@ -123,6 +145,110 @@ __device__ void wave_tile_report(const uint32_t (&u)[V], const int32_t (&j)[V],
     h.worst_u = wu;
     h.worst_j = wj;
     *hdr = h;
+  }
+}
+
+// Sub-tile reports of one tile of 64 V positions whose row uses sub-tiles of
+// S < 64 V positions (S a power of two, S >= V).  The tile holds NS = 64 V / S
+// sub-tiles; each is served by a group of g = S / V consecutive lanes, lane r
+// of group s holding the sub-tile's elements r + g i (i < V), so that the
+// order (i, r) is position order.  Every count is a wave ballot masked to the
+// group, so all groups bisect at once.  `get(e)` returns the score of tile
+// element e (e < n_valid); sub-tile s of the tile writes report s (header
+// hdr[s], slots rep[kRep s ..]) when it holds at least one valid element.
+template <int V, typename Get>
+__device__ void wave_subtile_reports(Get get, int n_valid, int64_t j0, int S, RepHeader* hdr,
+                                     uint32_t* rep_u, int32_t* rep_j) {
+  const int l = lane_id();
+  const int g = S / V;
+  const int lg = 31 - __clz(g);
+  const int grp = l >> lg, r = l & (g - 1);
+  const int sh = grp << lg;
+  const uint64_t gm = g >= 64 ? ~0ull : ((1ull << g) - 1ull);
+  const uint64_t below_r = (1ull << r) - 1ull;
+  const int e0 = grp * S + r;
+  uint32_t u[V];
+  uint32_t vmask = 0;
+  uint32_t nv = 0, mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const int e = e0 + g * i;
+    const bool v = e < n_valid;
+    u[i] = v ? order_key(get(e)) : 0u;
+    vmask |= (uint32_t)v << i;
+    nv += popc64((__ballot(v) >> sh) & gm);
+    if (v) {
+      mn = min(mn, u[i]);
+      mx = max(mx, u[i]);
+    }
+  }
+  for (int o = 1; o < g; o <<= 1) {
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+  }
+  const bool complete = nv <= (uint32_t)kRep;
+  // per group: largest T with count(key >= T) >= kRep (invalid keys are 0
+  // and every probe is >= 1); stops early on a probe with exactly kRep
+  uint32_t lo = mn, hi = mx;
+  bool done = complete || lo >= hi;
+  while (__ballot(!done) != 0ull) {
+    const uint32_t mid = lo + ((hi - lo) >> 1) + 1;
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i) c += popc64((__ballot(u[i] >= mid) >> sh) & gm);
+    if (!done) {
+      if (c == (uint32_t)kRep) {
+        lo = mid;
+        done = true;
+      } else {
+        if (c > (uint32_t)kRep) lo = mid; else hi = mid - 1;
+        done = lo >= hi;
+      }
+    }
+  }
+  const uint32_t T = lo;
+  uint32_t gt = 0;
+#pragma unroll
+  for (int i = 0; i < V; ++i) gt += popc64((__ballot(((vmask >> i) & 1u) && u[i] > T) >> sh) & gm);
+  const uint32_t need = (uint32_t)kRep - gt;  // copies of T kept, lowest positions first
+  uint32_t sel = 0, seen = 0;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const bool v = (vmask >> i) & 1u;
+    const bool eq = v && u[i] == T;
+    const uint64_t m = (__ballot(eq) >> sh) & gm;
+    const bool si = complete ? v : ((v && u[i] > T) || (eq && seen + popc64(m & below_r) < need));
+    sel |= (uint32_t)si << i;
+    seen += popc64(m);
+  }
+  // compaction in position order; worst reported element per group
+  const bool live = grp * S < n_valid;
+  uint32_t base = 0, wu = 0xffffffffu;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const bool si = (sel >> i) & 1u;
+    const uint64_t m = (__ballot(si) >> sh) & gm;
+    if (si && live) {
+      const uint32_t pos = base + popc64(m & below_r);
+      rep_u[grp * kRep + pos] = u[i];
+      rep_j[grp * kRep + pos] = (int32_t)(j0 + e0 + g * i);
+    }
+    if (si) wu = min(wu, u[i]);
+    base += popc64(m);
+  }
+  for (int o = 1; o < g; o <<= 1) wu = min(wu, (uint32_t)__shfl_xor((int)wu, o));
+  int32_t wj = -1;
+#pragma unroll
+  for (int i = 0; i < V; ++i)
+    if (((sel >> i) & 1u) && u[i] == wu) wj = max(wj, (int32_t)(j0 + e0 + g * i));
+  for (int o = 1; o < g; o <<= 1) wj = max(wj, __shfl_xor(wj, o));
+  if (r == 0 && live) {
+    RepHeader h;
+    h.count = base;
+    h.complete = complete ? 1u : 0u;
+    h.worst_u = wu;
+    h.worst_j = wj;
+    hdr[grp] = h;
   }
 }
 

@@ -164,6 +164,55 @@ def test_topk_one_million_rows(dsa):
     assert np.array_equal(got.cpu().numpy(), want)
 
 
+# Row lengths around each boundary of the selection paths, in one ragged
+# batch whose longest row sets the report tile: direct rows (at most 16384
+# positions), 32-position sub-tiles just above, sub-tiles smaller than the
+# tile (with up to 1024 of them per row), and the longest row itself.
+RAGGED_TOPK_LENS = [5000, 16384, 16385, 20000, 31000, 70000, 131071, 131072, 300000, 1 << 20]
+
+
+def _with_counters(dsa, fn):
+    cnt = torch.zeros(3, dtype=torch.int32, device=DEV)
+    dsa.dsa_set_topk_counters(cnt)
+    try:
+        res = fn()
+    finally:
+        dsa.dsa_set_topk_counters(None)
+    torch.cuda.synchronize()
+    return res, cnt.cpu().numpy()
+
+
+@pytest.mark.parametrize("kind", ["normal", "relu_like", "ties"])
+def test_topk_ragged_rows_subtile_reports(dsa, kind):
+    say(f"topk ragged rows {kind}: direct / sub-tile / full-tile paths")
+    lens, K = RAGGED_TOPK_LENS, 2048
+    L = max(lens)
+    s = torch.stack([_topk_case(kind, L, seed=100 + i) for i in range(len(lens))])
+    ctx = torch.tensor(lens, dtype=torch.int32)
+    got, c = _with_counters(dsa, lambda: dsa.dsa_topk(s.to(DEV), K, ctx.to(DEV), max_ctx=L))
+    want = oracle.topk(s.numpy(), K, ctx.numpy())
+    assert np.array_equal(got.cpu().numpy(), want)
+    n_direct = sum(1 for n in lens if K < n <= 16384)
+    assert c[2] == n_direct
+    assert c[0] + c[1] == len(lens) - n_direct
+    if kind != "ties":   # continuous scores: every long row certifies
+        assert c[1] == 0
+
+
+def test_topk_clustered_rows_take_the_exact_fallback(dsa):
+    say("topk clustered winners: exact fallback")
+    lens, K = [40000, 131072, 70001], 2048
+    L = max(lens)
+    s = torch.zeros(len(lens), L)
+    for i, n in enumerate(lens):
+        s[i, :n] = _topk_case("clustered", n, seed=7 + i)   # winners packed in a few tiles
+    ctx = torch.tensor(lens, dtype=torch.int32)
+    got, c = _with_counters(dsa, lambda: dsa.dsa_topk(s.to(DEV), K, ctx.to(DEV), max_ctx=L))
+    want = oracle.topk(s.numpy(), K, ctx.numpy())
+    assert np.array_equal(got.cpu().numpy(), want)
+    assert c[1] == len(lens)
+
+
 # --------------------------------------------------------------------------
 # Gated sparse attention
 # --------------------------------------------------------------------------
@@ -293,6 +342,15 @@ def test_layer_decode_ragged_batch_and_short_rows(dsa):
            plant_frac=0.05)
     inp = W.make_inputs(w)
     _layer_decode_check(dsa, w, inp, to_dev(inp))
+
+
+def test_layer_decode_ragged_lengths_take_the_fast_paths(dsa):
+    say("layer_decode ragged lengths 4096..400000: direct and sub-tile selection")
+    lens = [4096, 9000, 17000, 24000, 60000, 150000, 400000]
+    w = wl("t", lens, [1] * len(lens), 16, 128, 64, 128, 2048, seed=51, plant_frac=0.05)
+    inp = W.make_inputs(w)
+    _, c = _with_counters(dsa, lambda: _layer_decode_check(dsa, w, inp, to_dev(inp)))
+    assert c[2] == 2 and c[0] == len(lens) - 2 and c[1] == 0
 
 
 def test_layer_decode_k_at_least_context_is_dense_attention(dsa):

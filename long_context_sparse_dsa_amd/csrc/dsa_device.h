@@ -163,6 +163,13 @@ __device__ __forceinline__ float wave_max_f32(float v) {
   return __uint_as_float(x);
 }
 
+// max(x, 0) as one integer max on the bit pattern: every float with the
+// sign bit set (negative values, -0.0) becomes +0.0, the rest pass.  fmaxf
+// would first canonicalize x (a second instruction per element).
+__device__ __forceinline__ float relu(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
 // Workgroup barrier that orders LDS accesses only.  __syncthreads() also
 // waits for every outstanding global load and store of the wave (vmcnt(0));
 // none of the barriers in these kernels protects global memory, so they use
@@ -171,6 +178,20 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Workgroup barrier that waits only for this wave's own LDS instructions.
+// The release fence of lds_barrier() also waits for every direct
+// global-to-LDS load still in flight (they count as LDS writes) and for the
+// wave's global stores, which empties a prefetch pipeline at every barrier.
+// Waves that order their direct loads with explicit vmcnt waits, or only
+// have stores in flight, use this one; the empty asm statements keep the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void dma_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // Exclusive block-wide prefix sum of one value per thread.  `scratch` holds

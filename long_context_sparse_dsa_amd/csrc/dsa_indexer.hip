@@ -134,9 +134,14 @@ __global__ __launch_bounds__(64 * WPT) void index_decode_kernel(
   // One LDS object (with several objects the compiler adds a wait for every
   // load in flight before reading any of them):
   //   [query rows | head weights] [tile scores] [stage buffers of wave 0 | 1 ..]
+  // A single wave has its query rows and weights in registers before it
+  // writes its first score (LDS operations of one wave run in order), so
+  // there the scores overlay the query region: less LDS per workgroup, more
+  // workgroups (loads in flight) per CU.  Several waves read the shared
+  // query region at their own pace, so they keep the regions apart.
   constexpr int kQwBytes = 1024 * KS + 256;
-  constexpr int kScOff = kQwBytes;
-  constexpr int kStageOff = kScOff + 4 * TILE;
+  constexpr int kScOff = WPT == 1 ? 0 : kQwBytes;
+  constexpr int kStageOff = (kScOff + 4 * TILE) > kQwBytes ? (kScOff + 4 * TILE) : kQwBytes;
   constexpr int kWaveStage = St::kBufs * St::kBufBytes;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kStageOff + WPT * kWaveStage];
   uint8_t* const qw_lds = lds;
@@ -204,7 +209,7 @@ __global__ __launch_bounds__(64 * WPT) void index_decode_kernel(
   // so they have landed once no more than the stage loads are outstanding
   // (and, with several waves, once every wave got there).
   wait_vmcnt(St::kBufs * NL);
-  if constexpr (WPT > 1) lds_barrier();
+  if constexpr (WPT > 1) dma_barrier();
   __builtin_amdgcn_sched_barrier(0);
   bf16x8 qa[KS];
   float wr[16];
@@ -255,7 +260,7 @@ __global__ __launch_bounds__(64 * WPT) void index_decode_kernel(
       }
       float sl = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sl += wr[r] * fmaxf(sig * acc[r], 0.f);
+      for (int r = 0; r < 16; ++r) sl += wr[r] * relu(sig * acc[r]);
       sl = xor32_add(sl);
       // kept in LDS; global stores wait for the end: a store in flight would
       // count against the loads' waits
@@ -292,7 +297,7 @@ __global__ __launch_bounds__(64 * WPT) void index_decode_kernel(
     const int64_t nrow = p + 1;
     if (nrow <= kDirectMax) return;  // selected straight from its scores
     if constexpr (WPT > 1) {
-      lds_barrier();  // every wave's scores are in LDS
+      dma_barrier();  // every wave's scores are in LDS
       if (wv != 0) return;
     }
     const int S = topk_subtile(nrow, topk);  // divides TILE
@@ -423,18 +428,21 @@ struct RowMap {
   }
 };
 
-// Prefill workgroup = NCW compute waves + one loader wave + one storer wave.
+// Prefill workgroup = NCW compute waves + one loader wave.
 //   - the loader streams the key range in 64-key stages into a ring of
 //     NBUF LDS buffers with direct global-to-LDS loads; its load counter
 //     tracks nothing else, so its waits are exact;
 //   - the compute waves hold their query heads (A operand, MB blocks of 32
 //     (query, head) rows) in registers, run the MFMAs on the stage's keys,
-//     apply ReLU / head weights / head sum in registers and write the
-//     stage's scores into an LDS double buffer; they never touch global
-//     memory inside the loop;
-//   - the storer writes the previous stage's scores to global memory
-//     (causal positions only) and never waits on its stores.
-// One workgroup barrier per stage orders the three roles.
+//     apply ReLU / head weights / head sum in registers and store the
+//     stage's scores (causal positions only) straight from registers; they
+//     never wait on their stores.  Compute waves 4 and up run half a stage
+//     late: each stage they first finish the previous stage's epilogue
+//     (vector ALU) and then issue this stage's MFMAs, so on a SIMD shared
+//     with an on-time wave one wave's epilogue overlaps the other's matrix
+//     work instead of all waves alternating in step.
+// One workgroup barrier per stage orders the two roles; it waits for no
+// memory traffic (the loader waits for its stages explicitly).
 template <int DI, int HI, bool FP8>
 struct PrefillShape {
   static constexpr int KT = 64;                          // keys per stage
@@ -454,7 +462,7 @@ struct PrefillShape {
 };
 
 template <int DI, int HI, bool FP8, int MB, int NCW, int NBUF>
-__global__ __launch_bounds__(64 * (NCW + 2)) void index_prefill_kernel(
+__global__ __launch_bounds__(64 * (NCW + 1)) void index_prefill_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ w, int64_t w_ld,
     const uint8_t* __restrict__ k_idx, const float* __restrict__ k_scale,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ ctx_len,
@@ -469,9 +477,8 @@ __global__ __launch_bounds__(64 * (NCW + 2)) void index_prefill_kernel(
   constexpr int NLD = FP8 ? KS / 2 : KS;     // 16-byte operand chunks per lane per key block
   static_assert(PS::NL * (NBUF - 1) <= 63, "loads in flight");
 
-  __shared__ __attribute__((aligned(16))) uint8_t lds[NBUF * PS::BUFB + 2 * QWG * PS::SCW * 4];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NBUF * PS::BUFB];
   uint8_t* const ring = lds;
-  float* const sc = reinterpret_cast<float*>(lds + NBUF * PS::BUFB);
 
   const int b = blockIdx.z, qt = blockIdx.y, split = blockIdx.x;
   const int nq = cu_q[b + 1] - cu_q[b];
@@ -512,48 +519,11 @@ __global__ __launch_bounds__(64 * (NCW + 2)) void index_prefill_kernel(
       // stage i has landed once only the stages issued after it are in flight
       const int later = min(NBUF - 2, nst - 1 - i);
       wait_vmcnt(later * PS::NL);
-      lds_barrier();
+      dma_barrier();
       if (i + NBUF - 1 < nst) issue(i + NBUF - 1);  // into the buffer of stage i - 1
     }
-    lds_barrier();
     return;
   }
-  if (wv == NCW + 1) {
-    // ---------------- storer ----------------
-    const bool vec = (ld & 3) == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
-    auto store_stage = [&](int k) {
-      const float* src = sc + (k & 1) * QWG * PS::SCW;
-      const int64_t kb = (st_lo + k) * KT;
-#pragma unroll
-      for (int q4 = 0; q4 < (QWG + 3) / 4; ++q4) {
-        const int q = 4 * q4 + (l >> 4);          // query row of the workgroup
-        const int kk = 4 * (l & 15);              // first of 4 keys
-        const int qq = qbase + q;
-        if (q >= QWG || qq >= nq) continue;
-        const int64_t jmax = pos0 + qq;           // last visible key
-        const int64_t j = kb + kk;
-        if (j > jmax) continue;
-        const f32x4 v = *reinterpret_cast<const f32x4*>(src + q * PS::SCW + kk);
-        float* dst = scores + (t0 + qq) * ld + j;
-        if (vec && j + 3 <= jmax) {
-          *reinterpret_cast<f32x4*>(dst) = v;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (j + e <= jmax) dst[e] = v[e];
-        }
-      }
-    };
-#pragma unroll 1
-    for (int i = 0; i < nst; ++i) {
-      lds_barrier();
-      if (i > 0) store_stage(i - 1);
-    }
-    lds_barrier();
-    store_stage(nst - 1);
-    return;
-  }
-
   // ---------------- compute waves ----------------
   const int wq0 = qbase + wv * QW;
   bf16x8 qa[MB][KS];
@@ -574,16 +544,64 @@ __global__ __launch_bounds__(64 * (NCW + 2)) void index_prefill_kernel(
       wr[m][r] = q2 < nq ? wv2 : 0.f;
     }
   }
+  constexpr int NB = KT / 32;
+  f32x16 acc[MB][NB];
+  float sg[NB];
+  // epilogue of one stage: ReLU, head weights, head sum, then the causal
+  // store of each (query, key) score (lanes of a half-wave: 32 consecutive
+  // keys of one query)
+  auto put = [&](int q, int64_t j, float v) {  // q: query of the sequence
+    if (q < nq && j <= pos0 + q) scores[(t0 + q) * ld + j] = v;
+  };
+  // All sums first, each as two interleaved partial sums and outside any
+  // branch, so the independent chains overlap; then the predicated stores.
+  constexpr int NSUM = HI == 4 ? 4 : 1;  // sums per (block, key block) per lane
+  auto epilogue = [&](int k) {
+    const int64_t kb = (st_lo + k) * KT;
+    float sum[MB][NB][NSUM];
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+#pragma unroll
+      for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int c4 = 0; c4 < NSUM; ++c4) {
+          constexpr int RN = 16 / NSUM;  // heads per sum
+          float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+          for (int r = 0; r < RN; r += 2) {
+            s0 += wr[m][RN * c4 + r] * relu(sg[n] * acc[m][n][RN * c4 + r]);
+            s1 += wr[m][RN * c4 + r + 1] * relu(sg[n] * acc[m][n][RN * c4 + r + 1]);
+          }
+          sum[m][n][c4] = s0 + s1;
+          asm volatile("" : "+v"(sum[m][n][c4]));  // computed here, not in the store branch
+        }
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      const int64_t j = kb + 32 * n + (l & 31);
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+        const int q0 = wq0 + m * QPB;  // first query of block m
+        if constexpr (HI == 4) {
+#pragma unroll
+          for (int c4 = 0; c4 < 4; ++c4) put(q0 + 2 * c4 + g, j, sum[m][n][c4]);
+        } else if constexpr (HI == 32) {
+          const float v = xor32_add(sum[m][n][0]);
+          if (g == 0) put(q0, j, v);
+        } else {
+          put(q0 + g, j, sum[m][n][0]);
+        }
+      }
+    }
+  };
+  const bool late = wv >= 4;
 #pragma unroll 1
   for (int i = 0; i < nst; ++i) {
-    lds_barrier();
+    dma_barrier();  // stage i has landed; every wave is done with stage i - 1
+    if (late && i > 0) epilogue(i - 1);
     const uint8_t* buf = ring + (i % NBUF) * PS::BUFB;
-    float* dst = sc + (i & 1) * QWG * PS::SCW;
     // both 32-key blocks of the stage at once: 2 * MB independent
     // accumulator chains interleave on the MFMA pipe
-    constexpr int NB = KT / 32;
     u32x4 kv[NB][NLD];
-    float sg[NB];
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
       const int R = 32 * n + (l & 31);
@@ -592,11 +610,8 @@ __global__ __launch_bounds__(64 * (NCW + 2)) void index_prefill_kernel(
         kv[n][c] = *reinterpret_cast<const u32x4*>(buf + PS::offset(R, 2 * c + g));
       sg[n] = FP8 ? reinterpret_cast<const float*>(buf + PS::KEYB)[R] : 1.f;
     }
-    f32x16 acc[MB][NB];
-#pragma unroll
-    for (int m = 0; m < MB; ++m)
-#pragma unroll
-      for (int n = 0; n < NB; ++n) acc[m][n] = f32x16{};
+    // the first k-step starts from a zero accumulator operand (no register
+    // clearing per stage)
 #pragma unroll
     for (int c = 0; c < NLD; ++c) {
 #pragma unroll
@@ -606,46 +621,19 @@ __global__ __launch_bounds__(64 * (NCW + 2)) void index_prefill_kernel(
           const bf16x8 b1 = fp8x8_to_bf16x8(kv[n][c][2], kv[n][c][3]);
 #pragma unroll
           for (int m = 0; m < MB; ++m) {
-            acc[m][n] = mfma32(qa[m][2 * c], b0, acc[m][n]);
+            acc[m][n] = mfma32(qa[m][2 * c], b0, c == 0 ? f32x16{} : acc[m][n]);
             acc[m][n] = mfma32(qa[m][2 * c + 1], b1, acc[m][n]);
           }
         } else {
 #pragma unroll
-          for (int m = 0; m < MB; ++m) acc[m][n] = mfma32(qa[m][c], as_bf16x8(kv[n][c]), acc[m][n]);
+          for (int m = 0; m < MB; ++m)
+            acc[m][n] = mfma32(qa[m][c], as_bf16x8(kv[n][c]), c == 0 ? f32x16{} : acc[m][n]);
         }
       }
     }
-    // epilogue: ReLU, head weights, head sum -> LDS scores
-#pragma unroll
-    for (int n = 0; n < NB; ++n) {
-      const int R = 32 * n + (l & 31);
-#pragma unroll
-      for (int m = 0; m < MB; ++m) {
-        const int q0 = wv * QW + m * QPB;  // workgroup-local query of block m
-        if constexpr (HI == 4) {
-#pragma unroll
-          for (int c4 = 0; c4 < 4; ++c4) {
-            float sum = 0.f;
-#pragma unroll
-            for (int r = 4 * c4; r < 4 * c4 + 4; ++r)
-              sum += wr[m][r] * fmaxf(sg[n] * acc[m][n][r], 0.f);
-            dst[(q0 + 2 * c4 + g) * PS::SCW + R] = sum;
-          }
-        } else {
-          float sum = 0.f;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sum += wr[m][r] * fmaxf(sg[n] * acc[m][n][r], 0.f);
-          if constexpr (HI == 32) {
-            sum = xor32_add(sum);
-            if (g == 0) dst[q0 * PS::SCW + R] = sum;
-          } else {
-            dst[(q0 + g) * PS::SCW + R] = sum;
-          }
-        }
-      }
-    }
+    if (!late) epilogue(i);
   }
-  lds_barrier();
+  if (late) epilogue(nst - 1);
 }
 
 template <int DI, int HI, bool FP8>
@@ -654,9 +642,10 @@ static hipError_t launch_prefill_t(const uint16_t* q, const uint16_t* w, int64_t
                                    const int32_t* ctx_len, const int64_t* cu_ctx, int B,
                                    int max_q, int max_ctx, float* scores, int64_t ld,
                                    hipStream_t st) {
-  // 6 compute waves (+ loader + storer); two 32-row query blocks per compute
-  // wave where the registers allow it (8 queries of 4 heads fill a block)
-  constexpr int MB = HI == 4 ? 1 : 2, NCW = 6, NBUF = 3;
+  // 7 compute waves + the loader (two waves per SIMD at this register use);
+  // two 32-row query blocks per compute wave where the registers allow it
+  // (8 queries of 4 heads fill a block)
+  constexpr int MB = HI == 4 ? 1 : 2, NCW = 7, NBUF = 4;
   constexpr int QWG = NCW * MB * (32 / HI);
   const int qtiles = (max_q + QWG - 1) / QWG;
   // enough workgroups to fill the chip: split the key range when needed
@@ -666,7 +655,7 @@ static hipError_t launch_prefill_t(const uint16_t* q, const uint16_t* w, int64_t
     nsplit *= 2;
   dim3 grid(nsplit, qtiles, B);
   hipLaunchKernelGGL((index_prefill_kernel<DI, HI, FP8, MB, NCW, NBUF>), grid,
-                     dim3(64 * (NCW + 2)), 0, st, q, w, w_ld, k, ks, cu_q, ctx_len, cu_ctx,
+                     dim3(64 * (NCW + 1)), 0, st, q, w, w_ld, k, ks, cu_q, ctx_len, cu_ctx,
                      scores, ld, nsplit);
   return hipGetLastError();
 }

@@ -187,7 +187,12 @@ dsa_status_t dsa_topk(const float* scores, int64_t ld, const int32_t* cu_q,
   DSA_PTR(ws, "ws");
   hipStream_t s = static_cast<hipStream_t>(stream);
   dsa::TopkWs w = dsa::topk_ws_carve(ws, T, max_ctx, K);
-  hipError_t e = dsa::launch_tile_reports(scores, ld, cu_q, ctx_len, B, T, K, w, s);
+  hipError_t e;
+  if (dsa::topk_use_rows(T)) {
+    e = dsa::launch_topk_rows(scores, ld, cu_q, ctx_len, B, T, K, idx, t_topk_counters, s);
+    return hip_status(e, "dsa_topk");
+  }
+  e = dsa::launch_tile_reports(scores, ld, cu_q, ctx_len, B, T, K, w, s);
   if (e == hipSuccess) e = dsa::launch_topk_resolve(scores, ld, cu_q, ctx_len, B, T, K, w, idx,
                                                     t_topk_counters, s);
   return hip_status(e, "dsa_topk");
@@ -293,12 +298,17 @@ dsa_status_t dsa_layer_decode(const void* q_idx, const void* w, int64_t w_ld, co
   decode_ws_layout(B, max_ctx, K, Hq, D, static_cast<char*>(ws), &L);
   int32_t* idx = idx_out ? idx_out : L.idx;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  // few rows: the indexer writes candidate reports for the resolve; many
+  // rows: plain scores, each row selected by sweeps
+  const bool rows = dsa::topk_use_rows(B);
   hipError_t e = dsa::launch_index_decode(q_idx, w, w_ld, k_idx, k_dtype, k_scale, H_I, d_I,
-                                          ctx_len, cu_ctx, B, max_ctx, L.scores, L.ld, &L.topk, s,
-                                          t_ev_start, t_ev_stop);
+                                          ctx_len, cu_ctx, B, max_ctx, L.scores, L.ld,
+                                          rows ? nullptr : &L.topk, s, t_ev_start, t_ev_stop);
   if (e == hipSuccess)
-    e = dsa::launch_topk_resolve(L.scores, L.ld, nullptr, ctx_len, B, B, K, L.topk, idx,
-                                 t_topk_counters, s);
+    e = rows ? dsa::launch_topk_rows(L.scores, L.ld, nullptr, ctx_len, B, B, K, idx,
+                                     t_topk_counters, s)
+             : dsa::launch_topk_resolve(L.scores, L.ld, nullptr, ctx_len, B, B, K, L.topk, idx,
+                                        t_topk_counters, s);
   if (e == hipSuccess) {
     const dsa::AttnPlan plan = dsa::attn_plan(B, K, 0, Hq, D);
     e = dsa::launch_sparse_attn(q, k_cache, v_cache, idx, K, 0, gate, sm_scale, Hq, D, nullptr,
@@ -358,11 +368,15 @@ dsa_status_t dsa_layer_prefill(const void* q_idx, const void* w, int64_t w_ld, c
   hipError_t e = dsa::launch_index_prefill(q_idx, w, w_ld, k_idx, k_dtype, k_scale, H_I, d_I,
                                            cu_q, ctx_len, cu_ctx, B, max_q, max_ctx, L.scores,
                                            L.ld, s);
-  if (e == hipSuccess)
-    e = dsa::launch_tile_reports(L.scores, L.ld, cu_q, ctx_len, B, T, K, L.topk, s);
-  if (e == hipSuccess)
-    e = dsa::launch_topk_resolve(L.scores, L.ld, cu_q, ctx_len, B, T, K, L.topk, idx,
-                                 t_topk_counters, s);
+  if (e == hipSuccess && dsa::topk_use_rows(T)) {
+    e = dsa::launch_topk_rows(L.scores, L.ld, cu_q, ctx_len, B, T, K, idx, t_topk_counters, s);
+  } else {
+    if (e == hipSuccess)
+      e = dsa::launch_tile_reports(L.scores, L.ld, cu_q, ctx_len, B, T, K, L.topk, s);
+    if (e == hipSuccess)
+      e = dsa::launch_topk_resolve(L.scores, L.ld, cu_q, ctx_len, B, T, K, L.topk, idx,
+                                   t_topk_counters, s);
+  }
   if (e == hipSuccess) {
     const dsa::AttnPlan plan = dsa::attn_plan(T, K, 0, Hq, D);
     e = dsa::launch_sparse_attn(q, k_cache, v_cache, idx, K, 0, gate, sm_scale, Hq, D, cu_q,

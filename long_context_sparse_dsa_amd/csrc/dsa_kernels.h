@@ -32,6 +32,12 @@ TopkWs topk_ws_carve(void* ws, int T, int max_ctx, int K);
 hipError_t launch_tile_reports(const float* scores, int64_t ld, const int32_t* cu_q,
                                const int32_t* ctx_len, int B, int T, int K, const TopkWs& w,
                                hipStream_t stream);
+// Many rows (T >= a threshold): each row selected by sweeps over its scores,
+// no candidate reports (topk_report_bytes is then 0).
+bool topk_use_rows(int T);
+hipError_t launch_topk_rows(const float* scores, int64_t ld, const int32_t* cu_q,
+                            const int32_t* ctx_len, int B, int T, int K, int32_t* idx,
+                            uint32_t* stats, hipStream_t stream);
 hipError_t launch_topk_resolve(const float* scores, int64_t ld, const int32_t* cu_q,
                                const int32_t* ctx_len, int B, int T, int K, const TopkWs& w,
                                int32_t* idx, uint32_t* stats, hipStream_t stream);

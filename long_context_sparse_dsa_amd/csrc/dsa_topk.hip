@@ -69,21 +69,24 @@ __global__ __launch_bounds__(64) void tile_report_kernel(const float* __restrict
 // ---------------------------------------------------------------------------
 constexpr int kBucketMax = 64;  // boundary-bucket size ranked directly by wave 0
 
-struct ResolveSmem {
+template <int NTILE>
+struct ResolveSmemT {
   int32_t stage[4096];  // selected positions before the coalesced store (K <= 4096)
   uint32_t hist[2048];
   uint32_t hist2[2048];  // the union select alternates between hist and hist2
   alignas(16) uint32_t bu[kBucketMax];
   alignas(16) int32_t bj[kBucketMax];
-  // per tile: worst reported (key, position | complete << 31), kept for the
-  // certification so the headers need not stay in registers
-  uint32_t wu[kResolveTiles];
-  uint32_t wj[kResolveTiles];
+  // per sub-tile: worst reported (key, position | complete << 31), kept for
+  // the certification so the headers need not stay in registers
+  uint32_t wu[NTILE];
+  uint32_t wj[NTILE];
   uint32_t red[64];
   uint32_t flag[16];
   uint32_t scan[20];
   uint32_t st[8];
 };
+using ResolveSmem = ResolveSmemT<kResolveTiles>;
+using RowsSmem = ResolveSmemT<1>;  // no certification: no per-sub-tile words
 
 // Wave 0 of the block: given the 2048-bin histogram h of the current
 // bucket and `above` elements strictly above the bucket, find digit d with
@@ -91,7 +94,8 @@ struct ResolveSmem {
 // Writes st[0] = d, st[1] = above + gt(d), st[5] = h[d].  Two levels of one
 // wave scan each: the 64 chunks of 32 bins, then the 32 bins of the chunk
 // that holds d.
-__device__ void wave_find_digit(ResolveSmem& sm, const uint32_t* h, uint32_t above, uint32_t k) {
+template <class SM>
+__device__ void wave_find_digit(SM& sm, const uint32_t* h, uint32_t above, uint32_t k) {
   const int l = lane_id();
   // level 1: lane l sums bins 32 l .. 32 l + 31 (chunk reads in a
   // lane-rotated order, so fewer lanes share a bank)
@@ -143,8 +147,8 @@ __device__ __forceinline__ int slot_of(int q, int tid, int nt) { return 4 * nt *
 // total.  Also ORs the per-thread flag `bad` over the block into *any_bad
 // (same exchange).  One cross-wave exchange of the per-(group, wave) counts
 // (at most 64 of them: NSL/4 groups x nt/64 waves).  nt: active threads.
-template <int NSL>
-__device__ __forceinline__ void ordered_ranks(ResolveSmem& sm, uint32_t fmask, int qn, int nt,
+template <int NSL, class SM>
+__device__ __forceinline__ void ordered_ranks(SM& sm, uint32_t fmask, int qn, int nt,
                                               uint32_t (&rank)[NSL], uint32_t* total,
                                               bool bad = false, bool* any_bad = nullptr) {
   static_assert((NSL / 4) * (kResolveSlots / NSL / 64) <= 64, "exchange size");
@@ -184,8 +188,8 @@ __device__ __forceinline__ void ordered_ranks(ResolveSmem& sm, uint32_t fmask, i
 // Appends the candidates with keys in [lo, lo + width) to sm.bu / sm.bj:
 // per-wave ballot compaction at a base taken with one LDS atomic per wave
 // (sm.st[4] counts the bucket; the caller guarantees at most kBucketMax).
-template <int NSL>
-__device__ __forceinline__ void gather_bucket(ResolveSmem& sm, const UnionRegs<NSL>& R,
+template <int NSL, class SM>
+__device__ __forceinline__ void gather_bucket(SM& sm, const UnionRegs<NSL>& R,
                                               uint32_t lo, uint64_t width) {
   const int l = lane_id();
   uint32_t inb = 0, cnt = 0;
@@ -222,7 +226,8 @@ __device__ __forceinline__ void gather_bucket(ResolveSmem& sm, const UnionRegs<N
 // position asc) and writes the need-th one to st[2] (key), st[3] (position).
 // Every lane reads the whole bucket (broadcast reads, all issued at once).
 // Called by the whole block; ends with a barrier.
-__device__ __forceinline__ void rank_bucket(ResolveSmem& sm, uint32_t h, uint32_t need) {
+template <class SM>
+__device__ __forceinline__ void rank_bucket(SM& sm, uint32_t h, uint32_t need) {
   const int l = lane_id();
   if (wave_id() == 0) {
     const bool mine_ok = (uint32_t)l < h;
@@ -262,8 +267,8 @@ __device__ __forceinline__ void rank_bucket(ResolveSmem& sm, uint32_t h, uint32_
 // kBucketMax candidates they are gathered and wave 0 ranks them directly
 // under (key desc, position asc), which gives (tau_u, tau_j) at once.  Both
 // histograms are zero and st[4] is 0 on entry.  nt: active threads.
-template <int NSL>
-__device__ __forceinline__ void union_threshold(ResolveSmem& sm, const UnionRegs<NSL>& R,
+template <int NSL, class SM>
+__device__ __forceinline__ void union_threshold(SM& sm, const UnionRegs<NSL>& R,
                                                 uint32_t k, uint32_t mn, uint32_t mx, int nt,
                                                 uint32_t* tau_u, int32_t* tau_j) {
   const int tid = threadIdx.x, wv = wave_id();
@@ -339,8 +344,8 @@ __device__ __forceinline__ void union_threshold(ResolveSmem& sm, const UnionRegs
 // against the sub-tile headers kept in sm.wu / sm.wj.  Returns false,
 // leaving `out` untouched, when the set has fewer than k candidates or the
 // certification fails.  nt: active threads.
-template <int NSL>
-__device__ __forceinline__ bool select_from_regs(ResolveSmem& sm, const UnionRegs<NSL>& R,
+template <int NSL, class SM>
+__device__ __forceinline__ bool select_from_regs(SM& sm, const UnionRegs<NSL>& R,
                                                  uint32_t k, int K, int ntiles, int nt,
                                                  int32_t* out) {
   const int tid = threadIdx.x, l = lane_id(), wv = wave_id();
@@ -410,19 +415,51 @@ __device__ __forceinline__ bool select_from_regs(ResolveSmem& sm, const UnionReg
   return true;
 }
 
+// PER consecutive keys of a row from position p0 (a multiple of 4);
+// returns the validity mask.  Same conditions as load_keys16.
+template <int PER>
+__device__ __forceinline__ uint32_t load_keys(const float* row, int64_t n, int64_t p0, bool vec,
+                                              uint32_t (&u)[PER]) {
+  static_assert(PER % 4 == 0 && PER <= 32, "keys per thread");
+  uint32_t vm = 0;
+#pragma unroll
+  for (int c = 0; c < PER / 4; ++c) {
+    const int64_t p = p0 + 4 * c;
+    float f[4];
+    if (vec) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(row + (p < n ? p : 0));
+      f[0] = v[0];
+      f[1] = v[1];
+      f[2] = v[2];
+      f[3] = v[3];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f[e] = row[p + e < n ? p + e : 0];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool v = p + e < n;
+      u[4 * c + e] = v ? order_key(f[e]) : 0u;
+      vm |= (uint32_t)v << (4 * c + e);
+    }
+  }
+  return vm;
+}
+
 // Exclusive prefix sum of one value per thread over the nw active waves;
 // *total receives the sum.  Contains barriers.
-__device__ __forceinline__ uint32_t excl_scan_active(ResolveSmem& sm, uint32_t v, int nw,
+template <class SM>
+__device__ __forceinline__ uint32_t excl_scan_active(SM& sm, uint32_t v, int nw,
                                                      uint32_t* total) {
   const int l = lane_id(), wv = wave_id();
   const uint32_t inc = wave_incl_scan(v);
   if (l == 63) sm.scan[wv] = inc;
-  lds_barrier();
+  dma_barrier();  // LDS only: global loads in flight stay in flight
   const uint32_t x = l < nw ? sm.scan[l] : 0u;
   const uint32_t xi = wave_incl_scan(x);
   const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)(xi - x), wv);
   *total = (uint32_t)__builtin_amdgcn_readlane((int)xi, 63);
-  lds_barrier();
+  dma_barrier();
   return base + inc - v;
 }
 
@@ -465,7 +502,8 @@ __device__ __forceinline__ uint32_t load_keys16(const float* row, int64_t n, int
 // directly (or, for one key shared by many positions, its need lowest
 // positions are found with ordered block scans); a last ordered sweep
 // writes the selected positions in ascending order.
-__device__ __forceinline__ void exact_select_row(ResolveSmem& sm, const float* row, int64_t n,
+template <class SM>
+__device__ __forceinline__ void exact_select_row(SM& sm, const float* row, int64_t n,
                                                  uint32_t k, bool vec, int nt, int32_t* out) {
   const int tid = threadIdx.x, l = lane_id(), wv = wave_id(), nw = nt >> 6;
   const int64_t step = 16 * (int64_t)nt;
@@ -726,9 +764,145 @@ __global__ __launch_bounds__(kResolveSlots / NSL) void topk_resolve_kernel(
   }
 }
 
+// Exact Top-K of many rows straight from their scores (prefill: thousands
+// of long rows, where a report per sub-tile costs more than two sweeps over
+// the row).  One workgroup of kRowsThreads per row:
+//   1. a sweep builds the 2048-bin histogram of the keys' top 11 bits; one
+//      wave finds the bucket of the K-th key; while the keys at or above
+//      that bucket would not fit kRowsCap, further sweeps refine it by the
+//      next 11 bits;
+//   2. an ordered sweep (block prefix sums over 16 consecutive positions
+//      per thread) collects every key at or above the bucket into LDS in
+//      position order;
+//   3. the register path selects the K best of those candidates and writes
+//      them in ascending order.
+// Rows whose candidates cannot be narrowed to kRowsCap (a key shared by
+// very many positions) take the exact sweep select.
+constexpr int kRowsThreads = 512;
+constexpr int kRowsCap = 4096;  // = the staging buffer of the select, reused for positions
+constexpr int kRowsMinT = 1024;  // rows per call from which the row sweeps pay off
+
+__global__ __launch_bounds__(kRowsThreads) void topk_rows_kernel(
+    const float* __restrict__ scores, int64_t ld, const int32_t* cu_q, const int32_t* ctx_len,
+    int B, int K, int32_t* idx, uint32_t* stats) {
+  constexpr int NSL = 16;
+  __shared__ RowsSmem sm;
+  __shared__ uint32_t cand_u[kRowsCap];
+  int32_t* const cand_j = sm.stage;  // positions; the select reuses it only after loading them
+  const int t = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
+  const RowInfo ri = row_info(t, cu_q, ctx_len, B);
+  const int64_t n = ri.p + 1;
+  int32_t* out = idx + (int64_t)t * K;
+  if (n <= K) {
+    for (int i = tid; i < K; i += nt) out[i] = i < n ? i : -1;
+    return;
+  }
+  const uint32_t k = (uint32_t)K;
+  const float* row = scores + (int64_t)t * ld;
+  const bool vec = ((ld & 3) == 0) && ((reinterpret_cast<uintptr_t>(scores) & 15) == 0);
+  // Each sweep runs over rounds of PER consecutive keys per thread, the next
+  // round's loads in flight while the current one is processed (two key
+  // buffers); the barriers inside wait for LDS work only, not those loads.
+  constexpr int PER = 8;
+  const int64_t step = PER * (int64_t)nt;
+  uint32_t ua[PER], ub[PER];
+  // 1. bucket of the K-th key: [lo, lo + width), `above` keys beyond it
+  for (int i = tid; i < 2048; i += nt) sm.hist[i] = 0;
+  lds_barrier();
+  uint32_t lo = 0, above = 0, h = 0;
+  uint64_t width = 1ull << 32;
+  int shift = 21;
+  auto hist_add = [&](const uint32_t(&u)[PER], uint32_t vm) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (((vm >> i) & 1u) && u[i] >= lo && (uint64_t)(u[i] - lo) < width)
+        atomicAdd(&sm.hist[(u[i] - lo) >> shift], 1u);
+  };
+#pragma unroll 1
+  while (true) {
+    uint32_t va = load_keys<PER>(row, n, PER * tid, vec, ua);
+#pragma unroll 1
+    for (int64_t b0 = 0; b0 < n; b0 += 2 * step) {
+      const uint32_t vb = load_keys<PER>(row, n, b0 + step + PER * tid, vec, ub);
+      hist_add(ua, va);
+      va = load_keys<PER>(row, n, b0 + 2 * step + PER * tid, vec, ua);
+      hist_add(ub, vb);
+    }
+    dma_barrier();
+    if (wave_id() == 0) wave_find_digit(sm, sm.hist, above, k);
+    lds_barrier();
+    const uint32_t d = sm.st[0];
+    above = sm.st[1];
+    h = sm.st[5];
+    lo += d << shift;
+    width = 1ull << shift;
+    if (above + h <= (uint32_t)kRowsCap || shift == 0) break;
+    shift = max(0, shift - 11);
+    for (int i = tid; i < 2048; i += nt) sm.hist[i] = 0;
+    lds_barrier();
+  }
+  const uint32_t C = above + h;  // keys >= lo
+  if (C > (uint32_t)kRowsCap) {
+    exact_select_row(sm, row, n, k, vec, nt, out);
+    if (stats && tid == 0) atomicAdd(&stats[1], 1u);
+    return;
+  }
+  // 2. ordered collection of the keys >= lo
+  uint32_t cum = 0;
+  auto collect = [&](const uint32_t(&u)[PER], uint32_t vm, int64_t b0) {
+    const int64_t p0 = b0 + PER * tid;
+    uint32_t f = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) f |= (uint32_t)(((vm >> i) & 1u) && u[i] >= lo) << i;
+    uint32_t tot;
+    uint32_t r = cum + excl_scan_active(sm, (uint32_t)__popc(f), nt >> 6, &tot);
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if ((f >> i) & 1u) {
+        cand_u[r] = u[i];
+        cand_j[r] = (int32_t)(p0 + i);
+        ++r;
+      }
+    cum += tot;
+  };
+  {
+    uint32_t va = load_keys<PER>(row, n, PER * tid, vec, ua);
+#pragma unroll 1
+    for (int64_t b0 = 0; b0 < n && cum < C; b0 += 2 * step) {
+      const uint32_t vb = load_keys<PER>(row, n, b0 + step + PER * tid, vec, ub);
+      collect(ua, va, b0);
+      if (b0 + step >= n || cum >= C) break;
+      va = load_keys<PER>(row, n, b0 + 2 * step + PER * tid, vec, ua);
+      collect(ub, vb, b0 + step);
+    }
+  }
+  dma_barrier();
+  // 3. the register path over the candidates (slot s = candidate s)
+  UnionRegs<NSL> R;
+  R.vmask = 0;
+  R.qn = (int)((C + 4 * nt - 1) / (4 * nt));
+#pragma unroll
+  for (int q = 0; q < NSL / 4; ++q) {
+    if (q < R.qn) {
+      const int s0 = slot_of(q, tid, nt);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool v = (uint32_t)(s0 + e) < C;
+        R.u[4 * q + e] = v ? cand_u[s0 + e] : 0u;
+        R.j[4 * q + e] = v ? cand_j[s0 + e] : 0;
+        R.vmask |= (uint32_t)v << (4 * q + e);
+      }
+    }
+  }
+  select_from_regs(sm, R, k, K, 0, nt, out);  // C >= k: always succeeds
+  if (stats && tid == 0) atomicAdd(&stats[3], 1u);
+}
+
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
+bool topk_use_rows(int T) { return T >= kRowsMinT; }
+
 // Tile of the report-writing kernels (the indexer epilogue and
 // tile_report_kernel): the sub-tile size of the longest row, at least one
 // wave of positions.  Sub-tile sizes never decrease with the row length, so
@@ -759,6 +933,7 @@ int topk_report_stride(int max_ctx, int K) {
 }
 
 size_t topk_report_bytes(int T, int max_ctx, int K) {
+  if (topk_use_rows(T)) return 0;  // rows selected by sweeps write no reports
   return (size_t)T * topk_report_stride(max_ctx, K) * (sizeof(RepHeader) + kRep * 8);
 }
 
@@ -800,6 +975,14 @@ hipError_t launch_tile_reports(const float* scores, int64_t ld, const int32_t* c
     default:
       return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_rows(const float* scores, int64_t ld, const int32_t* cu_q,
+                            const int32_t* ctx_len, int B, int T, int K, int32_t* idx,
+                            uint32_t* stats, hipStream_t stream) {
+  hipLaunchKernelGGL(topk_rows_kernel, dim3(T), dim3(kRowsThreads), 0, stream, scores, ld, cu_q,
+                     ctx_len, B, K, idx, stats);
   return hipGetLastError();
 }
 

@@ -172,7 +172,7 @@ RAGGED_TOPK_LENS = [5000, 16384, 16385, 20000, 31000, 70000, 131071, 131072, 300
 
 
 def _with_counters(dsa, fn):
-    cnt = torch.zeros(3, dtype=torch.int32, device=DEV)
+    cnt = torch.zeros(4, dtype=torch.int32, device=DEV)
     dsa.dsa_set_topk_counters(cnt)
     try:
         res = fn()
@@ -211,6 +211,35 @@ def test_topk_clustered_rows_take_the_exact_fallback(dsa):
     want = oracle.topk(s.numpy(), K, ctx.numpy())
     assert np.array_equal(got.cpu().numpy(), want)
     assert c[1] == len(lens)
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties", "relu_like", "clustered", "equal"])
+def test_topk_many_rows_take_the_row_sweeps(dsa, kind):
+    """1024 rows and more (a prefill chunk) are selected by histogram and
+    collection sweeps over each row; a key shared by more positions than the
+    candidate buffer holds sends the row to the exact sweep select."""
+    say(f"topk many rows {kind}")
+    lens, nq, K = [30000, 1500, 9000], [700, 300, 100], 2048
+    T, L = sum(nq), max(lens)
+    s = torch.zeros(T, L)
+    t = 0
+    for b, (n_ctx, q) in enumerate(zip(lens, nq)):
+        for i in range(q):
+            p = n_ctx - q + i
+            s[t, :p + 1] = _topk_case(kind, p + 1, seed=1000 * b + i)
+            t += 1
+    cu_q = torch.tensor(np.concatenate([[0], np.cumsum(nq)]), dtype=torch.int32)
+    ctx = torch.tensor(lens, dtype=torch.int32)
+    got, c = _with_counters(dsa, lambda: dsa.dsa_topk(s.to(DEV), K, ctx.to(DEV),
+                                                      cu_q=cu_q.to(DEV), max_ctx=L))
+    want = oracle.topk(s.numpy(), K, ctx.numpy(), cu_q=cu_q.numpy())
+    assert np.array_equal(got.cpu().numpy(), want)
+    n_sel = sum(1 for n_ctx, q in zip(lens, nq) for i in range(q) if n_ctx - q + i + 1 > K)
+    assert c[0] == 0 and c[2] == 0 and c[1] + c[3] == n_sel
+    if kind == "equal":
+        assert c[1] == n_sel
+    elif kind in ("normal", "relu_like"):
+        assert c[3] == n_sel
 
 
 # --------------------------------------------------------------------------

@@ -68,7 +68,7 @@ struct VTile {
 };
 
 template <int D, int HB, bool FINAL>
-__global__ __launch_bounds__(256) void sparse_attn_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ idx, int K, int window,
     const uint16_t* __restrict__ gate, float scale_log2, int Hq, const int32_t* cu_q,
@@ -82,11 +82,20 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
   // merge state of one wave: per lane (m, l) and DB x 16 O values
   constexpr int ST_FLOATS = 2 + DB * 16;
   constexpr int MERGE_BYTES = (RB / 2) * HB * 64 * ST_FLOATS * 4;
-  constexpr int VT_BYTES = 4 * VT::kBytes;
+  constexpr int VT_BYTES = 8 * VT::kBytes;  // two V tiles per wave
   constexpr int SMEM_BYTES = MERGE_BYTES > VT_BYTES ? MERGE_BYTES : VT_BYTES;
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM_BYTES];
 
-  const int t = blockIdx.y, split = blockIdx.x;
+  // Workgroups go to the 8 XCDs (each with its own L2) in turn.  With one
+  // workgroup per query, query t + 1 would land on another XCD than query t,
+  // though neighbouring queries select mostly the same K/V rows; instead
+  // each XCD takes a contiguous run of queries.
+  int t = blockIdx.y;
+  if (gridDim.x == 1) {
+    const int T = gridDim.y, x = t & 7, i = t >> 3, q = T >> 3, r = T & 7;
+    t = x * q + min(x, r) + i;
+  }
+  const int split = blockIdx.x;
   const int l = lane_id(), g = l >> 5, wv = wave_id();
   const int hb = wv % HB, rb = wv / HB;
   const int lo = split * rows_per_split;
@@ -117,33 +126,58 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
 
-  uint8_t* vt = smem + wv * VT::kBytes;
-  const uint16_t* vt16 = reinterpret_cast<const uint16_t*>(vt);
+  // Two V tiles per wave: the next step's V rows land (direct loads) while
+  // this step computes, and the next step's indices are loaded a step
+  // ahead, so each step waits for one gather (its K rows), not for the
+  // index load and then the gather.
+  uint8_t* const vt_base = smem + 2 * wv * VT::kBytes;
   const int G = l >> 4, jj = l & 15;
-#pragma unroll 1
-  for (int base = lo + 32 * rb; base < hi; base += STEP) {
-    const int lp = base + (l & 31);
-    bool valid = lp < hi;
+  auto row_of = [&](int lp, int32_t jraw, bool* ok) {
+    bool v = lp < hi;
     int64_t j = 0;
-    if (valid) {
-      j = idx ? (int64_t)(base == lo + 32 * rb ? j_first : idx[(int64_t)t * K + lp]) : jw0 + lp;
-      valid = j >= 0;
+    if (v) {
+      j = idx ? (int64_t)jraw : jw0 + lp;
+      v = j >= 0;
     }
-    const int64_t row = row0 + (valid ? j : 0);
-    // K row chunks straight into A-operand registers, V rows into LDS; all
-    // issued before any is used
-    u32x4 kf[KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) kf[s] = ld16(kc + row * D + 16 * s + 8 * g);
+    *ok = v;
+    return row0 + (v ? j : 0);
+  };
+  auto issue_v = [&](int64_t row, int buf) {
+    uint8_t* vt = vt_base + buf * VT::kBytes;
 #pragma unroll
     for (int c = 0; c < VT::kBlocks; ++c)
       lds_dma16(vc + row * D + 8 * (2 * c + g), vt + c * VT::kStride);
+  };
+  bool valid;
+  int64_t row = row_of(lo + 32 * rb + (l & 31), j_first, &valid);
+  if (lo + 32 * rb < hi) issue_v(row, 0);
+  int buf = 0;
+#pragma unroll 1
+  for (int base = lo + 32 * rb; base < hi; base += STEP) {
+    const int lp_next = base + STEP + (l & 31);
+    const bool more = base + STEP < hi;
+    // next step's index, then this step's K row chunks into A-operand
+    // registers; all in flight before the wait
+    int32_t jn = -1;
+    if (idx && more && lp_next < hi) jn = idx[(int64_t)t * K + lp_next];
+    u32x4 kf[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kf[s] = ld16(kc + row * D + 16 * s + 8 * g);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): V tile, next index, K rows
     __builtin_amdgcn_sched_barrier(0);
     const uint32_t vmask = (uint32_t)__ballot(valid);
     // S^T = K . q^T, then the online softmax per head (exp2 domain)
     f32x16 sacc = {};
 #pragma unroll
     for (int s = 0; s < KS; ++s) sacc = mfma32(as_bf16x8(kf[s]), qb[s], sacc);
+    // the next step's V rows go to the other tile while this step computes
+    bool valid_n = false;
+    int64_t row_n = 0;
+    if (more) {
+      row_n = row_of(lp_next, jn, &valid_n);
+      issue_v(row_n, buf ^ 1);
+    }
     float sv[16];
     float mx = -INFINITY;
 #pragma unroll
@@ -169,13 +203,11 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int e = 0; e < 8; ++e) pb[s2][e] = static_cast<__bf16>(sv[8 * s2 + e]);
-    // V tile landed
-    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
-    __builtin_amdgcn_sched_barrier(0);
     // O^T += V^T . P^T.  k slot e of step s2 is accumulator row
     // 16 s2 + 8 (e / 4) + 4 g + e % 4, so the A operand's 8 rows for half g
     // are two 4-row groups; each comes from one transpose read: lane jj of
     // a 16-lane group addresses row k0 + jj / 4, dims n0 + 4 (jj % 4) .. + 3.
+    const uint16_t* vt16 = reinterpret_cast<const uint16_t*>(vt_base + buf * VT::kBytes);
     u32x2 av[DB][2][2];
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -196,6 +228,9 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
                                        av[db][s2][1][1]}),
                        pb[s2], o[db]);
     }
+    row = row_n;
+    valid = valid_n;
+    buf ^= 1;
   }
 
   // ---- merge the RB row-block waves of each head block pairwise through LDS ----

@@ -436,11 +436,10 @@ struct RowMap {
 //     (query, head) rows) in registers, run the MFMAs on the stage's keys,
 //     apply ReLU / head weights / head sum in registers and store the
 //     stage's scores (causal positions only) straight from registers; they
-//     never wait on their stores.  Compute waves 4 and up run half a stage
-//     late: each stage they first finish the previous stage's epilogue
-//     (vector ALU) and then issue this stage's MFMAs, so on a SIMD shared
-//     with an on-time wave one wave's epilogue overlaps the other's matrix
-//     work instead of all waves alternating in step.
+//     never wait on their stores.  Inside a wave the stage's two 32-key
+//     blocks form a pipeline: the MFMAs of one block run while the wave
+//     reduces the previous block (vector ALU), so the wave keeps its own
+//     matrix pipe busy through its epilogues.
 // One workgroup barrier per stage orders the two roles; it waits for no
 // memory traffic (the loader waits for its stages explicitly).
 template <int DI, int HI, bool FP8>
@@ -544,96 +543,119 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void index_prefill_kernel(
       wr[m][r] = q2 < nq ? wv2 : 0.f;
     }
   }
-  constexpr int NB = KT / 32;
-  f32x16 acc[MB][NB];
-  float sg[NB];
-  // epilogue of one stage: ReLU, head weights, head sum, then the causal
-  // store of each (query, key) score (lanes of a half-wave: 32 consecutive
+  constexpr int NB = KT / 32;  // 32-key blocks per stage
+  // The 32-key blocks form a pipeline inside each wave: while the MFMAs of
+  // one block run, the wave reduces the previous block (ReLU, head weights,
+  // head sum: vector ALU work that does not depend on those MFMAs) and
+  // stores its scores.  acc[p] holds the block of parity p.
+  static_assert(NB == 2, "block parity = block index within the stage");
+  f32x16 acc[2][MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) acc[1][m] = f32x16{};
+  constexpr int NSUM = HI == 4 ? 4 : 1;  // sums per query block per lane
+  auto reduce = [&](int p, float sgp, float (&sum)[MB][NSUM]) {
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int c4 = 0; c4 < NSUM; ++c4) {
+        constexpr int RN = 16 / NSUM;  // heads per sum
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int r = 0; r < RN; r += 2) {
+          s0 += wr[m][RN * c4 + r] * relu(sgp * acc[p][m][RN * c4 + r]);
+          s1 += wr[m][RN * c4 + r + 1] * relu(sgp * acc[p][m][RN * c4 + r + 1]);
+        }
+        sum[m][c4] = s0 + s1;
+      }
+  };
+  // causal store of a block's scores (lanes of a half-wave: 32 consecutive
   // keys of one query)
   auto put = [&](int q, int64_t j, float v) {  // q: query of the sequence
     if (q < nq && j <= pos0 + q) scores[(t0 + q) * ld + j] = v;
   };
-  // All sums first, each as two interleaved partial sums and outside any
-  // branch, so the independent chains overlap; then the predicated stores.
-  constexpr int NSUM = HI == 4 ? 4 : 1;  // sums per (block, key block) per lane
-  auto epilogue = [&](int k) {
-    const int64_t kb = (st_lo + k) * KT;
-    float sum[MB][NB][NSUM];
+  auto store = [&](int64_t j, const float (&sum)[MB][NSUM]) {
 #pragma unroll
-    for (int n = 0; n < NB; ++n)
+    for (int m = 0; m < MB; ++m) {
+      const int q0 = wq0 + m * QPB;  // first query of block m
+      if constexpr (HI == 4) {
 #pragma unroll
-      for (int m = 0; m < MB; ++m)
-#pragma unroll
-        for (int c4 = 0; c4 < NSUM; ++c4) {
-          constexpr int RN = 16 / NSUM;  // heads per sum
-          float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-          for (int r = 0; r < RN; r += 2) {
-            s0 += wr[m][RN * c4 + r] * relu(sg[n] * acc[m][n][RN * c4 + r]);
-            s1 += wr[m][RN * c4 + r + 1] * relu(sg[n] * acc[m][n][RN * c4 + r + 1]);
-          }
-          sum[m][n][c4] = s0 + s1;
-          asm volatile("" : "+v"(sum[m][n][c4]));  // computed here, not in the store branch
-        }
-#pragma unroll
-    for (int n = 0; n < NB; ++n) {
-      const int64_t j = kb + 32 * n + (l & 31);
-#pragma unroll
-      for (int m = 0; m < MB; ++m) {
-        const int q0 = wq0 + m * QPB;  // first query of block m
-        if constexpr (HI == 4) {
-#pragma unroll
-          for (int c4 = 0; c4 < 4; ++c4) put(q0 + 2 * c4 + g, j, sum[m][n][c4]);
-        } else if constexpr (HI == 32) {
-          const float v = xor32_add(sum[m][n][0]);
-          if (g == 0) put(q0, j, v);
-        } else {
-          put(q0 + g, j, sum[m][n][0]);
-        }
+        for (int c4 = 0; c4 < 4; ++c4) put(q0 + 2 * c4 + g, j, sum[m][c4]);
+      } else if constexpr (HI == 32) {
+        const float v = xor32_add(sum[m][0]);
+        if (g == 0) put(q0, j, v);
+      } else {
+        put(q0 + g, j, sum[m][0]);
       }
     }
   };
-  const bool late = wv >= 4;
+  int64_t j_prev = 0;  // key of this lane in the block awaiting its reduction
+  float sg_prev = 1.f;
 #pragma unroll 1
   for (int i = 0; i < nst; ++i) {
     dma_barrier();  // stage i has landed; every wave is done with stage i - 1
-    if (late && i > 0) epilogue(i - 1);
     const uint8_t* buf = ring + (i % NBUF) * PS::BUFB;
-    // both 32-key blocks of the stage at once: 2 * MB independent
-    // accumulator chains interleave on the MFMA pipe
-    u32x4 kv[NB][NLD];
+    const int64_t kb = (st_lo + i) * KT;
+    // B operands of both blocks: the second block's reads land during the
+    // first block's MFMAs
+    u32x4 kvs[NB][NLD];
+    float sgs[NB];
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
       const int R = 32 * n + (l & 31);
 #pragma unroll
       for (int c = 0; c < NLD; ++c)
-        kv[n][c] = *reinterpret_cast<const u32x4*>(buf + PS::offset(R, 2 * c + g));
-      sg[n] = FP8 ? reinterpret_cast<const float*>(buf + PS::KEYB)[R] : 1.f;
+        kvs[n][c] = *reinterpret_cast<const u32x4*>(buf + PS::offset(R, 2 * c + g));
+      sgs[n] = FP8 ? reinterpret_cast<const float*>(buf + PS::KEYB)[R] : 1.f;
     }
-    // the first k-step starts from a zero accumulator operand (no register
-    // clearing per stage)
 #pragma unroll
-    for (int c = 0; c < NLD; ++c) {
+    for (int n = 0; n < NB; ++n) {
+      const int R = 32 * n + (l & 31);
+      const u32x4(&kv)[NLD] = kvs[n];
+      const float sgn = sgs[n];
+      // MFMAs of this block (the first k-step from a zero accumulator)
 #pragma unroll
-      for (int n = 0; n < NB; ++n) {
+      for (int c = 0; c < NLD; ++c) {
         if constexpr (FP8) {
-          const bf16x8 b0 = fp8x8_to_bf16x8(kv[n][c][0], kv[n][c][1]);
-          const bf16x8 b1 = fp8x8_to_bf16x8(kv[n][c][2], kv[n][c][3]);
+          const bf16x8 b0 = fp8x8_to_bf16x8(kv[c][0], kv[c][1]);
+          const bf16x8 b1 = fp8x8_to_bf16x8(kv[c][2], kv[c][3]);
 #pragma unroll
           for (int m = 0; m < MB; ++m) {
-            acc[m][n] = mfma32(qa[m][2 * c], b0, c == 0 ? f32x16{} : acc[m][n]);
-            acc[m][n] = mfma32(qa[m][2 * c + 1], b1, acc[m][n]);
+            acc[n][m] = mfma32(qa[m][2 * c], b0, c == 0 ? f32x16{} : acc[n][m]);
+            acc[n][m] = mfma32(qa[m][2 * c + 1], b1, acc[n][m]);
           }
         } else {
 #pragma unroll
           for (int m = 0; m < MB; ++m)
-            acc[m][n] = mfma32(qa[m][c], as_bf16x8(kv[n][c]), c == 0 ? f32x16{} : acc[m][n]);
+            acc[n][m] = mfma32(qa[m][c], as_bf16x8(kv[c]), c == 0 ? f32x16{} : acc[n][m]);
         }
       }
+      // ... and the reduction of the previous block, meanwhile (its result
+      // is dropped for the very first block)
+      float sum[MB][NSUM];
+      reduce(n ^ 1, sg_prev, sum);
+      // issue order: the B reads (both blocks' with the first), then each
+      // MFMA followed by a few of the reduction's vector instructions
+      if (n == 0) __builtin_amdgcn_sched_group_barrier(0x100, NB * NLD, 0);
+#pragma unroll
+      for (int k = 0; k < KS * MB; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      }
+      // the sums exist here, not only inside the stores' branches
+#pragma unroll
+      for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int c4 = 0; c4 < NSUM; ++c4) asm volatile("" : "+v"(sum[m][c4]));
+      if (i > 0 || n > 0) store(j_prev, sum);
+      j_prev = kb + R;
+      sg_prev = sgn;
     }
-    if (!late) epilogue(i);
   }
-  if (late) epilogue(nst - 1);
+  {
+    float sum[MB][NSUM];
+    reduce(NB - 1, sg_prev, sum);
+    store(j_prev, sum);
+  }
 }
 
 template <int DI, int HI, bool FP8>

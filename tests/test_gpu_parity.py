@@ -382,6 +382,20 @@ def test_layer_decode_ragged_lengths_take_the_fast_paths(dsa):
     assert c[2] == 2 and c[0] == len(lens) - 2 and c[1] == 0
 
 
+def test_layer_decode_large_batch_takes_the_row_sweeps(dsa):
+    """1024 sequences and more: the indexer writes plain scores and every row
+    is selected by sweeps over them (no candidate reports)."""
+    say("layer_decode batch of 1024 ragged rows: row-sweep selection")
+    g = np.random.default_rng(77)
+    lens = [int(x) for x in g.integers(300, 3000, size=1024)]
+    w = wl("t", lens, [1] * len(lens), 4, 64, 8, 64, 256, seed=52)
+    inp = W.make_inputs(w)
+    sample = sorted(g.choice(len(lens), size=48, replace=False).tolist())
+    _, c = _with_counters(dsa, lambda: _layer_decode_check(dsa, w, inp, to_dev(inp),
+                                                           seqs=sample))
+    assert c[3] == len(lens) and c[0] == 0 and c[2] == 0 and c[1] == 0
+
+
 def test_layer_decode_k_at_least_context_is_dense_attention(dsa):
     say("layer_decode K >= ctx equals gated dense attention")
     w = wl("t", [1500], [1], 32, 128, 64, 128, 2048, seed=32)

@@ -71,7 +71,6 @@ constexpr int kBucketMax = 64;  // boundary-bucket size ranked directly by wave 
 
 template <int NTILE>
 struct ResolveSmemT {
-  int32_t stage[4096];  // selected positions before the coalesced store (K <= 4096)
   uint32_t hist[2048];
   uint32_t hist2[2048];  // the union select alternates between hist and hist2
   alignas(16) uint32_t bu[kBucketMax];
@@ -406,12 +405,11 @@ __device__ __forceinline__ bool select_from_regs(SM& sm, const UnionRegs<NSL>& R
   bool any_bad = false;
   ordered_ranks<NSL>(sm, smask, R.qn, nt, rk, &total, bad, &any_bad);
   if (any_bad) return false;
-  // stage in LDS, then store coalesced
+  // each selected slot goes straight to its rank (slots in position order:
+  // a group's four slots, and neighbouring lanes, land next to each other)
 #pragma unroll
   for (int i = 0; i < NSL; ++i)
-    if (((smask >> i) & 1u) && rk[i] < k) sm.stage[rk[i]] = R.j[i];
-  lds_barrier();
-  for (int i = tid; i < K; i += nt) out[i] = sm.stage[i];
+    if (((smask >> i) & 1u) && rk[i] < k) out[rk[i]] = R.j[i];
   return true;
 }
 
@@ -779,7 +777,7 @@ __global__ __launch_bounds__(kResolveSlots / NSL) void topk_resolve_kernel(
 // Rows whose candidates cannot be narrowed to kRowsCap (a key shared by
 // very many positions) take the exact sweep select.
 constexpr int kRowsThreads = 512;
-constexpr int kRowsCap = 4096;  // = the staging buffer of the select, reused for positions
+constexpr int kRowsCap = 4096;  // candidates collected per row
 constexpr int kRowsMinT = 1024;  // rows per call from which the row sweeps pay off
 
 __global__ __launch_bounds__(kRowsThreads) void topk_rows_kernel(
@@ -788,7 +786,7 @@ __global__ __launch_bounds__(kRowsThreads) void topk_rows_kernel(
   constexpr int NSL = 16;
   __shared__ RowsSmem sm;
   __shared__ uint32_t cand_u[kRowsCap];
-  int32_t* const cand_j = sm.stage;  // positions; the select reuses it only after loading them
+  __shared__ int32_t cand_j[kRowsCap];
   const int t = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
   const RowInfo ri = row_info(t, cu_q, ctx_len, B);
   const int64_t n = ri.p + 1;

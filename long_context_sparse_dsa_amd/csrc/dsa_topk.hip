@@ -80,6 +80,7 @@ struct ResolveSmemT {
   uint32_t wu[NTILE];
   uint32_t wj[NTILE];
   uint32_t red[64];
+  uint32_t red0[48];  // count / min / max per wave, read only by the register path's first step
   uint32_t flag[16];
   uint32_t scan[20];
   uint32_t st[8];
@@ -184,73 +185,60 @@ __device__ __forceinline__ void ordered_ranks(SM& sm, uint32_t fmask, int qn, in
   lds_barrier();
 }
 
-// Appends the candidates with keys in [lo, lo + width) to sm.bu / sm.bj:
-// per-wave ballot compaction at a base taken with one LDS atomic per wave
-// (sm.st[4] counts the bucket; the caller guarantees at most kBucketMax).
+// Appends the candidates with keys in [lo, lo + width) to sm.bu / sm.bj
+// (in no particular order): a wave scan of the per-lane counts places each
+// lane's candidates after those of the lanes below it, at a wave base taken
+// with one LDS atomic (sm.st[4] counts the bucket; the caller guarantees at
+// most kBucketMax).
 template <int NSL, class SM>
 __device__ __forceinline__ void gather_bucket(SM& sm, const UnionRegs<NSL>& R,
                                               uint32_t lo, uint64_t width) {
   const int l = lane_id();
-  uint32_t inb = 0, cnt = 0;
+  uint32_t inb = 0;
 #pragma unroll
   for (int i = 0; i < NSL; ++i) {
     if (i / 4 < R.qn) {
       const uint32_t x = R.u[i];
-      const bool in = ((R.vmask >> i) & 1u) && x >= lo && (uint64_t)(x - lo) < width;
-      inb |= (uint32_t)in << i;
-      cnt += popc64(__ballot(in));
+      inb |= (uint32_t)(((R.vmask >> i) & 1u) && x >= lo && (uint64_t)(x - lo) < width) << i;
     }
   }
-  if (cnt == 0) return;
+  const uint32_t c = (uint32_t)__popc(inb);
+  const uint32_t inc = wave_incl_scan(c);
+  const uint32_t wtot = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+  if (wtot == 0) return;
   uint32_t base = 0;
-  if (l == 0) base = atomicAdd(&sm.st[4], cnt);
-  base = (uint32_t)__builtin_amdgcn_readlane((int)base, 0);
-  const uint64_t below = lanes_below();
+  if (l == 0) base = atomicAdd(&sm.st[4], wtot);
+  uint32_t pos = (uint32_t)__builtin_amdgcn_readlane((int)base, 0) + inc - c;
 #pragma unroll
   for (int i = 0; i < NSL; ++i) {
-    if (i / 4 < R.qn) {
-      const bool in = (inb >> i) & 1u;
-      const uint64_t m = __ballot(in);
-      if (in) {
-        const uint32_t pos = base + popc64(m & below);
-        sm.bu[pos] = R.u[i];
-        sm.bj[pos] = R.j[i];
-      }
-      base += popc64(m);
+    if ((inb >> i) & 1u) {
+      sm.bu[pos] = R.u[i];
+      sm.bj[pos] = R.j[i];
+      ++pos;
     }
   }
 }
 
-// Wave 0 ranks the h <= kBucketMax gathered candidates under (key desc,
-// position asc) and writes the need-th one to st[2] (key), st[3] (position).
-// Every lane reads the whole bucket (broadcast reads, all issued at once).
-// Called by the whole block; ends with a barrier.
+// Finds the need-th best of the h <= kBucketMax gathered candidates under
+// (key desc, position asc) and writes it to st[2] (key), st[3] (position).
+// The nw waves share the work: lane i holds candidate i, and a wave takes
+// candidates e = wave, wave + nw, ...; the rank of e is the ballot count of
+// the lanes whose candidate beats it (ranks are distinct, so exactly one
+// candidate has rank need - 1).  Called by the block; ends with a barrier.
 template <class SM>
-__device__ __forceinline__ void rank_bucket(SM& sm, uint32_t h, uint32_t need) {
-  const int l = lane_id();
-  if (wave_id() == 0) {
-    const bool mine_ok = (uint32_t)l < h;
-    const uint32_t um = mine_ok ? sm.bu[l] : 0u;
-    const int32_t jm = mine_ok ? sm.bj[l] : 0;
-    uint32_t rank = 0;
+__device__ __forceinline__ void rank_bucket(SM& sm, uint32_t h, uint32_t need, int nw) {
+  const int l = lane_id(), wv = wave_id();
+  const bool mine_ok = (uint32_t)l < h;
+  const uint32_t um = mine_ok ? sm.bu[l] : 0u;
+  const int32_t jm = mine_ok ? sm.bj[l] : 0;
 #pragma unroll 1
-    for (int q0 = 0; q0 < (int)h; q0 += 16) {
-      u32x4 uq[4], jq[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        uq[c] = *reinterpret_cast<const u32x4*>(sm.bu + q0 + 4 * c);
-        jq[c] = *reinterpret_cast<const u32x4*>(sm.bj + q0 + 4 * c);
-      }
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          rank += (uint32_t)(q0 + 4 * c + e) < h &&
-                  ((uq[c][e] > um) || (uq[c][e] == um && (int32_t)jq[c][e] < jm));
-    }
-    if (mine_ok && rank == need - 1) {
-      sm.st[2] = um;
-      sm.st[3] = (uint32_t)jm;
+  for (int e = wv; e < (int)h; e += nw) {
+    const uint32_t ue = sm.bu[e];
+    const int32_t je = sm.bj[e];
+    const uint64_t beats = __ballot(mine_ok && (um > ue || (um == ue && jm < je)));
+    if (l == 0 && popc64(beats) == need - 1) {
+      sm.st[2] = ue;
+      sm.st[3] = (uint32_t)je;
     }
   }
   lds_barrier();
@@ -313,7 +301,7 @@ __device__ __forceinline__ void union_threshold(SM& sm, const UnionRegs<NSL>& R,
   if (h <= (uint32_t)kBucketMax) {
     gather_bucket(sm, R, lo, width);
     lds_barrier();
-    rank_bucket(sm, h, need);
+    rank_bucket(sm, h, need, nt >> 6);
     *tau_u = sm.st[2];
     *tau_j = (int32_t)sm.st[3];
     return;
@@ -363,9 +351,9 @@ __device__ __forceinline__ bool select_from_regs(SM& sm, const UnionRegs<NSL>& R
   mn = wave_min_u32(mn);
   mx = wave_max_u32(mx);
   if (l == 0) {
-    sm.red[wv] = cw;
-    sm.red[16 + wv] = mn;
-    sm.red[32 + wv] = mx;
+    sm.red0[wv] = cw;
+    sm.red0[16 + wv] = mn;
+    sm.red0[32 + wv] = mx;
   }
   for (int i = tid; i < 2048; i += nt) {
     sm.hist[i] = 0;
@@ -373,14 +361,15 @@ __device__ __forceinline__ bool select_from_regs(SM& sm, const UnionRegs<NSL>& R
   }
   if (tid == 0) sm.st[4] = 0;
   lds_barrier();
+  // red0 is written nowhere else, so no second barrier is needed before
+  // the next step reuses the LDS
   uint32_t C;
   {
     const int nw = nt >> 6;
-    C = wave_sum_u32(l < nw ? sm.red[l] : 0u);
-    mn = wave_min_u32(l < nw ? sm.red[16 + l] : 0xffffffffu);
-    mx = wave_max_u32(l < nw ? sm.red[32 + l] : 0u);
+    C = wave_sum_u32(l < nw ? sm.red0[l] : 0u);
+    mn = wave_min_u32(l < nw ? sm.red0[16 + l] : 0xffffffffu);
+    mx = wave_max_u32(l < nw ? sm.red0[32 + l] : 0u);
   }
-  lds_barrier();  // red[] is reused below
   if (C < k) return false;
   uint32_t tau_u;
   int32_t tau_j;
@@ -574,7 +563,7 @@ __device__ __forceinline__ void exact_select_row(SM& sm, const float* row, int64
         }
     }
     lds_barrier();
-    rank_bucket(sm, h, need);
+    rank_bucket(sm, h, need, nw);
     tau_u = sm.st[2];
     tau_j = (int32_t)sm.st[3];
   } else {

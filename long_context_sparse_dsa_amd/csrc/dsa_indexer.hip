@@ -300,8 +300,8 @@ __global__ __launch_bounds__(64 * WPT) void index_decode_kernel(
       dma_barrier();  // every wave's scores are in LDS
       if (wv != 0) return;
     }
-    const int S = topk_subtile(nrow, topk);  // divides TILE
-    const int64_t slot = (int64_t)b * stride + (int64_t)ti * (TILE / S);
+    const int S = topk_subtile(nrow, topk);  // a power of two dividing TILE
+    const int64_t slot = (int64_t)b * stride + (int64_t)ti * (TILE >> (31 - __clz(S)));
     if (S < TILE) {
       wave_subtile_reports<V>([&](int e) { return sc_lds[e]; }, n_valid, j0, S, hdr + slot,
                               rep_u + slot * kRep, rep_j + slot * kRep);

@@ -44,7 +44,7 @@ __global__ __launch_bounds__(64) void tile_report_kernel(const float* __restrict
   const int n = (int)min<int64_t>(TILE, nrow - j0);
   const float* row = scores + (int64_t)t * ld + j0;
   const int S = topk_subtile(nrow, K);  // <= TILE
-  const int64_t slot = (int64_t)t * stride + (int64_t)ti * (TILE / S);
+  const int64_t slot = (int64_t)t * stride + (int64_t)ti * (TILE >> (31 - __clz(S)));
   if (S < TILE) {
     wave_subtile_reports<V>([&](int e) { return row[e]; }, n, j0, S, hdr + slot,
                             rep_u + slot * kRep, rep_j + slot * kRep);
@@ -711,7 +711,7 @@ __global__ __launch_bounds__(kResolveSlots / NSL) void topk_resolve_kernel(
     path = 2;
   } else {
     const int S = topk_subtile(n, K);
-    const int nt_row = (int)((n + S - 1) / S);
+    const int nt_row = (int)((n + S - 1) >> (31 - __clz(S)));  // S: a power of two
     if (nt_row <= kResolveTiles && nt_row <= stride && nt_row * kRep <= nb * NSL) {
       nt = max(threads_for((int64_t)nt_row * kRep), eager_nt);
       if (tid >= nt) return;

@@ -37,10 +37,10 @@ constexpr int kSubTiles = 1024;  // most sub-tiles a row may have on the fast pa
 // has at most kSubTiles sub-tiles.  Non-decreasing in n.
 __host__ __device__ inline int topk_subtile(int64_t n, int K) {
   const int64_t k = K > 0 ? K : 1;
-  const int64_t per4 = 4 * n / k;
   const int64_t by_tiles = (n + kSubTiles - 1) / kSubTiles;
   int s = kSubMin;
-  while (s < kSubMax && 2 * (int64_t)s <= per4) s <<= 1;
+  // 2 s <= floor(4 n / k)  <=>  2 s k <= 4 n  (no division on the device)
+  while (s < kSubMax && 2 * (int64_t)s * k <= 4 * n) s <<= 1;
   while (s < kSubMax && s < by_tiles) s <<= 1;
   return s;
 }
@@ -66,30 +66,30 @@ template <int V>
 __device__ void wave_tile_report(const uint32_t (&u)[V], const int32_t (&j)[V],
                                  const bool (&valid)[V], RepHeader* hdr, uint32_t* rep_u,
                                  int32_t* rep_j) {
-  uint32_t n = 0;
+  uint32_t uz[V];  // invalid slots as key 0: every probe below is >= 1
+  uint32_t cnt = 0, mn = 0xffffffffu, mx = 0u;
 #pragma unroll
-  for (int i = 0; i < V; ++i) n += popc64(__ballot(valid[i]));
+  for (int i = 0; i < V; ++i) {
+    uz[i] = valid[i] ? u[i] : 0u;
+    cnt += valid[i] ? 1u : 0u;
+    mn = min(mn, valid[i] ? u[i] : 0xffffffffu);
+    mx = max(mx, uz[i]);
+  }
+  const uint32_t n = wave_sum_u32(cnt);
+  mn = wave_min_u32(mn);
   bool sel[V];
+  uint32_t wu;  // key of the worst reported element
   const bool complete = n <= (uint32_t)kRep;
   if (complete) {
 #pragma unroll
     for (int i = 0; i < V; ++i) sel[i] = valid[i];
+    wu = mn;
   } else {
-    uint32_t mn = 0xffffffffu, mx = 0u;
-#pragma unroll
-    for (int i = 0; i < V; ++i)
-      if (valid[i]) {
-        mn = min(mn, u[i]);
-        mx = max(mx, u[i]);
-      }
-    // largest T with count(key >= T) >= kRep: the kRep-th best key.  Every
-    // probe is >= 1, so invalid slots count as key 0 and drop out.  The
-    // search stops early once a probe has exactly kRep keys at or above it:
-    // that probe selects the same kRep elements.
-    uint32_t uz[V];
-#pragma unroll
-    for (int i = 0; i < V; ++i) uz[i] = valid[i] ? u[i] : 0u;
-    uint32_t lo = wave_min_u32(mn), hi = wave_max_u32(mx);
+    // largest T with count(key >= T) >= kRep: the kRep-th best key.  A
+    // probe with exactly kRep keys at or above it ends the search early:
+    // those kRep elements are the report.
+    uint32_t lo = mn, hi = wave_max_u32(mx);
+    bool exact = false;
     while (lo < hi) {
       const uint32_t mid = lo + ((hi - lo) >> 1) + 1;  // in (lo, hi]
       uint32_t c = 0;
@@ -97,29 +97,41 @@ __device__ void wave_tile_report(const uint32_t (&u)[V], const int32_t (&j)[V],
       for (int i = 0; i < V; ++i) c += popc64(__ballot(uz[i] >= mid));
       if (c == (uint32_t)kRep) {
         lo = mid;
+        exact = true;
         break;
       }
       if (c > (uint32_t)kRep) lo = mid; else hi = mid - 1;
     }
     const uint32_t T = lo;
-    uint32_t gt = 0;
+    if (exact) {
+      uint32_t m = 0xffffffffu;
 #pragma unroll
-    for (int i = 0; i < V; ++i) gt += popc64(__ballot(valid[i] && u[i] > T));
-    const uint32_t need = (uint32_t)kRep - gt;  // copies of T to keep, lowest positions first
-    const uint64_t below = lanes_below();
-    uint32_t seen = 0;
+      for (int i = 0; i < V; ++i) {
+        sel[i] = uz[i] >= T;
+        m = min(m, sel[i] ? u[i] : 0xffffffffu);
+      }
+      wu = wave_min_u32(m);
+    } else {
+      // T is a key: {key > T} plus the need lowest positions with key == T
+      uint32_t g = 0;
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-      const bool eq = valid[i] && u[i] == T;
-      const uint64_t m = __ballot(eq);
-      sel[i] = (valid[i] && u[i] > T) || (eq && seen + popc64(m & below) < need);
-      seen += popc64(m);
+      for (int i = 0; i < V; ++i) g += uz[i] > T ? 1u : 0u;
+      const uint32_t need = (uint32_t)kRep - wave_sum_u32(g);
+      const uint64_t below = lanes_below();
+      uint32_t seen = 0;
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        const bool eq = valid[i] && u[i] == T;
+        const uint64_t m = __ballot(eq);
+        sel[i] = uz[i] > T || (eq && seen + popc64(m & below) < need);
+        seen += popc64(m);
+      }
+      wu = T;
     }
   }
   // compaction in position order
   const uint64_t below = lanes_below();
   uint32_t base = 0;
-  uint32_t wu = 0xffffffffu;
 #pragma unroll
   for (int i = 0; i < V; ++i) {
     const uint64_t m = __ballot(sel[i]);
@@ -127,17 +139,20 @@ __device__ void wave_tile_report(const uint32_t (&u)[V], const int32_t (&j)[V],
       const uint32_t pos = base + popc64(m & below);
       rep_u[pos] = u[i];
       rep_j[pos] = j[i];
-      wu = min(wu, u[i]);
     }
     base += popc64(m);
   }
-  // worst reported element: smallest key, then largest position
-  wu = wave_min_u32(wu);
+  // worst position: the highest selected position holding key wu (the
+  // last slot in (i, lane) order)
   int32_t wj = -1;
 #pragma unroll
-  for (int i = 0; i < V; ++i)
-    if (sel[i] && u[i] == wu) wj = max(wj, j[i]);
-  wj = wave_max_i32(wj);
+  for (int i = V - 1; i >= 0; --i) {
+    const uint64_t m = __ballot(sel[i] && u[i] == wu);
+    if (m != 0ull) {
+      wj = __builtin_amdgcn_readlane(j[i], 63 - __clzll((long long)m));
+      break;
+    }
+  }
   if (lane_id() == 0) {
     RepHeader h;
     h.count = base;

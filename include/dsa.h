@@ -180,14 +180,16 @@ dsa_status_t dsa_set_indexer_events(void* start, void* stop);
 
 /* Diagnostic hook: on the calling thread, every later Top-K selection     */
 /* (dsa_topk, dsa_layer_decode, dsa_layer_prefill) adds, per row, 1 to one  */
-/* of four caller-owned device counters (uint32 [4], zeroed by the caller)  */
-/* naming the path that produced the row: [0] the union of the row's        */
-/* sub-tile candidate reports, certified exact; [1] the exact radix select  */
-/* over the whole score row (certification failed, or a key shared by too   */
-/* many positions); [2] the direct select of a row of at most 16384         */
-/* positions; [3] the histogram and collection sweeps over the row's scores */
-/* used when a call has 1024 rows or more.  Rows with at most K positions   */
-/* take none of them.  Pass NULL to stop.  Always DSA_OK.                   */
+/* of the first four of five caller-owned device counters (uint32 [5],     */
+/* zeroed by the caller) naming the path that produced the row: [0] the     */
+/* union of the row's sub-tile candidate reports, certified exact; [1] the  */
+/* exact radix select over the whole score row (certification failed, or a  */
+/* key shared by too many positions); [2] the direct select of a row of at  */
+/* most 16384 positions; [3] the collection sweep over the row's scores     */
+/* used when a call has 1024 rows or more.  [4] counts the rows of [3]      */
+/* whose collection threshold came from a sample of the row (one sweep      */
+/* instead of histogram sweeps first).  Rows with at most K positions take  */
+/* none of them.  Pass NULL to stop.  Always DSA_OK.                        */
 dsa_status_t dsa_set_topk_counters(uint32_t* counters);
 
 /* ------------------------------------------------------------------------ */

@@ -330,11 +330,12 @@ def dsa_set_indexer_events(start, stop):
 
 def dsa_set_topk_counters(counters):
     """Count, per Top-K row on this thread, the path that produced it into a
-    caller-owned uint32 [4] device tensor (certified union, exact fallback,
-    direct, row sweeps); None stops counting."""
+    caller-owned uint32 [5] device tensor (certified union, exact fallback,
+    direct, row sweeps, and of those the sampled-threshold ones); None stops
+    counting."""
     if counters is not None:
         assert counters.dtype == torch.int32
-        assert counters.is_cuda and counters.numel() >= 4 and counters.is_contiguous()
+        assert counters.is_cuda and counters.numel() >= 5 and counters.is_contiguous()
     _call("dsa_set_topk_counters", None if counters is None else counters.data_ptr())
 
 

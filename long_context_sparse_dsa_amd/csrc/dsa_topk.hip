@@ -754,6 +754,11 @@ __global__ __launch_bounds__(kResolveSlots / NSL) void topk_resolve_kernel(
 // Exact Top-K of many rows straight from their scores (prefill: thousands
 // of long rows, where a report per sub-tile costs more than two sweeps over
 // the row).  One workgroup of kRowsThreads per row:
+//   0. rows of at least kPilotMinRow positions first take a threshold from
+//      a sample of about 1/16 of the row, chosen so that about
+//      (K + kRowsCap) / 2 keys of the row are expected at or above it, and
+//      collect those keys in one ordered sweep (as in 2); if their count is
+//      not in [K, kRowsCap] the row continues with 1;
 //   1. a sweep builds the 2048-bin histogram of the keys' top 11 bits; one
 //      wave finds the bucket of the K-th key; while the keys at or above
 //      that bucket would not fit kRowsCap, further sweeps refine it by the
@@ -768,6 +773,7 @@ __global__ __launch_bounds__(kResolveSlots / NSL) void topk_resolve_kernel(
 constexpr int kRowsThreads = 512;
 constexpr int kRowsCap = 4096;  // candidates collected per row
 constexpr int kRowsMinT = 1024;  // rows per call from which the row sweeps pay off
+constexpr int kPilotMinRow = 16384;  // rows from this length first try a sampled threshold
 
 __global__ __launch_bounds__(kRowsThreads) void topk_rows_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* cu_q, const int32_t* ctx_len,
@@ -793,49 +799,9 @@ __global__ __launch_bounds__(kRowsThreads) void topk_rows_kernel(
   constexpr int PER = 8;
   const int64_t step = PER * (int64_t)nt;
   uint32_t ua[PER], ub[PER];
-  // 1. bucket of the K-th key: [lo, lo + width), `above` keys beyond it
-  for (int i = tid; i < 2048; i += nt) sm.hist[i] = 0;
-  lds_barrier();
-  uint32_t lo = 0, above = 0, h = 0;
-  uint64_t width = 1ull << 32;
-  int shift = 21;
-  auto hist_add = [&](const uint32_t(&u)[PER], uint32_t vm) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i)
-      if (((vm >> i) & 1u) && u[i] >= lo && (uint64_t)(u[i] - lo) < width)
-        atomicAdd(&sm.hist[(u[i] - lo) >> shift], 1u);
-  };
-#pragma unroll 1
-  while (true) {
-    uint32_t va = load_keys<PER>(row, n, PER * tid, vec, ua);
-#pragma unroll 1
-    for (int64_t b0 = 0; b0 < n; b0 += 2 * step) {
-      const uint32_t vb = load_keys<PER>(row, n, b0 + step + PER * tid, vec, ub);
-      hist_add(ua, va);
-      va = load_keys<PER>(row, n, b0 + 2 * step + PER * tid, vec, ua);
-      hist_add(ub, vb);
-    }
-    dma_barrier();
-    if (wave_id() == 0) wave_find_digit(sm, sm.hist, above, k);
-    lds_barrier();
-    const uint32_t d = sm.st[0];
-    above = sm.st[1];
-    h = sm.st[5];
-    lo += d << shift;
-    width = 1ull << shift;
-    if (above + h <= (uint32_t)kRowsCap || shift == 0) break;
-    shift = max(0, shift - 11);
-    for (int i = tid; i < 2048; i += nt) sm.hist[i] = 0;
-    lds_barrier();
-  }
-  const uint32_t C = above + h;  // keys >= lo
-  if (C > (uint32_t)kRowsCap) {
-    exact_select_row(sm, row, n, k, vec, nt, out);
-    if (stats && tid == 0) atomicAdd(&stats[1], 1u);
-    return;
-  }
-  // 2. ordered collection of the keys >= lo
-  uint32_t cum = 0;
+  // ordered collection of the keys >= lo into cand_u / cand_j (position
+  // order; positions past kRowsCap are counted, not stored)
+  uint32_t lo = 0, cum = 0;
   auto collect = [&](const uint32_t(&u)[PER], uint32_t vm, int64_t b0) {
     const int64_t p0 = b0 + PER * tid;
     uint32_t f = 0;
@@ -846,13 +812,119 @@ __global__ __launch_bounds__(kRowsThreads) void topk_rows_kernel(
 #pragma unroll
     for (int i = 0; i < PER; ++i)
       if ((f >> i) & 1u) {
-        cand_u[r] = u[i];
-        cand_j[r] = (int32_t)(p0 + i);
+        if (r < (uint32_t)kRowsCap) {
+          cand_u[r] = u[i];
+          cand_j[r] = (int32_t)(p0 + i);
+        }
         ++r;
       }
     cum += tot;
   };
-  {
+  uint32_t C = 0;  // candidates collected: every key >= lo, k <= C <= kRowsCap
+  bool have = false;
+  // 0. Long rows: a threshold from a sample (NC chunks of 512 consecutive
+  //    keys spread over the row, about 1/16 of it) whose rank in the row is
+  //    expected midway between k and kRowsCap; one ordered sweep then
+  //    collects every key at or above it.  If the count misses [k,
+  //    kRowsCap] (an unrepresentative sample), the row takes steps 1-2.
+  if (n >= kPilotMinRow && 4 * (kRowsCap - K) >= K) {
+    const int NC = (int)min<int64_t>(32, (n + 8191) / 8192);
+    const int64_t P = (n / NC) & ~(int64_t)3;  // chunk period, >= 512
+    const int wv = wave_id(), ln = lane_id();
+    uint32_t sk[4][PER], svm[4];
+#pragma unroll
+    for (int rd = 0; rd < 4; ++rd) {
+      const int c = 8 * rd + wv;  // one chunk per wave and round
+      svm[rd] = 0;
+      if (c < NC) svm[rd] = load_keys<PER>(row, n, c * P + PER * ln, vec, sk[rd]);
+    }
+    for (int i = tid; i < 2048; i += nt) {
+      sm.hist[i] = 0;
+      sm.hist2[i] = 0;
+    }
+    lds_barrier();
+    const uint32_t m = (uint32_t)NC * 512u;
+    const uint32_t target = k + ((uint32_t)kRowsCap - k) / 2;
+    const uint32_t rk = (uint32_t)(((uint64_t)target * m + (uint64_t)n - 1) / (uint64_t)n);
+    // rank rk of the sample: top 11 bits, then the next 11 within that bucket
+#pragma unroll
+    for (int rd = 0; rd < 4; ++rd)
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if ((svm[rd] >> i) & 1u) atomicAdd(&sm.hist[sk[rd][i] >> 21], 1u);
+    lds_barrier();
+    if (wv == 0) wave_find_digit(sm, sm.hist, 0u, rk);
+    lds_barrier();
+    const uint32_t lo_a = sm.st[0] << 21, above_a = sm.st[1];
+#pragma unroll
+    for (int rd = 0; rd < 4; ++rd)
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if (((svm[rd] >> i) & 1u) && (sk[rd][i] >> 21) == (lo_a >> 21))
+          atomicAdd(&sm.hist2[(sk[rd][i] - lo_a) >> 10], 1u);
+    lds_barrier();
+    if (wv == 0) wave_find_digit(sm, sm.hist2, above_a, rk);
+    lds_barrier();
+    lo = lo_a + (sm.st[0] << 10);
+    // one ordered sweep over the row
+    uint32_t va = load_keys<PER>(row, n, PER * tid, vec, ua);
+#pragma unroll 1
+    for (int64_t b0 = 0; b0 < n && cum <= (uint32_t)kRowsCap; b0 += 2 * step) {
+      const uint32_t vb = load_keys<PER>(row, n, b0 + step + PER * tid, vec, ub);
+      collect(ua, va, b0);
+      if (b0 + step >= n || cum > (uint32_t)kRowsCap) break;
+      va = load_keys<PER>(row, n, b0 + 2 * step + PER * tid, vec, ua);
+      collect(ub, vb, b0 + step);
+    }
+    have = cum >= k && cum <= (uint32_t)kRowsCap;
+    C = cum;
+    dma_barrier();  // the collection's LDS writes, and st[] reads, before reuse
+  }
+  if (!have) {
+    // 1. bucket of the K-th key: [lo, lo + width), `above` keys beyond it
+    for (int i = tid; i < 2048; i += nt) sm.hist[i] = 0;
+    lds_barrier();
+    lo = 0;
+    uint32_t above = 0, h = 0;
+    uint64_t width = 1ull << 32;
+    int shift = 21;
+    auto hist_add = [&](const uint32_t(&u)[PER], uint32_t vm) {
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if (((vm >> i) & 1u) && u[i] >= lo && (uint64_t)(u[i] - lo) < width)
+          atomicAdd(&sm.hist[(u[i] - lo) >> shift], 1u);
+    };
+#pragma unroll 1
+    while (true) {
+      uint32_t va = load_keys<PER>(row, n, PER * tid, vec, ua);
+#pragma unroll 1
+      for (int64_t b0 = 0; b0 < n; b0 += 2 * step) {
+        const uint32_t vb = load_keys<PER>(row, n, b0 + step + PER * tid, vec, ub);
+        hist_add(ua, va);
+        va = load_keys<PER>(row, n, b0 + 2 * step + PER * tid, vec, ua);
+        hist_add(ub, vb);
+      }
+      dma_barrier();
+      if (wave_id() == 0) wave_find_digit(sm, sm.hist, above, k);
+      lds_barrier();
+      const uint32_t d = sm.st[0];
+      above = sm.st[1];
+      h = sm.st[5];
+      lo += d << shift;
+      width = 1ull << shift;
+      if (above + h <= (uint32_t)kRowsCap || shift == 0) break;
+      shift = max(0, shift - 11);
+      for (int i = tid; i < 2048; i += nt) sm.hist[i] = 0;
+      lds_barrier();
+    }
+    C = above + h;  // keys >= lo
+    if (C > (uint32_t)kRowsCap) {
+      exact_select_row(sm, row, n, k, vec, nt, out);
+      if (stats && tid == 0) atomicAdd(&stats[1], 1u);
+      return;
+    }
+    // 2. ordered collection of the keys >= lo
+    cum = 0;
     uint32_t va = load_keys<PER>(row, n, PER * tid, vec, ua);
 #pragma unroll 1
     for (int64_t b0 = 0; b0 < n && cum < C; b0 += 2 * step) {
@@ -882,7 +954,10 @@ __global__ __launch_bounds__(kRowsThreads) void topk_rows_kernel(
     }
   }
   select_from_regs(sm, R, k, K, 0, nt, out);  // C >= k: always succeeds
-  if (stats && tid == 0) atomicAdd(&stats[3], 1u);
+  if (stats && tid == 0) {
+    atomicAdd(&stats[3], 1u);
+    if (have) atomicAdd(&stats[4], 1u);
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -172,7 +172,7 @@ RAGGED_TOPK_LENS = [5000, 16384, 16385, 20000, 31000, 70000, 131071, 131072, 300
 
 
 def _with_counters(dsa, fn):
-    cnt = torch.zeros(4, dtype=torch.int32, device=DEV)
+    cnt = torch.zeros(5, dtype=torch.int32, device=DEV)
     dsa.dsa_set_topk_counters(cnt)
     try:
         res = fn()
@@ -235,11 +235,13 @@ def test_topk_many_rows_take_the_row_sweeps(dsa, kind):
     want = oracle.topk(s.numpy(), K, ctx.numpy(), cu_q=cu_q.numpy())
     assert np.array_equal(got.cpu().numpy(), want)
     n_sel = sum(1 for n_ctx, q in zip(lens, nq) for i in range(q) if n_ctx - q + i + 1 > K)
-    assert c[0] == 0 and c[2] == 0 and c[1] + c[3] == n_sel
+    n_long = sum(1 for n_ctx, q in zip(lens, nq) for i in range(q) if n_ctx - q + i + 1 >= 16384)
+    assert c[0] == 0 and c[2] == 0 and c[1] + c[3] == n_sel and c[4] <= c[3]
     if kind == "equal":
         assert c[1] == n_sel
     elif kind in ("normal", "relu_like"):
-        assert c[3] == n_sel
+        # long rows: one collection sweep from a sampled threshold
+        assert c[3] == n_sel and c[4] == n_long
 
 
 # --------------------------------------------------------------------------

@@ -307,18 +307,12 @@ __global__ __launch_bounds__(64 * WPT) void index_decode_kernel(
                               rep_u + slot * kRep, rep_j + slot * kRep);
       return;
     }
-    // report value i of lane l is tile element 64 i + l
+    // report value i of lane l is tile element V l + i
     uint32_t uv[V];
-    int32_t jv[V];
-    bool vv[V];
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-      const int jl = 64 * i + l;
-      vv[i] = jl < n_valid;
-      uv[i] = order_key(sc_lds[jl]);
-      jv[i] = (int32_t)(j0 + jl);
-    }
-    wave_tile_report<V>(uv, jv, vv, hdr + slot, rep_u + slot * kRep, rep_j + slot * kRep);
+    for (int i = 0; i < V; ++i) uv[i] = order_key(sc_lds[V * l + i]);
+    wave_tile_report<V>(uv, min(max(n_valid - V * l, 0), V), j0 + V * l, hdr + slot,
+                        rep_u + slot * kRep, rep_j + slot * kRep);
   }
 }
 

@@ -51,17 +51,11 @@ __global__ __launch_bounds__(64) void tile_report_kernel(const float* __restrict
     return;
   }
   const int l = lane_id();
+  const int nv = min(max(n - V * l, 0), V);  // valid elements V l .. V l + nv - 1
   uint32_t uv[V];
-  int32_t jv[V];
-  bool vv[V];
 #pragma unroll
-  for (int i = 0; i < V; ++i) {
-    const int jl = 64 * i + l;
-    vv[i] = jl < n;
-    uv[i] = order_key(row[vv[i] ? jl : 0]);
-    jv[i] = (int32_t)(j0 + jl);
-  }
-  wave_tile_report<V>(uv, jv, vv, hdr + slot, rep_u + slot * kRep, rep_j + slot * kRep);
+  for (int i = 0; i < V; ++i) uv[i] = order_key(row[i < nv ? V * l + i : 0]);
+  wave_tile_report<V>(uv, nv, j0 + V * l, hdr + slot, rep_u + slot * kRep, rep_j + slot * kRep);
 }
 
 // ---------------------------------------------------------------------------

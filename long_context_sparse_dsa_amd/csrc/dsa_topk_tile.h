@@ -59,30 +59,32 @@ __device__ __forceinline__ uint64_t lanes_below() {
   return (l == 0) ? 0ull : (~0ull >> (64 - l));
 }
 
-// Wave-level tile report.  Lane l holds V order keys u[i] for the tile's
-// elements at index i*64 + l (index order == position order), with valid[i].
-// Writes the report (positions ascending) and its header.
+// Wave-level tile report.  Lane l holds the V order keys u[i] of the tile's
+// elements V l + i (lane-major, so position order is lane order, then i);
+// the first nv of them are valid and the lane's element 0 sits at position
+// jbase.  Writes the report (positions ascending) and its header.  Every
+// count, rank and placement is a per-lane sum joined by one wave scan or
+// reduction (DPP); the bisection of short lanes counts with ballots.
 template <int V>
-__device__ void wave_tile_report(const uint32_t (&u)[V], const int32_t (&j)[V],
-                                 const bool (&valid)[V], RepHeader* hdr, uint32_t* rep_u,
-                                 int32_t* rep_j) {
+__device__ void wave_tile_report(const uint32_t (&u)[V], int nv, int64_t jbase, RepHeader* hdr,
+                                 uint32_t* rep_u, int32_t* rep_j) {
   uint32_t uz[V];  // invalid slots as key 0: every probe below is >= 1
-  uint32_t cnt = 0, mn = 0xffffffffu, mx = 0u;
+  uint32_t mn = 0xffffffffu, mx = 0u;
 #pragma unroll
   for (int i = 0; i < V; ++i) {
-    uz[i] = valid[i] ? u[i] : 0u;
-    cnt += valid[i] ? 1u : 0u;
-    mn = min(mn, valid[i] ? u[i] : 0xffffffffu);
+    const bool v = i < nv;
+    uz[i] = v ? u[i] : 0u;
+    mn = min(mn, v ? u[i] : 0xffffffffu);
     mx = max(mx, uz[i]);
   }
-  const uint32_t n = wave_sum_u32(cnt);
+  const uint32_t n = wave_sum_u32((uint32_t)nv);
   mn = wave_min_u32(mn);
   bool sel[V];
   uint32_t wu;  // key of the worst reported element
   const bool complete = n <= (uint32_t)kRep;
   if (complete) {
 #pragma unroll
-    for (int i = 0; i < V; ++i) sel[i] = valid[i];
+    for (int i = 0; i < V; ++i) sel[i] = i < nv;
     wu = mn;
   } else {
     // largest T with count(key >= T) >= kRep: the kRep-th best key.  A
@@ -93,8 +95,14 @@ __device__ void wave_tile_report(const uint32_t (&u)[V], const int32_t (&j)[V],
     while (lo < hi) {
       const uint32_t mid = lo + ((hi - lo) >> 1) + 1;  // in (lo, hi]
       uint32_t c = 0;
+      if constexpr (V >= 8) {
 #pragma unroll
-      for (int i = 0; i < V; ++i) c += popc64(__ballot(uz[i] >= mid));
+        for (int i = 0; i < V; ++i) c += uz[i] >= mid ? 1u : 0u;
+        c = wave_sum_u32(c);
+      } else {
+#pragma unroll
+        for (int i = 0; i < V; ++i) c += popc64(__ballot(uz[i] >= mid));
+      }
       if (c == (uint32_t)kRep) {
         lo = mid;
         exact = true;
@@ -113,49 +121,44 @@ __device__ void wave_tile_report(const uint32_t (&u)[V], const int32_t (&j)[V],
       wu = wave_min_u32(m);
     } else {
       // T is a key: {key > T} plus the need lowest positions with key == T
-      uint32_t g = 0;
-#pragma unroll
-      for (int i = 0; i < V; ++i) g += uz[i] > T ? 1u : 0u;
-      const uint32_t need = (uint32_t)kRep - wave_sum_u32(g);
-      const uint64_t below = lanes_below();
-      uint32_t seen = 0;
+      uint32_t g = 0, ce = 0;
 #pragma unroll
       for (int i = 0; i < V; ++i) {
-        const bool eq = valid[i] && u[i] == T;
-        const uint64_t m = __ballot(eq);
-        sel[i] = uz[i] > T || (eq && seen + popc64(m & below) < need);
-        seen += popc64(m);
+        g += uz[i] > T ? 1u : 0u;
+        ce += (i < nv && u[i] == T) ? 1u : 0u;
+      }
+      const uint32_t need = (uint32_t)kRep - wave_sum_u32(g);
+      uint32_t r = wave_incl_scan(ce) - ce;  // copies of T in lower lanes
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        const bool eq = i < nv && u[i] == T;
+        sel[i] = uz[i] > T || (eq && r < need);
+        r += eq ? 1u : 0u;
       }
       wu = T;
     }
   }
-  // compaction in position order
-  const uint64_t below = lanes_below();
-  uint32_t base = 0;
+  // placement in position order: lanes in order, each lane's elements in order
+  uint32_t cs = 0;
+#pragma unroll
+  for (int i = 0; i < V; ++i) cs += sel[i] ? 1u : 0u;
+  const uint32_t incl = wave_incl_scan(cs);
+  const uint32_t count = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+  uint32_t pos = incl - cs;
+  int32_t wj = -1;  // highest selected position with key wu
 #pragma unroll
   for (int i = 0; i < V; ++i) {
-    const uint64_t m = __ballot(sel[i]);
     if (sel[i]) {
-      const uint32_t pos = base + popc64(m & below);
       rep_u[pos] = u[i];
-      rep_j[pos] = j[i];
-    }
-    base += popc64(m);
-  }
-  // worst position: the highest selected position holding key wu (the
-  // last slot in (i, lane) order)
-  int32_t wj = -1;
-#pragma unroll
-  for (int i = V - 1; i >= 0; --i) {
-    const uint64_t m = __ballot(sel[i] && u[i] == wu);
-    if (m != 0ull) {
-      wj = __builtin_amdgcn_readlane(j[i], 63 - __clzll((long long)m));
-      break;
+      rep_j[pos] = (int32_t)(jbase + i);
+      ++pos;
+      if (u[i] == wu) wj = (int32_t)(jbase + i);
     }
   }
+  wj = wave_max_i32(wj);
   if (lane_id() == 0) {
     RepHeader h;
-    h.count = base;
+    h.count = count;
     h.complete = complete ? 1u : 0u;
     h.worst_u = wu;
     h.worst_j = wj;

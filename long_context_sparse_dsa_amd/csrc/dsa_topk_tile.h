@@ -166,14 +166,75 @@ __device__ void wave_tile_report(const uint32_t (&u)[V], int nv, int64_t jbase, 
   }
 }
 
+// Segmented wave primitives over aligned groups of g lanes (g a power of
+// two, 1 <= g <= 64, uniform over the wave), built from DPP row shifts and
+// row broadcasts like the whole-wave scans.  Every step runs for every g
+// (steps that cross a group boundary are masked per lane), so there are no
+// branches.
+//   seg_scan:      inclusive scan with `op` (identity id) within each group;
+//   seg_last:      every lane of a group gets the value of the group's last
+//                  lane.
+template <typename Op>
+__device__ __forceinline__ uint32_t seg_scan(uint32_t v, uint32_t id, int g, Op op) {
+  // a row shift by k reads lane l - k; it stays in the group iff r >= k,
+  // which never holds for k >= g
+  const int r = lane_id() & (g - 1);
+  uint32_t t = dpp_u32<kDppRowShr1, 0xf, 0xf>(id, v);
+  v = op(v, r >= 1 ? t : id);
+  t = dpp_u32<kDppRowShr2, 0xf, 0xf>(id, v);
+  v = op(v, r >= 2 ? t : id);
+  t = dpp_u32<kDppRowShr4, 0xf, 0xf>(id, v);
+  v = op(v, r >= 4 ? t : id);
+  t = dpp_u32<kDppRowShr8, 0xf, 0xf>(id, v);
+  v = op(v, r >= 8 ? t : id);
+  // rows 1 and 3 add the previous row's last lane (groups of 32 and 64),
+  // rows 2 and 3 lane 31 (groups of 64)
+  t = dpp_u32<kDppRowBcast15, 0xa, 0xf>(id, v);
+  v = op(v, g >= 32 ? t : id);
+  t = dpp_u32<kDppRowBcast31, 0xc, 0xf>(id, v);
+  v = op(v, g >= 64 ? t : id);
+  return v;
+}
+
+constexpr int kDppRowShl1 = 0x101, kDppRowShl2 = 0x102, kDppRowShl4 = 0x104, kDppRowShl8 = 0x108;
+
+__device__ __forceinline__ uint32_t seg_last(uint32_t v, int g) {
+  const int l = lane_id(), r = l & (g - 1);
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+  const uint32_t wide = (g == 64 || l >= 32) ? b : a;  // groups of 32 or 64 lanes
+  // lane r takes lane r + k's value while that lane is in the group: after
+  // the steps k = 1, 2, 4, 8 it holds the value of lane g - 1 (g <= 16)
+  uint32_t t = dpp_u32<kDppRowShl1, 0xf, 0xf>(v, v);
+  v = r + 1 < g ? t : v;
+  t = dpp_u32<kDppRowShl2, 0xf, 0xf>(v, v);
+  v = r + 2 < g ? t : v;
+  t = dpp_u32<kDppRowShl4, 0xf, 0xf>(v, v);
+  v = r + 4 < g ? t : v;
+  t = dpp_u32<kDppRowShl8, 0xf, 0xf>(v, v);
+  v = r + 8 < g ? t : v;
+  return g >= 32 ? wide : v;
+}
+
+__device__ __forceinline__ uint32_t seg_sum(uint32_t v, int g) {
+  return seg_last(seg_scan(v, 0u, g, [](uint32_t a, uint32_t b) { return a + b; }), g);
+}
+__device__ __forceinline__ uint32_t seg_min(uint32_t v, int g) {
+  return seg_last(seg_scan(v, 0xffffffffu, g, [](uint32_t a, uint32_t b) { return a < b ? a : b; }), g);
+}
+__device__ __forceinline__ uint32_t seg_max(uint32_t v, int g) {
+  return seg_last(seg_scan(v, 0u, g, [](uint32_t a, uint32_t b) { return a > b ? a : b; }), g);
+}
+
 // Sub-tile reports of one tile of 64 V positions whose row uses sub-tiles of
 // S < 64 V positions (S a power of two, S >= V).  The tile holds NS = 64 V / S
 // sub-tiles; each is served by a group of g = S / V consecutive lanes, lane r
-// of group s holding the sub-tile's elements r + g i (i < V), so that the
-// order (i, r) is position order.  Every count is a wave ballot masked to the
-// group, so all groups bisect at once.  `get(e)` returns the score of tile
-// element e (e < n_valid); sub-tile s of the tile writes report s (header
-// hdr[s], slots rep[kRep s ..]) when it holds at least one valid element.
+// of group s holding the sub-tile's elements V r + i (i < V), so that
+// position order is lane order, then i.  Every count, rank and placement is
+// a per-lane sum joined by a segmented DPP scan over the group, so all
+// groups bisect at once.  `get(e)` returns the score of tile element e
+// (e < n_valid); sub-tile s of the tile writes report s (header hdr[s],
+// slots rep[kRep s ..]) when it holds at least one valid element.
 template <int V, typename Get>
 __device__ void wave_subtile_reports(Get get, int n_valid, int64_t j0, int S, RepHeader* hdr,
                                      uint32_t* rep_u, int32_t* rep_j) {
@@ -181,42 +242,35 @@ __device__ void wave_subtile_reports(Get get, int n_valid, int64_t j0, int S, Re
   const int g = S / V;
   const int lg = 31 - __clz(g);
   const int grp = l >> lg, r = l & (g - 1);
-  const int sh = grp << lg;
-  const uint64_t gm = g >= 64 ? ~0ull : ((1ull << g) - 1ull);
-  const uint64_t below_r = (1ull << r) - 1ull;
-  const int e0 = grp * S + r;
-  uint32_t u[V];
-  uint32_t vmask = 0;
-  uint32_t nv = 0, mn = 0xffffffffu, mx = 0u;
+  const int e0 = grp * S + V * r;  // tile index of this lane's element 0
+  const int nv = min(max(n_valid - e0, 0), V);
+  uint32_t u[V];  // invalid slots as key 0: every probe below is >= 1
+  uint32_t mn = 0xffffffffu, mx = 0u;
 #pragma unroll
   for (int i = 0; i < V; ++i) {
-    const int e = e0 + g * i;
-    const bool v = e < n_valid;
-    u[i] = v ? order_key(get(e)) : 0u;
-    vmask |= (uint32_t)v << i;
-    nv += popc64((__ballot(v) >> sh) & gm);
-    if (v) {
-      mn = min(mn, u[i]);
-      mx = max(mx, u[i]);
-    }
+    u[i] = i < nv ? order_key(get(e0 + i)) : 0u;
+    mn = min(mn, i < nv ? u[i] : 0xffffffffu);
+    mx = max(mx, u[i]);
   }
-  for (int o = 1; o < g; o <<= 1) {
-    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
-  }
-  const bool complete = nv <= (uint32_t)kRep;
-  // per group: largest T with count(key >= T) >= kRep (invalid keys are 0
-  // and every probe is >= 1); stops early on a probe with exactly kRep
+  const uint32_t n = seg_sum((uint32_t)nv, g);
+  mn = seg_min(mn, g);
+  mx = seg_max(mx, g);
+  const bool complete = n <= (uint32_t)kRep;
+  // per group: largest T with count(key >= T) >= kRep; a probe with exactly
+  // kRep keys at or above it ends the group's search early
   uint32_t lo = mn, hi = mx;
+  bool exact = false;
   bool done = complete || lo >= hi;
   while (__ballot(!done) != 0ull) {
     const uint32_t mid = lo + ((hi - lo) >> 1) + 1;
     uint32_t c = 0;
 #pragma unroll
-    for (int i = 0; i < V; ++i) c += popc64((__ballot(u[i] >= mid) >> sh) & gm);
+    for (int i = 0; i < V; ++i) c += u[i] >= mid ? 1u : 0u;
+    c = seg_sum(c, g);
     if (!done) {
       if (c == (uint32_t)kRep) {
         lo = mid;
+        exact = true;
         done = true;
       } else {
         if (c > (uint32_t)kRep) lo = mid; else hi = mid - 1;
@@ -225,47 +279,66 @@ __device__ void wave_subtile_reports(Get get, int n_valid, int64_t j0, int S, Re
     }
   }
   const uint32_t T = lo;
-  uint32_t gt = 0;
+  bool sel[V];
+  uint32_t wu;  // key of the worst reported element of the group
+  if (complete) {
 #pragma unroll
-  for (int i = 0; i < V; ++i) gt += popc64((__ballot(((vmask >> i) & 1u) && u[i] > T) >> sh) & gm);
-  const uint32_t need = (uint32_t)kRep - gt;  // copies of T kept, lowest positions first
-  uint32_t sel = 0, seen = 0;
+    for (int i = 0; i < V; ++i) sel[i] = i < nv;
+    wu = mn;
+  } else if (exact) {
+    uint32_t m = 0xffffffffu;
 #pragma unroll
-  for (int i = 0; i < V; ++i) {
-    const bool v = (vmask >> i) & 1u;
-    const bool eq = v && u[i] == T;
-    const uint64_t m = (__ballot(eq) >> sh) & gm;
-    const bool si = complete ? v : ((v && u[i] > T) || (eq && seen + popc64(m & below_r) < need));
-    sel |= (uint32_t)si << i;
-    seen += popc64(m);
-  }
-  // compaction in position order; worst reported element per group
-  const bool live = grp * S < n_valid;
-  uint32_t base = 0, wu = 0xffffffffu;
-#pragma unroll
-  for (int i = 0; i < V; ++i) {
-    const bool si = (sel >> i) & 1u;
-    const uint64_t m = (__ballot(si) >> sh) & gm;
-    if (si && live) {
-      const uint32_t pos = base + popc64(m & below_r);
-      rep_u[grp * kRep + pos] = u[i];
-      rep_j[grp * kRep + pos] = (int32_t)(j0 + e0 + g * i);
+    for (int i = 0; i < V; ++i) {
+      sel[i] = u[i] >= T;
+      m = min(m, sel[i] ? u[i] : 0xffffffffu);
     }
-    if (si) wu = min(wu, u[i]);
-    base += popc64(m);
-  }
-  for (int o = 1; o < g; o <<= 1) wu = min(wu, (uint32_t)__shfl_xor((int)wu, o));
-  int32_t wj = -1;
+    wu = seg_min(m, g);
+  } else {
+    // T is a key: {key > T} plus the need lowest positions with key == T
+    uint32_t gt = 0, ce = 0;
 #pragma unroll
-  for (int i = 0; i < V; ++i)
-    if (((sel >> i) & 1u) && u[i] == wu) wj = max(wj, (int32_t)(j0 + e0 + g * i));
-  for (int o = 1; o < g; o <<= 1) wj = max(wj, __shfl_xor(wj, o));
+    for (int i = 0; i < V; ++i) {
+      gt += u[i] > T ? 1u : 0u;
+      ce += (i < nv && u[i] == T) ? 1u : 0u;
+    }
+    const uint32_t need = (uint32_t)kRep - seg_sum(gt, g);
+    uint32_t rk = seg_scan(ce, 0u, g, [](uint32_t a, uint32_t b) { return a + b; }) - ce;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const bool eq = i < nv && u[i] == T;
+      sel[i] = u[i] > T || (eq && rk < need);
+      rk += eq ? 1u : 0u;
+    }
+    wu = T;
+  }
+  // placement in position order; worst position: the highest selected
+  // position with key wu (biased by 1 so that none is 0)
+  uint32_t cs = 0;
+#pragma unroll
+  for (int i = 0; i < V; ++i) cs += sel[i] ? 1u : 0u;
+  const uint32_t incl = seg_scan(cs, 0u, g, [](uint32_t a, uint32_t b) { return a + b; });
+  const uint32_t count = seg_last(incl, g);
+  const bool live = n > 0u;
+  uint32_t pos = incl - cs;
+  uint32_t wj1 = 0;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    if (sel[i]) {
+      if (live) {
+        rep_u[grp * kRep + pos] = u[i];
+        rep_j[grp * kRep + pos] = (int32_t)(j0 + e0 + i);
+      }
+      ++pos;
+      if (u[i] == wu) wj1 = (uint32_t)(j0 + e0 + i) + 1u;
+    }
+  }
+  wj1 = seg_max(wj1, g);
   if (r == 0 && live) {
     RepHeader h;
-    h.count = base;
+    h.count = count;
     h.complete = complete ? 1u : 0u;
     h.worst_u = wu;
-    h.worst_j = wj;
+    h.worst_j = (int32_t)wj1 - 1;
     hdr[grp] = h;
   }
 }

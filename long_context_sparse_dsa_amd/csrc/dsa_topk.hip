@@ -1,24 +1,29 @@
 // dsa_topk.hip -- exact per-query Top-K of fp32 score rows.
 //
-// Selection rule (the pages keep "the K highest-scoring historical
-// positions", K = 2048; ties, order and padding are the readings stated in
-// dsa.h): K_eff = min(K, p+1) best positions by (score desc, position asc),
-// -0.0 == +0.0, output ascending, padded with -1.
+// Selection ("Open-Source LLM Architecture Evolution ...", Architecture
+// Breakdown, Top-K selection: each query goes on with only its K = 2048
+// best-scoring past positions; ties, order and padding are the readings
+// stated in dsa.h): K_eff = min(K, p+1) best positions by (score desc,
+// position asc), -0.0 == +0.0, output ascending, padded with -1.
 //
-// Two kernels:
+// Three kernels:
 //   tile_report_kernel  one workgroup per (row, tile): loads the tile's
 //                       scores, writes its candidate prefix (dsa_topk_tile.h).
 //                       The decode indexer writes the same reports from its
 //                       epilogue, so the layer path skips this kernel.
-//   topk_resolve_kernel one workgroup per row: gathers the reports into LDS
-//                       (they arrive in ascending position order), finds the
-//                       K_eff-th best candidate with three radix passes
-//                       (11/11/10 bits) and a position-ordered tie rank,
-//                       certifies the union, and writes the selected
-//                       positions with a block prefix sum (already ascending).
-//                       If certification fails, or the union does not fit
-//                       LDS, it runs the same exact radix select over the
-//                       whole score row from global memory instead.
+//   topk_resolve_kernel one workgroup per row: loads the reports (they come
+//                       in ascending position order) into registers, finds
+//                       the K_eff-th best candidate with radix passes over
+//                       the candidates' key range and a directly ranked
+//                       boundary bucket, certifies the union, and writes the
+//                       selected positions in ascending order with a block
+//                       prefix sum.  If certification fails, or the union
+//                       does not fit the block, it runs an exact radix
+//                       select over the whole score row from global memory.
+//   topk_rows_kernel    calls with many rows (no reports): one workgroup per
+//                       row collects the keys at or above a threshold (from
+//                       a sample of the row, else from histogram sweeps) in
+//                       position order and selects among them the same way.
 #include <algorithm>
 
 #include "dsa_kernels.h"

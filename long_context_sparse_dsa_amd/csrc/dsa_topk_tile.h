@@ -10,11 +10,12 @@
 // union is the exact top K of the row.  If any tile fails the check, the
 // resolve kernel falls back to an exact radix select over the whole row.
 //
-// A tile is handled by one wave, its order keys in registers.  It reports
-// exactly min(kRep, n) elements: the kRep-th best key T is found by
-// bisection over the tile's key interval [min, max] with wave-ballot
-// counts, and the report is {key > T} plus the lowest positions with key
-// == T, which is an exact prefix.
+// A tile is handled by one wave, its order keys in registers (each lane a
+// run of consecutive elements).  It reports exactly min(kRep, n) elements:
+// the kRep-th best key T is found by bisection over the tile's key interval
+// [min, max] with per-lane counts joined across the wave (or across the
+// lane group of a sub-tile), and the report is {key > T} plus the lowest
+// positions with key == T, which is an exact prefix.
 #pragma once
 
 #include "dsa_device.h"

@@ -418,7 +418,7 @@ def cpu_baseline(s, wl, budget):
                      np.array([L], dtype=np.int32), nthreads=n)
         runs += 1
         el = time.perf_counter() - t0
-        if el >= budget or runs >= 200:
+        if el >= budget or runs >= 100000:
             break
     return {"value": round(runs / el, 3), "unit": "tokens/s", "cores": n, "kind": "oracle",
             "sample": f"{runs} whole decode-layer steps of one sequence (ctx {L}) in {el:.1f} s, "
@@ -473,7 +473,7 @@ def cpu_baseline_hybrid(s, swa, wl, budget):
                      c["gate"][b:b + 1], wl.K, ctx, nthreads=n)
         runs += 1
         el = time.perf_counter() - t0
-        if el >= budget or runs >= 200:
+        if el >= budget or runs >= 100000:
             break
     return {"value": round(runs / el, 3), "unit": "tokens/s", "cores": n, "kind": "oracle",
             "sample": f"{runs} whole hybrid steps (5 SWA + 1 DSA layers) of one sequence "

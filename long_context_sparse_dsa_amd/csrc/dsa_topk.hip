@@ -70,8 +70,11 @@ constexpr int kBucketMax = 64;  // boundary-bucket size ranked directly by wave 
 
 template <int NTILE>
 struct ResolveSmemT {
-  uint32_t hist[2048];
-  uint32_t hist2[2048];  // the union select alternates between hist and hist2
+  // two 2048-bin histograms (the union select alternates between them);
+  // once the threshold is known, the staging area of up to 4096 outputs
+  alignas(16) uint32_t hbuf[4096];
+  __device__ uint32_t* hist() { return hbuf; }
+  __device__ uint32_t* hist2() { return hbuf + 2048; }
   alignas(16) uint32_t bu[kBucketMax];
   alignas(16) int32_t bj[kBucketMax];
   // per sub-tile: worst reported (key, position | complete << 31), kept for
@@ -184,23 +187,20 @@ __device__ __forceinline__ void ordered_ranks(SM& sm, uint32_t fmask, int qn, in
   lds_barrier();
 }
 
-// Appends the candidates with keys in [lo, lo + width) to sm.bu / sm.bj
+// Appends the candidates with keys in [lo, lo + wm1] to sm.bu / sm.bj
 // (in no particular order): a wave scan of the per-lane counts places each
 // lane's candidates after those of the lanes below it, at a wave base taken
 // with one LDS atomic (sm.st[4] counts the bucket; the caller guarantees at
 // most kBucketMax).
 template <int NSL, class SM>
 __device__ __forceinline__ void gather_bucket(SM& sm, const UnionRegs<NSL>& R,
-                                              uint32_t lo, uint64_t width) {
+                                              uint32_t lo, uint32_t wm1) {
   const int l = lane_id();
   uint32_t inb = 0;
 #pragma unroll
-  for (int i = 0; i < NSL; ++i) {
-    if (i / 4 < R.qn) {
-      const uint32_t x = R.u[i];
-      inb |= (uint32_t)(((R.vmask >> i) & 1u) && x >= lo && (uint64_t)(x - lo) < width) << i;
-    }
-  }
+  for (int i = 0; i < NSL; ++i)
+    if (i / 4 < R.qn) inb |= (uint32_t)(R.u[i] - lo <= wm1) << i;  // wraps below lo
+  inb &= R.vmask;
   const uint32_t c = (uint32_t)__popc(inb);
   const uint32_t inc = wave_incl_scan(c);
   const uint32_t wtot = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
@@ -259,22 +259,23 @@ __device__ __forceinline__ void union_threshold(SM& sm, const UnionRegs<NSL>& R,
                                                 uint32_t* tau_u, int32_t* tau_j) {
   const int tid = threadIdx.x, wv = wave_id();
   const uint32_t range = mx - mn;
-  // bucket = keys in [lo, lo + width); digits (key - lo) >> shift are < 2048
+  // bucket = keys in [lo, lo + wm1]; digits (key - lo) >> shift are < 2048.
+  // A key below lo wraps to key - lo > wm1 (lo + wm1 never passes 2^32 - 1),
+  // so one unsigned compare tests membership.
   int shift = range == 0 ? 0 : max(0, 32 - __clz(range) - 11);
   uint32_t lo = mn;
-  uint64_t width = (uint64_t)range + 1;
+  uint32_t wm1 = range;
   uint32_t above = 0;  // candidates strictly above the bucket
   uint32_t h = 0;      // candidates in the bucket
   int pass = 0;
   while (true) {
-    uint32_t* hc = (pass & 1) ? sm.hist2 : sm.hist;
-    uint32_t* hn = (pass & 1) ? sm.hist : sm.hist2;
+    uint32_t* hc = (pass & 1) ? sm.hist2() : sm.hist();
+    uint32_t* hn = (pass & 1) ? sm.hist() : sm.hist2();
 #pragma unroll
     for (int i = 0; i < NSL; ++i) {
       if (i / 4 < R.qn) {
-        const uint32_t x = R.u[i];
-        const bool in = ((R.vmask >> i) & 1u) && x >= lo && (uint64_t)(x - lo) < width;
-        if (in) atomicAdd(&hc[(x - lo) >> shift], 1u);
+        const uint32_t x = R.u[i] - lo;
+        if (((R.vmask >> i) & 1u) & (uint32_t)(x <= wm1)) atomicAdd(&hc[x >> shift], 1u);
       }
     }
     lds_barrier();
@@ -289,16 +290,16 @@ __device__ __forceinline__ void union_threshold(SM& sm, const UnionRegs<NSL>& R,
     const uint32_t d = sm.st[0];
     above = sm.st[1];
     h = sm.st[5];
-    const uint64_t off = (uint64_t)d << shift;
-    lo += (uint32_t)off;
-    width = min<uint64_t>(width - off, 1ull << shift);
+    const uint32_t off = d << shift;
+    lo += off;
+    wm1 = min(wm1 - off, (1u << shift) - 1u);
     if (shift == 0 || h <= (uint32_t)kBucketMax) break;
     shift = max(0, shift - 11);
     ++pass;
   }
   const uint32_t need = k - above;  // 1..h: the need-th best of the bucket is theta
   if (h <= (uint32_t)kBucketMax) {
-    gather_bucket(sm, R, lo, width);
+    gather_bucket(sm, R, lo, wm1);
     lds_barrier();
     rank_bucket(sm, h, need, nt >> 6);
     *tau_u = sm.st[2];
@@ -355,8 +356,8 @@ __device__ __forceinline__ bool select_from_regs(SM& sm, const UnionRegs<NSL>& R
     sm.red0[32 + wv] = mx;
   }
   for (int i = tid; i < 2048; i += nt) {
-    sm.hist[i] = 0;
-    sm.hist2[i] = 0;
+    sm.hist()[i] = 0;
+    sm.hist2()[i] = 0;
   }
   if (tid == 0) sm.st[4] = 0;
   lds_barrier();
@@ -382,22 +383,35 @@ __device__ __forceinline__ bool select_from_regs(SM& sm, const UnionRegs<NSL>& R
     const int32_t wpos = (int32_t)(wj & 0x7fffffffu);
     bad |= !complete && !((wu < tau_u) || (wu == tau_u && wpos >= tau_j));
   }
+  // selection mask in bitwise form (no short-circuit branches per slot)
   uint32_t smask = 0;
 #pragma unroll
   for (int i = 0; i < NSL; ++i) {
-    const bool si = ((R.vmask >> i) & 1u) &&
-                    ((R.u[i] > tau_u) || (R.u[i] == tau_u && R.j[i] <= tau_j));
-    smask |= (uint32_t)si << i;
+    if (i / 4 < R.qn) {
+      const uint32_t si = (uint32_t)(R.u[i] > tau_u) |
+                          ((uint32_t)(R.u[i] == tau_u) & (uint32_t)(R.j[i] <= tau_j));
+      smask |= si << i;
+    }
   }
+  smask &= R.vmask;
   uint32_t rk[NSL], total;
   bool any_bad = false;
   ordered_ranks<NSL>(sm, smask, R.qn, nt, rk, &total, bad, &any_bad);
   if (any_bad) return false;
-  // each selected slot goes straight to its rank (slots in position order:
-  // a group's four slots, and neighbouring lanes, land next to each other)
+  // each selected slot's position goes to its rank in LDS (the histograms
+  // are free once theta is known; K <= 4096 words), then the block writes
+  // the K positions with coalesced 16-byte stores
+  uint32_t* stage = sm.hbuf;
 #pragma unroll
   for (int i = 0; i < NSL; ++i)
-    if (((smask >> i) & 1u) && rk[i] < k) out[rk[i]] = R.j[i];
+    if (((smask >> i) & 1u) & (uint32_t)(rk[i] < k)) stage[rk[i]] = (uint32_t)R.j[i];
+  lds_barrier();
+  if ((K & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
+    for (int i = tid; i < K / 4; i += nt)
+      *reinterpret_cast<u32x4*>(out + 4 * i) = *reinterpret_cast<const u32x4*>(stage + 4 * i);
+  } else {
+    for (int i = tid; i < K; i += nt) out[i] = (int32_t)stage[i];
+  }
   return true;
 }
 
@@ -511,7 +525,7 @@ __device__ __forceinline__ void exact_select_row(SM& sm, const float* row, int64
     sm.red[16 + wv] = mn;
     sm.red[32 + wv] = mx;
   }
-  for (int i = tid; i < 2048; i += nt) sm.hist[i] = 0;
+  for (int i = tid; i < 2048; i += nt) sm.hist()[i] = 0;
   if (tid == 0) sm.st[4] = 0;
   lds_barrier();
   mn = wave_min_u32(l < nw ? sm.red[16 + l] : 0xffffffffu);
@@ -519,7 +533,7 @@ __device__ __forceinline__ void exact_select_row(SM& sm, const float* row, int64
   const uint32_t range = mx - mn;
   int shift = range == 0 ? 0 : max(0, 32 - __clz(range) - 11);
   uint32_t lo = mn;
-  uint64_t width = (uint64_t)range + 1;
+  uint32_t wm1 = range;  // bucket [lo, lo + wm1]; keys below lo wrap past wm1
   uint32_t above = 0, h = 0;
 #pragma unroll 1
   while (true) {
@@ -527,22 +541,23 @@ __device__ __forceinline__ void exact_select_row(SM& sm, const float* row, int64
     for (int64_t b0 = 0; b0 < n; b0 += step) {
       const uint32_t vm = load_keys16(row, n, b0 + 16 * tid, vec, u);
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (((vm >> i) & 1u) && u[i] >= lo && (uint64_t)(u[i] - lo) < width)
-          atomicAdd(&sm.hist[(u[i] - lo) >> shift], 1u);
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t x = u[i] - lo;
+        if (((vm >> i) & 1u) & (uint32_t)(x <= wm1)) atomicAdd(&sm.hist()[x >> shift], 1u);
+      }
     }
     lds_barrier();
-    if (wv == 0) wave_find_digit(sm, sm.hist, above, k);
+    if (wv == 0) wave_find_digit(sm, sm.hist(), above, k);
     lds_barrier();
     const uint32_t d = sm.st[0];
     above = sm.st[1];
     h = sm.st[5];
-    const uint64_t off = (uint64_t)d << shift;
-    lo += (uint32_t)off;
-    width = min<uint64_t>(width - off, 1ull << shift);
+    const uint32_t off = d << shift;
+    lo += off;
+    wm1 = min(wm1 - off, (1u << shift) - 1u);
     if (shift == 0 || h <= (uint32_t)kBucketMax) break;
     shift = max(0, shift - 11);
-    for (int i = tid; i < 2048; i += nt) sm.hist[i] = 0;
+    for (int i = tid; i < 2048; i += nt) sm.hist()[i] = 0;
     lds_barrier();
   }
   const uint32_t need = k - above;  // 1..h
@@ -555,7 +570,7 @@ __device__ __forceinline__ void exact_select_row(SM& sm, const float* row, int64
       const uint32_t vm = load_keys16(row, n, p0, vec, u);
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        if (((vm >> i) & 1u) && u[i] >= lo && (uint64_t)(u[i] - lo) < width) {
+        if (((vm >> i) & 1u) & (uint32_t)(u[i] - lo <= wm1)) {
           const uint32_t pos = atomicAdd(&sm.st[4], 1u);
           sm.bu[pos] = u[i];
           sm.bj[pos] = (int32_t)(p0 + i);
@@ -805,7 +820,8 @@ __global__ __launch_bounds__(kRowsThreads) void topk_rows_kernel(
     const int64_t p0 = b0 + PER * tid;
     uint32_t f = 0;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) f |= (uint32_t)(((vm >> i) & 1u) && u[i] >= lo) << i;
+    for (int i = 0; i < PER; ++i) f |= (uint32_t)(u[i] >= lo) << i;
+    f &= vm;
     uint32_t tot;
     uint32_t r = cum + excl_scan_active(sm, (uint32_t)__popc(f), nt >> 6, &tot);
 #pragma unroll
@@ -838,8 +854,8 @@ __global__ __launch_bounds__(kRowsThreads) void topk_rows_kernel(
       if (c < NC) svm[rd] = load_keys<PER>(row, n, c * P + PER * ln, vec, sk[rd]);
     }
     for (int i = tid; i < 2048; i += nt) {
-      sm.hist[i] = 0;
-      sm.hist2[i] = 0;
+      sm.hist()[i] = 0;
+      sm.hist2()[i] = 0;
     }
     lds_barrier();
     const uint32_t m = (uint32_t)NC * 512u;
@@ -850,9 +866,9 @@ __global__ __launch_bounds__(kRowsThreads) void topk_rows_kernel(
     for (int rd = 0; rd < 4; ++rd)
 #pragma unroll
       for (int i = 0; i < PER; ++i)
-        if ((svm[rd] >> i) & 1u) atomicAdd(&sm.hist[sk[rd][i] >> 21], 1u);
+        if ((svm[rd] >> i) & 1u) atomicAdd(&sm.hist()[sk[rd][i] >> 21], 1u);
     lds_barrier();
-    if (wv == 0) wave_find_digit(sm, sm.hist, 0u, rk);
+    if (wv == 0) wave_find_digit(sm, sm.hist(), 0u, rk);
     lds_barrier();
     const uint32_t lo_a = sm.st[0] << 21, above_a = sm.st[1];
 #pragma unroll
@@ -860,9 +876,9 @@ __global__ __launch_bounds__(kRowsThreads) void topk_rows_kernel(
 #pragma unroll
       for (int i = 0; i < PER; ++i)
         if (((svm[rd] >> i) & 1u) && (sk[rd][i] >> 21) == (lo_a >> 21))
-          atomicAdd(&sm.hist2[(sk[rd][i] - lo_a) >> 10], 1u);
+          atomicAdd(&sm.hist2()[(sk[rd][i] - lo_a) >> 10], 1u);
     lds_barrier();
-    if (wv == 0) wave_find_digit(sm, sm.hist2, above_a, rk);
+    if (wv == 0) wave_find_digit(sm, sm.hist2(), above_a, rk);
     lds_barrier();
     lo = lo_a + (sm.st[0] << 10);
     // one ordered sweep over the row
@@ -880,18 +896,20 @@ __global__ __launch_bounds__(kRowsThreads) void topk_rows_kernel(
     dma_barrier();  // the collection's LDS writes, and st[] reads, before reuse
   }
   if (!have) {
-    // 1. bucket of the K-th key: [lo, lo + width), `above` keys beyond it
-    for (int i = tid; i < 2048; i += nt) sm.hist[i] = 0;
+    // 1. bucket of the K-th key: [lo, lo + wm1], `above` keys beyond it (a
+    //    key below lo wraps to key - lo > wm1: one unsigned compare)
+    for (int i = tid; i < 2048; i += nt) sm.hist()[i] = 0;
     lds_barrier();
     lo = 0;
     uint32_t above = 0, h = 0;
-    uint64_t width = 1ull << 32;
+    uint32_t wm1 = 0xffffffffu;
     int shift = 21;
     auto hist_add = [&](const uint32_t(&u)[PER], uint32_t vm) {
 #pragma unroll
-      for (int i = 0; i < PER; ++i)
-        if (((vm >> i) & 1u) && u[i] >= lo && (uint64_t)(u[i] - lo) < width)
-          atomicAdd(&sm.hist[(u[i] - lo) >> shift], 1u);
+      for (int i = 0; i < PER; ++i) {
+        const uint32_t x = u[i] - lo;
+        if (((vm >> i) & 1u) & (uint32_t)(x <= wm1)) atomicAdd(&sm.hist()[x >> shift], 1u);
+      }
     };
 #pragma unroll 1
     while (true) {
@@ -904,16 +922,16 @@ __global__ __launch_bounds__(kRowsThreads) void topk_rows_kernel(
         hist_add(ub, vb);
       }
       dma_barrier();
-      if (wave_id() == 0) wave_find_digit(sm, sm.hist, above, k);
+      if (wave_id() == 0) wave_find_digit(sm, sm.hist(), above, k);
       lds_barrier();
       const uint32_t d = sm.st[0];
       above = sm.st[1];
       h = sm.st[5];
       lo += d << shift;
-      width = 1ull << shift;
+      wm1 = (1u << shift) - 1u;
       if (above + h <= (uint32_t)kRowsCap || shift == 0) break;
       shift = max(0, shift - 11);
-      for (int i = tid; i < 2048; i += nt) sm.hist[i] = 0;
+      for (int i = tid; i < 2048; i += nt) sm.hist()[i] = 0;
       lds_barrier();
     }
     C = above + h;  // keys >= lo

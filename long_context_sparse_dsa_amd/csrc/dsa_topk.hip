@@ -149,10 +149,13 @@ __device__ __forceinline__ int slot_of(int q, int tid, int nt) { return 4 * nt *
 // total.  Also ORs the per-thread flag `bad` over the block into *any_bad
 // (same exchange).  One cross-wave exchange of the per-(group, wave) counts
 // (at most 64 of them: NSL/4 groups x nt/64 waves).  nt: active threads.
+// Ends with a barrier (sm.red / sm.flag free again) unless tail_barrier is
+// false.
 template <int NSL, class SM>
 __device__ __forceinline__ void ordered_ranks(SM& sm, uint32_t fmask, int qn, int nt,
                                               uint32_t (&rank)[NSL], uint32_t* total,
-                                              bool bad = false, bool* any_bad = nullptr) {
+                                              bool bad = false, bool* any_bad = nullptr,
+                                              bool tail_barrier = true) {
   static_assert((NSL / 4) * (kResolveSlots / NSL / 64) <= 64, "exchange size");
   const int l = lane_id(), wv = wave_id(), nw = nt >> 6;
   uint32_t lane_ex[NSL / 4];
@@ -184,7 +187,7 @@ __device__ __forceinline__ void ordered_ranks(SM& sm, uint32_t fmask, int qn, in
     rank[4 * q + 2] = r + __popc(m & 3u);
     rank[4 * q + 3] = r + __popc(m & 7u);
   }
-  lds_barrier();
+  if (tail_barrier) lds_barrier();
 }
 
 // Appends the candidates with keys in [lo, lo + wm1] to sm.bu / sm.bj
@@ -210,7 +213,7 @@ __device__ __forceinline__ void gather_bucket(SM& sm, const UnionRegs<NSL>& R,
   uint32_t pos = (uint32_t)__builtin_amdgcn_readlane((int)base, 0) + inc - c;
 #pragma unroll
   for (int i = 0; i < NSL; ++i) {
-    if ((inb >> i) & 1u) {
+    if (i / 4 < R.qn && ((inb >> i) & 1u)) {
       sm.bu[pos] = R.u[i];
       sm.bj[pos] = R.j[i];
       ++pos;
@@ -396,15 +399,20 @@ __device__ __forceinline__ bool select_from_regs(SM& sm, const UnionRegs<NSL>& R
   smask &= R.vmask;
   uint32_t rk[NSL], total;
   bool any_bad = false;
-  ordered_ranks<NSL>(sm, smask, R.qn, nt, rk, &total, bad, &any_bad);
-  if (any_bad) return false;
+  // no tail barrier: the staging below touches neither sm.red nor sm.flag
+  ordered_ranks<NSL>(sm, smask, R.qn, nt, rk, &total, bad, &any_bad, false);
+  if (any_bad) {
+    lds_barrier();  // the caller's exact select reuses sm.red
+    return false;
+  }
   // each selected slot's position goes to its rank in LDS (the histograms
   // are free once theta is known; K <= 4096 words), then the block writes
   // the K positions with coalesced 16-byte stores
   uint32_t* stage = sm.hbuf;
 #pragma unroll
   for (int i = 0; i < NSL; ++i)
-    if (((smask >> i) & 1u) & (uint32_t)(rk[i] < k)) stage[rk[i]] = (uint32_t)R.j[i];
+    if (i / 4 < R.qn && (((smask >> i) & 1u) & (uint32_t)(rk[i] < k)))
+      stage[rk[i]] = (uint32_t)R.j[i];
   lds_barrier();
   if ((K & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
     for (int i = tid; i < K / 4; i += nt)

@@ -26,6 +26,8 @@
 //     16-lane groups turn 4 rows x 16 dims into 16 dims x 4 rows;
 //   - with several splits per query the workgroups write partial (m, l, O)
 //     and a combine kernel merges them and applies the gate.
+#include <type_traits>
+
 #include "dsa_kernels.h"
 #include "dsa_device.h"
 
@@ -33,6 +35,8 @@ namespace dsa {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// Index rows a workgroup stages in LDS (index mode); longer lists are split.
+constexpr int kAttnMaxRows = 2048;
 
 // Hardware exp2 and reciprocal (v_exp_f32, v_rcp_f32: about 1 ulp), which
 // keep the latency-bound epilogues short; the outputs are bf16.
@@ -82,8 +86,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   // merge state of one wave: per lane (m, l) and DB x 16 O values
   constexpr int ST_FLOATS = 2 + DB * 16;
   constexpr int MERGE_BYTES = (RB / 2) * HB * 64 * ST_FLOATS * 4;
-  constexpr int VT_BYTES = 8 * VT::kBytes;  // two V tiles per wave
-  constexpr int SMEM_BYTES = MERGE_BYTES > VT_BYTES ? MERGE_BYTES : VT_BYTES;
+  constexpr int TILE_BYTES = 2 * RB * 2 * VT::kBytes;  // 2 buffers x RB row blocks x {K, V}
+  constexpr int SMEM_BYTES = MERGE_BYTES > TILE_BYTES ? MERGE_BYTES : TILE_BYTES;
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM_BYTES];
 
   // Workgroups go to the 8 XCDs (each with its own L2) in turn.  With one
@@ -99,12 +103,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   const int l = lane_id(), g = l >> 5, wv = wave_id();
   const int hb = wv % HB, rb = wv / HB;
   const int lo = split * rows_per_split;
-  // In index mode the first index load does not depend on the batch
-  // descriptor: issue it with the descriptor loads (one round trip).
-  int32_t j_first = -1;
+  // index-list entry of this lane's row in step i: lp0 + STEP i
+  const int lp0 = lo + 32 * rb + (l & 31);
+  // In index mode the workgroup's part of the index row (at most
+  // kAttnMaxRows entries) goes to LDS first; these loads do not depend on
+  // the batch descriptor, so they share its round trip.
+  __shared__ int32_t idx_lds[kAttnMaxRows];
   if (idx) {
-    const int lp = lo + 32 * rb + (l & 31);
-    j_first = lp < K ? idx[(int64_t)t * K + lp] : -1;
+    const int nr = min(K, lo + rows_per_split) - lo;
+    const int32_t* src = idx + (int64_t)t * K + lo;
+    constexpr int PT = kAttnMaxRows / 256;
+    int32_t v[PT];
+#pragma unroll
+    for (int r = 0; r < PT; ++r) {
+      const int e = (int)threadIdx.x + 256 * r;
+      v[r] = e < nr ? src[e] : -1;
+    }
+#pragma unroll
+    for (int r = 0; r < PT; ++r) idx_lds[threadIdx.x + 256 * r] = v[r];
   }
   const RowInfo ri = row_info(t, cu_q, ctx_len, B);
   const int64_t row0 = cu_ctx[ri.b];
@@ -126,112 +142,156 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
 
-  // Two V tiles per wave: the next step's V rows land (direct loads) while
-  // this step computes, and the next step's indices are loaded a step
-  // ahead, so each step waits for one gather (its K rows), not for the
-  // index load and then the gather.
-  uint8_t* const vt_base = smem + 2 * wv * VT::kBytes;
+  // The workgroup works in steps of STEP index rows; row block rb (32 rows)
+  // of a step is shared by the HB head-block waves rb * HB .. rb * HB + HB - 1,
+  // and each of its K and V rows is fetched once per workgroup: with two
+  // head blocks, wave hb = 0 loads the K rows and wave hb = 1 the V rows.
+  // A step's rows are loaded into registers during the previous step; at
+  // the step's start they go to LDS (double-buffered tiles, one barrier per
+  // step), the K loader keeping its rows as its own MFMA A operand.  The
+  // row indices come from LDS, so the only memory loads in flight are the
+  // row prefetches.  Tile layout (VTile, for K and V): block c holds chunks
+  // 2c, 2c + 1 (dims 16c .. 16c + 15) of the 32 rows, lane l's 16 bytes at
+  // byte 16 l; lane l loads chunk 2c + l / 32 of row l % 32, which is also
+  // its A operand of k-step c (row l % 32, dims 16 c + 8 (l / 32) .. + 7).
+  constexpr int KB = VT::kBlocks;  // 16-byte chunks per lane and tile (= KS)
+  static_assert(KB == KS, "tile blocks are the k-steps");
+  auto tile = [&](int b, int r, int kind) {
+    return smem + ((b * RB + r) * 2 + kind) * VT::kBytes;
+  };
   const int G = l >> 4, jj = l & 15;
-  auto row_of = [&](int lp, int32_t jraw, bool* ok) {
+  auto row_of = [&](int lp, bool* ok) {
     bool v = lp < hi;
     int64_t j = 0;
     if (v) {
-      j = idx ? (int64_t)jraw : jw0 + lp;
+      j = idx ? (int64_t)idx_lds[lp - lo] : jw0 + lp;
       v = j >= 0;
     }
     *ok = v;
     return row0 + (v ? j : 0);
   };
-  auto issue_v = [&](int64_t row, int buf) {
-    uint8_t* vt = vt_base + buf * VT::kBytes;
+  // steps of the workgroup (uniform: every wave passes every barrier; rows
+  // past hi are masked)
+  const int nsteps = hi > lo ? (hi - lo + STEP - 1) / STEP : 0;
+  lds_barrier();  // the index rows are in LDS
+  // The step loop, compiled once per wave role (LK: loads the K rows, LV:
+  // loads the V rows), so each role holds only its own prefetch registers.
+  auto run = [&](auto lk, auto lv) {
+    constexpr bool LK = decltype(lk)::value, LV = decltype(lv)::value;
+    u32x4 pk[KB], pv[KB];  // this lane's row chunks of the next step
+    auto load_k = [&](int64_t row) {
 #pragma unroll
-    for (int c = 0; c < VT::kBlocks; ++c)
-      lds_dma16(vc + row * D + 8 * (2 * c + g), vt + c * VT::kStride);
-  };
-  bool valid;
-  int64_t row = row_of(lo + 32 * rb + (l & 31), j_first, &valid);
-  if (lo + 32 * rb < hi) issue_v(row, 0);
-  int buf = 0;
+      for (int c = 0; c < KB; ++c) pk[c] = ld16(kc + row * D + 8 * (2 * c + g));
+    };
+    auto load_v = [&](int64_t row) {
+#pragma unroll
+      for (int c = 0; c < KB; ++c) pv[c] = ld16(vc + row * D + 8 * (2 * c + g));
+    };
+    bool valid;
+    const int64_t row = row_of(lp0, &valid);
+    if (nsteps > 0) {
+      if constexpr (LK) load_k(row);
+      if constexpr (LV) load_v(row);
+    }
 #pragma unroll 1
-  for (int base = lo + 32 * rb; base < hi; base += STEP) {
-    const int lp_next = base + STEP + (l & 31);
-    const bool more = base + STEP < hi;
-    // next step's index, then this step's K row chunks into A-operand
-    // registers; all in flight before the wait
-    int32_t jn = -1;
-    if (idx && more && lp_next < hi) jn = idx[(int64_t)t * K + lp_next];
-    u32x4 kf[KS];
+    for (int i = 0; i < nsteps; ++i) {
+      const int buf = i & 1;
+      // this step's rows to LDS (the K loader's only for the other head block)
+      if constexpr (LK && HB > 1) {
 #pragma unroll
-    for (int s = 0; s < KS; ++s) kf[s] = ld16(kc + row * D + 16 * s + 8 * g);
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): V tile, next index, K rows
-    __builtin_amdgcn_sched_barrier(0);
-    const uint32_t vmask = (uint32_t)__ballot(valid);
-    // S^T = K . q^T, then the online softmax per head (exp2 domain)
-    f32x16 sacc = {};
-#pragma unroll
-    for (int s = 0; s < KS; ++s) sacc = mfma32(as_bf16x8(kf[s]), qb[s], sacc);
-    // the next step's V rows go to the other tile while this step computes
-    bool valid_n = false;
-    int64_t row_n = 0;
-    if (more) {
-      row_n = row_of(lp_next, jn, &valid_n);
-      issue_v(row_n, buf ^ 1);
-    }
-    float sv[16];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int ir = 8 * (r >> 2) + 4 * g + (r & 3);
-      const bool ok = (vmask >> ir) & 1u;
-      sv[r] = ok ? sacc[r] * scale_log2 : -INFINITY;
-      mx = fmaxf(mx, sv[r]);
-    }
-    mx = xor32_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = (m_new == -INFINITY) ? 1.f : fexp2(m_run - m_new);
-    float psum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      sv[r] = (sv[r] == -INFINITY) ? 0.f : fexp2(sv[r] - m_new);
-      psum += sv[r];
-    }
-    l_run = l_run * alpha + xor32_add(psum);
-    m_run = m_new;
-    bf16x8 pb[2];
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pb[s2][e] = static_cast<__bf16>(sv[8 * s2 + e]);
-    // O^T += V^T . P^T.  k slot e of step s2 is accumulator row
-    // 16 s2 + 8 (e / 4) + 4 g + e % 4, so the A operand's 8 rows for half g
-    // are two 4-row groups; each comes from one transpose read: lane jj of
-    // a 16-lane group addresses row k0 + jj / 4, dims n0 + 4 (jj % 4) .. + 3.
-    const uint16_t* vt16 = reinterpret_cast<const uint16_t*>(vt_base + buf * VT::kBytes);
-    u32x2 av[DB][2][2];
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int n0 = 32 * db + 16 * (G & 1) + 4 * (jj & 3);
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const int k0 = 16 * s2 + 4 * g + (jj >> 2);
-        av[db][s2][0] = lds_read_tr16(vt16 + VT::offset(k0, n0) / 2);
-        av[db][s2][1] = lds_read_tr16(vt16 + VT::offset(k0 + 8, n0) / 2);
+        for (int c = 0; c < KB; ++c)
+          *reinterpret_cast<u32x4*>(tile(buf, rb, 0) + c * VT::kStride + 16 * l) = pk[c];
       }
-    }
+      if constexpr (LV) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      o[db] *= alpha;
+        for (int c = 0; c < KB; ++c)
+          *reinterpret_cast<u32x4*>(tile(buf, rb, 1) + c * VT::kStride + 16 * l) = pv[c];
+      }
+      dma_barrier();  // the step's tiles are complete; the other buffer is free
+      const bool more = i + 1 < nsteps;
+      bool valid_n = false;
+      const int64_t row_n = row_of(lp0 + STEP * (i + 1), &valid_n);
+      if constexpr (LV) {
+        if (more) load_v(row_n);
+      }
+      const uint32_t vmask = (uint32_t)__ballot(valid);
+      // S^T = K . q^T (the K loader's A operands are its own rows)
+      f32x16 sacc = {};
+      if constexpr (LK) {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) sacc = mfma32(as_bf16x8(pk[s]), qb[s], sacc);
+        if (more) load_k(row_n);
+      } else {
+        const uint8_t* kt = tile(buf, rb, 0);
+        u32x4 kf[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          kf[s] = *reinterpret_cast<const u32x4*>(kt + s * VT::kStride + 16 * l);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) sacc = mfma32(as_bf16x8(kf[s]), qb[s], sacc);
+      }
+      // online softmax per head (exp2 domain)
+      float sv[16];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ir = 8 * (r >> 2) + 4 * g + (r & 3);
+        const bool ok = (vmask >> ir) & 1u;
+        sv[r] = ok ? sacc[r] * scale_log2 : -INFINITY;
+        mx = fmaxf(mx, sv[r]);
+      }
+      mx = xor32_max(mx);
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = (m_new == -INFINITY) ? 1.f : fexp2(m_run - m_new);
+      float psum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sv[r] = (sv[r] == -INFINITY) ? 0.f : fexp2(sv[r] - m_new);
+        psum += sv[r];
+      }
+      l_run = l_run * alpha + xor32_add(psum);
+      m_run = m_new;
+      bf16x8 pb[2];
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
-        o[db] = mfma32(as_bf16x8(u32x4{av[db][s2][0][0], av[db][s2][0][1], av[db][s2][1][0],
-                                       av[db][s2][1][1]}),
-                       pb[s2], o[db]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[s2][e] = static_cast<__bf16>(sv[8 * s2 + e]);
+      // O^T += V^T . P^T.  k slot e of step s2 is accumulator row
+      // 16 s2 + 8 (e / 4) + 4 g + e % 4, so the A operand's 8 rows for half g
+      // are two 4-row groups; each comes from one transpose read: lane jj of
+      // a 16-lane group addresses row k0 + jj / 4, dims n0 + 4 (jj % 4) .. + 3.
+      const uint16_t* vt16 = reinterpret_cast<const uint16_t*>(tile(buf, rb, 1));
+      u32x2 av[DB][2][2];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int n0 = 32 * db + 16 * (G & 1) + 4 * (jj & 3);
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const int k0 = 16 * s2 + 4 * g + (jj >> 2);
+          av[db][s2][0] = lds_read_tr16(vt16 + VT::offset(k0, n0) / 2);
+          av[db][s2][1] = lds_read_tr16(vt16 + VT::offset(k0 + 8, n0) / 2);
+        }
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        o[db] *= alpha;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+          o[db] = mfma32(as_bf16x8(u32x4{av[db][s2][0][0], av[db][s2][0][1], av[db][s2][1][0],
+                                         av[db][s2][1][1]}),
+                         pb[s2], o[db]);
+      }
+      valid = valid_n;
     }
-    row = row_n;
-    valid = valid_n;
-    buf ^= 1;
-  }
+  };
+  using T1 = std::integral_constant<bool, true>;
+  using T0 = std::integral_constant<bool, false>;
+  if constexpr (HB == 1)
+    run(T1{}, T1{});
+  else if (hb == 0)
+    run(T1{}, T0{});
+  else
+    run(T0{}, T1{});
 
   // ---- merge the RB row-block waves of each head block pairwise through LDS ----
   float* ms = reinterpret_cast<float*>(smem);
@@ -416,6 +476,7 @@ AttnPlan attn_plan(int T, int K, int window, int Hq, int D) {
   int rows = step;
   if ((int64_t)T * ((nlist + step - 1) / step) > 2048) rows = nlist > 0 ? nlist : step;
   while ((nlist + rows - 1) / rows > kMaxSplit) rows *= 2;
+  if (K > 0 && rows > kAttnMaxRows) rows = kAttnMaxRows;  // the index rows fit the LDS
   p.rows_per_split = rows;
   p.nsplit = (nlist + rows - 1) / rows;
   if (p.nsplit < 1) p.nsplit = 1;

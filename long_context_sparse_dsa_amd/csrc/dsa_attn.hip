@@ -57,17 +57,32 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
   return r;
 }
 
-// Per-wave V tile in LDS: 32 rows of D bf16.  Direct load c (of D/8) puts
-// 16-byte chunk 2c + (l / 32) of row l % 32 at byte 16 l of block c.
+// A 32-row tile of K or V rows in LDS: row-major (2D bytes per row), its
+// 16-byte chunks permuted within each row by an XOR with f(r), a bijection
+// of r mod NC (NC = D / 8 chunks per row).  The accesses made of it stay
+// free of bank conflicts:
+//   - gathers write whole rows (one row's NC chunks per NC lanes): XOR with
+//     a constant permutes the chunks of a row;
+//   - the K operand reads one chunk of 16 consecutive rows per 16 lanes:
+//     f is a bijection, so the chunks land on distinct 16-byte slots;
+//   - the V transpose reads 8 bytes of two neighbouring chunks (c even,
+//     c + 1) of 4 aligned consecutive rows per 16 lanes: f(r) is 2r plus a
+//     constant bit within such a group, so the 8 slots differ.
+// Gathers: with RPI = 64 / NC rows per load instruction, instruction c of
+// a tile reads rows RPI c + l / NC, chunk l % NC: each instruction covers
+// RPI whole rows (RPI x 2D bytes), the fewest cache lines a 1 KiB load can
+// touch, where a lane-per-row layout would touch 32 rows.
 template <int D>
-struct VTile {
-  static constexpr int kBlocks = D / 16;       // direct loads per 32-row tile (chunk pairs)
-  static constexpr int kStride = 1024;         // bytes per block
-  static constexpr int kBytes = kBlocks * kStride;
-  // element (row r, dim d) of the tile
+struct RowTile {
+  static constexpr int kNC = D / 8;            // 16-byte chunks per row
+  static constexpr int kRPI = 64 / kNC;        // rows per load instruction
+  static constexpr int kLoads = 32 / kRPI;     // load instructions per tile
+  static constexpr int kBytes = 32 * D * 2;
+  static constexpr int kShift = kNC == 16 ? 3 : 2;  // log2(kNC) - 1
+  __device__ static int swz(int r) { return ((r << 1) | ((r >> kShift) & 1)) & (kNC - 1); }
+  // byte offset of element (row r, dim d)
   __device__ static int offset(int r, int d) {
-    const int ck = d >> 3;  // 16-byte chunk
-    return (ck >> 1) * kStride + (((ck & 1) << 5) + r) * 16 + (d & 7) * 2;
+    return r * (2 * D) + ((((d >> 3) ^ swz(r)) << 4) | ((d & 7) << 1));
   }
 };
 
@@ -82,7 +97,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   constexpr int DB = D / 32;   // 32-wide blocks of the output dim
   constexpr int RB = 4 / HB;   // row-block waves per head block
   constexpr int STEP = 32 * RB;  // rows per workgroup step
-  using VT = VTile<D>;
+  using VT = RowTile<D>;
   // merge state of one wave: per lane (m, l) and DB x 16 O values
   constexpr int ST_FLOATS = 2 + DB * 16;
   constexpr int MERGE_BYTES = (RB / 2) * HB * 64 * ST_FLOATS * 4;
@@ -146,87 +161,88 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   // of a step is shared by the HB head-block waves rb * HB .. rb * HB + HB - 1,
   // and each of its K and V rows is fetched once per workgroup: with two
   // head blocks, wave hb = 0 loads the K rows and wave hb = 1 the V rows.
-  // A step's rows are loaded into registers during the previous step; at
-  // the step's start they go to LDS (double-buffered tiles, one barrier per
-  // step), the K loader keeping its rows as its own MFMA A operand.  The
-  // row indices come from LDS, so the only memory loads in flight are the
-  // row prefetches.  Tile layout (VTile, for K and V): block c holds chunks
-  // 2c, 2c + 1 (dims 16c .. 16c + 15) of the 32 rows, lane l's 16 bytes at
-  // byte 16 l; lane l loads chunk 2c + l / 32 of row l % 32, which is also
-  // its A operand of k-step c (row l % 32, dims 16 c + 8 (l / 32) .. + 7).
-  constexpr int KB = VT::kBlocks;  // 16-byte chunks per lane and tile (= KS)
-  static_assert(KB == KS, "tile blocks are the k-steps");
+  // A step's rows are loaded into registers during the previous step (in
+  // the gather layout of RowTile); at the step's start they go to LDS
+  // (double-buffered tiles, one barrier per step) and every wave reads its
+  // K operands and V transposes from there.  The row indices come from LDS,
+  // so the only memory loads in flight are the row prefetches.
+  constexpr int KB = VT::kLoads;  // 16-byte chunks per lane and tile
+  static_assert(KB * 64 * 16 == VT::kBytes, "tile gather");
   auto tile = [&](int b, int r, int kind) {
     return smem + ((b * RB + r) * 2 + kind) * VT::kBytes;
   };
   const int G = l >> 4, jj = l & 15;
-  auto row_of = [&](int lp, bool* ok) {
-    bool v = lp < hi;
-    int64_t j = 0;
-    if (v) {
-      j = idx ? (int64_t)idx_lds[lp - lo] : jw0 + lp;
-      v = j >= 0;
-    }
+  // K/V row of list entry lp (lp >= lo) in index mode (IM) or window mode;
+  // entries past the list, and -1 entries, are invalid and map to row 0 of
+  // the sequence.  Branch-free: staged entries past the list read -1, and
+  // the LDS index is clamped.
+  auto row_of = [&](auto im, int lp, bool* ok) {
+    int64_t j;
+    if constexpr (decltype(im)::value)
+      j = idx_lds[min(lp - lo, kAttnMaxRows - 1)];
+    else
+      j = jw0 + lp;
+    const bool v = (lp < hi) & (j >= 0);
     *ok = v;
     return row0 + (v ? j : 0);
   };
+  // gather layout: this lane's chunk and its tile rows (one per load)
+  const int gch = l % VT::kNC, grow = l / VT::kNC;
   // steps of the workgroup (uniform: every wave passes every barrier; rows
   // past hi are masked)
   const int nsteps = hi > lo ? (hi - lo + STEP - 1) / STEP : 0;
   lds_barrier();  // the index rows are in LDS
   // The step loop, compiled once per wave role (LK: loads the K rows, LV:
   // loads the V rows), so each role holds only its own prefetch registers.
-  auto run = [&](auto lk, auto lv) {
+  auto run = [&](auto lk, auto lv, auto im) {
     constexpr bool LK = decltype(lk)::value, LV = decltype(lv)::value;
-    u32x4 pk[KB], pv[KB];  // this lane's row chunks of the next step
-    auto load_k = [&](int64_t row) {
+    u32x4 pk[KB], pv[KB];  // this lane's chunks of the next step's rows
+    // rows of step i's tile of row block rb (invalid ones read row 0 of
+    // the sequence; they are masked)
+    auto load_rows = [&](int i, const uint16_t* src, u32x4 (&p)[KB]) {
+      int64_t rows[KB];  // every index read before any load is issued
 #pragma unroll
-      for (int c = 0; c < KB; ++c) pk[c] = ld16(kc + row * D + 8 * (2 * c + g));
+      for (int c = 0; c < KB; ++c) {
+        bool ok;
+        rows[c] = row_of(im, lo + STEP * i + 32 * rb + VT::kRPI * c + grow, &ok);
+      }
+#pragma unroll
+      for (int c = 0; c < KB; ++c) p[c] = ld16(src + rows[c] * D + 8 * gch);
     };
-    auto load_v = [&](int64_t row) {
+    auto store_rows = [&](uint8_t* t, const u32x4 (&p)[KB]) {
 #pragma unroll
-      for (int c = 0; c < KB; ++c) pv[c] = ld16(vc + row * D + 8 * (2 * c + g));
+      for (int c = 0; c < KB; ++c)
+        *reinterpret_cast<u32x4*>(t + VT::offset(VT::kRPI * c + grow, 8 * gch)) = p[c];
     };
     bool valid;
-    const int64_t row = row_of(lp0, &valid);
+    row_of(im, lp0, &valid);
     if (nsteps > 0) {
-      if constexpr (LK) load_k(row);
-      if constexpr (LV) load_v(row);
+      if constexpr (LK) load_rows(0, kc, pk);
+      if constexpr (LV) load_rows(0, vc, pv);
     }
 #pragma unroll 1
     for (int i = 0; i < nsteps; ++i) {
       const int buf = i & 1;
-      // this step's rows to LDS (the K loader's only for the other head block)
-      if constexpr (LK && HB > 1) {
-#pragma unroll
-        for (int c = 0; c < KB; ++c)
-          *reinterpret_cast<u32x4*>(tile(buf, rb, 0) + c * VT::kStride + 16 * l) = pk[c];
-      }
-      if constexpr (LV) {
-#pragma unroll
-        for (int c = 0; c < KB; ++c)
-          *reinterpret_cast<u32x4*>(tile(buf, rb, 1) + c * VT::kStride + 16 * l) = pv[c];
-      }
+      // this step's rows to LDS
+      if constexpr (LK) store_rows(tile(buf, rb, 0), pk);
+      if constexpr (LV) store_rows(tile(buf, rb, 1), pv);
       dma_barrier();  // the step's tiles are complete; the other buffer is free
-      const bool more = i + 1 < nsteps;
-      bool valid_n = false;
-      const int64_t row_n = row_of(lp0 + STEP * (i + 1), &valid_n);
-      if constexpr (LV) {
-        if (more) load_v(row_n);
+      if (i + 1 < nsteps) {
+        if constexpr (LK) load_rows(i + 1, kc, pk);
+        if constexpr (LV) load_rows(i + 1, vc, pv);
       }
+      bool valid_n = false;
+      row_of(im, lp0 + STEP * (i + 1), &valid_n);
       const uint32_t vmask = (uint32_t)__ballot(valid);
-      // S^T = K . q^T (the K loader's A operands are its own rows)
+      // S^T = K . q^T: the A operand of k-step s is row l % 32, dims
+      // 16 s + 8 g .. + 7
       f32x16 sacc = {};
-      if constexpr (LK) {
-#pragma unroll
-        for (int s = 0; s < KS; ++s) sacc = mfma32(as_bf16x8(pk[s]), qb[s], sacc);
-        if (more) load_k(row_n);
-      } else {
+      {
         const uint8_t* kt = tile(buf, rb, 0);
         u32x4 kf[KS];
 #pragma unroll
         for (int s = 0; s < KS; ++s)
-          kf[s] = *reinterpret_cast<const u32x4*>(kt + s * VT::kStride + 16 * l);
+          kf[s] = *reinterpret_cast<const u32x4*>(kt + VT::offset(l & 31, 16 * s + 8 * g));
 #pragma unroll
         for (int s = 0; s < KS; ++s) sacc = mfma32(as_bf16x8(kf[s]), qb[s], sacc);
       }
@@ -286,12 +302,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   };
   using T1 = std::integral_constant<bool, true>;
   using T0 = std::integral_constant<bool, false>;
+  auto run_mode = [&](auto lk, auto lv) {
+    if (idx)
+      run(lk, lv, T1{});
+    else
+      run(lk, lv, T0{});
+  };
   if constexpr (HB == 1)
-    run(T1{}, T1{});
+    run_mode(T1{}, T1{});
   else if (hb == 0)
-    run(T1{}, T0{});
+    run_mode(T1{}, T0{});
   else
-    run(T0{}, T1{});
+    run_mode(T0{}, T1{});
 
   // ---- merge the RB row-block waves of each head block pairwise through LDS ----
   float* ms = reinterpret_cast<float*>(smem);

@@ -37,6 +37,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // Index rows a workgroup stages in LDS (index mode); longer lists are split.
 constexpr int kAttnMaxRows = 2048;
+// The online softmax moves its reference max only past this margin (log2).
+constexpr float kRescale = 8.f;
 
 // Hardware exp2 and reciprocal (v_exp_f32, v_rcp_f32: about 1 ulp), which
 // keep the latency-bound epilogues short; the outputs are bf16.
@@ -63,11 +65,12 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
 // free of bank conflicts:
 //   - gathers write whole rows (one row's NC chunks per NC lanes): XOR with
 //     a constant permutes the chunks of a row;
-//   - the K operand reads one chunk of 16 consecutive rows per 16 lanes:
-//     f is a bijection, so the chunks land on distinct 16-byte slots;
+//   - the K operand reads one chunk of 8 or 16 consecutive rows per LDS
+//     pass: f takes distinct values there, so the chunks land on distinct
+//     16-byte slots (32 or 64 banks);
 //   - the V transpose reads 8 bytes of two neighbouring chunks (c even,
-//     c + 1) of 4 aligned consecutive rows per 16 lanes: f(r) is 2r plus a
-//     constant bit within such a group, so the 8 slots differ.
+//     c + 1) of 4 aligned consecutive rows per 16 lanes: bits 1-2 of f
+//     differ over such rows, so the 8 slots differ.
 // Gathers: with RPI = 64 / NC rows per load instruction, instruction c of
 // a tile reads rows RPI c + l / NC, chunk l % NC: each instruction covers
 // RPI whole rows (RPI x 2D bytes), the fewest cache lines a 1 KiB load can
@@ -78,8 +81,13 @@ struct RowTile {
   static constexpr int kRPI = 64 / kNC;        // rows per load instruction
   static constexpr int kLoads = 32 / kRPI;     // load instructions per tile
   static constexpr int kBytes = 32 * D * 2;
-  static constexpr int kShift = kNC == 16 ? 3 : 2;  // log2(kNC) - 1
-  __device__ static int swz(int r) { return ((r << 1) | ((r >> kShift) & 1)) & (kNC - 1); }
+  // bits 1-2 of f(r) are r mod 4, bit 0 is bit 2 of r, bit 3 (kNC = 16) is
+  // bit 3 of r: a bijection whose low three bits differ over any 8 aligned
+  // rows (K operand reads, 8 or 16 lanes per LDS pass) and whose bits 1-2
+  // differ over any 4 aligned rows (V transposes)
+  __device__ static int swz(int r) {
+    return (((r & 3) << 1) | ((r >> 2) & 1) | (r & 8)) & (kNC - 1);
+  }
   // byte offset of element (row r, dim d)
   __device__ static int offset(int r, int d) {
     return r * (2 * D) + ((((d >> 3) ^ swz(r)) << 4) | ((d & 7) << 1));
@@ -177,17 +185,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   // the sequence.  Branch-free: staged entries past the list read -1, and
   // the LDS index is clamped.
   auto row_of = [&](auto im, int lp, bool* ok) {
-    int64_t j;
+    int32_t j;
     if constexpr (decltype(im)::value)
       j = idx_lds[min(lp - lo, kAttnMaxRows - 1)];
     else
-      j = jw0 + lp;
+      j = (int32_t)jw0 + lp;
     const bool v = (lp < hi) & (j >= 0);
     *ok = v;
-    return row0 + (v ? j : 0);
+    return v ? j : 0;
   };
-  // gather layout: this lane's chunk and its tile rows (one per load)
+  // gather layout: this lane's chunk and its tile rows (one per load); row
+  // j of the sequence is at 32-bit element offset j * D from these bases
   const int gch = l % VT::kNC, grow = l / VT::kNC;
+  const uint16_t* const kbase = kc + row0 * D + 8 * gch;
+  const uint16_t* const vbase = vc + row0 * D + 8 * gch;
   // steps of the workgroup (uniform: every wave passes every barrier; rows
   // past hi are masked)
   const int nsteps = hi > lo ? (hi - lo + STEP - 1) / STEP : 0;
@@ -199,15 +210,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     u32x4 pk[KB], pv[KB];  // this lane's chunks of the next step's rows
     // rows of step i's tile of row block rb (invalid ones read row 0 of
     // the sequence; they are masked)
-    auto load_rows = [&](int i, const uint16_t* src, u32x4 (&p)[KB]) {
-      int64_t rows[KB];  // every index read before any load is issued
+    auto load_rows = [&](int i, const uint16_t* base, u32x4 (&p)[KB]) {
+      uint32_t rows[KB];  // every index read before any load is issued
 #pragma unroll
       for (int c = 0; c < KB; ++c) {
         bool ok;
-        rows[c] = row_of(im, lo + STEP * i + 32 * rb + VT::kRPI * c + grow, &ok);
+        rows[c] = (uint32_t)row_of(im, lo + STEP * i + 32 * rb + VT::kRPI * c + grow, &ok);
       }
 #pragma unroll
-      for (int c = 0; c < KB; ++c) p[c] = ld16(src + rows[c] * D + 8 * gch);
+      for (int c = 0; c < KB; ++c) p[c] = ld16(base + rows[c] * (uint32_t)D);
     };
     auto store_rows = [&](uint8_t* t, const u32x4 (&p)[KB]) {
 #pragma unroll
@@ -217,8 +228,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     bool valid;
     row_of(im, lp0, &valid);
     if (nsteps > 0) {
-      if constexpr (LK) load_rows(0, kc, pk);
-      if constexpr (LV) load_rows(0, vc, pv);
+      if constexpr (LK) load_rows(0, kbase, pk);
+      if constexpr (LV) load_rows(0, vbase, pv);
     }
 #pragma unroll 1
     for (int i = 0; i < nsteps; ++i) {
@@ -228,8 +239,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
       if constexpr (LV) store_rows(tile(buf, rb, 1), pv);
       dma_barrier();  // the step's tiles are complete; the other buffer is free
       if (i + 1 < nsteps) {
-        if constexpr (LK) load_rows(i + 1, kc, pk);
-        if constexpr (LV) load_rows(i + 1, vc, pv);
+        if constexpr (LK) load_rows(i + 1, kbase, pk);
+        if constexpr (LV) load_rows(i + 1, vbase, pv);
       }
       bool valid_n = false;
       row_of(im, lp0 + STEP * (i + 1), &valid_n);
@@ -246,27 +257,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
 #pragma unroll
         for (int s = 0; s < KS; ++s) sacc = mfma32(as_bf16x8(kf[s]), qb[s], sacc);
       }
-      // online softmax per head (exp2 domain)
-      float sv[16];
+      // online softmax per head (exp2 domain).  The running max m_run moves
+      // only when some head's step max passes it by more than kRescale (a
+      // wave-uniform decision), so most steps leave O unscaled; the weights
+      // exp2(c s - m_run) then stay below 2^kRescale, and the result, O / l,
+      // does not depend on the reference point.  c > 0, so the max of the
+      // raw logits gives the max of the scaled ones.
       float mx = -INFINITY;
+      if (vmask == 0xffffffffu) {  // every row of the step valid
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ir = 8 * (r >> 2) + 4 * g + (r & 3);
-        const bool ok = (vmask >> ir) & 1u;
-        sv[r] = ok ? sacc[r] * scale_log2 : -INFINITY;
-        mx = fmaxf(mx, sv[r]);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ir = 8 * (r >> 2) + 4 * g + (r & 3);
+          if (!((vmask >> ir) & 1u)) sacc[r] = -INFINITY;
+          mx = fmaxf(mx, sacc[r]);
+        }
       }
-      mx = xor32_max(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = (m_new == -INFINITY) ? 1.f : fexp2(m_run - m_new);
+      mx = xor32_max(mx) * scale_log2;
+      const bool grow = __ballot(mx > m_run + kRescale) != 0;
+      float alpha = 1.f;
+      if (grow) {
+        const float m_new = fmaxf(m_run, mx);
+        alpha = (m_new == -INFINITY) ? 1.f : fexp2(m_run - m_new);
+        m_run = m_new;
+      }
+      // a head with no valid key yet keeps m_run = -inf; its weights are 0
+      const float mu = (m_run == -INFINITY) ? 0.f : m_run;
+      float sv[16];
       float psum = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        sv[r] = (sv[r] == -INFINITY) ? 0.f : fexp2(sv[r] - m_new);
+        sv[r] = fexp2(fmaf(sacc[r], scale_log2, -mu));
         psum += sv[r];
       }
       l_run = l_run * alpha + xor32_add(psum);
-      m_run = m_new;
       bf16x8 pb[2];
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
@@ -288,9 +314,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
           av[db][s2][1] = lds_read_tr16(vt16 + VT::offset(k0 + 8, n0) / 2);
         }
       }
+      if (grow) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      }
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        o[db] *= alpha;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
           o[db] = mfma32(as_bf16x8(u32x4{av[db][s2][0][0], av[db][s2][0][1], av[db][s2][1][0],

@@ -84,7 +84,7 @@ struct ResolveSmemT {
   uint32_t red[64];
   uint32_t red0[48];  // count / min / max per wave, read only by the register path's first step
   uint32_t flag[16];
-  uint32_t scan[20];
+  uint32_t scan[32];  // excl_scan_active uses [0, 16); the ping-pong scan both halves
   uint32_t st[8];
 };
 using ResolveSmem = ResolveSmemT<kResolveTiles>;
@@ -471,6 +471,25 @@ __device__ __forceinline__ uint32_t excl_scan_active(SM& sm, uint32_t v, int nw,
   return base + inc - v;
 }
 
+// The same with one barrier: calls alternate between two halves of
+// sm.scan (parity), so a call's writes cannot meet the previous call's
+// reads (every wave passed that call's barrier only after its reads).
+// Every wave sums the wave totals below it itself.  nw <= 16.
+template <class SM>
+__device__ __forceinline__ uint32_t excl_scan_pingpong(SM& sm, uint32_t v, int nw, uint32_t parity,
+                                                       uint32_t* total) {
+  const int l = lane_id(), wv = wave_id();
+  uint32_t* buf = sm.scan + 16 * (parity & 1u);
+  const uint32_t inc = wave_incl_scan(v);
+  if (l == 63) buf[wv] = inc;
+  dma_barrier();  // LDS only: global loads in flight stay in flight
+  const uint32_t x = l < nw ? buf[l] : 0u;
+  const uint32_t xi = wave_incl_scan(x);
+  const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)(xi - x), wv);
+  *total = (uint32_t)__builtin_amdgcn_readlane((int)xi, 63);
+  return base + inc - v;
+}
+
 // Sixteen consecutive keys of a row from position p0 (a multiple of 16);
 // returns the validity mask.  `vec`: the row is 16-byte aligned and its
 // stride a multiple of four, so 16-byte loads below n stay inside it.
@@ -823,7 +842,7 @@ __global__ __launch_bounds__(kRowsThreads) void topk_rows_kernel(
   uint32_t ua[PER], ub[PER];
   // ordered collection of the keys >= lo into cand_u / cand_j (position
   // order; positions past kRowsCap are counted, not stored)
-  uint32_t lo = 0, cum = 0;
+  uint32_t lo = 0, cum = 0, par = 0;
   auto collect = [&](const uint32_t(&u)[PER], uint32_t vm, int64_t b0) {
     const int64_t p0 = b0 + PER * tid;
     uint32_t f = 0;
@@ -831,7 +850,7 @@ __global__ __launch_bounds__(kRowsThreads) void topk_rows_kernel(
     for (int i = 0; i < PER; ++i) f |= (uint32_t)(u[i] >= lo) << i;
     f &= vm;
     uint32_t tot;
-    uint32_t r = cum + excl_scan_active(sm, (uint32_t)__popc(f), nt >> 6, &tot);
+    uint32_t r = cum + excl_scan_pingpong(sm, (uint32_t)__popc(f), nt >> 6, par++, &tot);
 #pragma unroll
     for (int i = 0; i < PER; ++i)
       if ((f >> i) & 1u) {

@@ -816,7 +816,9 @@ constexpr int kRowsCap = 4096;  // candidates collected per row
 constexpr int kRowsMinT = 1024;  // rows per call from which the row sweeps pay off
 constexpr int kPilotMinRow = 16384;  // rows from this length first try a sampled threshold
 
-__global__ __launch_bounds__(kRowsThreads) void topk_rows_kernel(
+// Six waves per SIMD (at most 80 VGPRs): three 8-wave workgroups per CU,
+// as many as its LDS (about 50 KB each) allows, for more loads in flight.
+__global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(6))) void topk_rows_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* cu_q, const int32_t* ctx_len,
     int B, int K, int32_t* idx, uint32_t* stats) {
   constexpr int NSL = 16;

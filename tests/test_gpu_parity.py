@@ -268,6 +268,10 @@ def _rand_idx(lens, nq, K, seed, full=False):
     (64, 128, 2048, [1000], [1], True),          # K > context: padded
     (64, 128, 300, [4000], [64], False),         # multi-query rows, ungated
     (8, 64, 256, [700, 3000], [9, 17], True),
+    # 40 queries of K = 4096: whole index rows per workgroup, capped at the
+    # 2048 rows a workgroup stages, so two splits and the combine
+    (64, 128, 4096, [6000], [40], True),
+    (8, 64, 4096, [6000], [40], False),
 ])
 def test_sparse_attn_indexed(dsa, Hq, D, K, lens, nq, gated):
     say(f"sparse_attn Hq={Hq} D={D} K={K} lens={lens} nq={nq}")

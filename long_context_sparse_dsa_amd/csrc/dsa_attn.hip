@@ -10,19 +10,26 @@
 //
 // Kernel layout (gfx950, wave64, 4 waves per workgroup):
 //   - a workgroup takes `rows_per_split` consecutive entries of the query's
-//     index row in steps of 128; wave w takes rows 32w..32w+31 of a step,
-//     for every head (NHB blocks of 32 heads), and keeps its own running
-//     softmax state (max, sum, O^T accumulators); the four states are merged
-//     pairwise through LDS at the end;
-//   - S^T = K_rows . q^T on MFMA (v_mfma_f32_32x32x16_bf16): the gathered K
-//     rows are loaded straight into A-operand registers (16-byte chunks of
-//     each row), q is the B operand, held in registers for the whole kernel;
+//     index row (staged in LDS first) in steps of 32 RB rows; wave
+//     (rb, hb) takes rows 32 rb .. 32 rb + 31 of a step for heads
+//     32 hb .. 32 hb + 31 and keeps its own running softmax state (max, sum,
+//     O^T accumulators); the row-block states are merged through LDS at the
+//     end;
+//   - each K and V row of a step is gathered once per workgroup: one wave
+//     of a row block loads its K rows, the other its V rows, a step ahead,
+//     into registers (four whole rows per load instruction); at the step's
+//     start they go to double-buffered, XOR-swizzled LDS tiles that both
+//     head blocks read (RowTile);
+//   - S^T = K_rows . q^T on MFMA (v_mfma_f32_32x32x16_bf16): the A operand
+//     comes from the K tile, q is the B operand, held in registers for the
+//     whole kernel;
 //   - in the S^T accumulator layout each lane holds one head and 16 rows, so
 //     the per-head max / sum need one cross-half exchange, and P^T is
 //     already a B operand once its k slots are taken in accumulator order;
-//   - the gathered V rows go to LDS with direct global-to-LDS loads, row
-//     major; the A operand of O^T = V^T . P^T (8 rows of one dim per lane)
-//     comes back with the LDS transpose read ds_read_b64_tr_b16, whose
+//     the reference max moves only when a head's step max passes it by a
+//     margin, so most steps leave O unscaled;
+//   - the A operand of O^T = V^T . P^T (8 rows of one dim per lane) comes
+//     from the V tile with the LDS transpose read ds_read_b64_tr_b16, whose
 //     16-lane groups turn 4 rows x 16 dims into 16 dims x 4 rows;
 //   - with several splits per query the workgroups write partial (m, l, O)
 //     and a combine kernel merges them and applies the gate.

@@ -307,6 +307,27 @@ def test_sparse_attn_window(dsa, lens, window):
     check_out(out, ref, ATOL_BF16)
 
 
+def test_sparse_attn_window_many_queries(dsa):
+    """100 query rows with a 3000-position window: each workgroup takes a
+    whole window (more rows than the index staging holds, which window mode
+    does not use), gated output, no split merge."""
+    say("sparse_attn window=3000, 100 queries of one sequence")
+    lens, nq = [6000], [100]
+    w = wl("t", lens, nq, 4, 64, 64, 128, 0, seed=23)
+    inp = W.make_inputs(w)
+    d = to_dev(inp)
+    lse = torch.empty(w.T, 64, device=DEV)
+    out = dsa.dsa_sparse_attn(d["q"], d["k_cache"], d["v_cache"], None, d["ctx_len"], d["cu_ctx"],
+                              gate=d["gate"], window=3000, cu_q=d["cu_q"], max_ctx=max(lens),
+                              lse=lse)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.sparse_attn(inp["q"], inp["k_cache"], inp["v_cache"], window=3000,
+                                      gate=inp["gate"], ctx_len=inp["ctx_len"], cu_q=inp["cu_q"],
+                                      cu_ctx=inp["cu_ctx"])
+    check_out(out, ref, ATOL_BF16)
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=1e-4, atol=1e-4)
+
+
 def test_hybrid_step_swa_layers_then_dsa_layer(dsa):
     """One decode step of the 5:1 hybrid at a small ragged shape: two
     sliding-window layers (own K/V caches, ungated, through the prepared-call

@@ -57,8 +57,6 @@ def _load():
         lib.orc_e4m3_to_f64.restype = D
         lib.orc_index_scores.argtypes = [P, P, L, P, I, P, I, I, P, P, P, I, P, L, I]
         lib.orc_index_scores.restype = I
-        lib.orc_index_scores_at.argtypes = [P, P, P, I, P, I, I, L, P]
-        lib.orc_index_scores_at.restype = I
         lib.orc_topk_f64.argtypes = [P, L, P, P, I, I, P, I]
         lib.orc_topk_f64.restype = I
         lib.orc_topk_f32.argtypes = [P, L, P, P, I, I, P, I]
@@ -167,20 +165,6 @@ def index_scores(q_idx, w, k_idx, k_scale=None, ctx_len=None, cu_q=None, cu_ctx=
     lib.orc_index_scores(_ptr(q), _ptr(wv), w_ld, _ptr(k), kdt, _ptr(ks), H, d, _ptr(cu_q),
                          _ptr(ctx_len), _ptr(cu_ctx), B, _ptr(out), ld,
                          nthreads or default_threads())
-    return out
-
-
-def index_scores_at(q_row, w_row, k_rows, k_scale_rows=None):
-    """Scores of one query ([H, d] bf16, weights [H]) against explicit key rows."""
-    lib = _load()
-    q = _np(q_row, np.uint16)
-    H, d = q.shape
-    wv = _np(w_row, np.uint16)
-    k, kdt = _keys(k_rows)
-    n = k.shape[0]
-    ks = None if k_scale_rows is None else _np(k_scale_rows).astype(np.float32)
-    out = np.zeros(n, dtype=np.float64)
-    lib.orc_index_scores_at(_ptr(q), _ptr(wv), _ptr(k), kdt, _ptr(ks), H, d, n, _ptr(out))
     return out
 
 

@@ -197,30 +197,6 @@ int orc_index_scores(const uint16_t* q_idx, const uint16_t* w, int64_t w_ld, con
   return 0;
 }
 
-/* Same score for one row t and an explicit list of positions (used to
- * check sampled outputs of full-size runs one by one). */
-int orc_index_scores_at(const uint16_t* q_row, const uint16_t* w_row, const void* k_rows,
-                        int k_dtype, const float* k_scale_rows, int H_I, int d_I,
-                        int64_t n_pos, double* out) {
-  for (int64_t i = 0; i < n_pos; ++i) {
-    double s = 0.0;
-    for (int h = 0; h < H_I; ++h) {
-      double dot = 0.0;
-      for (int dd = 0; dd < d_I; ++dd) {
-        double kv = k_dtype == ORC_KEY_BF16
-                        ? orc_bf16_to_f64(((const uint16_t*)k_rows)[i * d_I + dd])
-                        : orc_e4m3_to_f64(((const uint8_t*)k_rows)[i * d_I + dd]);
-        dot += orc_bf16_to_f64(q_row[h * d_I + dd]) * kv;
-      }
-      double sigma = k_scale_rows ? (double)k_scale_rows[i] : 1.0;
-      double x = sigma * dot;
-      s += orc_bf16_to_f64(w_row[h]) * (x > 0.0 ? x : 0.0);
-    }
-    out[i] = s;
-  }
-  return 0;
-}
-
 /* ---------------------------------------------------------------------- */
 /* Top-K select ([OSLLM] Architecture Breakdown item 2: keep the K best;   */
 /* [FGSA] 2.1: K = 2048 historical positions).                             */

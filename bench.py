@@ -161,30 +161,43 @@ def bench_decode(args, torch, dsa, W):
     ev = [(hip.create(), hip.create()) for _ in range(args.steps)]
     set_events = dsa.load().dsa_set_indexer_events
     rot = [args.rotate]
+    nxt = [0]   # next buffer set: the rotation continues across passes, so
+    #             every step takes the least recently used set
 
-    def timed(n, warm, with_events):
-        for i in range(warm):
-            calls[i % rot[0]]()
+    def call_next():
+        calls[nxt[0] % rot[0]]()
+        nxt[0] += 1
+
+    def timed(n, warm, with_events=False, per_step=False):
+        for _ in range(warm):
+            call_next()
+        if rot[0] > 1:
+            flush_infinity_cache(torch)
         torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1 if per_step else 2)]
+        marks[0].record()
         for i in range(n):
             if with_events:
                 set_events(ctypes.c_void_p(ev[i][0]), ctypes.c_void_p(ev[i][1]))
-            calls[i % rot[0]]()
-        e1.record()
+            call_next()
+            if per_step:
+                marks[i + 1].record()
+        marks[-1].record()
         torch.cuda.synchronize()
         set_events(None, None)
-        return e0.elapsed_time(e1) / n   # ms per step
+        if per_step:
+            return [marks[i].elapsed_time(marks[i + 1]) for i in range(n)]
+        return marks[0].elapsed_time(marks[1]) / n   # ms per step
 
     # ---- the timed region: K layer steps, inputs resident in HBM ----
-    ms = timed(args.steps, args.warmup, False)
+    ms = timed(args.steps, args.warmup)
     tok_s = wl.B / (ms * 1e-3)
-    # ---- the same K steps again, the indexer kernel of each step recording
-    # its own start / end events (attached to its dispatch); kept out of
-    # the headline figure, which the extra event packets would slow ----
-    timed(args.steps, 0, True)
+    # ---- the same K steps again with an event between consecutive steps
+    # (per-step percentiles), then with the indexer kernel of each step
+    # recording its own start / end events (attached to its dispatch); both
+    # kept out of the headline figure, which the extra packets would slow ----
+    per = sorted(timed(args.steps, 0, per_step=True))
+    timed(args.steps, 0, with_events=True)
     idx_ms = [hip.elapsed_ms(a, b) for a, b in ev]
     ms_idx = sum(idx_ms) / len(idx_ms)
     for a, b in ev:
@@ -192,7 +205,8 @@ def bench_decode(args, torch, dsa, W):
         hip.destroy(b)
     # warm-cache figure (same buffer set every step), reported for context
     rot[0] = 1
-    ms_warm = timed(args.steps, args.warmup, False)
+    ms_warm = timed(args.steps, args.warmup)
+    copy_gbs = measured_copy_bandwidth(torch)
 
     fp8 = wl.key_dtype == "fp8"
     key_bytes = sum(wl.ctx_lens) * (wl.d_I + 4 if fp8 else 2 * wl.d_I)   # keys (+ fp8 scales)
@@ -226,6 +240,9 @@ def bench_decode(args, torch, dsa, W):
         "layer_roofline": {"algorithmic_bytes_per_step": layer_bytes,
                            "frac_of_hbm_peak": round(layer_bytes / (ms * 1e-3) / 1e9 /
                                                      HBM_PEAK_GBS, 4)},
+        "step_ms_percentiles": percentiles(per),
+        "measured_copy_gbs": round(copy_gbs, 1),
+        "indexer_frac_of_measured_copy": round(achieved / copy_gbs, 4),
         "warm_cache": {"ms_per_step": round(ms_warm, 5),
                        "tokens_per_s": round(wl.B / (ms_warm * 1e-3), 1)},
     }
@@ -395,6 +412,48 @@ def bench_prefill(args, torch, dsa, W):
     return result
 
 
+def flush_infinity_cache(torch, mib=512):
+    """Write a buffer twice the 256 MiB Infinity Cache, so that no layer
+    buffer stays cached from set-up or warm-up."""
+    buf = torch.empty(mib << 20, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    del buf
+
+
+def measured_copy_bandwidth(torch, mib=2048, reps=5):
+    """Achievable HBM bandwidth on this GPU: best device-to-device copy of
+    `mib` MiB (bytes read + bytes written per second), in GB/s."""
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    best = None
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1)
+        best = t if best is None else min(best, t)
+    del src, dst
+    return 2 * n / (best * 1e-3) / 1e9
+
+
+def percentiles(ms_list):
+    import numpy as np
+    a = np.asarray(ms_list)
+    return {"p10": round(float(np.percentile(a, 10)), 5),
+            "p50": round(float(np.percentile(a, 50)), 5),
+            "p90": round(float(np.percentile(a, 90)), 5)}
+
+
+def host_cores():
+    n_aff = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None
+    return {"nproc": n_aff, "cpu_count": os.cpu_count()}
+
+
 def _host(s):
     return {k: (v.cpu() if hasattr(v, "cpu") else v) for k, v in s.items()}
 
@@ -410,19 +469,25 @@ def cpu_baseline(s, wl, budget):
            "k_scale": None if c["k_scale"] is None else c["k_scale"][:L], "q": c["q"][:1],
            "k_cache": c["k_cache"][:L], "v_cache": c["v_cache"][:L], "gate": c["gate"][:1]}
     n = oracle.default_threads()
-    t0 = time.perf_counter()
-    runs = 0
-    while True:
-        oracle.layer(one["q_idx"], one["w"], one["k_idx"], one["k_scale"], one["q"],
-                     one["k_cache"], one["v_cache"], one["gate"], wl.K,
-                     np.array([L], dtype=np.int32), nthreads=n)
-        runs += 1
-        el = time.perf_counter() - t0
-        if el >= budget or runs >= 100000:
-            break
+
+    def run(threads, secs):
+        t0 = time.perf_counter()
+        runs = 0
+        while True:
+            oracle.layer(one["q_idx"], one["w"], one["k_idx"], one["k_scale"], one["q"],
+                         one["k_cache"], one["v_cache"], one["gate"], wl.K,
+                         np.array([L], dtype=np.int32), nthreads=threads)
+            runs += 1
+            el = time.perf_counter() - t0
+            if el >= secs or runs >= 100000:
+                return runs, el
+
+    runs, el = run(n, budget)
+    runs1, el1 = run(1, budget / 4)
     return {"value": round(runs / el, 3), "unit": "tokens/s", "cores": n, "kind": "oracle",
+            "value_1thread": round(runs1 / el1, 3), "host": host_cores(),
             "sample": f"{runs} whole decode-layer steps of one sequence (ctx {L}) in {el:.1f} s, "
-                      f"fp64, {n} threads"}
+                      f"fp64, {n} threads; {runs1} steps in {el1:.1f} s on 1 thread"}
 
 
 def cpu_baseline_prefill(s, wl, budget):

@@ -141,14 +141,19 @@ dsa_status_t dsa_topk(const float* scores, int64_t ld, const int32_t* cu_q,
 /* c = sm_scale, or 1/sqrt(D) when sm_scale == 0.  lse (optional, fp32       */
 /* [T, Hq]) receives log(sum_j exp(c * q.K_j)).  An empty S gives out = 0.   */
 /*                                                                           */
-/*   q, gate, out  bf16 [T, Hq, D];  k_cache, v_cache bf16 [sum ctx_len, D]  */
+/*   q, out  bf16 [T, Hq, D];  k_cache, v_cache bf16 [sum ctx_len, D]        */
+/*   gate    bf16 [T, Hq, D] with gate_stride_d == 1 (one gate value per     */
+/*           output element), or [T, Hq] with gate_stride_d == 0 (one value  */
+/*           per head, applied to all D dims of it); ignored when NULL       */
 /*   idx int32 [T, K] or NULL                                                */
 /* Supported (Hq, D): (8, 64), (64, 128); K <= 4096; window <= 4096.         */
+/* gate_stride_d other than 0 or 1 is DSA_ERR_INVALID_ARG.                   */
 /* ------------------------------------------------------------------------ */
 size_t dsa_sparse_attn_workspace_size(int B, int T, int K, int window, int Hq, int D);
 dsa_status_t dsa_sparse_attn(const void* q, const void* k_cache, const void* v_cache,
                              const int32_t* idx, int K, int window, const void* gate,
-                             float sm_scale, int Hq, int D, const int32_t* cu_q,
+                             int64_t gate_stride_d, float sm_scale, int Hq, int D,
+                             const int32_t* cu_q,
                              const int32_t* ctx_len, const int64_t* cu_ctx, int B, int T,
                              int max_q, int max_ctx, void* out, float* lse, void* ws,
                              size_t ws_bytes, void* stream);
@@ -160,12 +165,17 @@ dsa_status_t dsa_sparse_attn(const void* q, const void* k_cache, const void* v_c
 /* selection is still exact).  Arguments are those of the three steps;       */
 /* idx_out (int32 [B, K], or NULL) receives the selected positions, which   */
 /* otherwise stay in the workspace.                                          */
+/* Workspace contents after the call (a diagnostic contract): its first      */
+/* B * ld fp32 values, ld = max_ctx rounded up to a multiple of 64, are the  */
+/* step-1 scores the selection was made from (row b at offset b * ld,       */
+/* positions 0 .. ctx_len[b]-1 written).                                     */
 /* ------------------------------------------------------------------------ */
 size_t dsa_layer_decode_workspace_size(int B, int max_ctx, int K, int Hq, int D);
 dsa_status_t dsa_layer_decode(const void* q_idx, const void* w, int64_t w_ld, const void* k_idx,
                               int k_dtype, const float* k_scale, int H_I, int d_I, const void* q,
                               const void* k_cache, const void* v_cache, const void* gate,
-                              float sm_scale, int Hq, int D, int K, const int32_t* ctx_len,
+                              int64_t gate_stride_d, float sm_scale, int Hq, int D, int K,
+                              const int32_t* ctx_len,
                               const int64_t* cu_ctx, int B, int max_ctx, void* out,
                               int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
 
@@ -196,12 +206,24 @@ dsa_status_t dsa_set_topk_counters(uint32_t* counters);
 /* Whole layer, prefill: a chunk of new queries per sequence (cu_q given).   */
 /* Same steps; the indexer runs as a dense bf16 MFMA contraction of the      */
 /* chunk's query heads against the key cache with causal tile skipping.      */
+/*                                                                           */
+/* Workspace: dsa_layer_prefill_workspace_size() bytes run the T query rows */
+/* in one pass (the fp32 score array alone is T x max_ctx).  Any smaller     */
+/* workspace of at least dsa_layer_prefill_min_workspace_size() bytes is     */
+/* used by running the rows in consecutive sub-chunks of as many rows as    */
+/* fit (same results: every step is row-wise); below that the call returns   */
+/* DSA_ERR_WORKSPACE.  After a one-pass call the first T * ld fp32 values of */
+/* the workspace (ld = max_ctx rounded up to a multiple of 64) are the       */
+/* step-1 scores the selection was made from; after a sub-chunked call they */
+/* hold the last sub-chunk's rows.                                           */
 /* ------------------------------------------------------------------------ */
 size_t dsa_layer_prefill_workspace_size(int B, int T, int max_ctx, int K, int Hq, int D);
+size_t dsa_layer_prefill_min_workspace_size(int B, int max_ctx, int K, int Hq, int D);
 dsa_status_t dsa_layer_prefill(const void* q_idx, const void* w, int64_t w_ld, const void* k_idx,
                                int k_dtype, const float* k_scale, int H_I, int d_I,
                                const void* q, const void* k_cache, const void* v_cache,
-                               const void* gate, float sm_scale, int Hq, int D, int K,
+                               const void* gate, int64_t gate_stride_d, float sm_scale, int Hq,
+                               int D, int K,
                                const int32_t* cu_q, const int32_t* ctx_len,
                                const int64_t* cu_ctx, int B, int T, int max_q, int max_ctx,
                                void* out, int32_t* idx_out, void* ws, size_t ws_bytes,

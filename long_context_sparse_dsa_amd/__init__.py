@@ -6,6 +6,13 @@ allocate outputs and workspaces with torch (device memory is the only thing
 torch provides), and pass raw pointers plus torch's current HIP stream.
 Every step of the layer runs in the library's HIP kernels.  There is no
 fallback: if libdsa.so is missing or fails to load, every call raises.
+
+Shapes are checked on the host before the call (the C ABI sees only
+pointers).  `max_ctx` / `max_q` are host bounds used for grid sizing; when
+they are omitted the wrappers read them from the device descriptor, a
+Python-side convenience that synchronises with the device (the C entry
+points themselves never synchronise).  Workspaces allocated here on behalf
+of a call on a non-current stream are kept alive for that stream's work.
 """
 from __future__ import annotations
 
@@ -29,7 +36,8 @@ EXPORTS = [
     "dsa_sparse_attn_workspace_size", "dsa_sparse_attn",
     "dsa_layer_decode_workspace_size", "dsa_layer_decode", "dsa_set_indexer_events",
     "dsa_set_topk_counters",
-    "dsa_layer_prefill_workspace_size", "dsa_layer_prefill",
+    "dsa_layer_prefill_workspace_size", "dsa_layer_prefill_min_workspace_size",
+    "dsa_layer_prefill",
 ]
 
 _lib = None
@@ -61,15 +69,17 @@ def load(path: str | None = None):
     lib.dsa_topk.argtypes = [P, L, P, P, I, I, I, I, I, P, P, S, P]
     lib.dsa_sparse_attn_workspace_size.argtypes = [I, I, I, I, I, I]
     lib.dsa_sparse_attn_workspace_size.restype = S
-    lib.dsa_sparse_attn.argtypes = [P, P, P, P, I, I, P, F, I, I, P, P, P, I, I, I, I, P, P, P,
-                                    S, P]
+    lib.dsa_sparse_attn.argtypes = [P, P, P, P, I, I, P, L, F, I, I, P, P, P, I, I, I, I, P, P,
+                                    P, S, P]
     lib.dsa_layer_decode_workspace_size.argtypes = [I, I, I, I, I]
     lib.dsa_layer_decode_workspace_size.restype = S
-    lib.dsa_layer_decode.argtypes = [P, P, L, P, I, P, I, I, P, P, P, P, F, I, I, I, P, P, I, I,
-                                     P, P, P, S, P]
+    lib.dsa_layer_decode.argtypes = [P, P, L, P, I, P, I, I, P, P, P, P, L, F, I, I, I, P, P, I,
+                                     I, P, P, P, S, P]
     lib.dsa_layer_prefill_workspace_size.argtypes = [I, I, I, I, I, I]
     lib.dsa_layer_prefill_workspace_size.restype = S
-    lib.dsa_layer_prefill.argtypes = [P, P, L, P, I, P, I, I, P, P, P, P, F, I, I, I, P, P, P,
+    lib.dsa_layer_prefill_min_workspace_size.argtypes = [I, I, I, I, I]
+    lib.dsa_layer_prefill_min_workspace_size.restype = S
+    lib.dsa_layer_prefill.argtypes = [P, P, L, P, I, P, I, I, P, P, P, P, L, F, I, I, I, P, P, P,
                                       I, I, I, I, P, P, P, S, P]
     lib.dsa_set_indexer_events.argtypes = [P, P]
     lib.dsa_set_topk_counters.argtypes = [P]
@@ -92,6 +102,33 @@ def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _keep_for(stream, *tensors):
+    """Tensors allocated here for work enqueued on `stream`: when that is not
+    the current stream, tell the caching allocator so that their memory is not
+    handed to later work before the stream's work is done."""
+    if stream is None or stream == torch.cuda.current_stream():
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
+def _shape(t, name, shape):
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _gate_stride(gate, T, Hq, D):
+    """1 for an elementwise gate [T, Hq, D], 0 for one gate per head [T, Hq]."""
+    if gate is None:
+        return 1
+    if gate.dim() == 3:
+        _shape(gate, "gate", (T, Hq, D))
+        return 1
+    _shape(gate, "gate", (T, Hq))
+    return 0
 
 
 def _check(t, name, dtypes, ndim=None):
@@ -121,7 +158,40 @@ def _workspace(nbytes, device):
 
 
 def _host_max(x, given):
+    """Host bound of a device descriptor; reading it synchronises (convenience)."""
     return int(given) if given is not None else int(x.max().item())
+
+
+def _host_max_q(cu_q, given):
+    """Largest per-sequence query count; reading it synchronises (convenience)."""
+    return int(given) if given is not None else int((cu_q[1:] - cu_q[:-1]).max().item())
+
+
+def _check_desc(ctx_len, cu_ctx, cu_q, T):
+    B = ctx_len.shape[0]
+    _shape(cu_ctx, "cu_ctx", (B + 1,))
+    _shape(cu_q, "cu_q", (B + 1,))
+    if cu_q is None and T != B:
+        raise ValueError(f"one query per sequence (no cu_q): {T} rows for {B} sequences")
+    return B
+
+
+def _check_w(w, T, H_I):
+    if w.dim() == 1:
+        _shape(w, "w", (H_I,))
+    else:
+        _shape(w, "w", (T, H_I))
+
+
+def _check_keys(k_idx, k_scale, d_I):
+    if k_idx.shape[1] != d_I:
+        raise ValueError(f"k_idx: rows of {k_idx.shape[1]}, expected {d_I}")
+    if k_idx.dtype == torch.float8_e4m3fn:
+        if k_scale is None:
+            raise ValueError("fp8 indexer keys need k_scale")
+        _shape(k_scale, "k_scale", (k_idx.shape[0],))
+    elif k_scale is not None:
+        raise ValueError("bf16 indexer keys take no k_scale")
 
 
 BF16 = (torch.bfloat16,)
@@ -155,13 +225,17 @@ def dsa_index_scores(q_idx, w, k_idx, k_scale, ctx_len, cu_ctx, cu_q=None, max_q
     _check(cu_ctx, "cu_ctx", (torch.int64,), 1)
     _check(cu_q, "cu_q", (torch.int32,), 1)
     T, H_I, d_I = q_idx.shape
-    B = ctx_len.shape[0]
+    B = _check_desc(ctx_len, cu_ctx, cu_q, T)
+    _check_w(w, T, H_I)
+    _check_keys(k_idx, k_scale, d_I)
     max_ctx = _host_max(ctx_len, max_ctx)
-    if cu_q is not None and max_q is None:
-        max_q = int((cu_q[1:] - cu_q[:-1]).max().item())
+    if cu_q is not None:
+        max_q = _host_max_q(cu_q, max_q)
     if scores is None:
         scores = torch.empty(T, max_ctx, dtype=torch.float32, device=q_idx.device)
     _check(scores, "scores", (torch.float32,), 2)
+    if scores.shape[0] != T or scores.shape[1] < max_ctx:
+        raise ValueError(f"scores: shape {tuple(scores.shape)}, need ({T}, >= {max_ctx})")
     if w_ld is None:
         w_ld = 0 if w.dim() == 1 else w.shape[-1]
     _call("dsa_index_scores", _p(q_idx), _p(w), w_ld, _p(k_idx), _key_dtype(k_idx), _p(k_scale),
@@ -176,17 +250,21 @@ def dsa_topk(scores, K, ctx_len, cu_q=None, max_q=None, max_ctx=None, idx=None, 
     _check(ctx_len, "ctx_len", (torch.int32,), 1)
     _check(cu_q, "cu_q", (torch.int32,), 1)
     T = scores.shape[0]
-    B = ctx_len.shape[0]
+    B = _check_desc(ctx_len, None, cu_q, T)
     max_ctx = _host_max(ctx_len, max_ctx)
-    if cu_q is not None and max_q is None:
-        max_q = int((cu_q[1:] - cu_q[:-1]).max().item())
+    if scores.shape[1] < max_ctx:
+        raise ValueError(f"scores: {scores.shape[1]} columns < max_ctx {max_ctx}")
+    if cu_q is not None:
+        max_q = _host_max_q(cu_q, max_q)
     if idx is None:
         idx = torch.empty(T, K, dtype=torch.int32, device=scores.device)
     _check(idx, "idx", (torch.int32,), 2)
+    _shape(idx, "idx", (T, K))
     nbytes = load().dsa_topk_workspace_size(B, T, max_ctx, K)
     ws = _workspace(nbytes, scores.device)
     _call("dsa_topk", _p(scores), scores.stride(0), _p(cu_q), _p(ctx_len), B, T, max_q or 1,
           max_ctx, K, _p(idx), _p(ws), ws.numel(), _stream(stream))
+    _keep_for(stream, ws, idx)
     return idx
 
 
@@ -197,25 +275,34 @@ def dsa_sparse_attn(q, k_cache, v_cache, idx, ctx_len, cu_ctx, window=0, gate=No
     _check(k_cache, "k_cache", BF16, 2)
     _check(v_cache, "v_cache", BF16, 2)
     _check(idx, "idx", (torch.int32,), 2)
-    _check(gate, "gate", BF16, 3)
+    _check(gate, "gate", BF16)
     _check(ctx_len, "ctx_len", (torch.int32,), 1)
     _check(cu_ctx, "cu_ctx", (torch.int64,), 1)
     _check(cu_q, "cu_q", (torch.int32,), 1)
     _check(lse, "lse", (torch.float32,), 2)
     T, Hq, D = q.shape
-    B = ctx_len.shape[0]
+    B = _check_desc(ctx_len, cu_ctx, cu_q, T)
+    _shape(v_cache, "v_cache", tuple(k_cache.shape))
+    if k_cache.shape[1] != D:
+        raise ValueError(f"k_cache: rows of {k_cache.shape[1]}, expected {D}")
     K = 0 if idx is None else idx.shape[1]
+    if idx is not None:
+        _shape(idx, "idx", (T, K))
+    gs = _gate_stride(gate, T, Hq, D)
+    _shape(lse, "lse", (T, Hq))
     max_ctx = _host_max(ctx_len, max_ctx)
-    if cu_q is not None and max_q is None:
-        max_q = int((cu_q[1:] - cu_q[:-1]).max().item())
+    if cu_q is not None:
+        max_q = _host_max_q(cu_q, max_q)
     if out is None:
         out = torch.empty_like(q)
     _check(out, "out", BF16, 3)
+    _shape(out, "out", (T, Hq, D))
     nbytes = load().dsa_sparse_attn_workspace_size(B, T, K, window, Hq, D)
     ws = _workspace(nbytes, q.device)
-    _call("dsa_sparse_attn", _p(q), _p(k_cache), _p(v_cache), _p(idx), K, window, _p(gate),
+    _call("dsa_sparse_attn", _p(q), _p(k_cache), _p(v_cache), _p(idx), K, window, _p(gate), gs,
           float(sm_scale), Hq, D, _p(cu_q), _p(ctx_len), _p(cu_ctx), B, T, max_q or 1, max_ctx,
           _p(out), _p(lse), _p(ws), ws.numel(), _stream(stream))
+    _keep_for(stream, ws, out)
     return out
 
 
@@ -228,19 +315,25 @@ def prepare_sparse_attn(q, k_cache, v_cache, idx, ctx_len, cu_ctx, max_ctx, out,
     _check(k_cache, "k_cache", BF16, 2)
     _check(v_cache, "v_cache", BF16, 2)
     _check(idx, "idx", (torch.int32,), 2)
-    _check(gate, "gate", BF16, 3)
+    _check(gate, "gate", BF16)
     _check(ctx_len, "ctx_len", (torch.int32,), 1)
     _check(cu_ctx, "cu_ctx", (torch.int64,), 1)
     _check(out, "out", BF16, 3)
     T, Hq, D = q.shape
-    B = ctx_len.shape[0]
+    B = _check_desc(ctx_len, cu_ctx, None, T)
     K = 0 if idx is None else idx.shape[1]
+    if idx is not None:
+        _shape(idx, "idx", (T, K))
+    gs = _gate_stride(gate, T, Hq, D)
+    _shape(out, "out", (T, Hq, D))
     nbytes = load().dsa_sparse_attn_workspace_size(B, T, K, window, Hq, D)
     if ws is None:
         ws = _workspace(nbytes, q.device)
+    if ws.numel() < nbytes:
+        raise ValueError(f"ws: {ws.numel()} bytes < {nbytes}")
     fn = load().dsa_sparse_attn
-    args = (_p(q), _p(k_cache), _p(v_cache), _p(idx), K, window, _p(gate), float(sm_scale), Hq,
-            D, None, _p(ctx_len), _p(cu_ctx), B, T, 1, int(max_ctx), _p(out), None, _p(ws),
+    args = (_p(q), _p(k_cache), _p(v_cache), _p(idx), K, window, _p(gate), gs, float(sm_scale),
+            Hq, D, None, _p(ctx_len), _p(cu_ctx), B, T, 1, int(max_ctx), _p(out), None, _p(ws),
             ws.numel(), _stream(stream))
 
     def call():
@@ -255,10 +348,8 @@ def dsa_layer_decode_workspace_size(B, max_ctx, K, Hq, D) -> int:
     return int(load().dsa_layer_decode_workspace_size(B, max_ctx, K, Hq, D))
 
 
-def dsa_layer_decode(q_idx, w, k_idx, k_scale, q, k_cache, v_cache, gate, K, ctx_len, cu_ctx,
-                     max_ctx=None, sm_scale=0.0, out=None, idx_out=None, ws=None, w_ld=None,
-                     stream=None):
-    """Whole layer for one new query per sequence; returns out bf16 [B, Hq, D]."""
+def _layer_checks(q_idx, w, k_idx, k_scale, q, k_cache, v_cache, gate, ctx_len, cu_ctx, cu_q,
+                  idx_out, K):
     _check(q_idx, "q_idx", BF16, 3)
     _check(w, "w", BF16)
     _check(k_idx, "k_idx", KEYS, 2)
@@ -266,24 +357,48 @@ def dsa_layer_decode(q_idx, w, k_idx, k_scale, q, k_cache, v_cache, gate, K, ctx
     _check(q, "q", BF16, 3)
     _check(k_cache, "k_cache", BF16, 2)
     _check(v_cache, "v_cache", BF16, 2)
-    _check(gate, "gate", BF16, 3)
+    _check(gate, "gate", BF16)
     _check(ctx_len, "ctx_len", (torch.int32,), 1)
     _check(cu_ctx, "cu_ctx", (torch.int64,), 1)
+    _check(cu_q, "cu_q", (torch.int32,), 1)
     _check(idx_out, "idx_out", (torch.int32,), 2)
-    B, H_I, d_I = q_idx.shape
-    _, Hq, D = q.shape
+    T, H_I, d_I = q_idx.shape
+    Tq, Hq, D = q.shape
+    if Tq != T:
+        raise ValueError(f"q has {Tq} rows, q_idx {T}")
+    B = _check_desc(ctx_len, cu_ctx, cu_q, T)
+    _check_w(w, T, H_I)
+    _check_keys(k_idx, k_scale, d_I)
+    _shape(v_cache, "v_cache", tuple(k_cache.shape))
+    if k_cache.shape[1] != D:
+        raise ValueError(f"k_cache: rows of {k_cache.shape[1]}, expected {D}")
+    gs = _gate_stride(gate, T, Hq, D)
+    _shape(idx_out, "idx_out", (T, K))
+    return B, T, H_I, d_I, Hq, D, gs
+
+
+def dsa_layer_decode(q_idx, w, k_idx, k_scale, q, k_cache, v_cache, gate, K, ctx_len, cu_ctx,
+                     max_ctx=None, sm_scale=0.0, out=None, idx_out=None, ws=None, w_ld=None,
+                     stream=None):
+    """Whole layer for one new query per sequence; returns out bf16 [B, Hq, D].
+    gate: [B, Hq, D] (elementwise), [B, Hq] (one per head) or None."""
+    B, T, H_I, d_I, Hq, D, gs = _layer_checks(q_idx, w, k_idx, k_scale, q, k_cache, v_cache,
+                                              gate, ctx_len, cu_ctx, None, idx_out, K)
     max_ctx = _host_max(ctx_len, max_ctx)
     if out is None:
         out = torch.empty_like(q)
     _check(out, "out", BF16, 3)
-    if ws is None:
+    _shape(out, "out", (T, Hq, D))
+    own_ws = ws is None
+    if own_ws:
         ws = _workspace(dsa_layer_decode_workspace_size(B, max_ctx, K, Hq, D), q.device)
     if w_ld is None:
         w_ld = 0 if w.dim() == 1 else w.shape[-1]
     _call("dsa_layer_decode", _p(q_idx), _p(w), w_ld, _p(k_idx), _key_dtype(k_idx), _p(k_scale),
-          H_I, d_I, _p(q), _p(k_cache), _p(v_cache), _p(gate), float(sm_scale), Hq, D, K,
+          H_I, d_I, _p(q), _p(k_cache), _p(v_cache), _p(gate), gs, float(sm_scale), Hq, D, K,
           _p(ctx_len), _p(cu_ctx), B, max_ctx, _p(out), _p(idx_out), _p(ws), ws.numel(),
           _stream(stream))
+    _keep_for(stream, ws if own_ws else None, out)
     return out
 
 
@@ -292,25 +407,18 @@ def prepare_layer_decode(q_idx, w, k_idx, k_scale, q, k_cache, v_cache, gate, K,
     """Marshal one dsa_layer_decode call once; returns a no-argument callable
     that re-issues it (one ctypes call, no per-call argument checks).  The
     tensors must stay alive and unchanged in shape while the callable is used."""
-    _check(q_idx, "q_idx", BF16, 3)
-    _check(w, "w", BF16)
-    _check(k_idx, "k_idx", KEYS, 2)
-    _check(k_scale, "k_scale", (torch.float32,), 1)
-    _check(q, "q", BF16, 3)
-    _check(k_cache, "k_cache", BF16, 2)
-    _check(v_cache, "v_cache", BF16, 2)
-    _check(gate, "gate", BF16, 3)
-    _check(ctx_len, "ctx_len", (torch.int32,), 1)
-    _check(cu_ctx, "cu_ctx", (torch.int64,), 1)
+    B, T, H_I, d_I, Hq, D, gs = _layer_checks(q_idx, w, k_idx, k_scale, q, k_cache, v_cache,
+                                              gate, ctx_len, cu_ctx, None, idx_out, K)
     _check(out, "out", BF16, 3)
-    _check(idx_out, "idx_out", (torch.int32,), 2)
-    B, H_I, d_I = q_idx.shape
-    _, Hq, D = q.shape
+    _shape(out, "out", (T, Hq, D))
+    need = dsa_layer_decode_workspace_size(B, int(max_ctx), K, Hq, D)
+    if ws.numel() < need:
+        raise ValueError(f"ws: {ws.numel()} bytes < {need}")
     if w_ld is None:
         w_ld = 0 if w.dim() == 1 else w.shape[-1]
     fn = load().dsa_layer_decode
     args = (_p(q_idx), _p(w), w_ld, _p(k_idx), _key_dtype(k_idx), _p(k_scale), H_I, d_I, _p(q),
-            _p(k_cache), _p(v_cache), _p(gate), float(sm_scale), Hq, D, K, _p(ctx_len),
+            _p(k_cache), _p(v_cache), _p(gate), gs, float(sm_scale), Hq, D, K, _p(ctx_len),
             _p(cu_ctx), B, int(max_ctx), _p(out), _p(idx_out), _p(ws), ws.numel(),
             _stream(stream))
 
@@ -319,6 +427,15 @@ def prepare_layer_decode(q_idx, w, k_idx, k_scale, q, k_cache, v_cache, gate, K,
         if st != 0:
             raise DSAError("dsa_layer_decode", st, dsa_last_error())
     return call
+
+
+def layer_scores(ws, rows, max_ctx):
+    """View of the fp32 indexer scores a layer call left at the start of its
+    workspace `ws` (uint8 tensor): [rows, ld] with ld = max_ctx rounded up to
+    a multiple of 64 (the documented workspace contract of dsa_layer_decode
+    and of a one-pass dsa_layer_prefill)."""
+    ld = (int(max_ctx) + 63) // 64 * 64
+    return ws[:rows * ld * 4].view(torch.float32).view(rows, ld)
 
 
 def dsa_set_indexer_events(start, stop):
@@ -340,40 +457,37 @@ def dsa_set_topk_counters(counters):
 
 
 def dsa_layer_prefill_workspace_size(B, T, max_ctx, K, Hq, D) -> int:
+    """Workspace bytes that run all T query rows in one pass."""
     return int(load().dsa_layer_prefill_workspace_size(B, T, max_ctx, K, Hq, D))
+
+
+def dsa_layer_prefill_min_workspace_size(B, max_ctx, K, Hq, D) -> int:
+    """Least workspace bytes a prefill call accepts (rows then run in sub-chunks)."""
+    return int(load().dsa_layer_prefill_min_workspace_size(B, max_ctx, K, Hq, D))
 
 
 def dsa_layer_prefill(q_idx, w, k_idx, k_scale, q, k_cache, v_cache, gate, K, cu_q, ctx_len,
                       cu_ctx, max_q=None, max_ctx=None, sm_scale=0.0, out=None, idx_out=None,
                       ws=None, w_ld=None, stream=None):
-    """Whole layer for a chunk of new queries per sequence; returns out bf16 [T, Hq, D]."""
-    _check(q_idx, "q_idx", BF16, 3)
-    _check(w, "w", BF16)
-    _check(k_idx, "k_idx", KEYS, 2)
-    _check(k_scale, "k_scale", (torch.float32,), 1)
-    _check(q, "q", BF16, 3)
-    _check(k_cache, "k_cache", BF16, 2)
-    _check(v_cache, "v_cache", BF16, 2)
-    _check(gate, "gate", BF16, 3)
-    _check(cu_q, "cu_q", (torch.int32,), 1)
-    _check(ctx_len, "ctx_len", (torch.int32,), 1)
-    _check(cu_ctx, "cu_ctx", (torch.int64,), 1)
-    _check(idx_out, "idx_out", (torch.int32,), 2)
-    T, H_I, d_I = q_idx.shape
-    _, Hq, D = q.shape
-    B = ctx_len.shape[0]
+    """Whole layer for a chunk of new queries per sequence; returns out bf16 [T, Hq, D].
+    A caller workspace smaller than the one-pass size (but at least the
+    minimum) makes the library run the rows in sub-chunks."""
+    B, T, H_I, d_I, Hq, D, gs = _layer_checks(q_idx, w, k_idx, k_scale, q, k_cache, v_cache,
+                                              gate, ctx_len, cu_ctx, cu_q, idx_out, K)
     max_ctx = _host_max(ctx_len, max_ctx)
-    if max_q is None:
-        max_q = int((cu_q[1:] - cu_q[:-1]).max().item())
+    max_q = _host_max_q(cu_q, max_q)
     if out is None:
         out = torch.empty_like(q)
     _check(out, "out", BF16, 3)
-    if ws is None:
+    _shape(out, "out", (T, Hq, D))
+    own_ws = ws is None
+    if own_ws:
         ws = _workspace(dsa_layer_prefill_workspace_size(B, T, max_ctx, K, Hq, D), q.device)
     if w_ld is None:
         w_ld = 0 if w.dim() == 1 else w.shape[-1]
     _call("dsa_layer_prefill", _p(q_idx), _p(w), w_ld, _p(k_idx), _key_dtype(k_idx),
-          _p(k_scale), H_I, d_I, _p(q), _p(k_cache), _p(v_cache), _p(gate), float(sm_scale), Hq,
-          D, K, _p(cu_q), _p(ctx_len), _p(cu_ctx), B, T, max_q, max_ctx, _p(out), _p(idx_out),
+          _p(k_scale), H_I, d_I, _p(q), _p(k_cache), _p(v_cache), _p(gate), gs, float(sm_scale),
+          Hq, D, K, _p(cu_q), _p(ctx_len), _p(cu_ctx), B, T, max_q, max_ctx, _p(out), _p(idx_out),
           _p(ws), ws.numel(), _stream(stream))
+    _keep_for(stream, ws if own_ws else None, out)
     return out

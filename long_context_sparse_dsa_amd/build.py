@@ -14,7 +14,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdsa.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["dsa_api.cpp", "dsa_indexer.hip", "dsa_topk.hip", "dsa_attn.hip"]
+SOURCES = ["dsa_api.cpp", "dsa_indexer.hip", "dsa_topk.hip", "dsa_attn.hip", "dsa_layer.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

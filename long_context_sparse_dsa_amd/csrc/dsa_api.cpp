@@ -12,6 +12,8 @@
 #include <cstdio>
 #include <cstring>
 
+#include <algorithm>
+
 #include "dsa_kernels.h"
 #include "dsa_topk_tile.h"
 
@@ -120,10 +122,87 @@ size_t prefill_ws_layout(int T, int max_ctx, int K, int Hq, int D, char* base, D
   return s_scores + s_rep + s_idx + s_attn;
 }
 
+// Device descriptor of one prefill sub-chunk: cu_q [B+1] and ctx_len [B]
+// (int32), each 256-byte aligned.
+size_t prefill_chunk_desc_bytes(int B) {
+  return align_up((size_t)B + 1, 64) * 4 + align_up((size_t)B * 4, 256);
+}
+
 }  // namespace
 
 // Caller-owned Top-K path counters (this thread), or null.
 thread_local uint32_t* t_topk_counters = nullptr;
+
+namespace {
+
+// Indexer -> Top-K -> attention for T query rows in the workspace carved as
+// L for T_plan >= T rows: the Top-K path and the attention split plan are
+// those of T_plan, so the carve holds their scratch for any T <= T_plan.
+hipError_t prefill_pass(const void* q_idx, const void* w, int64_t w_ld, const void* k_idx,
+                        int k_dtype, const float* k_scale, int H_I, int d_I, const void* q,
+                        const void* k_cache, const void* v_cache, const void* gate, int gstride,
+                        float sm_scale, int Hq, int D, int K, const int32_t* cu_q,
+                        const int32_t* ctx_len, const int64_t* cu_ctx, int B, int T, int T_plan,
+                        int max_q, int max_ctx, void* out, int32_t* idx, const DecodeWs& L,
+                        hipStream_t s) {
+  hipError_t e = dsa::launch_index_prefill(q_idx, w, w_ld, k_idx, k_dtype, k_scale, H_I, d_I,
+                                           cu_q, ctx_len, cu_ctx, B, max_q, max_ctx, L.scores,
+                                           L.ld, s);
+  if (e == hipSuccess && dsa::topk_use_rows(T_plan)) {
+    e = dsa::launch_topk_rows(L.scores, L.ld, cu_q, ctx_len, B, T, K, idx, t_topk_counters, s);
+  } else {
+    if (e == hipSuccess)
+      e = dsa::launch_tile_reports(L.scores, L.ld, cu_q, ctx_len, B, T, K, L.topk, s);
+    if (e == hipSuccess)
+      e = dsa::launch_topk_resolve(L.scores, L.ld, cu_q, ctx_len, B, T, K, L.topk, idx,
+                                   t_topk_counters, s);
+  }
+  if (e == hipSuccess) {
+    const dsa::AttnPlan plan = dsa::attn_plan(T_plan, K, 0, Hq, D);
+    e = dsa::launch_sparse_attn(q, k_cache, v_cache, idx, K, 0, gate, gstride, sm_scale, Hq, D,
+                                cu_q, ctx_len, cu_ctx, B, T, out, nullptr, L.attn, plan, s);
+  }
+  return e;
+}
+
+// Largest row count c in [1, T - 1] whose prefill layout fits `avail`
+// bytes, or 0.  The layout grows with c except where a call of more rows
+// drops a scratch region (Top-K reports below the row-sweep threshold,
+// attention partials while the split plan is in use), so each stretch
+// between those two break points is searched on its own, from the top.
+int prefill_chunk_rows(int T, int max_ctx, int K, int Hq, int D, size_t avail) {
+  auto fits = [&](int c) {
+    return prefill_ws_layout(c, max_ctx, K, Hq, D, nullptr, nullptr) <= avail;
+  };
+  // break points: the last c with Top-K reports and the last c with
+  // attention partials (both predicates hold for every smaller c)
+  auto last_true = [&](auto pred) {
+    int lo = 0, hi = T;
+    while (lo < hi) {
+      const int mid = lo + (hi - lo + 1) / 2;
+      if (pred(mid)) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  };
+  const int b_rep = last_true([](int c) { return !dsa::topk_use_rows(c); });
+  const int b_att = last_true([&](int c) { return dsa::attn_plan(c, K, 0, Hq, D).ws_bytes > 0; });
+  int cuts[4] = {T - 1, b_rep, b_att, 0};
+  std::sort(cuts, cuts + 4, [](int a, int b) { return a > b; });
+  for (int i = 0; i < 3; ++i) {
+    int hi = std::min(cuts[i], T - 1), lo = cuts[i + 1] + 1;
+    if (hi < lo || hi < 1) continue;
+    lo = std::max(lo, 1);
+    if (!fits(lo)) continue;
+    while (lo < hi) {  // the layout grows with c inside the stretch
+      const int mid = lo + (hi - lo + 1) / 2;
+      if (fits(mid)) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  }
+  return 0;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -206,7 +285,8 @@ size_t dsa_sparse_attn_workspace_size(int B, int T, int K, int window, int Hq, i
 
 dsa_status_t dsa_sparse_attn(const void* q, const void* k_cache, const void* v_cache,
                              const int32_t* idx, int K, int window, const void* gate,
-                             float sm_scale, int Hq, int D, const int32_t* cu_q,
+                             int64_t gate_stride_d, float sm_scale, int Hq, int D,
+                             const int32_t* cu_q,
                              const int32_t* ctx_len, const int64_t* cu_ctx, int B, int T,
                              int max_q, int max_ctx, void* out, float* lse, void* ws,
                              size_t ws_bytes, void* stream) {
@@ -216,6 +296,9 @@ dsa_status_t dsa_sparse_attn(const void* q, const void* k_cache, const void* v_c
   DSA_PTR(out, "out");
   if (gate) DSA_PTR(gate, "gate");
   if (idx) DSA_PTR(idx, "idx");
+  DSA_REQUIRE(gate_stride_d == 0 || gate_stride_d == 1, DSA_ERR_INVALID_ARG,
+              "gate_stride_d must be 1 (elementwise gate) or 0 (one gate per head), got %lld",
+              (long long)gate_stride_d);
   dsa_status_t st = check_batch(cu_q, ctx_len, cu_ctx, true, B, T, max_q, max_ctx);
   if (st != DSA_OK) return st;
   DSA_REQUIRE(attn_shape_ok(Hq, D), DSA_ERR_UNSUPPORTED,
@@ -233,8 +316,9 @@ dsa_status_t dsa_sparse_attn(const void* q, const void* k_cache, const void* v_c
               "workspace too small: %zu < %zu bytes", ws_bytes, plan.ws_bytes);
   if (plan.ws_bytes) DSA_PTR(ws, "ws");
   hipError_t e = dsa::launch_sparse_attn(q, k_cache, v_cache, idx, K, idx ? 0 : window, gate,
-                                         sm_scale, Hq, D, cu_q, ctx_len, cu_ctx, B, T, out, lse,
-                                         ws, plan, static_cast<hipStream_t>(stream));
+                                         (int)gate_stride_d, sm_scale, Hq, D, cu_q, ctx_len,
+                                         cu_ctx, B, T, out, lse, ws, plan,
+                                         static_cast<hipStream_t>(stream));
   return hip_status(e, "dsa_sparse_attn");
 }
 
@@ -262,9 +346,10 @@ dsa_status_t dsa_set_indexer_events(void* start, void* stop) {
 dsa_status_t dsa_layer_decode(const void* q_idx, const void* w, int64_t w_ld, const void* k_idx,
                               int k_dtype, const float* k_scale, int H_I, int d_I, const void* q,
                               const void* k_cache, const void* v_cache, const void* gate,
-                              float sm_scale, int Hq, int D, int K, const int32_t* ctx_len,
-                              const int64_t* cu_ctx, int B, int max_ctx, void* out,
-                              int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
+                              int64_t gate_stride_d, float sm_scale, int Hq, int D, int K,
+                              const int32_t* ctx_len, const int64_t* cu_ctx, int B, int max_ctx,
+                              void* out, int32_t* idx_out, void* ws, size_t ws_bytes,
+                              void* stream) {
   DSA_PTR(q_idx, "q_idx");
   DSA_PTR(w, "w");
   DSA_PTR(k_idx, "k_idx");
@@ -274,6 +359,9 @@ dsa_status_t dsa_layer_decode(const void* q_idx, const void* w, int64_t w_ld, co
   DSA_PTR(out, "out");
   if (gate) DSA_PTR(gate, "gate");
   if (idx_out) DSA_PTR(idx_out, "idx_out");
+  DSA_REQUIRE(gate_stride_d == 0 || gate_stride_d == 1, DSA_ERR_INVALID_ARG,
+              "gate_stride_d must be 1 (elementwise gate) or 0 (one gate per head), got %lld",
+              (long long)gate_stride_d);
   dsa_status_t st = check_batch(nullptr, ctx_len, cu_ctx, true, B, B, 1, max_ctx);
   if (st != DSA_OK) return st;
   DSA_REQUIRE(k_dtype == DSA_KEY_BF16 || k_dtype == DSA_KEY_FP8_E4M3, DSA_ERR_INVALID_ARG,
@@ -311,8 +399,9 @@ dsa_status_t dsa_layer_decode(const void* q_idx, const void* w, int64_t w_ld, co
                                         t_topk_counters, s);
   if (e == hipSuccess) {
     const dsa::AttnPlan plan = dsa::attn_plan(B, K, 0, Hq, D);
-    e = dsa::launch_sparse_attn(q, k_cache, v_cache, idx, K, 0, gate, sm_scale, Hq, D, nullptr,
-                                ctx_len, cu_ctx, B, B, out, nullptr, L.attn, plan, s);
+    e = dsa::launch_sparse_attn(q, k_cache, v_cache, idx, K, 0, gate, (int)gate_stride_d,
+                                sm_scale, Hq, D, nullptr, ctx_len, cu_ctx, B, B, out, nullptr,
+                                L.attn, plan, s);
   }
   return hip_status(e, "dsa_layer_decode");
 }
@@ -323,11 +412,16 @@ size_t dsa_layer_prefill_workspace_size(int B, int T, int max_ctx, int K, int Hq
   return prefill_ws_layout(T, max_ctx, K, Hq, D, nullptr, nullptr);
 }
 
+size_t dsa_layer_prefill_min_workspace_size(int B, int max_ctx, int K, int Hq, int D) {
+  if (B < 1 || max_ctx < 1 || K < 1) return 0;
+  return prefill_chunk_desc_bytes(B) + prefill_ws_layout(1, max_ctx, K, Hq, D, nullptr, nullptr);
+}
+
 dsa_status_t dsa_layer_prefill(const void* q_idx, const void* w, int64_t w_ld, const void* k_idx,
                                int k_dtype, const float* k_scale, int H_I, int d_I,
                                const void* q, const void* k_cache, const void* v_cache,
-                               const void* gate, float sm_scale, int Hq, int D, int K,
-                               const int32_t* cu_q, const int32_t* ctx_len,
+                               const void* gate, int64_t gate_stride_d, float sm_scale, int Hq,
+                               int D, int K, const int32_t* cu_q, const int32_t* ctx_len,
                                const int64_t* cu_ctx, int B, int T, int max_q, int max_ctx,
                                void* out, int32_t* idx_out, void* ws, size_t ws_bytes,
                                void* stream) {
@@ -341,6 +435,9 @@ dsa_status_t dsa_layer_prefill(const void* q_idx, const void* w, int64_t w_ld, c
   if (gate) DSA_PTR(gate, "gate");
   if (idx_out) DSA_PTR(idx_out, "idx_out");
   DSA_REQUIRE(cu_q != nullptr, DSA_ERR_INVALID_ARG, "prefill needs cu_q");
+  DSA_REQUIRE(gate_stride_d == 0 || gate_stride_d == 1, DSA_ERR_INVALID_ARG,
+              "gate_stride_d must be 1 (elementwise gate) or 0 (one gate per head), got %lld",
+              (long long)gate_stride_d);
   dsa_status_t st = check_batch(cu_q, ctx_len, cu_ctx, true, B, T, max_q, max_ctx);
   if (st != DSA_OK) return st;
   DSA_REQUIRE(k_dtype == DSA_KEY_BF16 || k_dtype == DSA_KEY_FP8_E4M3, DSA_ERR_INVALID_ARG,
@@ -357,30 +454,49 @@ dsa_status_t dsa_layer_prefill(const void* q_idx, const void* w, int64_t w_ld, c
               "unsupported attention shape Hq=%d D=%d (supported: 8x64, 64x128)", Hq, D);
   DSA_REQUIRE(K >= 1 && K <= 4096, DSA_ERR_UNSUPPORTED, "K must be in [1, 4096] (got %d)", K);
   DSA_REQUIRE(sm_scale >= 0.f, DSA_ERR_INVALID_ARG, "sm_scale must be >= 0");
-  const size_t need = prefill_ws_layout(T, max_ctx, K, Hq, D, nullptr, nullptr);
-  DSA_REQUIRE(ws_bytes >= need, DSA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes",
-              ws_bytes, need);
   DSA_PTR(ws, "ws");
-  DecodeWs L;
-  prefill_ws_layout(T, max_ctx, K, Hq, D, static_cast<char*>(ws), &L);
-  int32_t* idx = idx_out ? idx_out : L.idx;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = dsa::launch_index_prefill(q_idx, w, w_ld, k_idx, k_dtype, k_scale, H_I, d_I,
-                                           cu_q, ctx_len, cu_ctx, B, max_q, max_ctx, L.scores,
-                                           L.ld, s);
-  if (e == hipSuccess && dsa::topk_use_rows(T)) {
-    e = dsa::launch_topk_rows(L.scores, L.ld, cu_q, ctx_len, B, T, K, idx, t_topk_counters, s);
-  } else {
-    if (e == hipSuccess)
-      e = dsa::launch_tile_reports(L.scores, L.ld, cu_q, ctx_len, B, T, K, L.topk, s);
-    if (e == hipSuccess)
-      e = dsa::launch_topk_resolve(L.scores, L.ld, cu_q, ctx_len, B, T, K, L.topk, idx,
-                                   t_topk_counters, s);
+  const size_t full = prefill_ws_layout(T, max_ctx, K, Hq, D, nullptr, nullptr);
+  if (ws_bytes >= full) {
+    DecodeWs L;
+    prefill_ws_layout(T, max_ctx, K, Hq, D, static_cast<char*>(ws), &L);
+    const hipError_t e = prefill_pass(q_idx, w, w_ld, k_idx, k_dtype, k_scale, H_I, d_I, q,
+                                      k_cache, v_cache, gate, (int)gate_stride_d, sm_scale, Hq, D,
+                                      K, cu_q, ctx_len, cu_ctx, B, T, T, max_q, max_ctx, out,
+                                      idx_out ? idx_out : L.idx, L, s);
+    return hip_status(e, "dsa_layer_prefill");
   }
-  if (e == hipSuccess) {
-    const dsa::AttnPlan plan = dsa::attn_plan(T, K, 0, Hq, D);
-    e = dsa::launch_sparse_attn(q, k_cache, v_cache, idx, K, 0, gate, sm_scale, Hq, D, cu_q,
-                                ctx_len, cu_ctx, B, T, out, nullptr, L.attn, plan, s);
+  // Sub-chunks of tc rows: the largest tc whose layout fits next to the
+  // chunk descriptor.  (The layout is not monotone in the row count: calls
+  // of many rows skip the Top-K reports and the attention partials.)
+  const size_t desc = prefill_chunk_desc_bytes(B);
+  const size_t need_min = desc + prefill_ws_layout(1, max_ctx, K, Hq, D, nullptr, nullptr);
+  DSA_REQUIRE(ws_bytes >= need_min, DSA_ERR_WORKSPACE,
+              "workspace too small: %zu < %zu bytes (the least that runs one query row at a "
+              "time; %zu bytes run all %d rows in one pass)",
+              ws_bytes, need_min, full, T);
+  const int tc = prefill_chunk_rows(T, max_ctx, K, Hq, D, ws_bytes - desc);
+  DSA_REQUIRE(tc >= 1, DSA_ERR_WORKSPACE, "workspace too small: %zu bytes", ws_bytes);
+  char* base = static_cast<char*>(ws);
+  int32_t* cu_q_c = reinterpret_cast<int32_t*>(base);
+  int32_t* ctx_len_c = cu_q_c + align_up((size_t)B + 1, 64);
+  DecodeWs L;
+  prefill_ws_layout(tc, max_ctx, K, Hq, D, base + desc, &L);
+  const int64_t gate_row = (int64_t)Hq * (gate_stride_d ? D : 1);
+  hipError_t e = hipSuccess;
+  for (int t0 = 0; t0 < T && e == hipSuccess; t0 += tc) {
+    const int n = T - t0 < tc ? T - t0 : tc;
+    e = dsa::launch_chunk_desc(cu_q, ctx_len, B, t0, n, cu_q_c, ctx_len_c, s);
+    if (e != hipSuccess) break;
+    // every per-row input and output is row-major in the query rows
+    e = prefill_pass(
+        static_cast<const uint16_t*>(q_idx) + (int64_t)t0 * H_I * d_I,
+        static_cast<const uint16_t*>(w) + (int64_t)t0 * w_ld, w_ld, k_idx, k_dtype, k_scale,
+        H_I, d_I, static_cast<const uint16_t*>(q) + (int64_t)t0 * Hq * D, k_cache, v_cache,
+        gate ? static_cast<const uint16_t*>(gate) + t0 * gate_row : nullptr, (int)gate_stride_d,
+        sm_scale, Hq, D, K, cu_q_c, ctx_len_c, cu_ctx, B, n, tc, max_q < n ? max_q : n, max_ctx,
+        static_cast<uint16_t*>(out) + (int64_t)t0 * Hq * D,
+        idx_out ? idx_out + (int64_t)t0 * K : L.idx, L, s);
   }
   return hip_status(e, "dsa_layer_prefill");
 }

@@ -105,7 +105,7 @@ template <int D, int HB, bool FINAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ idx, int K, int window,
-    const uint16_t* __restrict__ gate, float scale_log2, int Hq, const int32_t* cu_q,
+    const uint16_t* __restrict__ gate, int gstride, float scale_log2, int Hq, const int32_t* cu_q,
     const int32_t* ctx_len, const int64_t* cu_ctx, int B, int rows_per_split,
     uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part, int nsplit) {
   constexpr int KS = D / 16;   // k-steps of q . K
@@ -395,14 +395,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   const float inv = (Lsum > 0.f) ? frcp(Lsum) : 0.f;
   float* pp = part + (((int64_t)t * nsplit + split) * Hq + head) * (D + 2);
   // gate values of this lane's outputs, all loaded before any is used
+  // (gstride == 0: one gate value per head, broadcast over the head's dims)
   u32x2 gw[DB][4];
+  float gsc = 1.f;
   if (final_out && gate) {
+    if (gstride) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4)
-        gw[db][r4] = *reinterpret_cast<const u32x2*>(gate + ((int64_t)t * Hq + head) * D +
-                                                     32 * db + 8 * r4 + 4 * g);
+        for (int r4 = 0; r4 < 4; ++r4)
+          gw[db][r4] = *reinterpret_cast<const u32x2*>(gate + ((int64_t)t * Hq + head) * D +
+                                                       32 * db + 8 * r4 + 4 * g);
+    } else {
+      gsc = sigmoidf(bf16_to_f32(gate[(int64_t)t * Hq + head]));
+    }
   }
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
@@ -415,8 +421,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
         for (int e = 0; e < 4; ++e) {
           float v = o[db][4 * r4 + e] * inv;
           if (gate) {
-            const uint32_t wd = gw[db][r4][e >> 1];
-            v *= sigmoidf(bf16_to_f32((uint16_t)((e & 1) ? (wd >> 16) : (wd & 0xffffu))));
+            if (gstride) {
+              const uint32_t wd = gw[db][r4][e >> 1];
+              v *= sigmoidf(bf16_to_f32((uint16_t)((e & 1) ? (wd >> 16) : (wd & 0xffffu))));
+            } else {
+              v *= gsc;
+            }
           }
           ob[e] = f32_to_bf16(v);
         }
@@ -449,7 +459,7 @@ constexpr int kMaxSplit = 64;
 template <int D, int NS>
 __global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restrict__ part, int nsplit,
                                                           int Hq, const uint16_t* __restrict__ gate,
-                                                          uint16_t* __restrict__ out,
+                                                          int gstride, uint16_t* __restrict__ out,
                                                           float* __restrict__ lse) {
   constexpr int PL = D / 64;  // dims per lane (1 or 2)
   static_assert(NS <= 64 && (PL == 1 || PL == 2), "combine shape");
@@ -474,8 +484,14 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restric
   const f32x2 ml = *reinterpret_cast<const f32x2*>(pp + si * stride + D);
   uint32_t graw = 0;
   if (gate) {
-    if constexpr (PL == 2) graw = *reinterpret_cast<const uint32_t*>(gate + off);
-    else graw = gate[off];
+    if (!gstride) {  // one gate value per head
+      graw = gate[(int64_t)t * Hq + h];
+      graw |= graw << 16;
+    } else if constexpr (PL == 2) {
+      graw = *reinterpret_cast<const uint32_t*>(gate + off);
+    } else {
+      graw = gate[off];
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
   if (i < NS) {
@@ -509,20 +525,20 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restric
 
 template <int D>
 static void launch_combine(int T, int Hq, const float* part, int nsplit, const uint16_t* gate,
-                           uint16_t* out, float* lse, hipStream_t stream) {
+                           int gstride, uint16_t* out, float* lse, hipStream_t stream) {
   const dim3 grid(T, Hq);
   if (nsplit <= 8)
     hipLaunchKernelGGL((attn_combine_kernel<D, 8>), grid, dim3(64), 0, stream, part, nsplit, Hq,
-                       gate, out, lse);
+                       gate, gstride, out, lse);
   else if (nsplit <= 16)
     hipLaunchKernelGGL((attn_combine_kernel<D, 16>), grid, dim3(64), 0, stream, part, nsplit, Hq,
-                       gate, out, lse);
+                       gate, gstride, out, lse);
   else if (nsplit <= 32)
     hipLaunchKernelGGL((attn_combine_kernel<D, 32>), grid, dim3(64), 0, stream, part, nsplit, Hq,
-                       gate, out, lse);
+                       gate, gstride, out, lse);
   else
     hipLaunchKernelGGL((attn_combine_kernel<D, 64>), grid, dim3(64), 0, stream, part, nsplit, Hq,
-                       gate, out, lse);
+                       gate, gstride, out, lse);
 }
 
 AttnPlan attn_plan(int T, int K, int window, int Hq, int D) {
@@ -544,7 +560,7 @@ AttnPlan attn_plan(int T, int K, int window, int Hq, int D) {
 
 hipError_t launch_sparse_attn(const void* q, const void* k_cache, const void* v_cache,
                               const int32_t* idx, int K, int window, const void* gate,
-                              float sm_scale, int Hq, int D, const int32_t* cu_q,
+                              int gstride, float sm_scale, int Hq, int D, const int32_t* cu_q,
                               const int32_t* ctx_len, const int64_t* cu_ctx, int B, int T,
                               void* out, float* lse, void* ws, const AttnPlan& plan,
                               hipStream_t stream) {
@@ -560,18 +576,18 @@ hipError_t launch_sparse_attn(const void* q, const void* k_cache, const void* v_
 #define DSA_ATTN_LAUNCH(D_, HB_)                                                               \
   if (final_out)                                                                               \
     hipLaunchKernelGGL((sparse_attn_kernel<D_, HB_, true>), grid, dim3(256), 0, stream, qp, kp, \
-                       vp, idx, K, window, gp, scale, Hq, cu_q, ctx_len, cu_ctx, B,            \
+                       vp, idx, K, window, gp, gstride, scale, Hq, cu_q, ctx_len, cu_ctx, B,   \
                        plan.rows_per_split, op, lse, part, plan.nsplit);                       \
   else                                                                                         \
     hipLaunchKernelGGL((sparse_attn_kernel<D_, HB_, false>), grid, dim3(256), 0, stream, qp,   \
-                       kp, vp, idx, K, window, gp, scale, Hq, cu_q, ctx_len, cu_ctx, B,        \
+                       kp, vp, idx, K, window, gp, gstride, scale, Hq, cu_q, ctx_len, cu_ctx, B,\
                        plan.rows_per_split, op, lse, part, plan.nsplit);
   if (D == 128 && Hq == 64) {
     DSA_ATTN_LAUNCH(128, 2)
-    if (!final_out) launch_combine<128>(T, Hq, part, plan.nsplit, gp, op, lse, stream);
+    if (!final_out) launch_combine<128>(T, Hq, part, plan.nsplit, gp, gstride, op, lse, stream);
   } else if (D == 64 && Hq == 8) {
     DSA_ATTN_LAUNCH(64, 1)
-    if (!final_out) launch_combine<64>(T, Hq, part, plan.nsplit, gp, op, lse, stream);
+    if (!final_out) launch_combine<64>(T, Hq, part, plan.nsplit, gp, gstride, op, lse, stream);
   } else {
     return hipErrorInvalidValue;
   }

@@ -68,9 +68,16 @@ struct AttnPlan {
 AttnPlan attn_plan(int T, int K, int window, int Hq, int D);
 hipError_t launch_sparse_attn(const void* q, const void* k_cache, const void* v_cache,
                               const int32_t* idx, int K, int window, const void* gate,
-                              float sm_scale, int Hq, int D, const int32_t* cu_q,
+                              int gate_stride_d, float sm_scale, int Hq, int D,
+                              const int32_t* cu_q,
                               const int32_t* ctx_len, const int64_t* cu_ctx, int B, int T,
                               void* out, float* lse, void* ws, const AttnPlan& plan,
                               hipStream_t stream);
+
+// Batch descriptor of query rows [t0, t0 + tc) of a prefill call, as a call
+// of its own whose row 0 is global row t0: cu_q_c [B+1] and ctx_len_c [B]
+// (a sequence without rows in the range gets none; positions are kept).
+hipError_t launch_chunk_desc(const int32_t* cu_q, const int32_t* ctx_len, int B, int t0, int tc,
+                             int32_t* cu_q_c, int32_t* ctx_len_c, hipStream_t stream);
 
 }  // namespace dsa

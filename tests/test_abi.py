@@ -97,30 +97,51 @@ def test_topk_validation(lib):
 def test_sparse_attn_validation(lib):
     f = lib.dsa_sparse_attn
     # unsupported head geometry
-    assert f(FAKE, FAKE, FAKE, FAKE, 16, 0, None, 0.0, 32, 128, None, FAKE, FAKE, 1, 1, 1, 100,
+    assert f(FAKE, FAKE, FAKE, FAKE, 16, 0, None, 1, 0.0, 32, 128, None, FAKE, FAKE, 1, 1, 1, 100,
              FAKE, None, FAKE, 1 << 20, None) == 2
     # window mode without a window
-    assert f(FAKE, FAKE, FAKE, None, 0, 0, None, 0.0, 64, 128, None, FAKE, FAKE, 1, 1, 1, 100,
+    assert f(FAKE, FAKE, FAKE, None, 0, 0, None, 1, 0.0, 64, 128, None, FAKE, FAKE, 1, 1, 1, 100,
              FAKE, None, FAKE, 1 << 20, None) == 2
     assert "window" in dsa.dsa_last_error()
     # negative scale
-    assert f(FAKE, FAKE, FAKE, FAKE, 16, 0, None, -1.0, 64, 128, None, FAKE, FAKE, 1, 1, 1, 100,
-             FAKE, None, FAKE, 1 << 20, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, 16, 0, None, 1, -1.0, 64, 128, None, FAKE, FAKE, 1, 1, 1,
+             100, FAKE, None, FAKE, 1 << 20, None) == 1
     # split plan needs a workspace
-    assert f(FAKE, FAKE, FAKE, FAKE, 2048, 0, None, 0.0, 64, 128, None, FAKE, FAKE, 1, 1, 1,
+    assert f(FAKE, FAKE, FAKE, FAKE, 2048, 0, None, 1, 0.0, 64, 128, None, FAKE, FAKE, 1, 1, 1,
              100000, FAKE, None, FAKE, 16, None) == 3
+    # the gate's dim stride is 1 (elementwise) or 0 (one value per head)
+    assert f(FAKE, FAKE, FAKE, FAKE, 16, 0, FAKE, 2, 0.0, 64, 128, None, FAKE, FAKE, 1, 1, 1, 100,
+             FAKE, None, FAKE, 1 << 20, None) == 1
+    assert "gate_stride_d" in dsa.dsa_last_error()
 
 
 def test_layer_validation(lib):
     f = lib.dsa_layer_decode
-    args = [FAKE, FAKE, 32, FAKE, 0, None, 32, 128, FAKE, FAKE, FAKE, FAKE, 0.0, 64, 128, 2048,
-            FAKE, FAKE, 1, 131072, FAKE, None, FAKE, 16, None]
+    args = [FAKE, FAKE, 32, FAKE, 0, None, 32, 128, FAKE, FAKE, FAKE, FAKE, 1, 0.0, 64, 128,
+            2048, FAKE, FAKE, 1, 131072, FAKE, None, FAKE, 16, None]
     assert f(*args) == 3
     args2 = list(args)
-    args2[15] = 0   # K
+    args2[16] = 0   # K
     assert f(*args2) == 2
+    args3 = list(args)
+    args3[12] = -1  # gate_stride_d
+    assert f(*args3) == 1 and "gate_stride_d" in dsa.dsa_last_error()
     g = lib.dsa_layer_prefill
-    pargs = [FAKE, FAKE, 16, FAKE, 0, None, 16, 128, FAKE, FAKE, FAKE, FAKE, 0.0, 64, 128, 2048,
-             None, FAKE, FAKE, 1, 8192, 8192, 139264, FAKE, None, FAKE, 1 << 40, None]
+    pargs = [FAKE, FAKE, 16, FAKE, 0, None, 16, 128, FAKE, FAKE, FAKE, FAKE, 1, 0.0, 64, 128,
+             2048, None, FAKE, FAKE, 1, 8192, 8192, 139264, FAKE, None, FAKE, 1 << 40, None]
     assert g(*pargs) == 1
     assert "cu_q" in dsa.dsa_last_error()
+    # below the least workspace: refused before any launch, sizes in the message
+    small = list(pargs)
+    small[17] = FAKE
+    small[27] = lib.dsa_layer_prefill_min_workspace_size(1, 139264, 2048, 64, 128) - 1
+    assert g(*small) == 3
+    assert "workspace too small" in dsa.dsa_last_error()
+
+
+def test_prefill_workspace_sizes(lib):
+    full = lib.dsa_layer_prefill_workspace_size(1, 8192, 139264, 2048, 64, 128)
+    least = lib.dsa_layer_prefill_min_workspace_size(1, 139264, 2048, 64, 128)
+    # one query row: its fp32 score row plus small scratch, far below one pass
+    assert 139264 * 4 < least < 8 * 1024 * 1024 < full
+    assert lib.dsa_layer_prefill_min_workspace_size(0, 139264, 2048, 64, 128) == 0

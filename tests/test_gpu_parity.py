@@ -358,29 +358,53 @@ def test_hybrid_step_swa_layers_then_dsa_layer(dsa):
 # Whole layer
 # --------------------------------------------------------------------------
 
-def _layer_decode_check(dsa, w, inp_cpu, d, seqs=None, atol=ATOL_BF16):
+def _gate_for_oracle(gate, D):
+    """The oracle takes an elementwise gate: a per-head gate [T, Hq] is
+    expanded to [T, Hq, D] (each head's value on all its dims)."""
+    if gate is None or gate.dim() == 3:
+        return gate
+    return gate[:, :, None].expand(-1, -1, D).contiguous()
+
+
+def _check_topk_on_gpu_scores(idx_row, s_gpu_row, p, K):
+    """Mode T: the layer's selection equals the oracle's selection on the
+    very fp32 scores the layer computed (read back from its workspace)."""
+    want = oracle.topk(np.ascontiguousarray(s_gpu_row[None, :p + 1], dtype=np.float32), K,
+                       np.array([p + 1], np.int32))[0]
+    assert np.array_equal(idx_row, want), "selection differs from the Top-K of the GPU's scores"
+
+
+def _layer_decode_check(dsa, w, inp_cpu, d, seqs=None, atol=ATOL_BF16, gate=None):
     B = w.B
+    L = max(w.ctx_lens)
+    gate_dev = d["gate"] if gate is None else gate.to(DEV)
+    gate_cpu = _gate_for_oracle(inp_cpu["gate"] if gate is None else gate, w.D)
     idx = torch.empty(B, w.K, dtype=torch.int32, device=DEV)
+    ws = torch.empty(dsa.dsa_layer_decode_workspace_size(B, L, w.K, w.Hq, w.D), dtype=torch.uint8,
+                     device=DEV)
     out = dsa.dsa_layer_decode(d["q_idx"], d["w"], d["k_idx"], d["k_scale"], d["q"], d["k_cache"],
-                               d["v_cache"], d["gate"], w.K, d["ctx_len"], d["cu_ctx"],
-                               max_ctx=max(w.ctx_lens), idx_out=idx)
+                               d["v_cache"], gate_dev, w.K, d["ctx_len"], d["cu_ctx"],
+                               max_ctx=L, idx_out=idx, ws=ws)
     torch.cuda.synchronize()
     idx_c = idx.cpu().numpy()
     seqs = range(B) if seqs is None else seqs
+    rows = torch.tensor(list(seqs), dtype=torch.int64, device=DEV)
+    s_gpu = dsa.layer_scores(ws, B, L)[rows].cpu().numpy()
     ndiff = 0
-    for b in seqs:
-        L = w.ctx_lens[b]
+    for i, b in enumerate(seqs):
+        Lb = w.ctx_lens[b]
         r0 = int(sum(w.ctx_lens[:b]))
-        ks = None if inp_cpu["k_scale"] is None else inp_cpu["k_scale"][r0:r0 + L]
+        ks = None if inp_cpu["k_scale"] is None else inp_cpu["k_scale"][r0:r0 + Lb]
         s_ref = oracle.index_scores(inp_cpu["q_idx"][b:b + 1], inp_cpu["w"][b:b + 1],
-                                    inp_cpu["k_idx"][r0:r0 + L], ks,
-                                    ctx_len=np.array([L], np.int32))[0]
-        sel = check_index_row(idx_c[b], L - 1, w.K)
-        ndiff += check_set_band(sel, s_ref, L - 1, w.K)
-        ref, _ = oracle.sparse_attn(inp_cpu["q"][b:b + 1], inp_cpu["k_cache"][r0:r0 + L],
-                                    inp_cpu["v_cache"][r0:r0 + L], idx=idx_c[b:b + 1],
-                                    gate=inp_cpu["gate"][b:b + 1],
-                                    ctx_len=np.array([L], np.int32))
+                                    inp_cpu["k_idx"][r0:r0 + Lb], ks,
+                                    ctx_len=np.array([Lb], np.int32))[0]
+        sel = check_index_row(idx_c[b], Lb - 1, w.K)
+        _check_topk_on_gpu_scores(idx_c[b], s_gpu[i], Lb - 1, w.K)
+        ndiff += check_set_band(sel, s_ref, Lb - 1, w.K)
+        g = None if gate_cpu is None else gate_cpu[b:b + 1]
+        ref, _ = oracle.sparse_attn(inp_cpu["q"][b:b + 1], inp_cpu["k_cache"][r0:r0 + Lb],
+                                    inp_cpu["v_cache"][r0:r0 + Lb], idx=idx_c[b:b + 1],
+                                    gate=g, ctx_len=np.array([Lb], np.int32))
         check_out(out[b:b + 1], ref, atol)
     return ndiff
 
@@ -485,12 +509,16 @@ def test_layer_decode_1m_fp8_batched_sampled(dsa):
         "k_idx": None, "k_scale": None, "k_cache": None, "v_cache": None,
     }
     idx = torch.empty(w.B, w.K, dtype=torch.int32, device=DEV)
+    ws = torch.empty(dsa.dsa_layer_decode_workspace_size(w.B, L, w.K, w.Hq, w.D),
+                     dtype=torch.uint8, device=DEV)
     out = dsa.dsa_layer_decode(inp["q_idx"], inp["w"], inp["k_idx"], inp["k_scale"], inp["q"],
                                inp["k_cache"], inp["v_cache"], inp["gate"], w.K, inp["ctx_len"],
-                               inp["cu_ctx"], max_ctx=L, idx_out=idx)
+                               inp["cu_ctx"], max_ctx=L, idx_out=idx, ws=ws)
     torch.cuda.synchronize()
     idx_c = idx.cpu().numpy()
+    s_gpu = dsa.layer_scores(ws, w.B, L)
     for b in samp:
+        _check_topk_on_gpu_scores(idx_c[b], s_gpu[b].cpu().numpy(), L - 1, w.K)
         r0 = b * L
         s_ref = oracle.index_scores(cpu_inp["q_idx"][b:b + 1], cpu_inp["w"][b:b + 1],
                                     cpu(inp["k_idx"][r0:r0 + L]), cpu(inp["k_scale"][r0:r0 + L]),
@@ -507,34 +535,54 @@ def test_layer_decode_1m_fp8_batched_sampled(dsa):
         check_out(out[b:b + 1], ref, ATOL_FP8)
 
 
-def _layer_prefill_check(dsa, w, inp, d, rows=None):
+def _layer_prefill_check(dsa, w, inp, d, rows=None, ws_bytes=None, gate=None):
+    """One prefill call, then per sampled row: the selection against the Top-K
+    of the GPU's own fp32 scores (bit-exact; one-pass calls only), against
+    the oracle's scores within the near-tie band, and the attention output
+    against the oracle on the GPU's selection.  Returns (out, idx)."""
+    L = max(w.ctx_lens)
+    gate_dev = d["gate"] if gate is None else gate.to(DEV)
+    gate_cpu = _gate_for_oracle(cpu(inp["gate"]) if gate is None else gate, w.D)
+    full = dsa.dsa_layer_prefill_workspace_size(w.B, w.T, L, w.K, w.Hq, w.D)
+    ws = torch.empty(full if ws_bytes is None else ws_bytes, dtype=torch.uint8, device=DEV)
     idx = torch.empty(w.T, w.K, dtype=torch.int32, device=DEV)
     out = dsa.dsa_layer_prefill(d["q_idx"], d["w"], d["k_idx"], d["k_scale"], d["q"],
-                                d["k_cache"], d["v_cache"], d["gate"], w.K, d["cu_q"],
-                                d["ctx_len"], d["cu_ctx"], max_q=max(w.n_q),
-                                max_ctx=max(w.ctx_lens), idx_out=idx)
+                                d["k_cache"], d["v_cache"], gate_dev, w.K, d["cu_q"],
+                                d["ctx_len"], d["cu_ctx"], max_q=max(w.n_q), max_ctx=L,
+                                idx_out=idx, ws=ws)
     torch.cuda.synchronize()
     idx_c = idx.cpu().numpy()
     pos = positions(w.ctx_lens, w.n_q)
     seq_of = np.repeat(np.arange(w.B), w.n_q)
-    rows = range(w.T) if rows is None else rows
+    rows = list(range(w.T)) if rows is None else list(rows)
     cu_ctx = np.concatenate([[0], np.cumsum(w.ctx_lens)])
-    for t in rows:
+    one_pass = ws.numel() >= full
+    if one_pass:
+        sel_rows = torch.tensor(rows, dtype=torch.int64, device=DEV)
+        s_gpu = dsa.layer_scores(ws, w.T, L)[sel_rows].cpu().numpy()
+    k_idx = cpu(inp["k_idx"])       # one host copy of the key cache, sliced per row
+    k_scale = cpu(inp["k_scale"])
+    for i, t in enumerate(rows):
         b, p = int(seq_of[t]), pos[t]
         r0 = int(cu_ctx[b])
-        ks = None if inp["k_scale"] is None else cpu(inp["k_scale"][r0:r0 + p + 1])
-        s_ref = oracle.index_scores_at(cpu(inp["q_idx"][t]), cpu(inp["w"][t]),
-                                       cpu(inp["k_idx"][r0:r0 + p + 1]), ks)
+        ks = None if k_scale is None else k_scale[r0:r0 + p + 1]
+        # the pinned indexer score on a one-query descriptor: the query at p sees 0..p
+        s_ref = oracle.index_scores(cpu(inp["q_idx"][t:t + 1]), cpu(inp["w"][t:t + 1]),
+                                    k_idx[r0:r0 + p + 1], ks,
+                                    ctx_len=np.array([p + 1], np.int32))[0]
         sel = check_index_row(idx_c[t], p, w.K)
+        if one_pass:
+            _check_topk_on_gpu_scores(idx_c[t], s_gpu[i], p, w.K)
         check_set_band(sel, s_ref, p, w.K)
         rr = torch.from_numpy(sel.astype(np.int64)) + r0
         dev = inp["k_cache"].device
+        g = None if gate_cpu is None else gate_cpu[t:t + 1]
         ref, _ = oracle.sparse_attn(cpu(inp["q"][t:t + 1]), cpu(inp["k_cache"][rr.to(dev)]),
                                     cpu(inp["v_cache"][rr.to(dev)]),
                                     idx=np.arange(len(sel), dtype=np.int32)[None],
-                                    gate=cpu(inp["gate"][t:t + 1]),
-                                    ctx_len=np.array([len(sel)], np.int32))
+                                    gate=g, ctx_len=np.array([len(sel)], np.int32))
         check_out(out[t:t + 1], ref, ATOL_BF16 if inp["k_scale"] is None else ATOL_FP8)
+    return out, idx
 
 
 def test_layer_prefill_small(dsa):
@@ -555,7 +603,12 @@ def test_layer_prefill_8k_chunk_sampled(dsa):
     say("layer_prefill 8192 queries on a 131072-token context (sampled rows)")
     w = W.prefill_8k()
     inp = W.make_inputs(w, device=DEV)
-    _layer_prefill_check(dsa, w, inp, inp, rows=[0, 1, 2047, 4096, 8190, 8191])
+    # 64 evenly spaced rows, the first and the last included: every compute
+    # wave of the indexer's 28-query workgroups is sampled
+    rows = np.unique(np.linspace(0, w.T - 1, 64).round().astype(int)).tolist()
+    assert len(rows) == 64 and rows[0] == 0 and rows[-1] == w.T - 1
+    assert len({(r % 28) // 4 for r in rows}) == 7
+    _layer_prefill_check(dsa, w, inp, inp, rows=rows)
 
 
 def test_layer_decode_replays_as_a_hip_graph(dsa):
@@ -606,3 +659,165 @@ def test_layer_decode_replays_as_a_hip_graph(dsa):
         call_o()  # eager work on other buffers between replays
         torch.cuda.synchronize()
         assert torch.equal(out_o, want_out_o)
+
+
+# --------------------------------------------------------------------------
+# Per-head scalar gate, poisoned workspaces, prefill sub-chunks, side streams
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("lens,nq,K", [([131072], [1], 2048),      # split + combine kernel
+                                       ([6000], [40], 2048),       # one workgroup per row
+                                       ([4096, 700], [1, 1], 256)])
+def test_sparse_attn_per_head_gate(dsa, lens, nq, K):
+    """gate_stride_d = 0: one gate value per head, applied to all its dims."""
+    say(f"sparse_attn per-head gate lens={lens} nq={nq} K={K}")
+    w = wl("t", lens, nq, 4, 64, 64, 128, K, seed=24)
+    inp = W.make_inputs(w)
+    gate = W.randn_bf16((w.T, 64), 24, "head_gate")
+    idx = _rand_idx(lens, nq, K, seed=6)
+    d = to_dev(inp)
+    cu_q = None if all(n == 1 for n in nq) else d["cu_q"]
+    out = dsa.dsa_sparse_attn(d["q"], d["k_cache"], d["v_cache"], idx.to(DEV), d["ctx_len"],
+                              d["cu_ctx"], gate=gate.to(DEV), cu_q=cu_q, max_ctx=max(lens))
+    torch.cuda.synchronize()
+    ref, _ = oracle.sparse_attn(inp["q"], inp["k_cache"], inp["v_cache"], idx=idx,
+                                gate=_gate_for_oracle(gate, 128), ctx_len=inp["ctx_len"],
+                                cu_q=inp["cu_q"], cu_ctx=inp["cu_ctx"])
+    check_out(out, ref, ATOL_BF16)
+
+
+def test_layer_decode_per_head_gate(dsa):
+    say("layer_decode with one gate value per head")
+    w = wl("t", [40000, 3000], [1, 1], 32, 128, 64, 128, 2048, seed=33, plant_frac=0.05)
+    inp = W.make_inputs(w)
+    gate = W.randn_bf16((w.B, w.Hq), 33, "head_gate")
+    _layer_decode_check(dsa, w, inp, to_dev(inp), gate=gate)
+
+
+def test_layer_prefill_per_head_gate(dsa):
+    say("layer_prefill with one gate value per head")
+    w = wl("t", [5000], [150], 16, 128, 64, 128, 2048, seed=34)
+    inp = W.make_inputs(w)
+    gate = W.randn_bf16((w.T, w.Hq), 34, "head_gate")
+    _layer_prefill_check(dsa, w, inp, to_dev(inp), rows=list(range(0, w.T, 13)) + [w.T - 1],
+                         gate=gate)
+
+
+def _run_decode(dsa, w, d, ws):
+    idx = torch.empty(w.B, w.K, dtype=torch.int32, device=DEV)
+    out = dsa.dsa_layer_decode(d["q_idx"], d["w"], d["k_idx"], d["k_scale"], d["q"], d["k_cache"],
+                               d["v_cache"], d["gate"], w.K, d["ctx_len"], d["cu_ctx"],
+                               max_ctx=max(w.ctx_lens), idx_out=idx, ws=ws)
+    return out, idx
+
+
+def test_layer_decode_poisoned_workspace(dsa):
+    """A workspace filled with 0xFF bytes (NaN scores, -1 words) gives the
+    same bits as a zeroed one: no step reads scratch it did not write."""
+    say("layer_decode 128K: workspace poisoned with 0xFF vs zeroed")
+    w = W.decode_128k()
+    d = W.make_inputs(w, device=DEV)
+    L = max(w.ctx_lens)
+    nb = dsa.dsa_layer_decode_workspace_size(w.B, L, w.K, w.Hq, w.D)
+    ws0 = torch.zeros(nb, dtype=torch.uint8, device=DEV)
+    ws1 = torch.full((nb,), 255, dtype=torch.uint8, device=DEV)
+    o0, i0 = _run_decode(dsa, w, d, ws0)
+    o1, i1 = _run_decode(dsa, w, d, ws1)
+    torch.cuda.synchronize()
+    assert torch.equal(i0, i1)
+    assert torch.equal(o0.view(torch.int16), o1.view(torch.int16))
+
+
+def _prefill_small():
+    return wl("t", [6000, 2500, 900], [300, 2500, 150], 16, 128, 64, 128, 2048, seed=43)
+
+
+def _run_prefill(dsa, w, d, ws):
+    idx = torch.empty(w.T, w.K, dtype=torch.int32, device=DEV)
+    out = dsa.dsa_layer_prefill(d["q_idx"], d["w"], d["k_idx"], d["k_scale"], d["q"],
+                                d["k_cache"], d["v_cache"], d["gate"], w.K, d["cu_q"],
+                                d["ctx_len"], d["cu_ctx"], max_q=max(w.n_q),
+                                max_ctx=max(w.ctx_lens), idx_out=idx, ws=ws)
+    return out, idx
+
+
+def test_layer_prefill_poisoned_workspace(dsa):
+    say("layer_prefill: workspace poisoned with 0xFF vs zeroed")
+    w = _prefill_small()
+    d = W.make_inputs(w, device=DEV)
+    nb = dsa.dsa_layer_prefill_workspace_size(w.B, w.T, max(w.ctx_lens), w.K, w.Hq, w.D)
+    o0, i0 = _run_prefill(dsa, w, d, torch.zeros(nb, dtype=torch.uint8, device=DEV))
+    o1, i1 = _run_prefill(dsa, w, d, torch.full((nb,), 255, dtype=torch.uint8, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(i0, i1)
+    assert torch.equal(o0.view(torch.int16), o1.view(torch.int16))
+
+
+def test_layer_prefill_sub_chunks(dsa):
+    """A workspace too small for the score array of all rows: the library runs
+    the rows in sub-chunks (here at least three, crossing sequence
+    boundaries).  Every step is row-wise and the chunks keep the Top-K and
+    attention plans of the one-pass call at these sizes, so the result is
+    bit-identical to it; sampled rows are also checked against the oracle.
+    The chunked call runs on a poisoned (0xFF) workspace."""
+    say("layer_prefill in sub-chunks (workspace for ~900 rows, 2950 rows)")
+    w = _prefill_small()
+    inp = W.make_inputs(w)
+    d = to_dev(inp)
+    L = max(w.ctx_lens)
+    full = dsa.dsa_layer_prefill_workspace_size(w.B, w.T, L, w.K, w.Hq, w.D)
+    small = (dsa.dsa_layer_prefill_workspace_size(w.B, 900, L, w.K, w.Hq, w.D) +
+             dsa.dsa_layer_prefill_min_workspace_size(w.B, L, w.K, w.Hq, w.D))
+    assert small < full / 3
+    o_full, i_full = _run_prefill(dsa, w, d, torch.empty(full, dtype=torch.uint8, device=DEV))
+    o_sub, i_sub = _run_prefill(dsa, w, d,
+                                torch.full((small,), 255, dtype=torch.uint8, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(i_full, i_sub)
+    assert torch.equal(o_full.view(torch.int16), o_sub.view(torch.int16))
+    rows = [0, 299, 300, 899, 900, 1799, 1800, 2799, 2800, 2949]
+    _layer_prefill_check(dsa, w, inp, d, rows=rows, ws_bytes=small)
+
+
+def test_layer_prefill_smallest_workspace(dsa):
+    """The least accepted workspace: one query row per sub-chunk."""
+    say("layer_prefill with the minimum workspace (one row per sub-chunk)")
+    w = wl("t", [3000, 2100], [5, 4], 16, 128, 64, 128, 2048, seed=44)
+    inp = W.make_inputs(w)
+    d = to_dev(inp)
+    L = max(w.ctx_lens)
+    nb = dsa.dsa_layer_prefill_min_workspace_size(w.B, L, w.K, w.Hq, w.D)
+    _layer_prefill_check(dsa, w, inp, d, ws_bytes=nb)
+    with pytest.raises(dsa.DSAError):
+        _run_prefill(dsa, w, d, torch.empty(nb - 256, dtype=torch.uint8, device=DEV))
+
+
+def test_internal_workspaces_on_a_side_stream(dsa):
+    """Calls on a stream that is not the current one, with the binding's own
+    workspaces: while they run, the current stream allocates and overwrites
+    fresh memory; the results still match the oracle."""
+    say("dsa_topk and dsa_sparse_attn on a side stream with internal workspaces")
+    side = torch.cuda.Stream()
+    n, K = 131072, 2048
+    x = _topk_case("relu_like", n, seed=9)
+    ctx = torch.tensor([n], dtype=torch.int32)
+    w = wl("t", [n], [1], 4, 64, 64, 128, K, seed=25)
+    inp = W.make_inputs(w)
+    idx_r = _rand_idx([n], [1], K, seed=8)
+    d = to_dev(inp)
+    xs, cs, ir = x[None].to(DEV).contiguous(), ctx.to(DEV), idx_r.to(DEV)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        pass
+    got = dsa.dsa_topk(xs, K, cs, max_ctx=n, stream=side)
+    out = dsa.dsa_sparse_attn(d["q"], d["k_cache"], d["v_cache"], ir, d["ctx_len"], d["cu_ctx"],
+                              gate=d["gate"], max_ctx=n, stream=side)
+    junk = [torch.full((1 << 20,), 7, dtype=torch.int32, device=DEV) for _ in range(8)]
+    side.synchronize()
+    torch.cuda.synchronize()
+    del junk
+    want = oracle.topk(x[None].numpy().astype(np.float32), K, ctx.numpy())
+    assert np.array_equal(got.cpu().numpy(), want)
+    ref, _ = oracle.sparse_attn(inp["q"], inp["k_cache"], inp["v_cache"], idx=idx_r,
+                                gate=inp["gate"], ctx_len=inp["ctx_len"], cu_ctx=inp["cu_ctx"])
+    check_out(out, ref, ATOL_BF16)

@@ -179,6 +179,27 @@ dsa_status_t dsa_layer_decode(const void* q_idx, const void* w, int64_t w_ld, co
                               const int64_t* cu_ctx, int B, int max_ctx, void* out,
                               int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
 
+/* Allocation-free decode, for callers that cannot allocate device memory   */
+/* (code under HIP graph capture, tight serving loops, harnesses that forbid */
+/* allocation): dsa_layer_decode with its workspace in a fixed scratch array */
+/* the library keeps in each GPU's memory until the process ends            */
+/* (dsa_layer_decode_noalloc_max_bytes() bytes, 64 MiB).  It never calls    */
+/* hipMalloc or hipFree.  A call whose workspace                            */
+/* (dsa_layer_decode_workspace_size) exceeds that size returns              */
+/* DSA_ERR_WORKSPACE without touching the GPU.  Every call on one GPU uses  */
+/* the same array: calls that overlap on one GPU (other streams, other host */
+/* threads) race and must be ordered by the caller.  No step needs the      */
+/* array cleared, so the previous call's contents are harmless.  Results    */
+/* are bit-identical to dsa_layer_decode's.                                 */
+size_t dsa_layer_decode_noalloc_max_bytes(void);
+dsa_status_t dsa_layer_decode_noalloc(const void* q_idx, const void* w, int64_t w_ld,
+                                      const void* k_idx, int k_dtype, const float* k_scale,
+                                      int H_I, int d_I, const void* q, const void* k_cache,
+                                      const void* v_cache, const void* gate,
+                                      int64_t gate_stride_d, float sm_scale, int Hq, int D, int K,
+                                      const int32_t* ctx_len, const int64_t* cu_ctx, int B,
+                                      int max_ctx, void* out, int32_t* idx_out, void* stream);
+
 /* Measurement hook: on the calling thread, every later dsa_layer_decode    */
 /* call launches its step-1 indexer kernel with `start` and `stop` (both    */
 /* hipEvent_t) attached to the dispatch, which records them when that       */

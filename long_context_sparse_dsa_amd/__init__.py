@@ -35,6 +35,7 @@ EXPORTS = [
     "dsa_topk_workspace_size", "dsa_topk",
     "dsa_sparse_attn_workspace_size", "dsa_sparse_attn",
     "dsa_layer_decode_workspace_size", "dsa_layer_decode", "dsa_set_indexer_events",
+    "dsa_layer_decode_noalloc_max_bytes", "dsa_layer_decode_noalloc",
     "dsa_set_topk_counters",
     "dsa_layer_prefill_workspace_size", "dsa_layer_prefill_min_workspace_size",
     "dsa_layer_prefill",
@@ -81,9 +82,14 @@ def load(path: str | None = None):
     lib.dsa_layer_prefill_min_workspace_size.restype = S
     lib.dsa_layer_prefill.argtypes = [P, P, L, P, I, P, I, I, P, P, P, P, L, F, I, I, I, P, P, P,
                                       I, I, I, I, P, P, P, S, P]
+    lib.dsa_layer_decode_noalloc_max_bytes.argtypes = []
+    lib.dsa_layer_decode_noalloc_max_bytes.restype = S
+    lib.dsa_layer_decode_noalloc.argtypes = [P, P, L, P, I, P, I, I, P, P, P, P, L, F, I, I, I,
+                                             P, P, I, I, P, P, P]
     lib.dsa_set_indexer_events.argtypes = [P, P]
     lib.dsa_set_topk_counters.argtypes = [P]
     for fn in ("dsa_index_scores", "dsa_topk", "dsa_sparse_attn", "dsa_layer_decode",
+               "dsa_layer_decode_noalloc",
                "dsa_layer_prefill", "dsa_set_indexer_events", "dsa_set_topk_counters"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
@@ -427,6 +433,25 @@ def prepare_layer_decode(q_idx, w, k_idx, k_scale, q, k_cache, v_cache, gate, K,
         if st != 0:
             raise DSAError("dsa_layer_decode", st, dsa_last_error())
     return call
+
+
+def dsa_layer_decode_noalloc(q_idx, w, k_idx, k_scale, q, k_cache, v_cache, gate, K, ctx_len,
+                             cu_ctx, max_ctx, out, idx_out=None, sm_scale=0.0, w_ld=None,
+                             stream=None):
+    """dsa_layer_decode without a workspace argument: the library's fixed
+    per-GPU scratch array serves as workspace and nothing is allocated (the
+    caller passes `out` and `max_ctx`).  Calls overlapping on one GPU race."""
+    B, T, H_I, d_I, Hq, D, gs = _layer_checks(q_idx, w, k_idx, k_scale, q, k_cache, v_cache,
+                                              gate, ctx_len, cu_ctx, None, idx_out, K)
+    _check(out, "out", BF16, 3)
+    _shape(out, "out", (T, Hq, D))
+    if w_ld is None:
+        w_ld = 0 if w.dim() == 1 else w.shape[-1]
+    _call("dsa_layer_decode_noalloc", _p(q_idx), _p(w), w_ld, _p(k_idx), _key_dtype(k_idx),
+          _p(k_scale), H_I, d_I, _p(q), _p(k_cache), _p(v_cache), _p(gate), gs, float(sm_scale),
+          Hq, D, K, _p(ctx_len), _p(cu_ctx), B, int(max_ctx), _p(out), _p(idx_out),
+          _stream(stream))
+    return out
 
 
 def layer_scores(ws, rows, max_ctx):

@@ -13,6 +13,8 @@
 #include <cstring>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "dsa_kernels.h"
 #include "dsa_topk_tile.h"
@@ -200,6 +202,45 @@ int prefill_chunk_rows(int T, int max_ctx, int K, int Hq, int D, size_t avail) {
     return lo;
   }
   return 0;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free decode entry point: one fixed array in each
+// GPU's memory, held until the process ends.  In host code `scratch` is only
+// a host-side handle; its device address (one per GPU) comes from
+// hipGetSymbolAddress on the entry point's first call on that GPU, with the
+// GPU current, and only that address is ever handed to kernels.
+// ---------------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current GPU (looked up once per GPU).
+hipError_t scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (p == nullptr) return hipErrorInvalidSymbol;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
 }
 
 }  // namespace
@@ -404,6 +445,35 @@ dsa_status_t dsa_layer_decode(const void* q_idx, const void* w, int64_t w_ld, co
                                 L.attn, plan, s);
   }
   return hip_status(e, "dsa_layer_decode");
+}
+
+size_t dsa_layer_decode_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+dsa_status_t dsa_layer_decode_noalloc(const void* q_idx, const void* w, int64_t w_ld,
+                                      const void* k_idx, int k_dtype, const float* k_scale,
+                                      int H_I, int d_I, const void* q, const void* k_cache,
+                                      const void* v_cache, const void* gate,
+                                      int64_t gate_stride_d, float sm_scale, int Hq, int D, int K,
+                                      const int32_t* ctx_len, const int64_t* cu_ctx, int B,
+                                      int max_ctx, void* out, int32_t* idx_out, void* stream) {
+  // the size check comes first: an oversize call is refused without
+  // touching the GPU
+  DSA_REQUIRE(B >= 1 && max_ctx >= 1 && K >= 1, DSA_ERR_INVALID_ARG,
+              "B, max_ctx and K must be >= 1 (got %d, %d, %d)", B, max_ctx, K);
+  const size_t need = (K <= 4096 && attn_shape_ok(Hq, D))
+                          ? decode_ws_layout(B, max_ctx, K, Hq, D, nullptr, nullptr)
+                          : 0;
+  DSA_REQUIRE(need <= kNoAllocScratchBytes, DSA_ERR_WORKSPACE,
+              "dsa_layer_decode_noalloc: this call needs %zu bytes of scratch, more than the "
+              "library's fixed %zu (B * max_ctx too large; use dsa_layer_decode with a "
+              "caller workspace)",
+              need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  const hipError_t e = scratch_for_current_device(&ws);
+  if (e != hipSuccess) return hip_status(e, "dsa_layer_decode_noalloc: scratch lookup");
+  return dsa_layer_decode(q_idx, w, w_ld, k_idx, k_dtype, k_scale, H_I, d_I, q, k_cache, v_cache,
+                          gate, gate_stride_d, sm_scale, Hq, D, K, ctx_len, cu_ctx, B, max_ctx,
+                          out, idx_out, ws, kNoAllocScratchBytes, stream);
 }
 
 size_t dsa_layer_prefill_workspace_size(int B, int T, int max_ctx, int K, int Hq, int D) {

@@ -55,6 +55,8 @@ def _load():
         lib.orc_bf16_to_f64.restype = D
         lib.orc_e4m3_to_f64.argtypes = [ctypes.c_uint8]
         lib.orc_e4m3_to_f64.restype = D
+        lib.orc_quantize_e4m3_rows.argtypes = [P, L, I, P, P]
+        lib.orc_quantize_e4m3_rows.restype = I
         lib.orc_index_scores.argtypes = [P, P, L, P, I, P, I, I, P, P, P, I, P, L, I]
         lib.orc_index_scores.restype = I
         lib.orc_topk_f64.argtypes = [P, L, P, P, I, I, P, I]
@@ -145,6 +147,19 @@ def e4m3_to_f64(codes) -> np.ndarray:
     lib = _load()
     c = _np(codes).astype(np.uint8).ravel()
     return np.array([lib.orc_e4m3_to_f64(int(v)) for v in c], dtype=np.float64)
+
+
+def quantize_e4m3_rows(k_rows):
+    """Cache-append quantisation of bf16 key rows [n, d]: returns (codes uint8
+    [n, d] (E4M3FN), scales float32 [n]) with per-row absolute-maximum
+    scaling (see dsa_oracle.c)."""
+    lib = _load()
+    k = _np(k_rows, np.uint16)
+    n, d = k.shape
+    codes = np.zeros((n, d), dtype=np.uint8)
+    scales = np.zeros(n, dtype=np.float32)
+    lib.orc_quantize_e4m3_rows(_ptr(k), n, d, _ptr(codes), _ptr(scales))
+    return codes, scales
 
 
 def index_scores(q_idx, w, k_idx, k_scale=None, ctx_len=None, cu_q=None, cu_ctx=None,

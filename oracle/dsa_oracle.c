@@ -198,6 +198,61 @@ int orc_index_scores(const uint16_t* q_idx, const uint16_t* w, int64_t w_ld, con
 }
 
 /* ---------------------------------------------------------------------- */
+/* Cache append: quantisation of a new token's indexer key row to the fp8  */
+/* key cache ([N05] Key Capabilities: FP8 mixed precision; the cache holds */
+/* OCP E4M3FN codes plus one fp32 scale per token).  The pages give no     */
+/* recipe; the reading taken is per-token absolute-maximum scaling:        */
+/*   amax  = max_d |x_d|                     (x: the bf16 row, exact)      */
+/*   sigma = amax / 448 in fp32 (1 for an all-zero row)                    */
+/*   y_d   = x_d / sigma in fp32, clamped to [-448, 448]                   */
+/*   code  = y_d rounded to the nearest E4M3FN value, ties to even         */
+/* so that sigma * decode(code) approximates x_d.  The rounding decision   */
+/* is taken on the fp32 value y_d (the precision the device computes in).  */
+/* ---------------------------------------------------------------------- */
+
+/* Nearest E4M3FN code of a finite fp32 value with |y| <= 448, ties to even.
+ * Worked in double, where every step below is exact: subnormal codes are
+ * multiples of 2^-9 below 2^-6; a normal code 1.mmm x 2^e has spacing
+ * 2^(e-3). */
+static uint8_t e4m3_nearest(float y) {
+  uint8_t sign = signbit(y) ? 0x80 : 0x00;
+  double a = fabs((double)y);
+  if (a < ldexp(1.0, -6)) {
+    double m = nearbyint(a * 512.0); /* 0..8; 8 is the smallest normal, code 0x08 */
+    return (uint8_t)(sign | (uint8_t)m);
+  }
+  int ex;
+  frexp(a, &ex);          /* a = f * 2^ex, f in [0.5, 1): a in [2^(ex-1), 2^ex) */
+  int e = ex - 1;         /* a = 1.xxx * 2^e, e in [-6, 8] */
+  double r = nearbyint(a / ldexp(1.0, e - 3));  /* 8..16 */
+  if (r == 16.0) {
+    e += 1;
+    r = 8.0;
+  }
+  return (uint8_t)(sign | (uint8_t)((e + 7) << 3) | (uint8_t)(r - 8.0));
+}
+
+int orc_quantize_e4m3_rows(const uint16_t* k, int64_t rows, int d, uint8_t* codes,
+                           float* scales) {
+  for (int64_t r = 0; r < rows; ++r) {
+    float amax = 0.f;
+    for (int i = 0; i < d; ++i) {
+      float x = (float)orc_bf16_to_f64(k[r * d + i]);
+      if (fabsf(x) > amax) amax = fabsf(x);
+    }
+    float sigma = amax > 0.f ? amax / 448.0f : 1.0f;
+    scales[r] = sigma;
+    for (int i = 0; i < d; ++i) {
+      float y = (float)orc_bf16_to_f64(k[r * d + i]) / sigma;
+      if (y > 448.0f) y = 448.0f;
+      if (y < -448.0f) y = -448.0f;
+      codes[r * d + i] = e4m3_nearest(y);
+    }
+  }
+  return 0;
+}
+
+/* ---------------------------------------------------------------------- */
 /* Top-K select ([OSLLM] Architecture Breakdown item 2: keep the K best;   */
 /* [FGSA] 2.1: K = 2048 historical positions).                             */
 /*                                                                         */

@@ -377,3 +377,71 @@ def test_layer_selection_is_topk_of_its_own_scores():
     assert np.array_equal(r["idx"], oracle.topk(s, K, np.array([L], np.int32)))
     out, _ = oracle.sparse_attn(q, kc, vc, idx=r["idx"], gate=g, ctx_len=np.array([L], np.int32))
     assert np.array_equal(r["out"], out)
+
+
+# --------------------------------------------------------------------------
+# Cache-append quantisation (bf16 key row -> E4M3FN codes + fp32 scale)
+# --------------------------------------------------------------------------
+
+def _torch_codes(k_bf16, sigma):
+    """Reference rounding: torch's own fp32 -> float8_e4m3fn cast (round to
+    nearest, ties to even) of y = x / sigma clamped to the format's range."""
+    y = k_bf16.float() / torch.from_numpy(sigma)[:, None]
+    y = y.clamp(-448.0, 448.0)
+    return y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_quantize_matches_torch_rounding_on_varied_rows():
+    rng = np.random.default_rng(20)
+    rows = [rng.standard_normal(128),
+            rng.standard_normal(128) * 1e-3,
+            rng.standard_normal(128) * 300.0,
+            np.where(rng.random(128) < 0.05, 40.0, 1.0) * rng.standard_normal(128),  # outliers
+            rng.standard_normal(128) * 1e-30,                                          # tiny scale
+            np.linspace(-1, 1, 128),
+            np.zeros(128)]
+    k = bf16(np.stack(rows))
+    codes, sigma = oracle.quantize_e4m3_rows(k)
+    amax = np.abs(k.float().numpy()).max(1)
+    want_sigma = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    assert np.array_equal(sigma, want_sigma)
+    assert np.array_equal(codes, _torch_codes(k, sigma))
+    # the largest magnitude of each non-zero row lands on +-448 (code 0x7E / 0xFE)
+    for r in range(len(rows) - 1):
+        i = int(np.abs(k[r].float().numpy()).argmax())
+        assert codes[r, i] & 0x7F == 0x7E
+    assert np.all(codes[-1] == 0) and sigma[-1] == 1.0
+
+
+def test_quantize_ties_go_to_even_codes():
+    # amax = 448 gives sigma = 1 exactly, so y = x: each value below sits
+    # exactly halfway between two E4M3FN neighbours (hand-computed codes)
+    vals = [448.0, 1.0625, 1.1875, 3 * 2.0 ** -10, 2.0 ** -10, 5 * 2.0 ** -10, -1.0625, 17.0,
+            2.0 ** -6 * (1 + 1 / 16), 0.0]
+    want = [0x7E,           # 448 = 1.75 * 2^8
+            0x38,           # 1.0625: between 1.0 (0x38) and 1.125 (0x39) -> even 0x38
+            0x3A,           # 1.1875: between 1.125 (0x39) and 1.25 (0x3A) -> even 0x3A
+            0x02,           # 1.5 * 2^-9 -> 2 * 2^-9 (even)
+            0x00,           # 0.5 * 2^-9 -> 0 (even)
+            0x02,           # 2.5 * 2^-9 -> 2 * 2^-9 (even)
+            0xB8,           # -1.0625 -> -1.0
+            0x58,           # 17 between 16 (0x58) and 18 (0x59) -> even 0x58
+            0x08,           # 2^-6 * 1.0625 between 2^-6 (0x08) and 2^-6*1.125 (0x09) -> 0x08
+            0x00]
+    row = np.zeros(64)
+    row[:len(vals)] = vals
+    codes, sigma = oracle.quantize_e4m3_rows(bf16(row[None]))
+    assert sigma[0] == 1.0
+    assert codes[0, :len(vals)].tolist() == want
+    assert np.array_equal(codes, _torch_codes(bf16(row[None]), sigma))
+
+
+def test_quantize_error_within_half_a_code_step():
+    rng = np.random.default_rng(21)
+    k = bf16(rng.standard_normal((50, 64)) * rng.uniform(0.01, 100, (50, 1)))
+    codes, sigma = oracle.quantize_e4m3_rows(k)
+    y = np.clip(k.float().numpy() / sigma[:, None], -448, 448)
+    dec = oracle.e4m3_to_f64(codes.ravel()).reshape(codes.shape)
+    a = np.abs(y)
+    step = np.where(a < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(a, 1e-30))) - 3))
+    assert np.all(np.abs(dec - y) <= step / 2 + 1e-12)

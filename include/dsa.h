@@ -125,6 +125,31 @@ dsa_status_t dsa_topk(const float* scores, int64_t ld, const int32_t* cu_q,
                       int32_t* idx, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Cache append: the new tokens' rows go into the caches before the layer    */
+/* reads them (the naive-n0-5-flash page, Key Capabilities: FP8 mixed        */
+/* precision; an fp8 indexer key cache holds E4M3FN codes and one fp32      */
+/* scale per token).  For query row t of the batch descriptor (position p_t */
+/* of sequence b), cache row r = cu_ctx[b] + p_t receives:                  */
+/*   k_idx_cache[r, :]  bf16 cache: k_idx_new[t, :] as is;                   */
+/*                      fp8 cache: codes of y_d = k_idx_new[t, d] / s,       */
+/*                      rounded to the nearest E4M3FN value (ties to even)   */
+/*                      after clamping to +-448, with s = max_d |k_idx_new|  */
+/*                      / 448 in fp32 (1 for an all-zero row);               */
+/*   k_scale_cache[r]   s (fp8 cache only);                                  */
+/*   k_cache[r, :], v_cache[r, :]  k_new[t, :], v_new[t, :].                 */
+/* Any of k_idx_new, k_new, v_new may be NULL (that cache is left alone).    */
+/* Call it with the descriptor of the layer call that follows (decode:       */
+/* cu_q = NULL, the new token at ctx_len[b] - 1).                            */
+/*   k_idx_new bf16 [T, d_I], d_I in {64, 128};  k_new, v_new bf16 [T, D],  */
+/*   D in {64, 128}.                                                         */
+/* ------------------------------------------------------------------------ */
+dsa_status_t dsa_cache_append(const void* k_idx_new, int d_I, const void* k_new,
+                              const void* v_new, int D, const int32_t* cu_q,
+                              const int32_t* ctx_len, const int64_t* cu_ctx, int B, int T,
+                              void* k_idx_cache, int k_dtype, float* k_scale_cache,
+                              void* k_cache, void* v_cache, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Step 3: gated sparse attention over the selected rows.                    */
 /* Pages: "Open-Source LLM Architecture Evolution ...", Technical Deep Dive  */
 /* item 2 (scores and softmax over the 2048 selected elements only) and      */
@@ -178,6 +203,24 @@ dsa_status_t dsa_layer_decode(const void* q_idx, const void* w, int64_t w_ld, co
                               const int32_t* ctx_len,
                               const int64_t* cu_ctx, int B, int max_ctx, void* out,
                               int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Whole layer, decode, with the new token appended first (the cache-append */
+/* step of dsa_cache_append fused into the layer's first kernel): for each   */
+/* sequence b, cache row cu_ctx[b] + ctx_len[b] - 1 receives k_idx_new[b]    */
+/* (bf16 [B, d_I]; an fp8 key cache gets its E4M3FN codes and k_scale its    */
+/* scale, exactly as dsa_cache_append computes them), k_new[b] and v_new[b] */
+/* (bf16 [B, D], either may be NULL), and the layer then runs on the updated */
+/* caches, the new position included.  Results and cache contents are       */
+/* bit-identical to dsa_cache_append followed by dsa_layer_decode.  The      */
+/* caches are therefore writable here.                                      */
+dsa_status_t dsa_layer_decode_append(const void* q_idx, const void* w, int64_t w_ld, void* k_idx,
+                                     int k_dtype, float* k_scale, int H_I, int d_I, const void* q,
+                                     void* k_cache, void* v_cache, const void* gate,
+                                     int64_t gate_stride_d, float sm_scale, int Hq, int D, int K,
+                                     const int32_t* ctx_len, const int64_t* cu_ctx, int B,
+                                     int max_ctx, const void* k_idx_new, const void* k_new,
+                                     const void* v_new, void* out, int32_t* idx_out, void* ws,
+                                     size_t ws_bytes, void* stream);
 
 /* Allocation-free decode, for callers that cannot allocate device memory   */
 /* (code under HIP graph capture, tight serving loops, harnesses that forbid */

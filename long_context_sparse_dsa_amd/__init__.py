@@ -31,11 +31,11 @@ _STATUS = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED",
 
 EXPORTS = [
     "dsa_version", "dsa_last_error",
-    "dsa_index_scores",
+    "dsa_index_scores", "dsa_cache_append",
     "dsa_topk_workspace_size", "dsa_topk",
     "dsa_sparse_attn_workspace_size", "dsa_sparse_attn",
     "dsa_layer_decode_workspace_size", "dsa_layer_decode", "dsa_set_indexer_events",
-    "dsa_layer_decode_noalloc_max_bytes", "dsa_layer_decode_noalloc",
+    "dsa_layer_decode_noalloc_max_bytes", "dsa_layer_decode_noalloc", "dsa_layer_decode_append",
     "dsa_set_topk_counters",
     "dsa_layer_prefill_workspace_size", "dsa_layer_prefill_min_workspace_size",
     "dsa_layer_prefill",
@@ -65,6 +65,7 @@ def load(path: str | None = None):
     lib.dsa_version.restype = ctypes.c_char_p
     lib.dsa_last_error.restype = ctypes.c_char_p
     lib.dsa_index_scores.argtypes = [P, P, L, P, I, P, I, I, P, P, P, I, I, I, I, P, L, P]
+    lib.dsa_cache_append.argtypes = [P, I, P, P, I, P, P, P, I, I, P, I, P, P, P, P]
     lib.dsa_topk_workspace_size.argtypes = [I, I, I, I]
     lib.dsa_topk_workspace_size.restype = S
     lib.dsa_topk.argtypes = [P, L, P, P, I, I, I, I, I, P, P, S, P]
@@ -82,14 +83,17 @@ def load(path: str | None = None):
     lib.dsa_layer_prefill_min_workspace_size.restype = S
     lib.dsa_layer_prefill.argtypes = [P, P, L, P, I, P, I, I, P, P, P, P, L, F, I, I, I, P, P, P,
                                       I, I, I, I, P, P, P, S, P]
+    lib.dsa_layer_decode_append.argtypes = [P, P, L, P, I, P, I, I, P, P, P, P, L, F, I, I, I,
+                                            P, P, I, I, P, P, P, P, P, P, S, P]
     lib.dsa_layer_decode_noalloc_max_bytes.argtypes = []
     lib.dsa_layer_decode_noalloc_max_bytes.restype = S
     lib.dsa_layer_decode_noalloc.argtypes = [P, P, L, P, I, P, I, I, P, P, P, P, L, F, I, I, I,
                                              P, P, I, I, P, P, P]
     lib.dsa_set_indexer_events.argtypes = [P, P]
     lib.dsa_set_topk_counters.argtypes = [P]
-    for fn in ("dsa_index_scores", "dsa_topk", "dsa_sparse_attn", "dsa_layer_decode",
-               "dsa_layer_decode_noalloc",
+    for fn in ("dsa_index_scores", "dsa_cache_append", "dsa_topk", "dsa_sparse_attn",
+               "dsa_layer_decode",
+               "dsa_layer_decode_noalloc", "dsa_layer_decode_append",
                "dsa_layer_prefill", "dsa_set_indexer_events", "dsa_set_topk_counters"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
@@ -250,6 +254,45 @@ def dsa_index_scores(q_idx, w, k_idx, k_scale, ctx_len, cu_ctx, cu_q=None, max_q
     return scores
 
 
+def dsa_cache_append(ctx_len, cu_ctx, k_idx_cache=None, k_idx_new=None, k_scale_cache=None,
+                     k_cache=None, k_new=None, v_cache=None, v_new=None, cu_q=None, stream=None):
+    """Write new tokens' rows into the caches at their positions (query row t
+    of the descriptor -> cache row cu_ctx[b] + p_t): the indexer key (bf16, or
+    E4M3FN codes plus a per-token fp32 scale for an fp8 cache) and the K / V
+    rows.  Any of the *_new tensors may be None."""
+    _check(ctx_len, "ctx_len", (torch.int32,), 1)
+    _check(cu_ctx, "cu_ctx", (torch.int64,), 1)
+    _check(cu_q, "cu_q", (torch.int32,), 1)
+    _check(k_idx_new, "k_idx_new", BF16, 2)
+    _check(k_idx_cache, "k_idx_cache", KEYS, 2)
+    _check(k_scale_cache, "k_scale_cache", (torch.float32,), 1)
+    for n, t in (("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _check(t, n, BF16, 2)
+    news = [t for t in (k_idx_new, k_new, v_new) if t is not None]
+    if not news:
+        return
+    T = news[0].shape[0]
+    B = _check_desc(ctx_len, cu_ctx, cu_q, T)
+    d_I, D, kdt = 0, 0, DSA_KEY_BF16
+    if k_idx_new is not None:
+        if k_idx_cache is None:
+            raise ValueError("k_idx_new needs k_idx_cache")
+        d_I = k_idx_new.shape[1]
+        _check_keys(k_idx_cache, k_scale_cache, d_I)
+        kdt = _key_dtype(k_idx_cache)
+    for n, new, cache in (("k", k_new, k_cache), ("v", v_new, v_cache)):
+        if new is not None:
+            if cache is None:
+                raise ValueError(f"{n}_new needs {n}_cache")
+            if new.shape[0] != T or cache.shape[1] != new.shape[1]:
+                raise ValueError(f"{n}_new {tuple(new.shape)} does not fit {n}_cache "
+                                 f"{tuple(cache.shape)} with {T} rows")
+            D = new.shape[1]
+    _call("dsa_cache_append", _p(k_idx_new), d_I, _p(k_new), _p(v_new), D, _p(cu_q), _p(ctx_len),
+          _p(cu_ctx), B, T, _p(k_idx_cache), kdt, _p(k_scale_cache), _p(k_cache), _p(v_cache),
+          _stream(stream))
+
+
 def dsa_topk(scores, K, ctx_len, cu_q=None, max_q=None, max_ctx=None, idx=None, stream=None):
     """Exact Top-K positions per row, ascending, -1 padded: int32 [T, K]."""
     _check(scores, "scores", (torch.float32,), 2)
@@ -404,6 +447,38 @@ def dsa_layer_decode(q_idx, w, k_idx, k_scale, q, k_cache, v_cache, gate, K, ctx
           H_I, d_I, _p(q), _p(k_cache), _p(v_cache), _p(gate), gs, float(sm_scale), Hq, D, K,
           _p(ctx_len), _p(cu_ctx), B, max_ctx, _p(out), _p(idx_out), _p(ws), ws.numel(),
           _stream(stream))
+    _keep_for(stream, ws if own_ws else None, out)
+    return out
+
+
+def dsa_layer_decode_append(q_idx, w, k_idx, k_scale, q, k_cache, v_cache, gate, K, ctx_len,
+                            cu_ctx, k_idx_new, k_new=None, v_new=None, max_ctx=None, sm_scale=0.0,
+                            out=None, idx_out=None, ws=None, w_ld=None, stream=None):
+    """Decode layer with each sequence's new token appended to the caches first
+    (row cu_ctx[b] + ctx_len[b] - 1): k_idx_new bf16 [B, d_I] (quantised for an
+    fp8 key cache), k_new / v_new bf16 [B, D].  The caches are written."""
+    B, T, H_I, d_I, Hq, D, gs = _layer_checks(q_idx, w, k_idx, k_scale, q, k_cache, v_cache,
+                                              gate, ctx_len, cu_ctx, None, idx_out, K)
+    _check(k_idx_new, "k_idx_new", BF16, 2)
+    _shape(k_idx_new, "k_idx_new", (B, d_I))
+    _check(k_new, "k_new", BF16, 2)
+    _check(v_new, "v_new", BF16, 2)
+    _shape(k_new, "k_new", (B, D))
+    _shape(v_new, "v_new", (B, D))
+    max_ctx = _host_max(ctx_len, max_ctx)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", BF16, 3)
+    _shape(out, "out", (T, Hq, D))
+    own_ws = ws is None
+    if own_ws:
+        ws = _workspace(dsa_layer_decode_workspace_size(B, max_ctx, K, Hq, D), q.device)
+    if w_ld is None:
+        w_ld = 0 if w.dim() == 1 else w.shape[-1]
+    _call("dsa_layer_decode_append", _p(q_idx), _p(w), w_ld, _p(k_idx), _key_dtype(k_idx),
+          _p(k_scale), H_I, d_I, _p(q), _p(k_cache), _p(v_cache), _p(gate), gs, float(sm_scale),
+          Hq, D, K, _p(ctx_len), _p(cu_ctx), B, max_ctx, _p(k_idx_new), _p(k_new), _p(v_new),
+          _p(out), _p(idx_out), _p(ws), ws.numel(), _stream(stream))
     _keep_for(stream, ws if own_ws else None, out)
     return out
 

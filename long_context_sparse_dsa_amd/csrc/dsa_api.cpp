@@ -278,7 +278,7 @@ dsa_status_t dsa_index_scores(const void* q_idx, const void* w, int64_t w_ld, co
   hipError_t e;
   if (cu_q == nullptr)
     e = dsa::launch_index_decode(q_idx, w, w_ld, k_idx, k_dtype, k_scale, H_I, d_I, ctx_len,
-                                 cu_ctx, B, max_ctx, scores, ld, nullptr, s);
+                                 cu_ctx, B, max_ctx, scores, ld, nullptr, nullptr, s);
   else
     e = dsa::launch_index_prefill(q_idx, w, w_ld, k_idx, k_dtype, k_scale, H_I, d_I, cu_q,
                                   ctx_len, cu_ctx, B, max_q, max_ctx, scores, ld, s);
@@ -316,6 +316,44 @@ dsa_status_t dsa_topk(const float* scores, int64_t ld, const int32_t* cu_q,
   if (e == hipSuccess) e = dsa::launch_topk_resolve(scores, ld, cu_q, ctx_len, B, T, K, w, idx,
                                                     t_topk_counters, s);
   return hip_status(e, "dsa_topk");
+}
+
+dsa_status_t dsa_cache_append(const void* k_idx_new, int d_I, const void* k_new,
+                              const void* v_new, int D, const int32_t* cu_q,
+                              const int32_t* ctx_len, const int64_t* cu_ctx, int B, int T,
+                              void* k_idx_cache, int k_dtype, float* k_scale_cache,
+                              void* k_cache, void* v_cache, void* stream) {
+  DSA_REQUIRE(B >= 1 && T >= 1, DSA_ERR_INVALID_ARG, "B and T must be >= 1 (got %d, %d)", B, T);
+  DSA_REQUIRE(ctx_len != nullptr && cu_ctx != nullptr, DSA_ERR_INVALID_ARG,
+              "ctx_len and cu_ctx must not be NULL");
+  DSA_REQUIRE(cu_q != nullptr || T == B, DSA_ERR_INVALID_ARG,
+              "cu_q == NULL means one new token per sequence: T (%d) must equal B (%d)", T, B);
+  if (k_idx_new) {
+    DSA_PTR(k_idx_new, "k_idx_new");
+    DSA_PTR(k_idx_cache, "k_idx_cache");
+    DSA_REQUIRE(d_I == 64 || d_I == 128, DSA_ERR_UNSUPPORTED, "d_I must be 64 or 128 (got %d)",
+                d_I);
+    DSA_REQUIRE(k_dtype == DSA_KEY_BF16 || k_dtype == DSA_KEY_FP8_E4M3, DSA_ERR_INVALID_ARG,
+                "k_dtype must be DSA_KEY_BF16 or DSA_KEY_FP8_E4M3 (got %d)", k_dtype);
+    if (k_dtype == DSA_KEY_FP8_E4M3)
+      DSA_REQUIRE(k_scale_cache != nullptr, DSA_ERR_INVALID_ARG, "an fp8 key cache needs k_scale_cache");
+  }
+  if (k_new || v_new) {
+    DSA_REQUIRE(D == 64 || D == 128, DSA_ERR_UNSUPPORTED, "D must be 64 or 128 (got %d)", D);
+    if (k_new) {
+      DSA_PTR(k_new, "k_new");
+      DSA_PTR(k_cache, "k_cache");
+    }
+    if (v_new) {
+      DSA_PTR(v_new, "v_new");
+      DSA_PTR(v_cache, "v_cache");
+    }
+  }
+  if (!k_idx_new && !k_new && !v_new) return ok();
+  hipError_t e = dsa::launch_cache_append(k_idx_new, d_I, k_new, v_new, D, cu_q, ctx_len, cu_ctx,
+                                          B, T, k_idx_cache, k_dtype, k_scale_cache, k_cache,
+                                          v_cache, static_cast<hipStream_t>(stream));
+  return hip_status(e, "dsa_cache_append");
 }
 
 size_t dsa_sparse_attn_workspace_size(int B, int T, int K, int window, int Hq, int D) {
@@ -384,13 +422,13 @@ dsa_status_t dsa_set_indexer_events(void* start, void* stop) {
   return DSA_OK;
 }
 
-dsa_status_t dsa_layer_decode(const void* q_idx, const void* w, int64_t w_ld, const void* k_idx,
-                              int k_dtype, const float* k_scale, int H_I, int d_I, const void* q,
-                              const void* k_cache, const void* v_cache, const void* gate,
-                              int64_t gate_stride_d, float sm_scale, int Hq, int D, int K,
-                              const int32_t* ctx_len, const int64_t* cu_ctx, int B, int max_ctx,
-                              void* out, int32_t* idx_out, void* ws, size_t ws_bytes,
-                              void* stream) {
+static dsa_status_t layer_decode_impl(
+    const void* q_idx, const void* w, int64_t w_ld, const void* k_idx, int k_dtype,
+    const float* k_scale, int H_I, int d_I, const void* q, const void* k_cache,
+    const void* v_cache, const void* gate, int64_t gate_stride_d, float sm_scale, int Hq, int D,
+    int K, const int32_t* ctx_len, const int64_t* cu_ctx, int B, int max_ctx, void* out,
+    int32_t* idx_out, void* ws, size_t ws_bytes, const dsa::DecodeAppend* app, void* stream,
+    const char* fn) {
   DSA_PTR(q_idx, "q_idx");
   DSA_PTR(w, "w");
   DSA_PTR(k_idx, "k_idx");
@@ -419,6 +457,11 @@ dsa_status_t dsa_layer_decode(const void* q_idx, const void* w, int64_t w_ld, co
               "unsupported attention shape Hq=%d D=%d (supported: 8x64, 64x128)", Hq, D);
   DSA_REQUIRE(K >= 1 && K <= 4096, DSA_ERR_UNSUPPORTED, "K must be in [1, 4096] (got %d)", K);
   DSA_REQUIRE(sm_scale >= 0.f, DSA_ERR_INVALID_ARG, "sm_scale must be >= 0");
+  if (app) {
+    DSA_PTR(app->k_idx_new, "k_idx_new");
+    if (app->k_new) DSA_PTR(app->k_new, "k_new");
+    if (app->v_new) DSA_PTR(app->v_new, "v_new");
+  }
   const size_t need = decode_ws_layout(B, max_ctx, K, Hq, D, nullptr, nullptr);
   DSA_REQUIRE(ws_bytes >= need, DSA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes",
               ws_bytes, need);
@@ -432,7 +475,8 @@ dsa_status_t dsa_layer_decode(const void* q_idx, const void* w, int64_t w_ld, co
   const bool rows = dsa::topk_use_rows(B);
   hipError_t e = dsa::launch_index_decode(q_idx, w, w_ld, k_idx, k_dtype, k_scale, H_I, d_I,
                                           ctx_len, cu_ctx, B, max_ctx, L.scores, L.ld,
-                                          rows ? nullptr : &L.topk, s, t_ev_start, t_ev_stop);
+                                          rows ? nullptr : &L.topk, app, s, t_ev_start,
+                                          t_ev_stop);
   if (e == hipSuccess)
     e = rows ? dsa::launch_topk_rows(L.scores, L.ld, nullptr, ctx_len, B, B, K, idx,
                                      t_topk_counters, s)
@@ -444,7 +488,43 @@ dsa_status_t dsa_layer_decode(const void* q_idx, const void* w, int64_t w_ld, co
                                 sm_scale, Hq, D, nullptr, ctx_len, cu_ctx, B, B, out, nullptr,
                                 L.attn, plan, s);
   }
-  return hip_status(e, "dsa_layer_decode");
+  return hip_status(e, fn);
+}
+
+dsa_status_t dsa_layer_decode(const void* q_idx, const void* w, int64_t w_ld, const void* k_idx,
+                              int k_dtype, const float* k_scale, int H_I, int d_I, const void* q,
+                              const void* k_cache, const void* v_cache, const void* gate,
+                              int64_t gate_stride_d, float sm_scale, int Hq, int D, int K,
+                              const int32_t* ctx_len, const int64_t* cu_ctx, int B, int max_ctx,
+                              void* out, int32_t* idx_out, void* ws, size_t ws_bytes,
+                              void* stream) {
+  return layer_decode_impl(q_idx, w, w_ld, k_idx, k_dtype, k_scale, H_I, d_I, q, k_cache,
+                           v_cache, gate, gate_stride_d, sm_scale, Hq, D, K, ctx_len, cu_ctx, B,
+                           max_ctx, out, idx_out, ws, ws_bytes, nullptr, stream,
+                           "dsa_layer_decode");
+}
+
+dsa_status_t dsa_layer_decode_append(const void* q_idx, const void* w, int64_t w_ld, void* k_idx,
+                                     int k_dtype, float* k_scale, int H_I, int d_I, const void* q,
+                                     void* k_cache, void* v_cache, const void* gate,
+                                     int64_t gate_stride_d, float sm_scale, int Hq, int D, int K,
+                                     const int32_t* ctx_len, const int64_t* cu_ctx, int B,
+                                     int max_ctx, const void* k_idx_new, const void* k_new,
+                                     const void* v_new, void* out, int32_t* idx_out, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  dsa::DecodeAppend app;
+  app.k_idx_new = static_cast<const uint16_t*>(k_idx_new);
+  app.k_new = static_cast<const uint16_t*>(k_new);
+  app.v_new = static_cast<const uint16_t*>(v_new);
+  app.k_idx_cache = static_cast<uint8_t*>(k_idx);
+  app.k_scale_cache = k_scale;
+  app.k_cache = static_cast<uint16_t*>(k_cache);
+  app.v_cache = static_cast<uint16_t*>(v_cache);
+  app.D = D;
+  return layer_decode_impl(q_idx, w, w_ld, k_idx, k_dtype, k_scale, H_I, d_I, q, k_cache,
+                           v_cache, gate, gate_stride_d, sm_scale, Hq, D, K, ctx_len, cu_ctx, B,
+                           max_ctx, out, idx_out, ws, ws_bytes, &app, stream,
+                           "dsa_layer_decode_append");
 }
 
 size_t dsa_layer_decode_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }

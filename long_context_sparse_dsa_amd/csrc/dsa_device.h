@@ -216,6 +216,43 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* scratc
   return r;
 }
 
+// ---------------------------------------------------------------------------
+// fp8 indexer key cache: OCP E4M3FN codes plus one fp32 scale per token (the
+// naive-n0-5-flash page, Key Capabilities: FP8).  The scale is the row's
+// absolute maximum over 448, the format's largest finite value, and each
+// element is rounded to the nearest code, ties to even, from its fp32
+// quotient by the scale clamped to +-448.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fabsf(y);
+  if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.f);  // multiples of 2^-9; 8 -> 0x08
+  const uint32_t au = __float_as_uint(a);
+  int e = (int)(au >> 23) - 127;  // -6 .. 8
+  const uint32_t mant = au & 0x7fffffu;
+  uint32_t m3 = mant >> 20;
+  const uint32_t rest = mant & 0xfffffu;
+  m3 += (uint32_t)(rest > 0x80000u) | ((uint32_t)(rest == 0x80000u) & (m3 & 1u));
+  if (m3 == 8u) {
+    ++e;
+    m3 = 0;
+  }
+  return sign | ((uint32_t)(e + 7) << 3) | m3;
+}
+
+// Quantise one indexer key row held two elements per lane (x0, x1 = row
+// elements 2 l, 2 l + 1): returns the two codes packed in 16 bits (element
+// 2 l in the low byte) and the row's scale.
+__device__ __forceinline__ uint32_t e4m3_row_pair(float x0, float x1, float* sigma_out) {
+  const uint32_t m = wave_max_u32(max(__float_as_uint(fabsf(x0)), __float_as_uint(fabsf(x1))));
+  const float amax = __uint_as_float(m);
+  const float sigma = amax > 0.f ? amax / 448.f : 1.f;
+  const float y0 = fminf(fmaxf(x0 / sigma, -448.f), 448.f);
+  const float y1 = fminf(fmaxf(x1 / sigma, -448.f), 448.f);
+  *sigma_out = sigma;
+  return e4m3_code(y0) | (e4m3_code(y1) << 8);
+}
+
 // Position of query row t: decode (cu_q == nullptr) has one query per
 // sequence at position ctx_len-1; otherwise query i of sequence b sits at
 // ctx_len[b] - n_q[b] + i.

@@ -107,13 +107,22 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 }
 #undef DSA_WAITV
 
-template <int DI, bool FP8, int TILE, bool REPORT, bool DEEP, int WPT>
+// With APPEND the kernel also performs the cache append of each sequence's
+// new token (position p = ctx_len - 1): the wave whose key range holds p
+// loads the new rows before anything else, patches row p of its LDS stage
+// (the new key, quantised for an fp8 cache) before scoring it, and writes
+// the rows into the caches after its last load was consumed (a store in
+// flight would disturb the exact load counts of the waits).  Only this wave
+// uses row p's score; the attention reads K / V in a later kernel.  The key
+// cache is then written by this kernel, so k_idx / k_scale are not
+// declared restrict.
+template <int DI, bool FP8, int TILE, bool REPORT, bool DEEP, int WPT, bool APPEND>
 __global__ __launch_bounds__(64 * WPT) void index_decode_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ w, int64_t w_ld,
-    const uint8_t* __restrict__ k_idx, const float* __restrict__ k_scale, int H_I,
+    const uint8_t* k_idx, const float* k_scale, int H_I,
     const int32_t* __restrict__ ctx_len, const int64_t* __restrict__ cu_ctx,
     float* __restrict__ scores, int64_t ld, RepHeader* hdr, uint32_t* rep_u, int32_t* rep_j,
-    int stride, int topk) {
+    int stride, int topk, DecodeAppend app) {
   constexpr int KS = DI / 16;                       // MFMA k-steps
   constexpr int ROWB = FP8 ? DI : 2 * DI;           // bytes per key row
   constexpr int TW = TILE / WPT;                    // keys per wave
@@ -158,6 +167,24 @@ __global__ __launch_bounds__(64 * WPT) void index_decode_kernel(
   const int l = lane_id(), g = l >> 5, wv = WPT > 1 ? wave_id() : 0;
   const int64_t jw0 = j0 + wv * TW;               // first key of this wave
   uint8_t* const stage = lds + kStageOff + wv * kWaveStage;
+
+  // fused cache append: the wave holding position p loads the new rows first
+  // (the oldest loads, so every later wait covers them)
+  [[maybe_unused]] bool own = false;
+  [[maybe_unused]] int r_p = 0;           // p's row within this wave's range
+  [[maybe_unused]] uint32_t kpair = 0;    // new key elements 2 l, 2 l + 1 (bf16)
+  [[maybe_unused]] u32x4 kvrow = {};      // new K (lanes < D/8) or V chunk
+  if constexpr (APPEND) {
+    own = p >= jw0 && p < jw0 + TW;  // wave-uniform
+    if (own) {
+      r_p = (int)(p - jw0);
+      if (2 * l < DI) kpair = *reinterpret_cast<const uint32_t*>(app.k_idx_new + (int64_t)b * DI + 2 * l);
+      const int nc = app.D / 8;
+      const bool is_v = l >= nc;
+      const uint16_t* src = is_v ? app.v_new : app.k_new;
+      if (l < 2 * nc && src != nullptr) kvrow = ld16(src + (int64_t)b * app.D + 8 * (is_v ? l - nc : l));
+    }
+  }
 
   // A operand: query heads (rows).  Rows past H_I repeat the last head and
   // get head weight 0, so they add nothing.  The query rows and the head
@@ -226,6 +253,14 @@ __global__ __launch_bounds__(64 * WPT) void index_decode_kernel(
       wr[r] = hr < H_I ? bf16_to_f32((uint16_t)v) : 0.f;
     }
   }
+  // the new key as it goes into the cache (fp8: codes + scale), landed with
+  // the query rows
+  [[maybe_unused]] uint32_t kcode = kpair;
+  [[maybe_unused]] float ksig = 1.f;
+  if constexpr (APPEND && FP8) {
+    if (own) kcode = e4m3_row_pair(bf16_to_f32((uint16_t)(kpair & 0xffffu)),
+                                   bf16_to_f32((uint16_t)(kpair >> 16)), &ksig);
+  }
 
   // Score one stage.  `later` (a compile-time constant) is the number of
   // stages issued after this one that are still in flight.  Scores go to
@@ -241,6 +276,21 @@ __global__ __launch_bounds__(64 * WPT) void index_decode_kernel(
       // keep the scheduler from hoisting consumers of loaded registers above
       // the wait (the compiler would then wait for every load instead)
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (APPEND) {
+        // row p of this block (its old contents have landed): the new key
+        if (own && st * SROWS + 32 * bl <= r_p && r_p < st * SROWS + 32 * bl + 32) {
+          uint8_t* bufw = stage + (st % St::kBufs) * St::kBufBytes;
+          const int Rp = r_p - st * SROWS;
+          if (2 * l < DI) {
+            if constexpr (FP8)
+              *reinterpret_cast<uint16_t*>(bufw + St::offset(Rp, l >> 3) + 2 * (l & 7)) =
+                  (uint16_t)kcode;
+            else
+              *reinterpret_cast<uint32_t*>(bufw + St::offset(Rp, l >> 2) + 4 * (l & 3)) = kcode;
+          }
+          if (FP8 && l == 0) *reinterpret_cast<float*>(bufw + St::kKeyBytes + 4 * Rp) = ksig;
+        }
+      }
       const int R = 32 * bl + (l & 31);  // stage row of this lane's key
       u32x4 kv[NLD];
 #pragma unroll
@@ -293,6 +343,25 @@ __global__ __launch_bounds__(64 * WPT) void index_decode_kernel(
     const int jl = wv * TW + 64 * i + l;
     if (jl < n_valid) out_row[jl] = sc_lds[jl];
   }
+  if constexpr (APPEND) {
+    // every load is consumed: the new rows go into the caches
+    if (own) {
+      const int64_t row = row0 + p;
+      if (2 * l < DI) {
+        if constexpr (FP8)
+          *reinterpret_cast<uint16_t*>(app.k_idx_cache + row * DI + 2 * l) = (uint16_t)kcode;
+        else
+          *reinterpret_cast<uint32_t*>(app.k_idx_cache + row * 2 * DI + 4 * l) = kcode;
+      }
+      if (FP8 && l == 0) app.k_scale_cache[row] = ksig;
+      const int nc = app.D / 8;
+      const bool is_v = l >= nc;
+      uint16_t* dst = is_v ? app.v_cache : app.k_cache;
+      const uint16_t* src = is_v ? app.v_new : app.k_new;
+      if (l < 2 * nc && src != nullptr)
+        *reinterpret_cast<u32x4*>(dst + row * app.D + 8 * (is_v ? l - nc : l)) = kvrow;
+    }
+  }
   if constexpr (REPORT) {
     const int64_t nrow = p + 1;
     if (nrow <= kDirectMax) return;  // selected straight from its scores
@@ -316,13 +385,14 @@ __global__ __launch_bounds__(64 * WPT) void index_decode_kernel(
   }
 }
 
-template <int DI, bool FP8, bool REPORT>
+template <int DI, bool FP8, bool REPORT, bool APPEND>
 static hipError_t launch_decode_tiled(int tile, const uint16_t* q, const uint16_t* w,
                                       int64_t w_ld, const uint8_t* k, const float* ks, int H_I,
                                       const int32_t* ctx_len, const int64_t* cu_ctx, int B,
                                       int max_ctx, float* scores, int64_t ld, RepHeader* hdr,
                                       uint32_t* ru, int32_t* rj, int stride, int topk,
-                                      hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+                                      const DecodeAppend& app, hipStream_t st, hipEvent_t ev0,
+                                      hipEvent_t ev1) {
   dim3 grid((max_ctx + tile - 1) / tile, B);
   // Few tiles per CU (256 CUs): two waves per tile, each with a deep
   // pipeline, so more loads are in flight per CU; many tiles: one wave per
@@ -332,17 +402,18 @@ static hipError_t launch_decode_tiled(int tile, const uint16_t* q, const uint16_
 #define DSA_DECODE_LAUNCH(KER, NT)                                                             \
   if (ev0)                                                                                     \
     hipExtLaunchKernelGGL(KER, grid, dim3(NT), 0, st, ev0, ev1, 0, q, w, w_ld, k, ks, H_I,     \
-                          ctx_len, cu_ctx, scores, ld, hdr, ru, rj, stride, topk);             \
+                          ctx_len, cu_ctx, scores, ld, hdr, ru, rj, stride, topk, app);        \
   else                                                                                         \
     hipLaunchKernelGGL(KER, grid, dim3(NT), 0, st, q, w, w_ld, k, ks, H_I, ctx_len, cu_ctx,    \
-                       scores, ld, hdr, ru, rj, stride, topk);
+                       scores, ld, hdr, ru, rj, stride, topk, app);
 #define DSA_DECODE_TILE(T_)                                                                    \
   case T_:                                                                                     \
     if (deep) {                                                                                \
-      DSA_DECODE_LAUNCH((index_decode_kernel<DI, FP8, T_, REPORT, true, (T_ >= 128 ? 2 : 1)>), \
+      DSA_DECODE_LAUNCH((index_decode_kernel<DI, FP8, T_, REPORT, true, (T_ >= 128 ? 2 : 1),   \
+                                             APPEND>),                                         \
                         64 * (T_ >= 128 ? 2 : 1))                                              \
     } else {                                                                                   \
-      DSA_DECODE_LAUNCH((index_decode_kernel<DI, FP8, T_, REPORT, false, 1>), 64)              \
+      DSA_DECODE_LAUNCH((index_decode_kernel<DI, FP8, T_, REPORT, false, 1, APPEND>), 64)      \
     }                                                                                          \
     break;
   switch (tile) {
@@ -365,21 +436,29 @@ static hipError_t launch_decode_any(bool report, int tile, const uint16_t* q, co
                                     int64_t w_ld, const uint8_t* k, const float* ks, int H_I,
                                     const int32_t* ctx_len, const int64_t* cu_ctx, int B,
                                     int max_ctx, float* scores, int64_t ld, RepHeader* hdr,
-                                    uint32_t* ru, int32_t* rj, int stride, int topk, hipStream_t st,
-                                    hipEvent_t ev0, hipEvent_t ev1) {
-  return report ? launch_decode_tiled<DI, FP8, true>(tile, q, w, w_ld, k, ks, H_I, ctx_len,
-                                                     cu_ctx, B, max_ctx, scores, ld, hdr, ru, rj,
-                                                     stride, topk, st, ev0, ev1)
-                : launch_decode_tiled<DI, FP8, false>(tile, q, w, w_ld, k, ks, H_I, ctx_len,
-                                                      cu_ctx, B, max_ctx, scores, ld, hdr, ru,
-                                                      rj, stride, topk, st, ev0, ev1);
+                                    uint32_t* ru, int32_t* rj, int stride, int topk,
+                                    const DecodeAppend* app, hipStream_t st, hipEvent_t ev0,
+                                    hipEvent_t ev1) {
+  const DecodeAppend none = {};
+#define DSA_DECODE_ANY(R_, A_)                                                                 \
+  return launch_decode_tiled<DI, FP8, R_, A_>(tile, q, w, w_ld, k, ks, H_I, ctx_len, cu_ctx, B, \
+                                              max_ctx, scores, ld, hdr, ru, rj, stride, topk,  \
+                                              app ? *app : none, st, ev0, ev1)
+  if (report) {
+    if (app) DSA_DECODE_ANY(true, true);
+    DSA_DECODE_ANY(true, false);
+  }
+  if (app) DSA_DECODE_ANY(false, true);
+  DSA_DECODE_ANY(false, false);
+#undef DSA_DECODE_ANY
 }
 
 hipError_t launch_index_decode(const void* q_idx, const void* w, int64_t w_ld, const void* k_idx,
                                int k_dtype, const float* k_scale, int H_I, int d_I,
                                const int32_t* ctx_len, const int64_t* cu_ctx, int B, int max_ctx,
                                float* scores, int64_t ld, const TopkWs* reports,
-                               hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+                               const DecodeAppend* app, hipStream_t stream, hipEvent_t ev0,
+                               hipEvent_t ev1) {
   const int tile = reports ? reports->tile : 256;
   RepHeader* hdr = reports ? reports->hdr : nullptr;
   uint32_t* ru = reports ? reports->rep_u : nullptr;
@@ -393,16 +472,16 @@ hipError_t launch_index_decode(const void* q_idx, const void* w, int64_t w_ld, c
   const bool rep = reports != nullptr;
   if (d_I == 128 && !fp8)
     return launch_decode_any<128, false>(rep, tile, q, wp, w_ld, k, k_scale, H_I, ctx_len,
-                                         cu_ctx, B, max_ctx, scores, ld, hdr, ru, rj, ntm, topk, stream, ev0, ev1);
+                                         cu_ctx, B, max_ctx, scores, ld, hdr, ru, rj, ntm, topk, app, stream, ev0, ev1);
   if (d_I == 128 && fp8)
     return launch_decode_any<128, true>(rep, tile, q, wp, w_ld, k, k_scale, H_I, ctx_len, cu_ctx,
-                                        B, max_ctx, scores, ld, hdr, ru, rj, ntm, topk, stream, ev0, ev1);
+                                        B, max_ctx, scores, ld, hdr, ru, rj, ntm, topk, app, stream, ev0, ev1);
   if (d_I == 64 && !fp8)
     return launch_decode_any<64, false>(rep, tile, q, wp, w_ld, k, k_scale, H_I, ctx_len, cu_ctx,
-                                        B, max_ctx, scores, ld, hdr, ru, rj, ntm, topk, stream, ev0, ev1);
+                                        B, max_ctx, scores, ld, hdr, ru, rj, ntm, topk, app, stream, ev0, ev1);
   if (d_I == 64 && fp8)
     return launch_decode_any<64, true>(rep, tile, q, wp, w_ld, k, k_scale, H_I, ctx_len, cu_ctx,
-                                       B, max_ctx, scores, ld, hdr, ru, rj, ntm, topk, stream, ev0, ev1);
+                                       B, max_ctx, scores, ld, hdr, ru, rj, ntm, topk, app, stream, ev0, ev1);
   return hipErrorInvalidValue;
 }
 

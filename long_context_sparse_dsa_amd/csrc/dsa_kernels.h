@@ -42,15 +42,29 @@ hipError_t launch_topk_resolve(const float* scores, int64_t ld, const int32_t* c
                                const int32_t* ctx_len, int B, int T, int K, const TopkWs& w,
                                int32_t* idx, uint32_t* stats, hipStream_t stream);
 
+// New rows of a fused decode cache append (one new token per sequence, at
+// position ctx_len - 1): bf16 sources and the caches they go into.
+struct DecodeAppend {
+  const uint16_t* k_idx_new;  // [B, d_I]
+  const uint16_t* k_new;      // [B, D] or null
+  const uint16_t* v_new;      // [B, D] or null
+  uint8_t* k_idx_cache;       // the indexer key cache (bf16 or fp8 codes)
+  float* k_scale_cache;       // fp8 scales, or null
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  int D;
+};
+
 // Indexer, one query per sequence.  When `reports` is non-null the kernel
 // also writes the Top-K candidate reports of its tiles (tile = reports->tile).
+// With `app`, it also appends each sequence's new token to the caches.
 // With events, the dispatch records ev0 / ev1 at the kernel's start / end.
 hipError_t launch_index_decode(const void* q_idx, const void* w, int64_t w_ld, const void* k_idx,
                                int k_dtype, const float* k_scale, int H_I, int d_I,
                                const int32_t* ctx_len, const int64_t* cu_ctx, int B, int max_ctx,
                                float* scores, int64_t ld, const TopkWs* reports,
-                               hipStream_t stream, hipEvent_t ev0 = nullptr,
-                               hipEvent_t ev1 = nullptr);
+                               const DecodeAppend* app, hipStream_t stream,
+                               hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
 // Indexer, a chunk of queries per sequence (dense MFMA contraction).
 hipError_t launch_index_prefill(const void* q_idx, const void* w, int64_t w_ld, const void* k_idx,
@@ -79,5 +93,13 @@ hipError_t launch_sparse_attn(const void* q, const void* k_cache, const void* v_
 // (a sequence without rows in the range gets none; positions are kept).
 hipError_t launch_chunk_desc(const int32_t* cu_q, const int32_t* ctx_len, int B, int t0, int tc,
                              int32_t* cu_q_c, int32_t* ctx_len_c, hipStream_t stream);
+
+// New tokens' rows into the caches: query row t goes to cache row
+// cu_ctx[b] + p_t (indexer key: bf16 copy, or E4M3FN codes + fp32 scale).
+hipError_t launch_cache_append(const void* k_idx_new, int d_I, const void* k_new,
+                               const void* v_new, int D, const int32_t* cu_q,
+                               const int32_t* ctx_len, const int64_t* cu_ctx, int B, int T,
+                               void* k_idx_cache, int k_dtype, float* k_scale_cache,
+                               void* k_cache, void* v_cache, hipStream_t stream);
 
 }  // namespace dsa

@@ -10,6 +10,7 @@
 // i0 .. i0 + n' - 1, which a descriptor with n' queries and context length
 // ctx_len - n_q + i0 + n' places at the same positions.
 #include "dsa_kernels.h"
+#include "dsa_device.h"
 
 namespace dsa {
 
@@ -34,6 +35,75 @@ hipError_t launch_chunk_desc(const int32_t* cu_q, const int32_t* ctx_len, int B,
   const int n = B + 1;
   hipLaunchKernelGGL(chunk_desc_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, cu_q, ctx_len,
                      B, t0, tc, cu_q_c, ctx_len_c);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Cache append: the new tokens' rows go into the caches at their positions
+// (fp8 indexer keys quantised by e4m3_row_pair, dsa_device.h).
+// ---------------------------------------------------------------------------
+// One wave per new token row t, written to cache row cu_ctx[b] + p_t.
+template <int DI, bool FP8>
+__global__ __launch_bounds__(64) void cache_append_kernel(
+    const uint16_t* __restrict__ k_idx_new, const uint16_t* __restrict__ k_new,
+    const uint16_t* __restrict__ v_new, int D, const int32_t* cu_q, const int32_t* ctx_len,
+    const int64_t* cu_ctx, int B, uint8_t* __restrict__ k_idx_cache,
+    float* __restrict__ k_scale_cache, uint16_t* __restrict__ k_cache,
+    uint16_t* __restrict__ v_cache) {
+  const int t = blockIdx.x, l = lane_id();
+  const RowInfo ri = row_info(t, cu_q, ctx_len, B);
+  const int64_t row = cu_ctx[ri.b] + ri.p;
+  if (k_idx_new) {
+    if constexpr (FP8) {
+      // DI / 2 lanes hold two elements each; the rest hold zeros (no effect on the maximum)
+      uint32_t pair = 0;
+      if (2 * l < DI) pair = *reinterpret_cast<const uint32_t*>(k_idx_new + (int64_t)t * DI + 2 * l);
+      float sigma;
+      const uint32_t codes = e4m3_row_pair(bf16_to_f32((uint16_t)(pair & 0xffffu)),
+                                           bf16_to_f32((uint16_t)(pair >> 16)), &sigma);
+      if (2 * l < DI)
+        *reinterpret_cast<uint16_t*>(k_idx_cache + row * DI + 2 * l) = (uint16_t)codes;
+      if (l == 0) k_scale_cache[row] = sigma;
+    } else {
+      constexpr int NC = DI / 8;  // 16-byte chunks of a bf16 row
+      if (l < NC)
+        *reinterpret_cast<u32x4*>(k_idx_cache + row * 2 * DI + 16 * l) =
+            ld16(k_idx_new + (int64_t)t * DI + 8 * l);
+    }
+  }
+  // K and V rows: one 16-byte chunk per lane, K in the low lanes, V above
+  const int nc = D / 8;
+  const bool is_v = l >= nc;
+  const int c = is_v ? l - nc : l;
+  const uint16_t* src = is_v ? v_new : k_new;
+  uint16_t* dst = is_v ? v_cache : k_cache;
+  if (l < 2 * nc && src != nullptr)
+    *reinterpret_cast<u32x4*>(dst + row * D + 8 * c) = ld16(src + (int64_t)t * D + 8 * c);
+}
+
+hipError_t launch_cache_append(const void* k_idx_new, int d_I, const void* k_new,
+                               const void* v_new, int D, const int32_t* cu_q,
+                               const int32_t* ctx_len, const int64_t* cu_ctx, int B, int T,
+                               void* k_idx_cache, int k_dtype, float* k_scale_cache,
+                               void* k_cache, void* v_cache, hipStream_t stream) {
+  auto ki = static_cast<const uint16_t*>(k_idx_new);
+  auto kn = static_cast<const uint16_t*>(k_new);
+  auto vn = static_cast<const uint16_t*>(v_new);
+  auto kic = static_cast<uint8_t*>(k_idx_cache);
+  auto kc = static_cast<uint16_t*>(k_cache);
+  auto vc = static_cast<uint16_t*>(v_cache);
+  const bool fp8 = k_dtype == 1;
+#define DSA_APPEND(DI_, F_)                                                                   \
+  hipLaunchKernelGGL((cache_append_kernel<DI_, F_>), dim3(T), dim3(64), 0, stream, ki, kn, vn, \
+                     D, cu_q, ctx_len, cu_ctx, B, kic, k_scale_cache, kc, vc)
+  if (d_I == 128) {
+    if (fp8) DSA_APPEND(128, true); else DSA_APPEND(128, false);
+  } else if (d_I == 64) {
+    if (fp8) DSA_APPEND(64, true); else DSA_APPEND(64, false);
+  } else {
+    return hipErrorInvalidValue;
+  }
+#undef DSA_APPEND
   return hipGetLastError();
 }
 

@@ -821,3 +821,126 @@ def test_internal_workspaces_on_a_side_stream(dsa):
     ref, _ = oracle.sparse_attn(inp["q"], inp["k_cache"], inp["v_cache"], idx=idx_r,
                                 gate=inp["gate"], ctx_len=inp["ctx_len"], cu_ctx=inp["cu_ctx"])
     check_out(out, ref, ATOL_BF16)
+
+
+# --------------------------------------------------------------------------
+# Cache append (standalone and fused with the decode layer)
+# --------------------------------------------------------------------------
+
+def _append_rows(ctx_lens, n_q):
+    """Cache row of every query row: cu_ctx[b] + p."""
+    cu = np.concatenate([[0], np.cumsum(ctx_lens)])
+    return [int(cu[b] + p) for b, (L, n) in enumerate(zip(ctx_lens, n_q))
+            for p in range(L - n, L)]
+
+
+@pytest.mark.parametrize("key,d_I,lens,nq", [("fp8", 128, [5000, 300, 77], [1, 1, 1]),
+                                             ("bf16", 128, [5000, 300, 77], [1, 1, 1]),
+                                             ("fp8", 128, [6000, 2500], [40, 130]),
+                                             ("fp8", 64, [900, 4000], [3, 1])])
+def test_cache_append_bit_exact(dsa, key, d_I, lens, nq):
+    say(f"cache append {key} d_I={d_I} lens={lens} nq={nq}")
+    w = wl("t", lens, nq, 4 if d_I == 64 else 32, d_I, 64, 128, 64, key_dtype=key, seed=71)
+    d = W.make_inputs(w, device=DEV)
+    T, L_tot = w.T, sum(lens)
+    k_idx_new = W.randn_bf16((T, d_I), 71, "k_idx_new", DEV)
+    k_idx_new[0] *= 300.0                      # a row with a large range
+    k_idx_new[-1] = 0                          # an all-zero row
+    k_new = W.randn_bf16((T, 128), 71, "k_new", DEV)
+    v_new = W.randn_bf16((T, 128), 71, "v_new", DEV)
+    before = {n: d[n].clone() for n in ("k_idx", "k_cache", "v_cache")}
+    ks_before = None if d["k_scale"] is None else d["k_scale"].clone()
+    cu_q = None if all(n == 1 for n in nq) else d["cu_q"]
+    dsa.dsa_cache_append(d["ctx_len"], d["cu_ctx"], k_idx_cache=d["k_idx"], k_idx_new=k_idx_new,
+                         k_scale_cache=d["k_scale"], k_cache=d["k_cache"], k_new=k_new,
+                         v_cache=d["v_cache"], v_new=v_new, cu_q=cu_q)
+    torch.cuda.synchronize()
+    rows = torch.tensor(_append_rows(lens, nq), dtype=torch.int64, device=DEV)
+    mask = torch.ones(L_tot, dtype=torch.bool, device=DEV)
+    mask[rows] = False
+    for n, new in (("k_cache", k_new), ("v_cache", v_new)):
+        assert torch.equal(d[n][rows], new)
+        assert torch.equal(d[n][mask], before[n][mask])
+    if key == "fp8":
+        codes, scales = oracle.quantize_e4m3_rows(cpu(k_idx_new))
+        assert np.array_equal(d["k_idx"][rows].view(torch.uint8).cpu().numpy(), codes)
+        assert np.array_equal(d["k_scale"][rows].cpu().numpy(), scales)
+        assert torch.equal(d["k_scale"][mask], ks_before[mask])
+        assert torch.equal(d["k_idx"].view(torch.uint8)[mask],
+                           before["k_idx"].view(torch.uint8)[mask])
+    else:
+        assert torch.equal(d["k_idx"][rows], k_idx_new)
+        assert torch.equal(d["k_idx"][mask], before["k_idx"][mask])
+
+
+@pytest.mark.parametrize("key,lens,H_I", [
+    ("bf16", [131072], 32),               # deep tiles of two waves; p in the second wave
+    ("fp8", [131072, 40000, 23001], 32),  # p in either wave, ragged
+    ("bf16", [4096, 70000, 2048, 129], 16),
+    ("fp8", [300000, 1 << 20], 32),       # shallow one-wave tiles
+])
+def test_layer_decode_append_fused(dsa, key, lens, H_I):
+    """The fused append-and-decode call leaves the same caches and gives the
+    same bits as dsa_cache_append followed by dsa_layer_decode; the result
+    is also checked against the oracle on the appended caches."""
+    say(f"layer_decode_append {key} lens={lens}")
+    w = wl("t", lens, [1] * len(lens), H_I, 128, 64, 128, 2048, key_dtype=key, seed=72,
+           plant_frac=0.05 if key == "bf16" else 0.0)
+    a = W.make_inputs(w, device=DEV)
+    b = {n: (v.clone() if isinstance(v, torch.Tensor) else v) for n, v in a.items()}
+    k_idx_new = W.randn_bf16((w.B, 128), 72, "k_idx_new", DEV) * 3
+    k_new = W.randn_bf16((w.B, 128), 72, "k_new", DEV)
+    v_new = W.randn_bf16((w.B, 128), 72, "v_new", DEV)
+    L = max(lens)
+    nb = dsa.dsa_layer_decode_workspace_size(w.B, L, w.K, w.Hq, w.D)
+    idx_a = torch.empty(w.B, w.K, dtype=torch.int32, device=DEV)
+    out_a = dsa.dsa_layer_decode_append(a["q_idx"], a["w"], a["k_idx"], a["k_scale"], a["q"],
+                                        a["k_cache"], a["v_cache"], a["gate"], w.K, a["ctx_len"],
+                                        a["cu_ctx"], k_idx_new, k_new, v_new, max_ctx=L,
+                                        idx_out=idx_a,
+                                        ws=torch.full((nb,), 255, dtype=torch.uint8, device=DEV))
+    dsa.dsa_cache_append(b["ctx_len"], b["cu_ctx"], k_idx_cache=b["k_idx"], k_idx_new=k_idx_new,
+                         k_scale_cache=b["k_scale"], k_cache=b["k_cache"], k_new=k_new,
+                         v_cache=b["v_cache"], v_new=v_new)
+    idx_b = torch.empty_like(idx_a)
+    out_b = dsa.dsa_layer_decode(b["q_idx"], b["w"], b["k_idx"], b["k_scale"], b["q"],
+                                 b["k_cache"], b["v_cache"], b["gate"], w.K, b["ctx_len"],
+                                 b["cu_ctx"], max_ctx=L, idx_out=idx_b)
+    torch.cuda.synchronize()
+    for n in ("k_idx", "k_cache", "v_cache"):
+        assert torch.equal(a[n].view(torch.uint8), b[n].view(torch.uint8)), n
+    if key == "fp8":
+        assert torch.equal(a["k_scale"], b["k_scale"])
+    assert torch.equal(idx_a, idx_b)
+    assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16))
+    if sum(lens) <= 300000:
+        cpu_in = {n: cpu(v) if isinstance(v, torch.Tensor) else v for n, v in a.items()}
+        _layer_decode_check(dsa, w, cpu_in, a, atol=ATOL_FP8 if key == "fp8" else ATOL_BF16)
+
+
+def test_layer_decode_append_large_batch_row_sweeps(dsa):
+    """1024 sequences: the fused append in the indexer without Top-K reports."""
+    say("layer_decode_append, 1024 ragged sequences")
+    g = np.random.default_rng(73)
+    lens = [int(x) for x in g.integers(300, 3000, size=1024)]
+    w = wl("t", lens, [1] * len(lens), 4, 64, 8, 64, 256, key_dtype="fp8", seed=73)
+    a = W.make_inputs(w, device=DEV)
+    b = {n: (v.clone() if isinstance(v, torch.Tensor) else v) for n, v in a.items()}
+    k_idx_new = W.randn_bf16((w.B, 64), 73, "k_idx_new", DEV)
+    k_new = W.randn_bf16((w.B, 64), 73, "k_new", DEV)
+    v_new = W.randn_bf16((w.B, 64), 73, "v_new", DEV)
+    L = max(lens)
+    out_a = dsa.dsa_layer_decode_append(a["q_idx"], a["w"], a["k_idx"], a["k_scale"], a["q"],
+                                        a["k_cache"], a["v_cache"], a["gate"], w.K, a["ctx_len"],
+                                        a["cu_ctx"], k_idx_new, k_new, v_new, max_ctx=L)
+    dsa.dsa_cache_append(b["ctx_len"], b["cu_ctx"], k_idx_cache=b["k_idx"], k_idx_new=k_idx_new,
+                         k_scale_cache=b["k_scale"], k_cache=b["k_cache"], k_new=k_new,
+                         v_cache=b["v_cache"], v_new=v_new)
+    out_b = dsa.dsa_layer_decode(b["q_idx"], b["w"], b["k_idx"], b["k_scale"], b["q"],
+                                 b["k_cache"], b["v_cache"], b["gate"], w.K, b["ctx_len"],
+                                 b["cu_ctx"], max_ctx=L)
+    torch.cuda.synchronize()
+    for n in ("k_idx", "k_cache", "v_cache"):
+        assert torch.equal(a[n].view(torch.uint8), b[n].view(torch.uint8)), n
+    assert torch.equal(a["k_scale"], b["k_scale"])
+    assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16))

@@ -57,7 +57,7 @@ def _load():
         lib.orc_e4m3_to_f64.restype = D
         lib.orc_quantize_e4m3_rows.argtypes = [P, L, I, P, P]
         lib.orc_quantize_e4m3_rows.restype = I
-        lib.orc_index_scores.argtypes = [P, P, L, P, I, P, I, I, P, P, P, I, P, L, I]
+        lib.orc_index_scores.argtypes = [P, I, P, P, L, P, I, P, I, I, P, P, P, I, P, L, I]
         lib.orc_index_scores.restype = I
         lib.orc_topk_f64.argtypes = [P, L, P, P, I, I, P, I]
         lib.orc_topk_f64.restype = I
@@ -163,11 +163,18 @@ def quantize_e4m3_rows(k_rows):
 
 
 def index_scores(q_idx, w, k_idx, k_scale=None, ctx_len=None, cu_q=None, cu_ctx=None,
-                 w_ld=None, ld=None, nthreads=None):
-    """Indexer scores [T, ld] in fp64; entries j > p_t are NaN."""
+                 w_ld=None, ld=None, nthreads=None, q_scale=None):
+    """Indexer scores [T, ld] in fp64; entries j > p_t are NaN.  Query heads
+    are bf16, or E4M3FN codes with q_scale fp32 [T, H] (one per query and
+    head)."""
     lib = _load()
-    q = _np(q_idx, np.uint16)
+    q, qdt = _keys(q_idx)
+    if (qdt == KEY_FP8_E4M3) != (q_scale is not None):
+        raise ValueError("E4M3FN query heads take a q_scale, bf16 ones none")
+    qs = None if q_scale is None else _np(q_scale).astype(np.float32)
     T, H, d = q.shape
+    if qs is not None and qs.shape != (T, H):
+        raise ValueError("q_scale must be [T, H]")
     wv = _np(w, np.uint16)
     if w_ld is None:
         w_ld = 0 if wv.ndim == 1 else wv.shape[-1]
@@ -177,8 +184,8 @@ def index_scores(q_idx, w, k_idx, k_scale=None, ctx_len=None, cu_q=None, cu_ctx=
     if ld is None:
         ld = int(ctx_len.max())
     out = np.full((T, ld), np.nan, dtype=np.float64)
-    lib.orc_index_scores(_ptr(q), _ptr(wv), w_ld, _ptr(k), kdt, _ptr(ks), H, d, _ptr(cu_q),
-                         _ptr(ctx_len), _ptr(cu_ctx), B, _ptr(out), ld,
+    lib.orc_index_scores(_ptr(q), qdt, _ptr(qs), _ptr(wv), w_ld, _ptr(k), kdt, _ptr(ks), H, d,
+                         _ptr(cu_q), _ptr(ctx_len), _ptr(cu_ctx), B, _ptr(out), ld,
                          nthreads or default_threads())
     return out
 

@@ -118,16 +118,23 @@ static void parallel_for(int64_t n, int nthreads, range_fn fn, void* ctx) {
 /* ---------------------------------------------------------------------- */
 /* Indexer score ([OSLLM] Architecture Breakdown item 2; [FGSA] 2.1-2.3).  */
 /*                                                                         */
-/*   s[t, j] = sum_h w[t,h] * max(0, sigma_j * sum_d qI[t,h,d] * kI[j,d])  */
+/*   s[t, j] = sum_h w[t,h] * max(0, rho_th * sigma_j *                    */
+/*                                   sum_d qI[t,h,d] * kI[j,d])            */
 /*                                                                         */
 /* for j = 0..p_t.  One indexer key row per position is shared by all      */
 /* heads; positions are not rotated (no RoPE, [FGSA] 2.2); the per-head    */
 /* dot products are combined by a ReLU and a per-query head weight; sigma  */
-/* is the per-token fp32 scale of an fp8 key cache, 1 for bf16 keys.       */
+/* is the per-token fp32 scale of an fp8 key cache, 1 for bf16 keys.  The  */
+/* query heads are bf16 (rho = 1) or, for the fp8 prefill contraction      */
+/* ([N05] Key Capabilities: FP8; [OWD] sections 1 and 3: FP8 activations), */
+/* E4M3FN codes with one fp32 scale rho_th per query and head: like the    */
+/* key scale, it multiplies the dot product of the decoded codes.          */
 /* ---------------------------------------------------------------------- */
 
 typedef struct {
-  const uint16_t* q;   /* [T, H, d] bf16 bits */
+  const void* q;       /* [T, H, d] bf16 bits or E4M3FN codes */
+  int q_dtype;
+  const float* q_scale; /* [T, H] for E4M3FN queries */
   const uint16_t* w;   /* [T, w_ld] bf16 bits */
   int64_t w_ld;
   const void* k;       /* [sum L, d] bf16 bits or e4m3 codes */
@@ -158,6 +165,7 @@ static void score_units(void* vctx, int64_t lo, int64_t hi) {
   double* qd = (double*)malloc(sizeof(double) * (size_t)c->H * c->d);
   double* wd = (double*)malloc(sizeof(double) * (size_t)c->H);
   double* kd = (double*)malloc(sizeof(double) * (size_t)c->d);
+  double* rho = (double*)malloc(sizeof(double) * (size_t)c->H);
   for (int64_t u = lo; u < hi; ++u) {
     int64_t t = u / SCORE_CHUNKS, part = u % SCORE_CHUNKS;
     int b = seq_of_row(c->cu_q, c->B, t);
@@ -165,8 +173,13 @@ static void score_units(void* vctx, int64_t lo, int64_t hi) {
     int64_t j0 = (p + 1) * part / SCORE_CHUNKS, j1 = (p + 1) * (part + 1) / SCORE_CHUNKS;
     for (int h = 0; h < c->H; ++h) {
       wd[h] = orc_bf16_to_f64(c->w[t * c->w_ld + h]);
-      for (int dd = 0; dd < c->d; ++dd)
-        qd[h * c->d + dd] = orc_bf16_to_f64(c->q[(t * c->H + h) * c->d + dd]);
+      rho[h] = c->q_scale ? (double)c->q_scale[t * c->H + h] : 1.0;
+      for (int dd = 0; dd < c->d; ++dd) {
+        const int64_t qi = (t * c->H + h) * c->d + dd;
+        qd[h * c->d + dd] = c->q_dtype == ORC_KEY_BF16
+                                ? orc_bf16_to_f64(((const uint16_t*)c->q)[qi])
+                                : orc_e4m3_to_f64(((const uint8_t*)c->q)[qi]);
+      }
     }
     for (int64_t j = j0; j < j1; ++j) {
       int64_t row = c->cu_ctx[b] + j;
@@ -176,7 +189,7 @@ static void score_units(void* vctx, int64_t lo, int64_t hi) {
       for (int h = 0; h < c->H; ++h) {
         double dot = 0.0;
         for (int dd = 0; dd < c->d; ++dd) dot += qd[h * c->d + dd] * kd[dd];
-        double x = sigma * dot;
+        double x = rho[h] * sigma * dot;
         s += wd[h] * (x > 0.0 ? x : 0.0);
       }
       c->scores[t * c->ld + j] = s;
@@ -185,14 +198,15 @@ static void score_units(void* vctx, int64_t lo, int64_t hi) {
   free(qd);
   free(wd);
   free(kd);
+  free(rho);
 }
 
-int orc_index_scores(const uint16_t* q_idx, const uint16_t* w, int64_t w_ld, const void* k_idx,
-                     int k_dtype, const float* k_scale, int H_I, int d_I, const int32_t* cu_q,
-                     const int32_t* ctx_len, const int64_t* cu_ctx, int B, double* scores,
-                     int64_t ld, int nthreads) {
-  score_ctx c = {q_idx, w, w_ld, k_idx, k_dtype, k_scale, H_I, d_I, cu_q, ctx_len, cu_ctx, B,
-                 scores, ld};
+int orc_index_scores(const void* q_idx, int q_dtype, const float* q_scale, const uint16_t* w,
+                     int64_t w_ld, const void* k_idx, int k_dtype, const float* k_scale, int H_I,
+                     int d_I, const int32_t* cu_q, const int32_t* ctx_len, const int64_t* cu_ctx,
+                     int B, double* scores, int64_t ld, int nthreads) {
+  score_ctx c = {q_idx, q_dtype, q_scale, w, w_ld, k_idx, k_dtype, k_scale, H_I, d_I, cu_q,
+                 ctx_len, cu_ctx, B, scores, ld};
   parallel_for((int64_t)cu_q[B] * SCORE_CHUNKS, nthreads, score_units, &c);
   return 0;
 }
@@ -444,8 +458,8 @@ int orc_layer(const uint16_t* q_idx, const uint16_t* w, int64_t w_ld, const void
   if (!s) s = (double*)malloc(sizeof(double) * (size_t)(T * ld));
   if (!id) id = (int32_t*)malloc(sizeof(int32_t) * (size_t)(T * K));
   if (!s || !id) return 1;
-  orc_index_scores(q_idx, w, w_ld, k_idx, k_dtype, k_scale, H_I, d_I, cu_q, ctx_len, cu_ctx, B, s,
-                   ld, nthreads);
+  orc_index_scores(q_idx, ORC_KEY_BF16, NULL, w, w_ld, k_idx, k_dtype, k_scale, H_I, d_I, cu_q,
+                   ctx_len, cu_ctx, B, s, ld, nthreads);
   orc_topk_f64(s, ld, cu_q, ctx_len, B, K, id, nthreads);
   orc_sparse_attn(q, k_cache, v_cache, id, K, 0, gate, sm_scale, Hq, D, cu_q,
                   ctx_len, cu_ctx, B, out, lse, nthreads);

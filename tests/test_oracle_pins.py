@@ -445,3 +445,74 @@ def test_quantize_error_within_half_a_code_step():
     a = np.abs(y)
     step = np.where(a < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(a, 1e-30))) - 3))
     assert np.all(np.abs(dec - y) <= step / 2 + 1e-12)
+
+
+# --------------------------------------------------------------------------
+# E4M3FN query heads with a per-(query, head) scale
+# --------------------------------------------------------------------------
+
+def _fp8(x):
+    return torch.as_tensor(np.asarray(x, dtype=np.float32)).to(torch.float8_e4m3fn)
+
+
+def test_fp8_queries_with_unit_scale_equal_bf16_queries_of_the_same_values():
+    # every E4M3FN value is a bf16 value: torch's own widening gives the bf16 twin
+    rng = np.random.default_rng(30)
+    q8 = _fp8(rng.standard_normal((3, 4, 16)) * 4)
+    k = bf16(rng.standard_normal((60, 16)))
+    w = bf16(rng.uniform(0, 1, (3, 4)))
+    kw = dict(ctx_len=np.array([60], np.int32), cu_q=np.array([0, 3], np.int32))
+    s8 = oracle.index_scores(q8, w, k, q_scale=np.ones((3, 4), np.float32), **kw)
+    s16 = oracle.index_scores(q8.to(torch.bfloat16), w, k, **kw)
+    assert np.array_equal(s8, s16, equal_nan=True)
+
+
+def test_fp8_query_scale_is_linear_per_head_and_acts_before_the_relu():
+    rng = np.random.default_rng(31)
+    H, d, L = 4, 16, 50
+    q8 = _fp8(rng.standard_normal((1, H, d)) * 3)
+    k8 = _fp8(rng.standard_normal((L, d)))
+    ks = rng.uniform(0.5, 2.0, L).astype(np.float32)
+    w = bf16(rng.uniform(0, 1, (1, H)))
+    one = np.ones((1, H), np.float32)
+    base = oracle.index_scores(q8, w, k8, ks, q_scale=one, **seq(L))[0]
+    # a common positive factor on every head scales the score
+    c = np.float32(1.75)
+    np.testing.assert_allclose(oracle.index_scores(q8, w, k8, ks, q_scale=one * c, **seq(L))[0],
+                               c * base, rtol=1e-13, atol=0)
+    # one head's scale acts like that head's weight (a positive power of two,
+    # exact in the bf16 weight too)
+    rho = one.copy()
+    rho[0, 2] = 4.0
+    w2 = w.float().clone()
+    w2[0, 2] *= 4.0
+    np.testing.assert_allclose(oracle.index_scores(q8, w, k8, ks, q_scale=rho, **seq(L))[0],
+                               oracle.index_scores(q8, bf16(w2.numpy()), k8, ks, q_scale=one,
+                                                   **seq(L))[0], rtol=1e-13, atol=0)
+    # a negative query scale flips the sign inside the ReLU (closed form)
+    neg = oracle.index_scores(q8, w, k8, ks, q_scale=-one, **seq(L))[0]
+    dots = k8.double().numpy() @ q8[0].double().numpy().T          # [L, H]
+    want = (np.maximum(-(ks[:, None].astype(np.float64) * dots), 0) *
+            w[0].double().numpy()[None]).sum(1)
+    np.testing.assert_allclose(neg, want, rtol=1e-12, atol=1e-12)
+
+
+def test_fp8_queries_and_keys_match_a_dense_fp64_formula():
+    # brute force through numpy on decoded values (an independent code path)
+    rng = np.random.default_rng(32)
+    T, H, d, L = 3, 4, 64, 40
+    q8 = _fp8(rng.standard_normal((T, H, d)) * 2)
+    rho = rng.uniform(0.25, 4.0, (T, H)).astype(np.float32)
+    k8 = _fp8(rng.standard_normal((L, d)))
+    ks = rng.uniform(0.5, 2.0, L).astype(np.float32)
+    w = bf16(rng.uniform(0, 1, (T, H)))
+    s = oracle.index_scores(q8, w, k8, ks, q_scale=rho, ctx_len=np.array([L], np.int32),
+                            cu_q=np.array([0, T], np.int32))
+    qd, kd = q8.double().numpy(), k8.double().numpy()
+    dots = np.einsum("thd,jd->thj", qd, kd)
+    x = rho.astype(np.float64)[:, :, None] * ks.astype(np.float64)[None, None, :] * dots
+    ref = (w.double().numpy()[:, :, None] * np.maximum(x, 0)).sum(1)
+    for t in range(T):
+        p = L - T + t
+        np.testing.assert_allclose(s[t, :p + 1], ref[t, :p + 1], rtol=1e-12, atol=1e-12)
+        assert np.all(np.isnan(s[t, p + 1:]))

@@ -39,11 +39,13 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--workload", default="dec128k",
-                    choices=["dec128k", "dec1m_b32_fp8", "prefill8k", "hybrid51"],
+                    choices=["dec128k", "dec1m_b32_fp8", "prefill8k", "prefill8k_fp8",
+                             "hybrid51"],
                     help="dec128k (default, the headline metric); the others time the "
                          "same path on the batched 1M-context fp8 decode, on the 8K "
-                         "prefill chunk, and on one 5:1 SWA/DSA hybrid decode step of a "
-                         "ragged batch of 8")
+                         "prefill chunk (bf16, or fp8 query heads and keys on the fp8 "
+                         "MFMA), and on one 5:1 SWA/DSA hybrid decode step of a ragged "
+                         "batch of 8")
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--rotate", type=int, default=None, help="distinct layer buffer sets")
@@ -54,7 +56,7 @@ def parse():
                          "kernel of known traffic for hardware-counter runs)")
     a = ap.parse_args()
     dflt = {"dec128k": (200, 20, 16), "dec1m_b32_fp8": (20, 3, 1), "prefill8k": (5, 1, 1),
-            "hybrid51": (50, 5, 1)}
+            "prefill8k_fp8": (5, 1, 1), "hybrid51": (50, 5, 1)}
     st, wu, rot = dflt[a.workload]
     a.steps = a.steps if a.steps is not None else st
     a.warmup = a.warmup if a.warmup is not None else wu
@@ -132,7 +134,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    if args.workload == "prefill8k":
+    if args.workload in ("prefill8k", "prefill8k_fp8"):
         result = bench_prefill(args, torch, dsa, W)
     elif args.workload == "hybrid51":
         result = bench_hybrid(args, torch, dsa, W)
@@ -347,7 +349,8 @@ def bench_prefill(args, torch, dsa, W):
     """The 8K prefill chunk: tokens/s of dsa_layer_prefill, and the MFMA
     roofline of its indexer (timed with HIP events around back-to-back
     dsa_index_scores launches on the same stream)."""
-    wl = W.prefill_8k()
+    fp8 = args.workload == "prefill8k_fp8"
+    wl = W.prefill_8k_fp8() if fp8 else W.prefill_8k()
     s = W.make_inputs(wl, device="cuda")
     L = wl.ctx_lens[0]
     ws = torch.empty(dsa.dsa_layer_prefill_workspace_size(wl.B, wl.T, L, wl.K, wl.Hq, wl.D),
@@ -357,7 +360,7 @@ def bench_prefill(args, torch, dsa, W):
     def layer():
         dsa.dsa_layer_prefill(s["q_idx"], s["w"], s["k_idx"], s["k_scale"], s["q"], s["k_cache"],
                               s["v_cache"], s["gate"], wl.K, s["cu_q"], s["ctx_len"], s["cu_ctx"],
-                              max_q=wl.T, max_ctx=L, out=out, ws=ws)
+                              max_q=wl.T, max_ctx=L, out=out, ws=ws, q_scale=s["q_scale"])
 
     def timed(fn, n, warm):
         for _ in range(warm):
@@ -379,13 +382,15 @@ def bench_prefill(args, torch, dsa, W):
 
     def indexer():
         dsa.dsa_index_scores(s["q_idx"], s["w"], s["k_idx"], s["k_scale"], s["ctx_len"],
-                             s["cu_ctx"], cu_q=s["cu_q"], max_q=wl.T, max_ctx=L, scores=scores)
+                             s["cu_ctx"], cu_q=s["cu_q"], max_q=wl.T, max_ctx=L, scores=scores,
+                             q_scale=s["q_scale"])
 
     ms_idx = timed(indexer, args.steps, args.warmup)
     p0 = L - wl.T
     visible = sum(p0 + i + 1 for i in range(wl.T))
     flops = visible * 2 * wl.H_I * wl.d_I
     achieved = flops / (ms_idx * 1e-3) / 1e12
+    peak = 5000.0 if fp8 else 2500.0   # dense fp8 / bf16 MFMA, published
     result = {
         "metric": "DSA layer prefill tokens/s (8K chunk at 131K context; indexer MFMA TFLOP/s)",
         "value": round(wl.T / (ms * 1e-3), 1),
@@ -397,13 +402,13 @@ def bench_prefill(args, torch, dsa, W):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8" if fp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "queries": wl.T, "ctx": L,
                    "indexer": f"{wl.H_I}x{wl.d_I}", "topk": wl.K, "q_heads": wl.Hq,
-                   "head_dim": wl.D},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": 2500.0,
-                     "unit": "TFLOP/s", "frac": round(achieved / 2500.0, 4), "traffic": None,
+                   "head_dim": wl.D, "indexer_queries": wl.q_dtype, "indexer_keys": wl.key_dtype},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
                      "kernel": "index_prefill_kernel", "kernel_us": round(ms_idx * 1e3, 1),
                      "algorithmic_flops_per_launch": flops},
     }
@@ -502,9 +507,18 @@ def cpu_baseline_prefill(s, wl, budget):
     done = 0
     while True:
         i = wl.T - 1 - done
-        oracle.layer(c["q_idx"][i:i + 1], c["w"][i:i + 1], c["k_idx"], c["k_scale"],
-                     c["q"][i:i + 1], c["k_cache"], c["v_cache"], c["gate"][i:i + 1], wl.K,
-                     np.array([L - wl.T + i + 1], dtype=np.int32), nthreads=n)
+        ctx = np.array([L - wl.T + i + 1], dtype=np.int32)
+        if c.get("q_scale") is None:
+            oracle.layer(c["q_idx"][i:i + 1], c["w"][i:i + 1], c["k_idx"], c["k_scale"],
+                         c["q"][i:i + 1], c["k_cache"], c["v_cache"], c["gate"][i:i + 1], wl.K,
+                         ctx, nthreads=n)
+        else:   # fp8 query heads: the same three steps, composed
+            sc = oracle.index_scores(c["q_idx"][i:i + 1], c["w"][i:i + 1], c["k_idx"],
+                                     c["k_scale"], ctx_len=ctx, q_scale=c["q_scale"][i:i + 1],
+                                     nthreads=n)
+            sel = oracle.topk(sc, wl.K, ctx, nthreads=n)
+            oracle.sparse_attn(c["q"][i:i + 1], c["k_cache"], c["v_cache"], idx=sel,
+                               gate=c["gate"][i:i + 1], ctx_len=ctx, nthreads=n)
         done += 1
         el = time.perf_counter() - t0
         if el >= budget or done >= wl.T:

@@ -73,6 +73,18 @@ typedef enum dsa_key_dtype {
   DSA_KEY_FP8_E4M3 = 1  /* indexer keys fp8 e4m3fn [rows, d_I] + fp32 scale [rows] */
 } dsa_key_dtype_t;
 
+/* Indexer query heads: bf16 [T, H_I, d_I] (q_scale NULL), or E4M3FN codes   */
+/* [T, H_I, d_I] with one positive fp32 scale per query and head, q_scale    */
+/* [T, H_I], which multiplies that head's dot product like the key scale.    */
+/* fp8 query heads need an fp8 key cache and run on the fp8 MFMA; they are   */
+/* taken by the prefill contraction (cu_q given), not by the decode kernel.  */
+/* The fp8 MFMA epilogue assumes both scales positive (what a quantiser's    */
+/* absolute-maximum scale is); other scales give unspecified scores.        */
+typedef enum dsa_query_dtype {
+  DSA_QUERY_BF16 = 0,
+  DSA_QUERY_FP8_E4M3 = 1
+} dsa_query_dtype_t;
+
 /* Library version string, e.g. "dsa-mi355x 0.1.0 gfx950".  Never fails. */
 const char* dsa_version(void);
 
@@ -87,11 +99,13 @@ const char* dsa_last_error(void);
 /* (32 heads x 128 dim); the naive-n0-5-flash page (16-head indexer).        */
 /*                                                                           */
 /*   scores[t, j] = sum_h w[t*w_ld + h] *                                    */
-/*                  max(0, sigma_j * sum_d q_idx[t,h,d] * k_idx[row(j), d])  */
-/* for j = 0..p_t, with sigma_j = k_scale[row(j)] for fp8 keys, 1 for bf16.  */
+/*                  max(0, rho_th * sigma_j *                                */
+/*                         sum_d q_idx[t,h,d] * k_idx[row(j), d])            */
+/* for j = 0..p_t, with sigma_j = k_scale[row(j)] for fp8 keys, 1 for bf16, */
+/* and rho_th = q_scale[t, h] for fp8 query heads, 1 for bf16.               */
 /* Entries j > p_t of each score row are left untouched.                     */
 /*                                                                           */
-/*   q_idx   bf16 [T, H_I, d_I]                                              */
+/*   q_idx   [T, H_I, d_I], bf16 or E4M3FN codes (q_dtype, q_scale: above)   */
 /*   w       bf16 head weights; row t at w + t*w_ld (w_ld == 0: one row     */
 /*           shared by every query, i.e. static per-layer weights)           */
 /*   k_idx   indexer key cache [sum ctx_len, d_I], bf16 or fp8 e4m3fn        */
@@ -99,7 +113,8 @@ const char* dsa_last_error(void);
 /*   scores  fp32 [T, ld], ld >= max_ctx                                     */
 /* Supported (H_I, d_I): (4,64), (16,128), (32,128).                         */
 /* ------------------------------------------------------------------------ */
-dsa_status_t dsa_index_scores(const void* q_idx, const void* w, int64_t w_ld, const void* k_idx,
+dsa_status_t dsa_index_scores(const void* q_idx, int q_dtype, const float* q_scale,
+                              const void* w, int64_t w_ld, const void* k_idx,
                               int k_dtype, const float* k_scale, int H_I, int d_I,
                               const int32_t* cu_q, const int32_t* ctx_len, const int64_t* cu_ctx,
                               int B, int T, int max_q, int max_ctx, float* scores, int64_t ld,
@@ -268,8 +283,9 @@ dsa_status_t dsa_set_topk_counters(uint32_t* counters);
 
 /* ------------------------------------------------------------------------ */
 /* Whole layer, prefill: a chunk of new queries per sequence (cu_q given).   */
-/* Same steps; the indexer runs as a dense bf16 MFMA contraction of the      */
-/* chunk's query heads against the key cache with causal tile skipping.      */
+/* Same steps; the indexer runs as a dense MFMA contraction of the chunk's   */
+/* query heads against the key cache with causal tile skipping (bf16, or fp8 */
+/* with fp8 query heads and keys).                                           */
 /*                                                                           */
 /* Workspace: dsa_layer_prefill_workspace_size() bytes run the T query rows */
 /* in one pass (the fp32 score array alone is T x max_ctx).  Any smaller     */
@@ -283,7 +299,8 @@ dsa_status_t dsa_set_topk_counters(uint32_t* counters);
 /* ------------------------------------------------------------------------ */
 size_t dsa_layer_prefill_workspace_size(int B, int T, int max_ctx, int K, int Hq, int D);
 size_t dsa_layer_prefill_min_workspace_size(int B, int max_ctx, int K, int Hq, int D);
-dsa_status_t dsa_layer_prefill(const void* q_idx, const void* w, int64_t w_ld, const void* k_idx,
+dsa_status_t dsa_layer_prefill(const void* q_idx, int q_dtype, const float* q_scale,
+                               const void* w, int64_t w_ld, const void* k_idx,
                                int k_dtype, const float* k_scale, int H_I, int d_I,
                                const void* q, const void* k_cache, const void* v_cache,
                                const void* gate, int64_t gate_stride_d, float sm_scale, int Hq,

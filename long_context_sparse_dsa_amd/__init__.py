@@ -64,7 +64,7 @@ def load(path: str | None = None):
                      ctypes.c_size_t)
     lib.dsa_version.restype = ctypes.c_char_p
     lib.dsa_last_error.restype = ctypes.c_char_p
-    lib.dsa_index_scores.argtypes = [P, P, L, P, I, P, I, I, P, P, P, I, I, I, I, P, L, P]
+    lib.dsa_index_scores.argtypes = [P, I, P, P, L, P, I, P, I, I, P, P, P, I, I, I, I, P, L, P]
     lib.dsa_cache_append.argtypes = [P, I, P, P, I, P, P, P, I, I, P, I, P, P, P, P]
     lib.dsa_topk_workspace_size.argtypes = [I, I, I, I]
     lib.dsa_topk_workspace_size.restype = S
@@ -81,8 +81,8 @@ def load(path: str | None = None):
     lib.dsa_layer_prefill_workspace_size.restype = S
     lib.dsa_layer_prefill_min_workspace_size.argtypes = [I, I, I, I, I]
     lib.dsa_layer_prefill_min_workspace_size.restype = S
-    lib.dsa_layer_prefill.argtypes = [P, P, L, P, I, P, I, I, P, P, P, P, L, F, I, I, I, P, P, P,
-                                      I, I, I, I, P, P, P, S, P]
+    lib.dsa_layer_prefill.argtypes = [P, I, P, P, L, P, I, P, I, I, P, P, P, P, L, F, I, I, I, P,
+                                      P, P, I, I, I, I, P, P, P, S, P]
     lib.dsa_layer_decode_append.argtypes = [P, P, L, P, I, P, I, I, P, P, P, P, L, F, I, I, I,
                                             P, P, I, I, P, P, P, P, P, P, S, P]
     lib.dsa_layer_decode_noalloc_max_bytes.argtypes = []
@@ -224,10 +224,25 @@ def dsa_last_error() -> str:
     return load().dsa_last_error().decode()
 
 
+def _check_q(q_idx, q_scale):
+    """Query-head dtype code; fp8 (E4M3FN) heads carry q_scale fp32 [T, H_I]."""
+    _check(q_idx, "q_idx", KEYS, 3)
+    _check(q_scale, "q_scale", (torch.float32,), 2)
+    if q_idx.dtype == torch.float8_e4m3fn:
+        if q_scale is None:
+            raise ValueError("fp8 query heads need q_scale [T, H_I]")
+        _shape(q_scale, "q_scale", q_idx.shape[:2])
+        return 1
+    if q_scale is not None:
+        raise ValueError("bf16 query heads take no q_scale")
+    return 0
+
+
 def dsa_index_scores(q_idx, w, k_idx, k_scale, ctx_len, cu_ctx, cu_q=None, max_q=None,
-                     max_ctx=None, scores=None, w_ld=None, stream=None):
-    """Indexer scores [T, ld] fp32 (entries past each query's position untouched)."""
-    _check(q_idx, "q_idx", BF16, 3)
+                     max_ctx=None, scores=None, w_ld=None, stream=None, q_scale=None):
+    """Indexer scores [T, ld] fp32 (entries past each query's position untouched).
+    q_idx is bf16, or E4M3FN with q_scale [T, H_I] (prefill contraction, fp8 keys)."""
+    qdt = _check_q(q_idx, q_scale)
     _check(w, "w", BF16)
     _check(k_idx, "k_idx", KEYS, 2)
     _check(k_scale, "k_scale", (torch.float32,), 1)
@@ -248,9 +263,9 @@ def dsa_index_scores(q_idx, w, k_idx, k_scale, ctx_len, cu_ctx, cu_q=None, max_q
         raise ValueError(f"scores: shape {tuple(scores.shape)}, need ({T}, >= {max_ctx})")
     if w_ld is None:
         w_ld = 0 if w.dim() == 1 else w.shape[-1]
-    _call("dsa_index_scores", _p(q_idx), _p(w), w_ld, _p(k_idx), _key_dtype(k_idx), _p(k_scale),
-          H_I, d_I, _p(cu_q), _p(ctx_len), _p(cu_ctx), B, T, max_q or 1, max_ctx, _p(scores),
-          scores.stride(0), _stream(stream))
+    _call("dsa_index_scores", _p(q_idx), qdt, _p(q_scale), _p(w), w_ld, _p(k_idx),
+          _key_dtype(k_idx), _p(k_scale), H_I, d_I, _p(cu_q), _p(ctx_len), _p(cu_ctx), B, T,
+          max_q or 1, max_ctx, _p(scores), scores.stride(0), _stream(stream))
     return scores
 
 
@@ -398,8 +413,8 @@ def dsa_layer_decode_workspace_size(B, max_ctx, K, Hq, D) -> int:
 
 
 def _layer_checks(q_idx, w, k_idx, k_scale, q, k_cache, v_cache, gate, ctx_len, cu_ctx, cu_q,
-                  idx_out, K):
-    _check(q_idx, "q_idx", BF16, 3)
+                  idx_out, K, q_dtypes=BF16):
+    _check(q_idx, "q_idx", q_dtypes, 3)
     _check(w, "w", BF16)
     _check(k_idx, "k_idx", KEYS, 2)
     _check(k_scale, "k_scale", (torch.float32,), 1)
@@ -568,12 +583,14 @@ def dsa_layer_prefill_min_workspace_size(B, max_ctx, K, Hq, D) -> int:
 
 def dsa_layer_prefill(q_idx, w, k_idx, k_scale, q, k_cache, v_cache, gate, K, cu_q, ctx_len,
                       cu_ctx, max_q=None, max_ctx=None, sm_scale=0.0, out=None, idx_out=None,
-                      ws=None, w_ld=None, stream=None):
+                      ws=None, w_ld=None, stream=None, q_scale=None):
     """Whole layer for a chunk of new queries per sequence; returns out bf16 [T, Hq, D].
     A caller workspace smaller than the one-pass size (but at least the
-    minimum) makes the library run the rows in sub-chunks."""
+    minimum) makes the library run the rows in sub-chunks.  q_idx is bf16, or
+    E4M3FN with q_scale [T, H_I] (fp8 MFMA indexer; needs fp8 keys)."""
+    qdt = _check_q(q_idx, q_scale)
     B, T, H_I, d_I, Hq, D, gs = _layer_checks(q_idx, w, k_idx, k_scale, q, k_cache, v_cache,
-                                              gate, ctx_len, cu_ctx, cu_q, idx_out, K)
+                                              gate, ctx_len, cu_ctx, cu_q, idx_out, K, KEYS)
     max_ctx = _host_max(ctx_len, max_ctx)
     max_q = _host_max_q(cu_q, max_q)
     if out is None:
@@ -585,7 +602,8 @@ def dsa_layer_prefill(q_idx, w, k_idx, k_scale, q, k_cache, v_cache, gate, K, cu
         ws = _workspace(dsa_layer_prefill_workspace_size(B, T, max_ctx, K, Hq, D), q.device)
     if w_ld is None:
         w_ld = 0 if w.dim() == 1 else w.shape[-1]
-    _call("dsa_layer_prefill", _p(q_idx), _p(w), w_ld, _p(k_idx), _key_dtype(k_idx),
+    _call("dsa_layer_prefill", _p(q_idx), qdt, _p(q_scale), _p(w), w_ld, _p(k_idx),
+          _key_dtype(k_idx),
           _p(k_scale), H_I, d_I, _p(q), _p(k_cache), _p(v_cache), _p(gate), gs, float(sm_scale),
           Hq, D, K, _p(cu_q), _p(ctx_len), _p(cu_ctx), B, T, max_q, max_ctx, _p(out), _p(idx_out),
           _p(ws), ws.numel(), _stream(stream))

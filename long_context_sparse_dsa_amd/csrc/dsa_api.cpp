@@ -124,6 +124,19 @@ size_t prefill_ws_layout(int T, int max_ctx, int K, int Hq, int D, char* base, D
   return s_scores + s_rep + s_idx + s_attn;
 }
 
+dsa_status_t check_query_dtype(int q_dtype, const float* q_scale, int k_dtype) {
+  DSA_REQUIRE(q_dtype == DSA_QUERY_BF16 || q_dtype == DSA_QUERY_FP8_E4M3, DSA_ERR_INVALID_ARG,
+              "q_dtype must be DSA_QUERY_BF16 or DSA_QUERY_FP8_E4M3 (got %d)", q_dtype);
+  if (q_dtype == DSA_QUERY_FP8_E4M3) {
+    DSA_REQUIRE(q_scale != nullptr, DSA_ERR_INVALID_ARG, "fp8 query heads need q_scale");
+    DSA_REQUIRE(k_dtype == DSA_KEY_FP8_E4M3, DSA_ERR_UNSUPPORTED,
+                "fp8 query heads need an fp8 key cache (the fp8 MFMA takes both operands)");
+  } else {
+    DSA_REQUIRE(q_scale == nullptr, DSA_ERR_INVALID_ARG, "bf16 query heads take no q_scale");
+  }
+  return DSA_OK;
+}
+
 // Device descriptor of one prefill sub-chunk: cu_q [B+1] and ctx_len [B]
 // (int32), each 256-byte aligned.
 size_t prefill_chunk_desc_bytes(int B) {
@@ -140,16 +153,17 @@ namespace {
 // Indexer -> Top-K -> attention for T query rows in the workspace carved as
 // L for T_plan >= T rows: the Top-K path and the attention split plan are
 // those of T_plan, so the carve holds their scratch for any T <= T_plan.
-hipError_t prefill_pass(const void* q_idx, const void* w, int64_t w_ld, const void* k_idx,
-                        int k_dtype, const float* k_scale, int H_I, int d_I, const void* q,
+hipError_t prefill_pass(const void* q_idx, int q_dtype, const float* q_scale, const void* w,
+                        int64_t w_ld, const void* k_idx, int k_dtype, const float* k_scale,
+                        int H_I, int d_I, const void* q,
                         const void* k_cache, const void* v_cache, const void* gate, int gstride,
                         float sm_scale, int Hq, int D, int K, const int32_t* cu_q,
                         const int32_t* ctx_len, const int64_t* cu_ctx, int B, int T, int T_plan,
                         int max_q, int max_ctx, void* out, int32_t* idx, const DecodeWs& L,
                         hipStream_t s) {
-  hipError_t e = dsa::launch_index_prefill(q_idx, w, w_ld, k_idx, k_dtype, k_scale, H_I, d_I,
-                                           cu_q, ctx_len, cu_ctx, B, max_q, max_ctx, L.scores,
-                                           L.ld, s);
+  hipError_t e = dsa::launch_index_prefill(q_idx, q_dtype, q_scale, w, w_ld, k_idx, k_dtype,
+                                           k_scale, H_I, d_I, cu_q, ctx_len, cu_ctx, B, max_q,
+                                           max_ctx, L.scores, L.ld, s);
   if (e == hipSuccess && dsa::topk_use_rows(T_plan)) {
     e = dsa::launch_topk_rows(L.scores, L.ld, cu_q, ctx_len, B, T, K, idx, t_topk_counters, s);
   } else {
@@ -251,12 +265,19 @@ const char* dsa_version(void) { return "dsa-mi355x 0.1.0 gfx950"; }
 
 const char* dsa_last_error(void) { return g_err; }
 
-dsa_status_t dsa_index_scores(const void* q_idx, const void* w, int64_t w_ld, const void* k_idx,
+dsa_status_t dsa_index_scores(const void* q_idx, int q_dtype, const float* q_scale,
+                              const void* w, int64_t w_ld, const void* k_idx,
                               int k_dtype, const float* k_scale, int H_I, int d_I,
                               const int32_t* cu_q, const int32_t* ctx_len, const int64_t* cu_ctx,
                               int B, int T, int max_q, int max_ctx, float* scores, int64_t ld,
                               void* stream) {
   DSA_PTR(q_idx, "q_idx");
+  {
+    const dsa_status_t qs = check_query_dtype(q_dtype, q_scale, k_dtype);
+    if (qs != DSA_OK) return qs;
+  }
+  DSA_REQUIRE(q_dtype == DSA_QUERY_BF16 || cu_q != nullptr, DSA_ERR_UNSUPPORTED,
+              "fp8 query heads are scored by the prefill contraction: pass cu_q");
   DSA_PTR(w, "w");
   DSA_PTR(k_idx, "k_idx");
   DSA_PTR(scores, "scores");
@@ -280,8 +301,8 @@ dsa_status_t dsa_index_scores(const void* q_idx, const void* w, int64_t w_ld, co
     e = dsa::launch_index_decode(q_idx, w, w_ld, k_idx, k_dtype, k_scale, H_I, d_I, ctx_len,
                                  cu_ctx, B, max_ctx, scores, ld, nullptr, nullptr, s);
   else
-    e = dsa::launch_index_prefill(q_idx, w, w_ld, k_idx, k_dtype, k_scale, H_I, d_I, cu_q,
-                                  ctx_len, cu_ctx, B, max_q, max_ctx, scores, ld, s);
+    e = dsa::launch_index_prefill(q_idx, q_dtype, q_scale, w, w_ld, k_idx, k_dtype, k_scale, H_I,
+                                  d_I, cu_q, ctx_len, cu_ctx, B, max_q, max_ctx, scores, ld, s);
   return hip_status(e, "dsa_index_scores");
 }
 
@@ -567,7 +588,8 @@ size_t dsa_layer_prefill_min_workspace_size(int B, int max_ctx, int K, int Hq, i
   return prefill_chunk_desc_bytes(B) + prefill_ws_layout(1, max_ctx, K, Hq, D, nullptr, nullptr);
 }
 
-dsa_status_t dsa_layer_prefill(const void* q_idx, const void* w, int64_t w_ld, const void* k_idx,
+dsa_status_t dsa_layer_prefill(const void* q_idx, int q_dtype, const float* q_scale,
+                               const void* w, int64_t w_ld, const void* k_idx,
                                int k_dtype, const float* k_scale, int H_I, int d_I,
                                const void* q, const void* k_cache, const void* v_cache,
                                const void* gate, int64_t gate_stride_d, float sm_scale, int Hq,
@@ -585,6 +607,10 @@ dsa_status_t dsa_layer_prefill(const void* q_idx, const void* w, int64_t w_ld, c
   if (gate) DSA_PTR(gate, "gate");
   if (idx_out) DSA_PTR(idx_out, "idx_out");
   DSA_REQUIRE(cu_q != nullptr, DSA_ERR_INVALID_ARG, "prefill needs cu_q");
+  {
+    const dsa_status_t qs = check_query_dtype(q_dtype, q_scale, k_dtype);
+    if (qs != DSA_OK) return qs;
+  }
   DSA_REQUIRE(gate_stride_d == 0 || gate_stride_d == 1, DSA_ERR_INVALID_ARG,
               "gate_stride_d must be 1 (elementwise gate) or 0 (one gate per head), got %lld",
               (long long)gate_stride_d);
@@ -610,7 +636,8 @@ dsa_status_t dsa_layer_prefill(const void* q_idx, const void* w, int64_t w_ld, c
   if (ws_bytes >= full) {
     DecodeWs L;
     prefill_ws_layout(T, max_ctx, K, Hq, D, static_cast<char*>(ws), &L);
-    const hipError_t e = prefill_pass(q_idx, w, w_ld, k_idx, k_dtype, k_scale, H_I, d_I, q,
+    const hipError_t e = prefill_pass(q_idx, q_dtype, q_scale, w, w_ld, k_idx, k_dtype, k_scale,
+                                      H_I, d_I, q,
                                       k_cache, v_cache, gate, (int)gate_stride_d, sm_scale, Hq, D,
                                       K, cu_q, ctx_len, cu_ctx, B, T, T, max_q, max_ctx, out,
                                       idx_out ? idx_out : L.idx, L, s);
@@ -640,7 +667,8 @@ dsa_status_t dsa_layer_prefill(const void* q_idx, const void* w, int64_t w_ld, c
     if (e != hipSuccess) break;
     // every per-row input and output is row-major in the query rows
     e = prefill_pass(
-        static_cast<const uint16_t*>(q_idx) + (int64_t)t0 * H_I * d_I,
+        static_cast<const uint8_t*>(q_idx) + (int64_t)t0 * H_I * d_I * (q_dtype ? 1 : 2),
+        q_dtype, q_scale ? q_scale + (int64_t)t0 * H_I : nullptr,
         static_cast<const uint16_t*>(w) + (int64_t)t0 * w_ld, w_ld, k_idx, k_dtype, k_scale,
         H_I, d_I, static_cast<const uint16_t*>(q) + (int64_t)t0 * Hq * D, k_cache, v_cache,
         gate ? static_cast<const uint16_t*>(gate) + t0 * gate_row : nullptr, (int)gate_stride_d,

@@ -29,6 +29,15 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef int v8i32 __attribute__((ext_vector_type(8)));
+
+// fp8 MFMA (E4M3FN x E4M3FN, 32x32x64, fp32 accumulation).  Operands: 32
+// bytes per lane, row / column l % 32, k slots 32 (l / 32) + 0..31; C as in
+// mfma32.  Zero scale operands select the unscaled instruction.
+__device__ __forceinline__ f32x16 mfma_f8(const v8i32& a, const v8i32& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 // float -> bf16 bits, round to nearest even (NaN kept quiet).

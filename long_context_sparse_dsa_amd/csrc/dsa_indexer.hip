@@ -533,12 +533,26 @@ struct PrefillShape {
   }
 };
 
-template <int DI, int HI, bool FP8, int MB, int NCW, int NBUF>
+// Q8 (fp8 keys only): the query heads are E4M3FN codes with one fp32 scale
+// per (query, head), and the contraction runs on the fp8 MFMA
+// (v_mfma_f32_32x32x64_f8f6f4, two k-steps of 64 dims at d_I = 128).  Its
+// operands are 32 bytes per lane: row / column l % 32, k slots 32 (l / 32)
+// + e (checked on the GPU); k-step s of lane half g takes the key row's
+// 16-byte chunks 4 s + g and 4 s + 2 + g (the chunks the fp8-key B reads
+// already fetch) and the query row's same bytes.  With positive scales
+// (the quantiser's amax / 448) the epilogue folds the query scale into the
+// head weight and applies the key scale once per key after the head sum:
+// s = sigma_j * sum_h (w_h rho_h) ReLU(acc_h).
+template <int DI, int HI, bool FP8, int MB, int NCW, int NBUF, bool Q8>
 __global__ __launch_bounds__(64 * (NCW + 1)) void index_prefill_kernel(
-    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ w, int64_t w_ld,
-    const uint8_t* __restrict__ k_idx, const float* __restrict__ k_scale,
-    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ ctx_len,
-    const int64_t* __restrict__ cu_ctx, float* __restrict__ scores, int64_t ld, int nsplit) {
+    const void* __restrict__ q_idx_v, const float* __restrict__ q_scale,
+    const uint16_t* __restrict__ w, int64_t w_ld, const uint8_t* __restrict__ k_idx,
+    const float* __restrict__ k_scale, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ ctx_len, const int64_t* __restrict__ cu_ctx,
+    float* __restrict__ scores, int64_t ld, int nsplit) {
+  static_assert(!Q8 || FP8, "fp8 query heads need fp8 keys");
+  const uint16_t* __restrict__ q_idx = static_cast<const uint16_t*>(q_idx_v);
+  const uint8_t* __restrict__ q8 = static_cast<const uint8_t*>(q_idx_v);
   using PS = PrefillShape<DI, HI, FP8>;
   constexpr int KT = PS::KT;
   constexpr int KS = DI / 16;
@@ -598,21 +612,36 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void index_prefill_kernel(
   }
   // ---------------- compute waves ----------------
   const int wq0 = qbase + wv * QW;
-  bf16x8 qa[MB][KS];
+  constexpr int KS8 = DI / 64;  // fp8 MFMA k-steps
+  bf16x8 qa[Q8 ? 1 : MB][Q8 ? 1 : KS];
+  v8i32 qa8[Q8 ? MB : 1][Q8 ? KS8 : 1];
   float wr[MB][16];
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
     const int i = l & 31;
     const int qq = min(wq0 + m * QPB + RowMap<HI>::query_of_row(i), nq - 1);
     const int hh = RowMap<HI>::head_of_row(i);
+    if constexpr (Q8) {
+      const uint8_t* qr = q8 + ((t0 + qq) * HI + hh) * DI;
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
-      qa[m][s] = as_bf16x8(ld16(q_idx + ((t0 + qq) * HI + hh) * DI + kslot_dim<FP8>(s, g)));
+      for (int s = 0; s < KS8; ++s) {
+        const u32x4 lo = ld16(qr + 16 * (4 * s + g)), hi = ld16(qr + 16 * (4 * s + 2 + g));
+        qa8[m][s] = v8i32{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                          (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        qa[m][s] = as_bf16x8(ld16(q_idx + ((t0 + qq) * HI + hh) * DI + kslot_dim<FP8>(s, g)));
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int ir = 8 * (r >> 2) + 4 * g + (r & 3);
       const int q2 = wq0 + m * QPB + RowMap<HI>::query_of_row(ir);
-      const float wv2 = bf16_to_f32(w[(t0 + min(q2, nq - 1)) * w_ld + RowMap<HI>::head_of_row(ir)]);
+      const int64_t qrow = t0 + min(q2, nq - 1);
+      const int head = RowMap<HI>::head_of_row(ir);
+      float wv2 = bf16_to_f32(w[qrow * w_ld + head]);
+      if constexpr (Q8) wv2 *= q_scale[qrow * HI + head];
       wr[m][r] = q2 < nq ? wv2 : 0.f;
     }
   }
@@ -633,12 +662,21 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void index_prefill_kernel(
       for (int c4 = 0; c4 < NSUM; ++c4) {
         constexpr int RN = 16 / NSUM;  // heads per sum
         float s0 = 0.f, s1 = 0.f;
+        if constexpr (Q8) {
 #pragma unroll
-        for (int r = 0; r < RN; r += 2) {
-          s0 += wr[m][RN * c4 + r] * relu(sgp * acc[p][m][RN * c4 + r]);
-          s1 += wr[m][RN * c4 + r + 1] * relu(sgp * acc[p][m][RN * c4 + r + 1]);
+          for (int r = 0; r < RN; r += 2) {
+            s0 += wr[m][RN * c4 + r] * relu(acc[p][m][RN * c4 + r]);
+            s1 += wr[m][RN * c4 + r + 1] * relu(acc[p][m][RN * c4 + r + 1]);
+          }
+          sum[m][c4] = sgp * (s0 + s1);
+        } else {
+#pragma unroll
+          for (int r = 0; r < RN; r += 2) {
+            s0 += wr[m][RN * c4 + r] * relu(sgp * acc[p][m][RN * c4 + r]);
+            s1 += wr[m][RN * c4 + r + 1] * relu(sgp * acc[p][m][RN * c4 + r + 1]);
+          }
+          sum[m][c4] = s0 + s1;
         }
-        sum[m][c4] = s0 + s1;
       }
   };
   // causal store of a block's scores (lanes of a half-wave: 32 consecutive
@@ -686,8 +724,19 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void index_prefill_kernel(
       const u32x4(&kv)[NLD] = kvs[n];
       const float sgn = sgs[n];
       // MFMAs of this block (the first k-step from a zero accumulator)
+      if constexpr (Q8) {
 #pragma unroll
-      for (int c = 0; c < NLD; ++c) {
+        for (int s8 = 0; s8 < KS8; ++s8) {
+          const u32x4 lo = kv[2 * s8], hi = kv[2 * s8 + 1];
+          const v8i32 b8 = v8i32{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                 (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+#pragma unroll
+          for (int m = 0; m < MB; ++m)
+            acc[n][m] = mfma_f8(qa8[m][s8], b8, s8 == 0 ? f32x16{} : acc[n][m]);
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < (Q8 ? 0 : NLD); ++c) {
         if constexpr (FP8) {
           const bf16x8 b0 = fp8x8_to_bf16x8(kv[c][0], kv[c][1]);
           const bf16x8 b1 = fp8x8_to_bf16x8(kv[c][2], kv[c][3]);
@@ -710,9 +759,9 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void index_prefill_kernel(
       // MFMA followed by a few of the reduction's vector instructions
       if (n == 0) __builtin_amdgcn_sched_group_barrier(0x100, NB * NLD, 0);
 #pragma unroll
-      for (int k = 0; k < KS * MB; ++k) {
+      for (int k = 0; k < (Q8 ? KS8 : KS) * MB; ++k) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, Q8 ? 18 : 5, 0);
       }
       // the sums exist here, not only inside the stores' branches
 #pragma unroll
@@ -731,8 +780,8 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void index_prefill_kernel(
   }
 }
 
-template <int DI, int HI, bool FP8>
-static hipError_t launch_prefill_t(const uint16_t* q, const uint16_t* w, int64_t w_ld,
+template <int DI, int HI, bool FP8, bool Q8>
+static hipError_t launch_prefill_t(const void* q, const float* qs, const uint16_t* w, int64_t w_ld,
                                    const uint8_t* k, const float* ks, const int32_t* cu_q,
                                    const int32_t* ctx_len, const int64_t* cu_ctx, int B,
                                    int max_q, int max_ctx, float* scores, int64_t ld,
@@ -749,29 +798,33 @@ static hipError_t launch_prefill_t(const uint16_t* q, const uint16_t* w, int64_t
          (int64_t)max_ctx / (nsplit * 2) >= 1024)
     nsplit *= 2;
   dim3 grid(nsplit, qtiles, B);
-  hipLaunchKernelGGL((index_prefill_kernel<DI, HI, FP8, MB, NCW, NBUF>), grid,
-                     dim3(64 * (NCW + 1)), 0, st, q, w, w_ld, k, ks, cu_q, ctx_len, cu_ctx,
+  hipLaunchKernelGGL((index_prefill_kernel<DI, HI, FP8, MB, NCW, NBUF, Q8>), grid,
+                     dim3(64 * (NCW + 1)), 0, st, q, qs, w, w_ld, k, ks, cu_q, ctx_len, cu_ctx,
                      scores, ld, nsplit);
   return hipGetLastError();
 }
 
-hipError_t launch_index_prefill(const void* q_idx, const void* w, int64_t w_ld, const void* k_idx,
-                                int k_dtype, const float* k_scale, int H_I, int d_I,
-                                const int32_t* cu_q, const int32_t* ctx_len,
-                                const int64_t* cu_ctx, int B, int max_q, int max_ctx,
-                                float* scores, int64_t ld, hipStream_t stream) {
-  auto q = static_cast<const uint16_t*>(q_idx);
+hipError_t launch_index_prefill(const void* q_idx, int q_dtype, const float* q_scale,
+                                const void* w, int64_t w_ld, const void* k_idx, int k_dtype,
+                                const float* k_scale, int H_I, int d_I, const int32_t* cu_q,
+                                const int32_t* ctx_len, const int64_t* cu_ctx, int B, int max_q,
+                                int max_ctx, float* scores, int64_t ld, hipStream_t stream) {
   auto wp = static_cast<const uint16_t*>(w);
   auto k = static_cast<const uint8_t*>(k_idx);
-  const bool fp8 = k_dtype == 1;
+  const bool fp8 = k_dtype == 1, q8 = q_dtype == 1;
+  if (q8 && !fp8) return hipErrorInvalidValue;
 #define DSA_PREFILL_CASE(DI_, HI_)                                                              \
   if (d_I == DI_ && H_I == HI_) {                                                               \
-    return fp8 ? launch_prefill_t<DI_, HI_, true>(q, wp, w_ld, k, k_scale, cu_q, ctx_len,      \
-                                                  cu_ctx, B, max_q, max_ctx, scores, ld,      \
-                                                  stream)                                      \
-               : launch_prefill_t<DI_, HI_, false>(q, wp, w_ld, k, k_scale, cu_q, ctx_len,     \
-                                                   cu_ctx, B, max_q, max_ctx, scores, ld,     \
-                                                   stream);                                    \
+    if (q8)                                                                                     \
+      return launch_prefill_t<DI_, HI_, true, true>(q_idx, q_scale, wp, w_ld, k, k_scale, cu_q, \
+                                                    ctx_len, cu_ctx, B, max_q, max_ctx, scores, \
+                                                    ld, stream);                                \
+    return fp8 ? launch_prefill_t<DI_, HI_, true, false>(q_idx, nullptr, wp, w_ld, k, k_scale,  \
+                                                         cu_q, ctx_len, cu_ctx, B, max_q,      \
+                                                         max_ctx, scores, ld, stream)          \
+               : launch_prefill_t<DI_, HI_, false, false>(q_idx, nullptr, wp, w_ld, k, k_scale, \
+                                                          cu_q, ctx_len, cu_ctx, B, max_q,     \
+                                                          max_ctx, scores, ld, stream);        \
   }
   DSA_PREFILL_CASE(128, 32)
   DSA_PREFILL_CASE(128, 16)

@@ -66,12 +66,13 @@ hipError_t launch_index_decode(const void* q_idx, const void* w, int64_t w_ld, c
                                const DecodeAppend* app, hipStream_t stream,
                                hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
-// Indexer, a chunk of queries per sequence (dense MFMA contraction).
-hipError_t launch_index_prefill(const void* q_idx, const void* w, int64_t w_ld, const void* k_idx,
-                                int k_dtype, const float* k_scale, int H_I, int d_I,
-                                const int32_t* cu_q, const int32_t* ctx_len,
-                                const int64_t* cu_ctx, int B, int max_q, int max_ctx,
-                                float* scores, int64_t ld, hipStream_t stream);
+// Indexer, a chunk of queries per sequence (dense MFMA contraction).  Query
+// heads bf16 (q_dtype 0) or E4M3FN codes with q_scale (q_dtype 1, fp8 keys).
+hipError_t launch_index_prefill(const void* q_idx, int q_dtype, const float* q_scale,
+                                const void* w, int64_t w_ld, const void* k_idx, int k_dtype,
+                                const float* k_scale, int H_I, int d_I, const int32_t* cu_q,
+                                const int32_t* ctx_len, const int64_t* cu_ctx, int B, int max_q,
+                                int max_ctx, float* scores, int64_t ld, hipStream_t stream);
 
 // Sparse attention.
 struct AttnPlan {

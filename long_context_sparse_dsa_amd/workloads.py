@@ -9,6 +9,8 @@ Recipe (shapes and distributions of the workloads named in the design notes):
   - w (indexer head weights): U(0, 1), rounded to bf16.
   - fp8 indexer keys: N(0, 1) rounded to fp8 e4m3fn (RNE); per-token fp32
     scale U(0.5, 2).
+  - fp8 indexer query heads (the fp8 prefill contraction): the same, with one
+    fp32 scale U(0.5, 2) per (query, head).
   - "planted" keys: each position independently with probability
     plant_frac has its indexer key row multiplied by plant_mult (exact in
     bf16 for powers of two), giving a long-tailed score distribution.
@@ -98,6 +100,7 @@ class Workload:
     D: int
     K: int
     key_dtype: str = "bf16"
+    q_dtype: str = "bf16"
     plant_frac: float = 0.0
     plant_mult: float = 4.0
     seed: int = 0
@@ -131,6 +134,11 @@ def prefill_8k(seed=2):
                     seed=seed)
 
 
+def prefill_8k_fp8(seed=2):
+    return Workload("dsa_prefill_q8192_ctx139264_fp8", [139264], [8192], 16, 128, 64, 128, 2048,
+                    key_dtype="fp8", q_dtype="fp8", seed=seed)
+
+
 def decode_1m_b32_fp8(seed=3):
     return Workload("dsa_decode_b32_ctx1048576_fp8", [1 << 20] * 32, [1] * 32, 32, 128, 64,
                     128, 2048, key_dtype="fp8", seed=seed)
@@ -146,6 +154,7 @@ WORKLOADS = {
     "tiny": tiny_decode,
     "dec128k": decode_128k,
     "prefill8k": prefill_8k,
+    "prefill8k_fp8": prefill_8k_fp8,
     "dec1m_b32_fp8": decode_1m_b32_fp8,
     "hybrid51": hybrid_5to1,
 }
@@ -163,7 +172,12 @@ def make_inputs(wl: Workload, device="cpu", seed_offset: int = 0) -> dict:
     for n in wl.n_q:
         cu_q.append(cu_q[-1] + n)
     t = {}
-    t["q_idx"] = randn_bf16((T, wl.H_I, wl.d_I), s, "q_idx", device)
+    if wl.q_dtype == "fp8":
+        t["q_idx"] = randn_fp8((T, wl.H_I, wl.d_I), s, "q_idx", device)
+        t["q_scale"] = rand_f32((T, wl.H_I), s, "q_scale", 0.5, 2.0, device)
+    else:
+        t["q_idx"] = randn_bf16((T, wl.H_I, wl.d_I), s, "q_idx", device)
+        t["q_scale"] = None
     t["w"] = rand_bf16((T, wl.H_I), s, "w", 0.0, 1.0, device)
     if wl.key_dtype == "fp8":
         t["k_idx"] = randn_fp8((L_tot, wl.d_I), s, "k_idx", device)

@@ -55,12 +55,12 @@ def test_workspace_sizes_are_sane(lib):
 
 
 def _idx_scores(lib, **kw):
-    a = dict(q=FAKE, w=FAKE, w_ld=32, k=FAKE, kdt=0, ks=None, H=32, d=128, cu_q=None,
+    a = dict(q=FAKE, qdt=0, qs=None, w=FAKE, w_ld=32, k=FAKE, kdt=0, ks=None, H=32, d=128, cu_q=None,
              ctx=FAKE, cu_ctx=FAKE, B=1, T=1, max_q=1, max_ctx=1000, scores=FAKE, ld=1000)
     a.update(kw)
-    return lib.dsa_index_scores(a["q"], a["w"], a["w_ld"], a["k"], a["kdt"], a["ks"], a["H"],
-                                a["d"], a["cu_q"], a["ctx"], a["cu_ctx"], a["B"], a["T"],
-                                a["max_q"], a["max_ctx"], a["scores"], a["ld"], None)
+    return lib.dsa_index_scores(a["q"], a["qdt"], a["qs"], a["w"], a["w_ld"], a["k"], a["kdt"],
+                                a["ks"], a["H"], a["d"], a["cu_q"], a["ctx"], a["cu_ctx"], a["B"],
+                                a["T"], a["max_q"], a["max_ctx"], a["scores"], a["ld"], None)
 
 
 @pytest.mark.parametrize("kw,code,frag", [
@@ -77,6 +77,11 @@ def _idx_scores(lib, **kw):
     (dict(w_ld=5), 1, "w_ld"),
     (dict(cu_q=FAKE, max_q=0), 1, "max_q"),
     (dict(ctx=None), 1, "ctx_len"),
+    (dict(qdt=1), 1, "q_scale"),
+    (dict(qdt=1, qs=FAKE), 2, "fp8 key cache"),
+    (dict(qdt=1, qs=FAKE, kdt=1, ks=FAKE), 2, "prefill contraction"),
+    (dict(qs=FAKE), 1, "bf16 query heads"),
+    (dict(qdt=3), 1, "q_dtype"),
 ])
 def test_index_scores_validation(lib, kw, code, frag):
     assert _idx_scores(lib, **kw) == code
@@ -127,14 +132,14 @@ def test_layer_validation(lib):
     args3[12] = -1  # gate_stride_d
     assert f(*args3) == 1 and "gate_stride_d" in dsa.dsa_last_error()
     g = lib.dsa_layer_prefill
-    pargs = [FAKE, FAKE, 16, FAKE, 0, None, 16, 128, FAKE, FAKE, FAKE, FAKE, 1, 0.0, 64, 128,
-             2048, None, FAKE, FAKE, 1, 8192, 8192, 139264, FAKE, None, FAKE, 1 << 40, None]
+    pargs = [FAKE, 0, None, FAKE, 16, FAKE, 0, None, 16, 128, FAKE, FAKE, FAKE, FAKE, 1, 0.0, 64,
+             128, 2048, None, FAKE, FAKE, 1, 8192, 8192, 139264, FAKE, None, FAKE, 1 << 40, None]
     assert g(*pargs) == 1
     assert "cu_q" in dsa.dsa_last_error()
     # below the least workspace: refused before any launch, sizes in the message
     small = list(pargs)
-    small[17] = FAKE
-    small[27] = lib.dsa_layer_prefill_min_workspace_size(1, 139264, 2048, 64, 128) - 1
+    small[19] = FAKE
+    small[29] = lib.dsa_layer_prefill_min_workspace_size(1, 139264, 2048, 64, 128) - 1
     assert g(*small) == 3
     assert "workspace too small" in dsa.dsa_last_error()
 

@@ -15,8 +15,8 @@ import torch
 
 import oracle
 from long_context_sparse_dsa_amd import workloads as W
-from tests.parity import (ATOL_BF16, ATOL_FP8, check_index_row, check_out, check_set_band, cpu,
-                          positions)
+from tests.parity import (ATOL_BF16, ATOL_FP8, FP8_MFMA_REL, check_index_row, check_out,
+                          check_set_band, cpu, fp8_score_bound, positions)
 
 pytestmark = pytest.mark.gpu
 
@@ -68,27 +68,41 @@ def test_index_scores_decode(dsa, H_I, d_I, key, lens):
         assert np.all(err <= _score_tol(ref[b, :L])), f"row {b}: max err {err.max():.3g}"
 
 
-@pytest.mark.parametrize("H_I,d_I,key,lens,nq", [
-    (16, 128, "bf16", [3000], [200]),
-    (32, 128, "bf16", [2500, 700], [70, 33]),
-    (4, 64, "bf16", [1200], [130]),
-    (16, 128, "fp8", [2100], [90]),
+@pytest.mark.parametrize("H_I,d_I,key,lens,nq,qdt", [
+    (16, 128, "bf16", [3000], [200], "bf16"),
+    (32, 128, "bf16", [2500, 700], [70, 33], "bf16"),
+    (4, 64, "bf16", [1200], [130], "bf16"),
+    (16, 128, "fp8", [2100], [90], "bf16"),
+    # fp8 query heads with per-(query, head) scales on the fp8 MFMA
+    (16, 128, "fp8", [3000, 700], [200, 45], "fp8"),
+    (32, 128, "fp8", [2500], [70], "fp8"),
+    (4, 64, "fp8", [1200, 300], [130, 7], "fp8"),
 ])
-def test_index_scores_prefill(dsa, H_I, d_I, key, lens, nq):
-    say(f"index_scores prefill H_I={H_I} {key} lens={lens} nq={nq}")
-    w = wl("t", lens, nq, H_I, d_I, 8, 64, 64, key_dtype=key, seed=12)
+def test_index_scores_prefill(dsa, H_I, d_I, key, lens, nq, qdt):
+    say(f"index_scores prefill H_I={H_I} keys {key} queries {qdt} lens={lens} nq={nq}")
+    w = wl("t", lens, nq, H_I, d_I, 8, 64, 64, key_dtype=key, q_dtype=qdt, seed=12)
     inp = W.make_inputs(w)
     d = to_dev(inp)
     s = torch.full((w.T, max(lens)), float("nan"), device=DEV)
     dsa.dsa_index_scores(d["q_idx"], d["w"], d["k_idx"], d["k_scale"], d["ctx_len"], d["cu_ctx"],
-                         cu_q=d["cu_q"], max_ctx=max(lens), scores=s)
+                         cu_q=d["cu_q"], max_ctx=max(lens), scores=s, q_scale=d["q_scale"])
     torch.cuda.synchronize()
     ref = oracle.index_scores(inp["q_idx"], inp["w"], inp["k_idx"], inp["k_scale"],
-                              ctx_len=inp["ctx_len"], cu_q=inp["cu_q"], cu_ctx=inp["cu_ctx"])
+                              ctx_len=inp["ctx_len"], cu_q=inp["cu_q"], cu_ctx=inp["cu_ctx"],
+                              q_scale=inp["q_scale"])
     got = s.cpu().numpy().astype(np.float64)
+    bound = None
+    if qdt == "fp8":
+        bound = fp8_score_bound(inp["q_idx"], inp["w"], inp["k_idx"], inp["k_scale"],
+                                inp["q_scale"], ctx_len=inp["ctx_len"], cu_q=inp["cu_q"],
+                                cu_ctx=inp["cu_ctx"])
     for t, p in enumerate(positions(lens, nq)):
         err = np.abs(got[t, :p + 1] - ref[t, :p + 1])
-        assert np.all(err <= _score_tol(ref[t, :p + 1])), f"row {t}: max err {err.max():.3g}"
+        if bound is None:
+            tol = _score_tol(ref[t, :p + 1])
+        else:
+            tol = FP8_MFMA_REL * bound[t, :p + 1] + 1e-6 * np.abs(ref[t, :p + 1])
+        assert np.all(err <= tol), f"row {t}: max err {err.max():.3g}"
         assert np.all(np.isnan(got[t, p + 1:])), f"row {t}: wrote past its position"
 
 
@@ -549,7 +563,7 @@ def _layer_prefill_check(dsa, w, inp, d, rows=None, ws_bytes=None, gate=None):
     out = dsa.dsa_layer_prefill(d["q_idx"], d["w"], d["k_idx"], d["k_scale"], d["q"],
                                 d["k_cache"], d["v_cache"], gate_dev, w.K, d["cu_q"],
                                 d["ctx_len"], d["cu_ctx"], max_q=max(w.n_q), max_ctx=L,
-                                idx_out=idx, ws=ws)
+                                idx_out=idx, ws=ws, q_scale=d.get("q_scale"))
     torch.cuda.synchronize()
     idx_c = idx.cpu().numpy()
     pos = positions(w.ctx_lens, w.n_q)
@@ -567,9 +581,11 @@ def _layer_prefill_check(dsa, w, inp, d, rows=None, ws_bytes=None, gate=None):
         r0 = int(cu_ctx[b])
         ks = None if k_scale is None else k_scale[r0:r0 + p + 1]
         # the pinned indexer score on a one-query descriptor: the query at p sees 0..p
+        qs = inp.get("q_scale")
         s_ref = oracle.index_scores(cpu(inp["q_idx"][t:t + 1]), cpu(inp["w"][t:t + 1]),
                                     k_idx[r0:r0 + p + 1], ks,
-                                    ctx_len=np.array([p + 1], np.int32))[0]
+                                    ctx_len=np.array([p + 1], np.int32),
+                                    q_scale=None if qs is None else cpu(qs[t:t + 1]))[0]
         sel = check_index_row(idx_c[t], p, w.K)
         if one_pass:
             _check_topk_on_gpu_scores(idx_c[t], s_gpu[i], p, w.K)
@@ -592,6 +608,32 @@ def test_layer_prefill_small(dsa):
     _layer_prefill_check(dsa, w, inp, to_dev(inp), rows=list(range(0, w.T, 37)) + [w.T - 1])
 
 
+@pytest.mark.parametrize("lens,nq,H_I,d_I", [([6000, 2500], [300, 2500], 16, 128),
+                                             ([4096], [64], 4, 64)])
+def test_layer_prefill_fp8_queries(dsa, lens, nq, H_I, d_I):
+    """fp8 query heads and keys: the fp8 MFMA indexer inside the layer."""
+    say(f"layer_prefill fp8 queries lens={lens} nq={nq} H_I={H_I}")
+    w = wl("t", lens, nq, H_I, d_I, 64 if d_I == 128 else 8, d_I, 2048 if d_I == 128 else 256,
+           key_dtype="fp8", q_dtype="fp8", seed=45)
+    inp = W.make_inputs(w)
+    rows = list(range(0, w.T, 29)) + [w.T - 1]
+    _layer_prefill_check(dsa, w, inp, to_dev(inp), rows=rows)
+
+
+def test_layer_prefill_fp8_queries_sub_chunks(dsa):
+    """fp8 query heads through the sub-chunked prefill (pointer offsets of
+    one-byte query rows and of their scales)."""
+    say("layer_prefill fp8 queries in sub-chunks")
+    w = wl("t", [5000, 1200], [700, 400], 16, 128, 64, 128, 2048, key_dtype="fp8",
+           q_dtype="fp8", seed=46)
+    inp = W.make_inputs(w)
+    d = to_dev(inp)
+    L = max(w.ctx_lens)
+    small = (dsa.dsa_layer_prefill_workspace_size(w.B, 300, L, w.K, w.Hq, w.D) +
+             dsa.dsa_layer_prefill_min_workspace_size(w.B, L, w.K, w.Hq, w.D))
+    _layer_prefill_check(dsa, w, inp, d, rows=[0, 299, 300, 699, 700, 1099], ws_bytes=small)
+
+
 def test_layer_prefill_tiny_shape(dsa):
     say("layer_prefill tiny shape (4x64 indexer, 8 heads x 64)")
     w = wl("t", [4096], [64], 4, 64, 8, 64, 256, seed=42)
@@ -599,9 +641,10 @@ def test_layer_prefill_tiny_shape(dsa):
     _layer_prefill_check(dsa, w, inp, to_dev(inp))
 
 
-def test_layer_prefill_8k_chunk_sampled(dsa):
-    say("layer_prefill 8192 queries on a 131072-token context (sampled rows)")
-    w = W.prefill_8k()
+@pytest.mark.parametrize("fp8", [False, True])
+def test_layer_prefill_8k_chunk_sampled(dsa, fp8):
+    say(f"layer_prefill 8192 queries on a 131072-token context (sampled rows), fp8={fp8}")
+    w = W.prefill_8k_fp8() if fp8 else W.prefill_8k()
     inp = W.make_inputs(w, device=DEV)
     # 64 evenly spaced rows, the first and the last included: every compute
     # wave of the indexer's 28-query workgroups is sampled

@@ -271,6 +271,11 @@ def bench_hybrid(args, torch, dsa, W):
                     "k": W.randn_bf16((ntot, wl.D), wl.seed, f"swa{i}_k", dev),
                     "v": W.randn_bf16((ntot, wl.D), wl.seed, f"swa{i}_v", dev),
                     "out": torch.empty(wl.B, wl.Hq, wl.D, dtype=torch.bfloat16, device=dev)})
+    # the five window layers in one launch (the fused step), and the same
+    # layers issued one dsa_sparse_attn call each (timed beside it)
+    swa_fused = dsa.prepare_swa_decode_layers([x["q"] for x in swa], [x["k"] for x in swa],
+                                              [x["v"] for x in swa], s["ctx_len"], s["cu_ctx"],
+                                              L, [x["out"] for x in swa], window)
     swa_calls = [dsa.prepare_sparse_attn(x["q"], x["k"], x["v"], None, s["ctx_len"], s["cu_ctx"],
                                          L, x["out"], window=window) for x in swa]
     ws = torch.empty(dsa.dsa_layer_decode_workspace_size(wl.B, L, wl.K, wl.Hq, wl.D),
@@ -284,13 +289,17 @@ def bench_hybrid(args, torch, dsa, W):
     set_events = dsa.load().dsa_set_indexer_events
 
     def step():
+        swa_fused()
+        dsa_call()
+
+    def step_per_layer():
         for c in swa_calls:
             c()
         dsa_call()
 
-    def timed(n, warm, with_events):
+    def timed(n, warm, with_events, fn=step):
         for _ in range(warm):
-            step()
+            fn()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
@@ -298,13 +307,14 @@ def bench_hybrid(args, torch, dsa, W):
         for i in range(n):
             if with_events:
                 set_events(ctypes.c_void_p(ev[i][0]), ctypes.c_void_p(ev[i][1]))
-            step()
+            fn()
         e1.record()
         torch.cuda.synchronize()
         set_events(None, None)
         return e0.elapsed_time(e1) / n
 
     ms = timed(args.steps, args.warmup, False)
+    ms_per_layer = timed(args.steps, args.warmup, False, step_per_layer)
     timed(args.steps, 0, True)
     ms_idx = sum(hip.elapsed_ms(a, b) for a, b in ev) / len(ev)
     for a, b in ev:
@@ -339,6 +349,8 @@ def bench_hybrid(args, torch, dsa, W):
         "layer_roofline": {"algorithmic_bytes_per_step": dsa_bytes + swa_bytes,
                            "frac_of_hbm_peak": round((dsa_bytes + swa_bytes) / (ms * 1e-3) /
                                                      1e9 / HBM_PEAK_GBS, 4)},
+        "window_layers_one_call_each": {"ms_per_step": round(ms_per_layer, 5),
+                                        "tokens_per_s": round(wl.B / (ms_per_layer * 1e-3), 1)},
     }
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline_hybrid(s, swa, wl, args.cpu_seconds)

@@ -199,6 +199,28 @@ dsa_status_t dsa_sparse_attn(const void* q, const void* k_cache, const void* v_c
                              size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* The sliding-window layers of a hybrid decode step, in one launch: the     */
+/* naive-n0-5-flash page (Key Capabilities) interleaves five sliding-window  */
+/* attention layers (128-token window) with each DSA layer.  For each of the */
+/* n_layers layers L (1 <= n_layers <= 8), each with its own tensors, and   */
+/* each sequence b of the shared descriptor (one new query at p = ctx_len[b] */
+/* - 1; every layer's caches packed the same way by cu_ctx):                */
+/*   out[L][b] = dsa_sparse_attn over S = {max(0, p - window + 1) .. p}      */
+/*               of q[L][b] against k_cache[L], v_cache[L],                  */
+/*               gated by gate[L] when gate != NULL and gate[L] != NULL.     */
+/* q, k_cache, v_cache, out (and gate, if not NULL) are host arrays of       */
+/* n_layers device pointers.  One workgroup per (layer, sequence) takes the  */
+/* whole window; no workspace.  Results equal n_layers dsa_sparse_attn       */
+/* calls in window mode up to the order of the softmax sums.                 */
+/* Supported: (Hq, D) as dsa_sparse_attn; 1 <= window <= 4096.               */
+/* ------------------------------------------------------------------------ */
+dsa_status_t dsa_swa_decode_layers(int n_layers, const void* const* q, const void* const* k_cache,
+                                   const void* const* v_cache, const void* const* gate,
+                                   int64_t gate_stride_d, int window, float sm_scale, int Hq,
+                                   int D, const int32_t* ctx_len, const int64_t* cu_ctx, int B,
+                                   int max_ctx, void* const* out, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Whole layer, decode: one new query per sequence (T == B).                 */
 /* Steps 1 -> 2 -> 3 above on the caller's stream, with the step-1 kernel   */
 /* also emitting the per-tile candidate lists that step 2 certifies (the     */

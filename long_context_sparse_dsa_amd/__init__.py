@@ -33,7 +33,7 @@ EXPORTS = [
     "dsa_version", "dsa_last_error",
     "dsa_index_scores", "dsa_cache_append",
     "dsa_topk_workspace_size", "dsa_topk",
-    "dsa_sparse_attn_workspace_size", "dsa_sparse_attn",
+    "dsa_sparse_attn_workspace_size", "dsa_sparse_attn", "dsa_swa_decode_layers",
     "dsa_layer_decode_workspace_size", "dsa_layer_decode", "dsa_set_indexer_events",
     "dsa_layer_decode_noalloc_max_bytes", "dsa_layer_decode_noalloc", "dsa_layer_decode_append",
     "dsa_set_topk_counters",
@@ -73,6 +73,7 @@ def load(path: str | None = None):
     lib.dsa_sparse_attn_workspace_size.restype = S
     lib.dsa_sparse_attn.argtypes = [P, P, P, P, I, I, P, L, F, I, I, P, P, P, I, I, I, I, P, P,
                                     P, S, P]
+    lib.dsa_swa_decode_layers.argtypes = [I, P, P, P, P, L, I, F, I, I, P, P, I, I, P, P]
     lib.dsa_layer_decode_workspace_size.argtypes = [I, I, I, I, I]
     lib.dsa_layer_decode_workspace_size.restype = S
     lib.dsa_layer_decode.argtypes = [P, P, L, P, I, P, I, I, P, P, P, P, L, F, I, I, I, P, P, I,
@@ -92,6 +93,7 @@ def load(path: str | None = None):
     lib.dsa_set_indexer_events.argtypes = [P, P]
     lib.dsa_set_topk_counters.argtypes = [P]
     for fn in ("dsa_index_scores", "dsa_cache_append", "dsa_topk", "dsa_sparse_attn",
+               "dsa_swa_decode_layers",
                "dsa_layer_decode",
                "dsa_layer_decode_noalloc", "dsa_layer_decode_append",
                "dsa_layer_prefill", "dsa_set_indexer_events", "dsa_set_topk_counters"):
@@ -406,6 +408,67 @@ def prepare_sparse_attn(q, k_cache, v_cache, idx, ctx_len, cu_ctx, max_ctx, out,
             raise DSAError("dsa_sparse_attn", st, dsa_last_error())
     call.workspace = ws
     return call
+
+
+def _ptr_array(tensors):
+    arr = (ctypes.c_void_p * len(tensors))()
+    for i, t in enumerate(tensors):
+        arr[i] = None if t is None else t.data_ptr()
+    return arr
+
+
+def prepare_swa_decode_layers(qs, k_caches, v_caches, ctx_len, cu_ctx, max_ctx, outs, window,
+                              gates=None, sm_scale=0.0, stream=None):
+    """Marshal one dsa_swa_decode_layers call (all sliding-window layers of a
+    decode step in one launch); returns a no-argument callable that re-issues
+    it.  qs, k_caches, v_caches, outs (and gates, if given): one tensor per
+    layer, kept alive and unchanged in shape while the callable is used."""
+    n = len(qs)
+    if not (len(k_caches) == len(v_caches) == len(outs) == n) or (gates and len(gates) != n):
+        raise ValueError("one q, k_cache, v_cache, out (and gate) per layer")
+    _check(ctx_len, "ctx_len", (torch.int32,), 1)
+    _check(cu_ctx, "cu_ctx", (torch.int64,), 1)
+    B = _check_desc(ctx_len, cu_ctx, None, qs[0].shape[0])
+    T, Hq, D = qs[0].shape
+    gs = 1
+    for i in range(n):
+        _check(qs[i], "q", BF16, 3)
+        _shape(qs[i], "q", (T, Hq, D))
+        _check(k_caches[i], "k_cache", BF16, 2)
+        _check(v_caches[i], "v_cache", BF16, 2)
+        _shape(v_caches[i], "v_cache", tuple(k_caches[i].shape))
+        if k_caches[i].shape[1] != D:
+            raise ValueError(f"k_cache: rows of {k_caches[i].shape[1]}, expected {D}")
+        _check(outs[i], "out", BF16, 3)
+        _shape(outs[i], "out", (T, Hq, D))
+        if gates and gates[i] is not None:
+            _check(gates[i], "gate", BF16)
+            gs = _gate_stride(gates[i], T, Hq, D)
+    arrays = [_ptr_array(x) for x in (qs, k_caches, v_caches)]
+    garr = _ptr_array(gates) if gates else None
+    oarr = _ptr_array(outs)
+    fn = load().dsa_swa_decode_layers
+    args = (n, arrays[0], arrays[1], arrays[2], garr, gs, int(window), float(sm_scale), Hq, D,
+            _p(ctx_len), _p(cu_ctx), B, int(max_ctx), oarr, _stream(stream))
+
+    def call():
+        st = fn(*args)
+        if st != 0:
+            raise DSAError("dsa_swa_decode_layers", st, dsa_last_error())
+    call.keep = (arrays, garr, oarr)
+    return call
+
+
+def dsa_swa_decode_layers(qs, k_caches, v_caches, ctx_len, cu_ctx, window, outs=None, gates=None,
+                          max_ctx=None, sm_scale=0.0, stream=None):
+    """All sliding-window layers of a decode step in one launch; returns the
+    list of per-layer outputs bf16 [B, Hq, D]."""
+    if outs is None:
+        outs = [torch.empty_like(q) for q in qs]
+    max_ctx = _host_max(ctx_len, max_ctx)
+    prepare_swa_decode_layers(qs, k_caches, v_caches, ctx_len, cu_ctx, max_ctx, outs, window,
+                              gates=gates, sm_scale=sm_scale, stream=stream)()
+    return outs
 
 
 def dsa_layer_decode_workspace_size(B, max_ctx, K, Hq, D) -> int:

@@ -422,6 +422,52 @@ dsa_status_t dsa_sparse_attn(const void* q, const void* k_cache, const void* v_c
   return hip_status(e, "dsa_sparse_attn");
 }
 
+dsa_status_t dsa_swa_decode_layers(int n_layers, const void* const* q, const void* const* k_cache,
+                                   const void* const* v_cache, const void* const* gate,
+                                   int64_t gate_stride_d, int window, float sm_scale, int Hq,
+                                   int D, const int32_t* ctx_len, const int64_t* cu_ctx, int B,
+                                   int max_ctx, void* const* out, void* stream) {
+  DSA_REQUIRE(n_layers >= 1 && n_layers <= dsa::kMaxAttnLayers, DSA_ERR_UNSUPPORTED,
+              "n_layers must be in [1, %d] (got %d)", dsa::kMaxAttnLayers, n_layers);
+  DSA_REQUIRE(q && k_cache && v_cache && out, DSA_ERR_INVALID_ARG,
+              "q, k_cache, v_cache and out must be arrays of n_layers pointers");
+  DSA_REQUIRE(gate_stride_d == 0 || gate_stride_d == 1, DSA_ERR_INVALID_ARG,
+              "gate_stride_d must be 1 (elementwise gate) or 0 (one gate per head), got %lld",
+              (long long)gate_stride_d);
+  dsa::AttnLayers lay;
+  lay.n = n_layers;
+  for (int i = 0; i < n_layers; ++i) {
+    DSA_PTR(q[i], "q[layer]");
+    DSA_PTR(k_cache[i], "k_cache[layer]");
+    DSA_PTR(v_cache[i], "v_cache[layer]");
+    DSA_PTR(out[i], "out[layer]");
+    const void* g = gate ? gate[i] : nullptr;
+    if (g) DSA_PTR(g, "gate[layer]");
+    lay.q[i] = static_cast<const uint16_t*>(q[i]);
+    lay.kc[i] = static_cast<const uint16_t*>(k_cache[i]);
+    lay.vc[i] = static_cast<const uint16_t*>(v_cache[i]);
+    lay.gate[i] = static_cast<const uint16_t*>(g);
+    lay.out[i] = static_cast<uint16_t*>(out[i]);
+  }
+  dsa_status_t st = check_batch(nullptr, ctx_len, cu_ctx, true, B, B, 1, max_ctx);
+  if (st != DSA_OK) return st;
+  DSA_REQUIRE(attn_shape_ok(Hq, D), DSA_ERR_UNSUPPORTED,
+              "unsupported attention shape Hq=%d D=%d (supported: 8x64, 64x128)", Hq, D);
+  DSA_REQUIRE(window >= 1 && window <= 4096, DSA_ERR_UNSUPPORTED,
+              "window must be in [1, 4096] (got %d)", window);
+  DSA_REQUIRE(sm_scale >= 0.f, DSA_ERR_INVALID_ARG, "sm_scale must be >= 0");
+  // one workgroup per (layer, sequence) over its whole window
+  dsa::AttnPlan plan;
+  plan.nsplit = 1;
+  plan.rows_per_split = window;
+  plan.ws_bytes = 0;
+  hipError_t e = dsa::launch_sparse_attn(lay.q[0], lay.kc[0], lay.vc[0], nullptr, 0, window,
+                                         lay.gate[0], (int)gate_stride_d, sm_scale, Hq, D,
+                                         nullptr, ctx_len, cu_ctx, B, B, lay.out[0], nullptr,
+                                         nullptr, plan, static_cast<hipStream_t>(stream), &lay);
+  return hip_status(e, "dsa_swa_decode_layers");
+}
+
 size_t dsa_layer_decode_workspace_size(int B, int max_ctx, int K, int Hq, int D) {
   if (B < 1 || max_ctx < 1 || K < 1) return 0;
   return decode_ws_layout(B, max_ctx, K, Hq, D, nullptr, nullptr);

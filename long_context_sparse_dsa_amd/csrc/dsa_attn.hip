@@ -107,7 +107,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ idx, int K, int window,
     const uint16_t* __restrict__ gate, int gstride, float scale_log2, int Hq, const int32_t* cu_q,
     const int32_t* ctx_len, const int64_t* cu_ctx, int B, int rows_per_split,
-    uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part, int nsplit) {
+    uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part, int nsplit,
+    AttnLayers layers) {
+  if (layers.n > 0) {  // one of several layers (grid z), each with its own tensors
+    const int z = blockIdx.z;
+    q = layers.q[z];
+    kc = layers.kc[z];
+    vc = layers.vc[z];
+    gate = layers.gate[z];
+    out = layers.out[z];
+  }
   constexpr int KS = D / 16;   // k-steps of q . K
   constexpr int DB = D / 32;   // 32-wide blocks of the output dim
   constexpr int RB = 4 / HB;   // row-block waves per head block
@@ -563,7 +572,7 @@ hipError_t launch_sparse_attn(const void* q, const void* k_cache, const void* v_
                               int gstride, float sm_scale, int Hq, int D, const int32_t* cu_q,
                               const int32_t* ctx_len, const int64_t* cu_ctx, int B, int T,
                               void* out, float* lse, void* ws, const AttnPlan& plan,
-                              hipStream_t stream) {
+                              hipStream_t stream, const AttnLayers* layers) {
   const float scale = (sm_scale != 0.f ? sm_scale : 1.f / sqrtf((float)D)) * kLog2e;
   auto qp = static_cast<const uint16_t*>(q);
   auto kp = static_cast<const uint16_t*>(k_cache);
@@ -571,17 +580,21 @@ hipError_t launch_sparse_attn(const void* q, const void* k_cache, const void* v_
   auto gp = static_cast<const uint16_t*>(gate);
   auto op = static_cast<uint16_t*>(out);
   float* part = static_cast<float*>(ws);
-  dim3 grid(plan.nsplit, T);
+  AttnLayers one;
+  one.n = 0;
+  const AttnLayers& lay = layers ? *layers : one;
+  dim3 grid(plan.nsplit, T, lay.n > 0 ? lay.n : 1);
   const bool final_out = plan.nsplit == 1;
+  if (lay.n > 0 && !final_out) return hipErrorInvalidValue;  // layers: unsplit plans only
 #define DSA_ATTN_LAUNCH(D_, HB_)                                                               \
   if (final_out)                                                                               \
     hipLaunchKernelGGL((sparse_attn_kernel<D_, HB_, true>), grid, dim3(256), 0, stream, qp, kp, \
                        vp, idx, K, window, gp, gstride, scale, Hq, cu_q, ctx_len, cu_ctx, B,   \
-                       plan.rows_per_split, op, lse, part, plan.nsplit);                       \
+                       plan.rows_per_split, op, lse, part, plan.nsplit, lay);                  \
   else                                                                                         \
     hipLaunchKernelGGL((sparse_attn_kernel<D_, HB_, false>), grid, dim3(256), 0, stream, qp,   \
                        kp, vp, idx, K, window, gp, gstride, scale, Hq, cu_q, ctx_len, cu_ctx, B,\
-                       plan.rows_per_split, op, lse, part, plan.nsplit);
+                       plan.rows_per_split, op, lse, part, plan.nsplit, lay);
   if (D == 128 && Hq == 64) {
     DSA_ATTN_LAUNCH(128, 2)
     if (!final_out) launch_combine<128>(T, Hq, part, plan.nsplit, gp, gstride, op, lse, stream);

@@ -81,13 +81,27 @@ struct AttnPlan {
   size_t ws_bytes;   // partial (m, l, o) buffers when nsplit > 1
 };
 AttnPlan attn_plan(int T, int K, int window, int Hq, int D);
+
+// Several attention layers over one batch descriptor in one launch (grid z
+// = layer): layer z reads q[z], k_cache[z], v_cache[z], gate[z] and writes
+// out[z] in place of the single-layer pointers.
+constexpr int kMaxAttnLayers = 8;
+struct AttnLayers {
+  int n;  // 0: a single layer (the plain pointers)
+  const uint16_t* q[kMaxAttnLayers];
+  const uint16_t* kc[kMaxAttnLayers];
+  const uint16_t* vc[kMaxAttnLayers];
+  const uint16_t* gate[kMaxAttnLayers];
+  uint16_t* out[kMaxAttnLayers];
+};
+
 hipError_t launch_sparse_attn(const void* q, const void* k_cache, const void* v_cache,
                               const int32_t* idx, int K, int window, const void* gate,
                               int gate_stride_d, float sm_scale, int Hq, int D,
                               const int32_t* cu_q,
                               const int32_t* ctx_len, const int64_t* cu_ctx, int B, int T,
                               void* out, float* lse, void* ws, const AttnPlan& plan,
-                              hipStream_t stream);
+                              hipStream_t stream, const AttnLayers* layers = nullptr);
 
 // Batch descriptor of query rows [t0, t0 + tc) of a prefill call, as a call
 // of its own whose row 0 is global row t0: cu_q_c [B+1] and ctx_len_c [B]

@@ -342,29 +342,64 @@ def test_sparse_attn_window_many_queries(dsa):
     np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=1e-4, atol=1e-4)
 
 
-def test_hybrid_step_swa_layers_then_dsa_layer(dsa):
-    """One decode step of the 5:1 hybrid at a small ragged shape: two
-    sliding-window layers (own K/V caches, ungated, through the prepared-call
-    path the bench uses) and one Gated DSA layer, each against the oracle."""
-    say("hybrid step: 2 SWA layers (window 128) + 1 DSA layer, ragged batch")
-    lens = [130, 5000, 777]
-    w = wl("t", lens, [1] * 3, 16, 128, 64, 128, 256, seed=41)
+def _swa_layers(B, ntot, n, seed, device="cpu", Hq=64, D=128):
+    return [{"q": W.randn_bf16((B, Hq, D), seed, f"swa{i}_q", device),
+             "k": W.randn_bf16((ntot, D), seed, f"swa{i}_k", device),
+             "v": W.randn_bf16((ntot, D), seed, f"swa{i}_v", device)} for i in range(n)]
+
+
+@pytest.mark.parametrize("lens,gated", [([130, 5000, 777, 3, 128, 129, 64000, 4096], False),
+                                        ([4096, 100], True)])
+def test_swa_decode_layers_one_launch(dsa, lens, gated):
+    """All sliding-window layers of a decode step in one launch, each layer
+    with its own tensors, checked layer by layer against the oracle's window
+    attention (contexts shorter than, equal to and longer than the window)."""
+    say(f"swa_decode_layers: 5 layers, window 128, lens={lens}, gated={gated}")
+    w = wl("t", lens, [1] * len(lens), 16, 128, 64, 128, 256, seed=42)
     inp = W.make_inputs(w)
     d = to_dev(inp)
-    ntot = sum(lens)
-    for i in range(2):
-        q = W.randn_bf16((3, 64, 128), 41, f"swa{i}_q")
-        k = W.randn_bf16((ntot, 128), 41, f"swa{i}_k")
-        v = W.randn_bf16((ntot, 128), 41, f"swa{i}_v")
-        out = torch.empty(3, 64, 128, dtype=torch.bfloat16, device=DEV)
-        call = dsa.prepare_sparse_attn(q.to(DEV), k.to(DEV), v.to(DEV), None, d["ctx_len"],
-                                       d["cu_ctx"], max(lens), out, window=128)
-        call()
-        call()  # re-issued: same result
-        torch.cuda.synchronize()
-        ref, _ = oracle.sparse_attn(q, k, v, window=128, ctx_len=inp["ctx_len"],
+    layers = _swa_layers(w.B, sum(lens), 5, 42)
+    gates = None
+    if gated:   # elementwise gates on some layers, per-head ones on none (one stride per call)
+        gates = [W.randn_bf16((w.B, 64, 128), 42, f"swa{i}_g") if i % 2 == 0 else None
+                 for i in range(5)]
+    outs = dsa.dsa_swa_decode_layers([x["q"].to(DEV) for x in layers],
+                                     [x["k"].to(DEV) for x in layers],
+                                     [x["v"].to(DEV) for x in layers], d["ctx_len"], d["cu_ctx"],
+                                     128, gates=None if gates is None else
+                                     [None if g is None else g.to(DEV) for g in gates],
+                                     max_ctx=max(lens))
+    torch.cuda.synchronize()
+    for i, x in enumerate(layers):
+        ref, _ = oracle.sparse_attn(x["q"], x["k"], x["v"], window=128,
+                                    gate=None if gates is None else gates[i],
+                                    ctx_len=inp["ctx_len"], cu_ctx=inp["cu_ctx"])
+        check_out(outs[i], ref, ATOL_BF16)
+
+
+def test_hybrid_step_swa_layers_then_dsa_layer(dsa):
+    """One decode step of the 5:1 hybrid at a small ragged shape, as the bench
+    issues it: the five sliding-window layers (own K/V caches, ungated) in one
+    launch through the prepared call, re-issued once, then the Gated DSA
+    layer; every layer against the oracle."""
+    say("hybrid step: 5 SWA layers (window 128) in one launch + 1 DSA layer, ragged batch")
+    lens = [130, 5000, 777, 20000, 4096, 3, 129, 70000]
+    w = wl("t", lens, [1] * len(lens), 16, 128, 64, 128, 2048, seed=41)
+    inp = W.make_inputs(w)
+    d = to_dev(inp)
+    layers = _swa_layers(w.B, sum(lens), 5, 41)
+    dl = [{k: v.to(DEV) for k, v in x.items()} for x in layers]
+    outs = [torch.empty(w.B, 64, 128, dtype=torch.bfloat16, device=DEV) for _ in range(5)]
+    call = dsa.prepare_swa_decode_layers([x["q"] for x in dl], [x["k"] for x in dl],
+                                         [x["v"] for x in dl], d["ctx_len"], d["cu_ctx"],
+                                         max(lens), outs, 128)
+    call()
+    call()  # re-issued: same result
+    torch.cuda.synchronize()
+    for i, x in enumerate(layers):
+        ref, _ = oracle.sparse_attn(x["q"], x["k"], x["v"], window=128, ctx_len=inp["ctx_len"],
                                     cu_ctx=inp["cu_ctx"])
-        check_out(out, ref, ATOL_BF16)
+        check_out(outs[i], ref, ATOL_BF16)
     _layer_decode_check(dsa, w, inp, d)
 
 

@@ -385,6 +385,9 @@ __global__ __launch_bounds__(64 * WPT) void index_decode_kernel(
   }
 }
 
+// waves per tile of the deep pipeline
+constexpr int kDeepWaves(int tile) { return tile == 256 ? 4 : (tile >= 128 ? 2 : 1); }
+
 template <int DI, bool FP8, bool REPORT, bool APPEND>
 static hipError_t launch_decode_tiled(int tile, const uint16_t* q, const uint16_t* w,
                                       int64_t w_ld, const uint8_t* k, const float* ks, int H_I,
@@ -394,9 +397,11 @@ static hipError_t launch_decode_tiled(int tile, const uint16_t* q, const uint16_
                                       const DecodeAppend& app, hipStream_t st, hipEvent_t ev0,
                                       hipEvent_t ev1) {
   dim3 grid((max_ctx + tile - 1) / tile, B);
-  // Few tiles per CU (256 CUs): two waves per tile, each with a deep
-  // pipeline, so more loads are in flight per CU; many tiles: one wave per
-  // tile with a shallow pipeline, so more waves fit in LDS.
+  // Few tiles per CU (256 CUs): several waves per tile, each with a deep
+  // pipeline, so more loads are in flight per CU (256-key tiles: four waves
+  // of 64 keys, measured 0.7 us faster per 128K decode step than two of
+  // 128); many tiles: one wave per tile with a shallow pipeline, so more
+  // waves fit in LDS.
   const bool deep = (int64_t)grid.x * B <= 1024;
   // with events: the dispatch itself records them at the kernel's start and end
 #define DSA_DECODE_LAUNCH(KER, NT)                                                             \
@@ -409,9 +414,8 @@ static hipError_t launch_decode_tiled(int tile, const uint16_t* q, const uint16_
 #define DSA_DECODE_TILE(T_)                                                                    \
   case T_:                                                                                     \
     if (deep) {                                                                                \
-      DSA_DECODE_LAUNCH((index_decode_kernel<DI, FP8, T_, REPORT, true, (T_ >= 128 ? 2 : 1),   \
-                                             APPEND>),                                         \
-                        64 * (T_ >= 128 ? 2 : 1))                                              \
+      DSA_DECODE_LAUNCH((index_decode_kernel<DI, FP8, T_, REPORT, true, kDeepWaves(T_), APPEND>), \
+                        64 * kDeepWaves(T_))                                              \
     } else {                                                                                   \
       DSA_DECODE_LAUNCH((index_decode_kernel<DI, FP8, T_, REPORT, false, 1, APPEND>), 64)      \
     }                                                                                          \

@@ -681,8 +681,27 @@ __global__ __launch_bounds__(kResolveSlots / NSL) void topk_resolve_kernel(
   const int nslots = min(stride, kResolveTiles) * kRep;  // a row's slots in the workspace
   UnionRegs<NSL> R;
   RepHeader hq[QN];
-  // report loads of groups [q0, q1) in the layout of nt threads: slots,
-  // positions and sub-tile headers
+  // eager report loads in the layout of nt threads: every group is loaded,
+  // groups at or beyond qe from slot 0 (a cached line), so the loads are
+  // straight-line code and all go out before the first wait (loads under
+  // per-group branches would each wait at the join)
+  auto load_eager = [&](int qe, int nt) {
+#pragma unroll
+    for (int q = 0; q < QN; ++q) {
+      const int sidx = slot_of(q, tid, nt);
+      const int sc = (q < qe && sidx < nslots) ? sidx : 0;
+      const u32x4 a = *reinterpret_cast<const u32x4*>(rep_u + slot0 * kRep + sc);
+      const u32x4 c = *reinterpret_cast<const u32x4*>(rep_j + slot0 * kRep + sc);
+      hq[q] = hdr[slot0 + sc / kRep];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        R.u[4 * q + e] = a[e];
+        R.j[4 * q + e] = (int32_t)c[e];
+      }
+    }
+  };
+  // report loads of groups [q0, q1) in the layout of nt threads, keeping
+  // the other groups: slots, positions and sub-tile headers
   auto load_reports = [&](int q0, int q1, int nt) {
 #pragma unroll
     for (int q = 0; q < QN; ++q) {
@@ -700,7 +719,7 @@ __global__ __launch_bounds__(kResolveSlots / NSL) void topk_resolve_kernel(
       }
     }
   };
-  if (tid < eager_nt) load_reports(0, eager_q, eager_nt);
+  if (eager_q > 0 && tid < eager_nt) load_eager(eager_q, eager_nt);
   const RowInfo ri = row_info(t, cu_q, ctx_len, B);
   const int64_t n = ri.p + 1;
   int32_t* out = idx + (int64_t)t * K;
@@ -725,28 +744,28 @@ __global__ __launch_bounds__(kResolveSlots / NSL) void topk_resolve_kernel(
     nt = threads_for(n);
     if (tid >= nt) return;
     R.qn = (int)((n + 4 * nt - 1) / (4 * nt));
+    // every group is loaded (straight-line loads, one round trip); groups
+    // past the row read position 0 and are invalid
 #pragma unroll
     for (int q = 0; q < QN; ++q) {
-      if (q < R.qn) {
-        const int p = slot_of(q, tid, nt);
-        float f[4];
-        if (vec) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(row + (p < n ? p : 0));
-          f[0] = v[0];
-          f[1] = v[1];
-          f[2] = v[2];
-          f[3] = v[3];
-        } else {
+      const int p = slot_of(q, tid, nt);
+      float f[4];
+      if (vec) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(row + (p < n ? p : 0));
+        f[0] = v[0];
+        f[1] = v[1];
+        f[2] = v[2];
+        f[3] = v[3];
+      } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) f[e] = row[p + e < n ? p + e : 0];
-        }
+        for (int e = 0; e < 4; ++e) f[e] = row[p + e < n ? p + e : 0];
+      }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool v = p + e < n;
-          R.u[4 * q + e] = v ? order_key(f[e]) : 0u;
-          R.j[4 * q + e] = p + e;
-          R.vmask |= (uint32_t)v << (4 * q + e);
-        }
+      for (int e = 0; e < 4; ++e) {
+        const bool v = p + e < n;
+        R.u[4 * q + e] = v ? order_key(f[e]) : 0u;
+        R.j[4 * q + e] = p + e;
+        R.vmask |= (uint32_t)v << (4 * q + e);
       }
     }
     path = 2;
@@ -757,7 +776,7 @@ __global__ __launch_bounds__(kResolveSlots / NSL) void topk_resolve_kernel(
       nt = max(threads_for((int64_t)nt_row * kRep), eager_nt);
       if (tid >= nt) return;
       R.qn = (nt_row * kRep + 4 * nt - 1) / (4 * nt);
-      if (nt != eager_nt)
+      if (nt != eager_nt || eager_q == 0)
         load_reports(0, R.qn, nt);  // another layout: load every group
       else if (R.qn > eager_q)
         load_reports(eager_q, R.qn, nt);

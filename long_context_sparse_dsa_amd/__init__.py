@@ -55,7 +55,7 @@ def load(path: str | None = None):
     global _lib
     if _lib is not None:
         return _lib
-    path = path or LIB_PATH
+    path = path or os.environ.get("DSA_LIBRARY") or LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(f"{path} not found: build it first "
                            "(python -m long_context_sparse_dsa_amd.build)")

@@ -150,3 +150,39 @@ def test_prefill_workspace_sizes(lib):
     # one query row: its fp32 score row plus small scratch, far below one pass
     assert 139264 * 4 < least < 8 * 1024 * 1024 < full
     assert lib.dsa_layer_prefill_min_workspace_size(0, 139264, 2048, 64, 128) == 0
+
+
+def test_workspace_sizes_over_a_grid_of_extreme_shapes(lib):
+    """Every size function over extreme but representable shapes: no
+    overflow (the sanitized build traps signed overflow), sizes grow with
+    the problem, and an empty batch needs nothing."""
+    prev = 0
+    for max_ctx in (1, 2047, 2048, 16384, 16385, 131072, 1 << 20, 1 << 24, (1 << 31) - 1):
+        d = lib.dsa_layer_decode_workspace_size(1, max_ctx, 2048, 64, 128)
+        assert d >= prev and d >= 4 * max_ctx
+        prev = d
+        for B in (1, 7, 1024, 4096):
+            for K in (1, 256, 2048, 4096):
+                assert lib.dsa_layer_decode_workspace_size(B, max_ctx, K, 8, 64) > 0
+                assert lib.dsa_topk_workspace_size(B, B, max_ctx, K) >= 0
+                assert lib.dsa_layer_prefill_min_workspace_size(B, max_ctx, K, 64, 128) > 0
+        assert lib.dsa_layer_prefill_workspace_size(1, 8192, max_ctx, 2048, 64, 128) > 0
+    for T in (1, 255, 256, 8192, 1 << 20):
+        assert lib.dsa_sparse_attn_workspace_size(1, T, 2048, 0, 64, 128) >= 0
+        assert lib.dsa_sparse_attn_workspace_size(8, T, 0, 128, 64, 128) >= 0
+    assert lib.dsa_layer_decode_workspace_size(0, 131072, 2048, 64, 128) >= 0
+    assert lib.dsa_layer_decode_noalloc_max_bytes() > 0
+
+
+def test_device_calls_without_a_device_report_a_hip_error(lib):
+    """On a host with no GPU the library loads, validation still answers,
+    and a well-formed call reports DSA_ERR_HIP instead of crashing."""
+    import torch
+    if torch.cuda.device_count() != 0:
+        pytest.skip("a GPU is visible: this check runs only where none is")
+    n = 4096
+    ws_bytes = lib.dsa_layer_decode_workspace_size(1, n, 256, 8, 64)
+    st = lib.dsa_layer_decode(FAKE, FAKE, 4, FAKE, 0, None, 4, 64, FAKE, FAKE, FAKE, FAKE, 1, 0.0,
+                              8, 64, 256, FAKE, FAKE, 1, n, FAKE, None, FAKE, ws_bytes, None)
+    assert st == 4
+    assert dsa.dsa_last_error()

@@ -303,6 +303,32 @@ dsa_status_t dsa_set_indexer_events(void* start, void* stop);
 /* none of them.  Pass NULL to stop.  Always DSA_OK.                        */
 dsa_status_t dsa_set_topk_counters(uint32_t* counters);
 
+/* Debug check of index rows (the Top-K output rows of the Architecture     */
+/* Breakdown's selection step, and the index rows the sparse attention     */
+/* gathers with).  For T rows of K int32 entries `idx` [T, K] on the        */
+/* device, with the batch descriptor giving each row's query position p,   */
+/* adds to four caller-owned device counters (uint32 [4], zeroed by the    */
+/* caller): [0] the entries outside [0, p] other than -1; with full != 0   */
+/* (rows that are Top-K outputs: K_eff = min(K, p + 1) positions ascending, */
+/* then -1 padding) [1] the neighbouring pairs that break that order and  */
+/* [2] the rows whose count of positions is not K_eff; [3] the rows        */
+/* checked.  Reads only idx and the descriptor (cu_q NULL: one row per     */
+/* sequence, at p = ctx_len[b] - 1).  Asynchronous on `stream`.             */
+/* Returns DSA_ERR_INVALID_ARG for a NULL or misaligned pointer, T or B    */
+/* out of range, or K < 1.                                                  */
+dsa_status_t dsa_check_index_rows(const int32_t* idx, int K, const int32_t* cu_q,
+                                  const int32_t* ctx_len, int B, int T, int full,
+                                  uint32_t* counters, void* stream);
+
+/* Debug hook: on the calling thread, every later selection (dsa_topk,      */
+/* dsa_layer_decode and its variants, dsa_layer_prefill) runs              */
+/* dsa_check_index_rows(full = 1) on the rows it selected, and every later  */
+/* dsa_sparse_attn call with index rows runs it (full = 0) on the caller's */
+/* rows before the attention, adding into `counters` (device uint32 [4],   */
+/* as above).  One extra small kernel per call while set.  Pass NULL to    */
+/* stop.  Always DSA_OK.                                                   */
+dsa_status_t dsa_set_index_checks(uint32_t* counters);
+
 /* ------------------------------------------------------------------------ */
 /* Whole layer, prefill: a chunk of new queries per sequence (cu_q given).   */
 /* Same steps; the indexer runs as a dense MFMA contraction of the chunk's   */

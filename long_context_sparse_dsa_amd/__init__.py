@@ -36,7 +36,7 @@ EXPORTS = [
     "dsa_sparse_attn_workspace_size", "dsa_sparse_attn", "dsa_swa_decode_layers",
     "dsa_layer_decode_workspace_size", "dsa_layer_decode", "dsa_set_indexer_events",
     "dsa_layer_decode_noalloc_max_bytes", "dsa_layer_decode_noalloc", "dsa_layer_decode_append",
-    "dsa_set_topk_counters",
+    "dsa_set_topk_counters", "dsa_check_index_rows", "dsa_set_index_checks",
     "dsa_layer_prefill_workspace_size", "dsa_layer_prefill_min_workspace_size",
     "dsa_layer_prefill",
 ]
@@ -92,11 +92,14 @@ def load(path: str | None = None):
                                              P, P, I, I, P, P, P]
     lib.dsa_set_indexer_events.argtypes = [P, P]
     lib.dsa_set_topk_counters.argtypes = [P]
+    lib.dsa_check_index_rows.argtypes = [P, I, P, P, I, I, I, P, P]
+    lib.dsa_set_index_checks.argtypes = [P]
     for fn in ("dsa_index_scores", "dsa_cache_append", "dsa_topk", "dsa_sparse_attn",
                "dsa_swa_decode_layers",
                "dsa_layer_decode",
                "dsa_layer_decode_noalloc", "dsa_layer_decode_append",
-               "dsa_layer_prefill", "dsa_set_indexer_events", "dsa_set_topk_counters"):
+               "dsa_layer_prefill", "dsa_set_indexer_events", "dsa_set_topk_counters",
+               "dsa_check_index_rows", "dsa_set_index_checks"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -632,6 +635,41 @@ def dsa_set_topk_counters(counters):
         assert counters.dtype == torch.int32
         assert counters.is_cuda and counters.numel() >= 5 and counters.is_contiguous()
     _call("dsa_set_topk_counters", None if counters is None else counters.data_ptr())
+
+
+def _check_counters(counters, n):
+    _check(counters, "counters", (torch.int32,), 1)
+    if counters.numel() < n:
+        raise ValueError(f"counters: need {n} entries, got {counters.numel()}")
+
+
+def dsa_check_index_rows(idx, ctx_len, cu_q=None, full=True, counters=None, stream=None):
+    """Debug check of index rows idx [T, K] (int32) against each row's query
+    position: adds into counters (int32 [4] on the device; a zeroed one is
+    made when None) the entries outside [0, p] other than -1, with `full`
+    the order breaks and the rows whose count is not min(K, p + 1), and the
+    rows checked.  Returns the counters tensor (not synchronised)."""
+    _check(idx, "idx", (torch.int32,), 2)
+    _check(ctx_len, "ctx_len", (torch.int32,), 1)
+    _check(cu_q, "cu_q", (torch.int32,), 1)
+    T, K = idx.shape
+    B = ctx_len.numel() if cu_q is None else cu_q.numel() - 1
+    if counters is None:
+        counters = torch.zeros(4, dtype=torch.int32, device=idx.device)
+    _check_counters(counters, 4)
+    _call("dsa_check_index_rows", _p(idx), K, _p(cu_q), _p(ctx_len), B, T, 1 if full else 0,
+          _p(counters), _stream(stream))
+    _keep_for(stream, counters)
+    return counters
+
+
+def dsa_set_index_checks(counters):
+    """Run the index-row check after every selection (and on the caller's rows
+    before dsa_sparse_attn gathers with them) on this thread, adding into a
+    caller-owned int32 [4] device tensor; None stops."""
+    if counters is not None:
+        _check_counters(counters, 4)
+    _call("dsa_set_index_checks", None if counters is None else counters.data_ptr())
 
 
 def dsa_layer_prefill_workspace_size(B, T, max_ctx, K, Hq, D) -> int:

@@ -8,8 +8,11 @@
 
 #include <hip/hip_runtime.h>
 
+#include <dlfcn.h>
+
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include <algorithm>
@@ -40,6 +43,52 @@ dsa_status_t hip_status(hipError_t e, const char* where) {
   if (e == hipSuccess) return ok();
   return fail(DSA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
 }
+
+// Optional roctx ranges (DSA_TRACE=1 in the environment): each entry point
+// that enqueues GPU work brackets its host side, so a profiler's marker
+// trace shows which call launched which kernels.  The marker library is
+// opened on first use, not linked.
+struct Roctx {
+  int (*push)(const char*);
+  int (*pop)();
+};
+
+const Roctx* roctx() {
+  static const Roctx* r = []() -> const Roctx* {
+    const char* e = std::getenv("DSA_TRACE");
+    if (e == nullptr || e[0] == '\0' || e[0] == '0') return nullptr;
+    // the profiler SDK's marker library (what rocprofv3 --marker-trace
+    // records), else the older roctracer one
+    void* h = nullptr;
+    for (const char* lib : {"librocprofiler-sdk-roctx.so.1", "librocprofiler-sdk-roctx.so",
+                            "/opt/rocm/lib/librocprofiler-sdk-roctx.so", "libroctx64.so",
+                            "/opt/rocm/lib/libroctx64.so"}) {
+      h = dlopen(lib, RTLD_NOW | RTLD_LOCAL);
+      if (h != nullptr) break;
+    }
+    if (h == nullptr) return nullptr;
+    static Roctx t;
+    t.push = reinterpret_cast<int (*)(const char*)>(dlsym(h, "roctxRangePushA"));
+    t.pop = reinterpret_cast<int (*)()>(dlsym(h, "roctxRangePop"));
+    return (t.push && t.pop) ? &t : nullptr;
+  }();
+  return r;
+}
+
+class TraceRange {
+ public:
+  explicit TraceRange(const char* name) : r_(roctx()) {
+    if (r_) r_->push(name);
+  }
+  ~TraceRange() {
+    if (r_) r_->pop();
+  }
+  TraceRange(const TraceRange&) = delete;
+  TraceRange& operator=(const TraceRange&) = delete;
+
+ private:
+  const Roctx* r_;
+};
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -147,6 +196,19 @@ size_t prefill_chunk_desc_bytes(int B) {
 
 // Caller-owned Top-K path counters (this thread), or null.
 thread_local uint32_t* t_topk_counters = nullptr;
+// Caller-owned index-row check counters (this thread), or null.
+thread_local uint32_t* t_idx_checks = nullptr;
+
+namespace {
+
+// The debug check of freshly selected index rows, while enabled.
+hipError_t check_selected(const int32_t* idx, int K, const int32_t* cu_q, const int32_t* ctx_len,
+                          int B, int T, hipStream_t s) {
+  if (t_idx_checks == nullptr) return hipSuccess;
+  return dsa::launch_check_index_rows(idx, K, cu_q, ctx_len, B, T, true, t_idx_checks, s);
+}
+
+}  // namespace
 
 namespace {
 
@@ -173,6 +235,7 @@ hipError_t prefill_pass(const void* q_idx, int q_dtype, const float* q_scale, co
       e = dsa::launch_topk_resolve(L.scores, L.ld, cu_q, ctx_len, B, T, K, L.topk, idx,
                                    t_topk_counters, s);
   }
+  if (e == hipSuccess) e = check_selected(idx, K, cu_q, ctx_len, B, T, s);
   if (e == hipSuccess) {
     const dsa::AttnPlan plan = dsa::attn_plan(T_plan, K, 0, Hq, D);
     e = dsa::launch_sparse_attn(q, k_cache, v_cache, idx, K, 0, gate, gstride, sm_scale, Hq, D,
@@ -271,6 +334,7 @@ dsa_status_t dsa_index_scores(const void* q_idx, int q_dtype, const float* q_sca
                               const int32_t* cu_q, const int32_t* ctx_len, const int64_t* cu_ctx,
                               int B, int T, int max_q, int max_ctx, float* scores, int64_t ld,
                               void* stream) {
+  TraceRange tr("dsa_index_scores");
   DSA_PTR(q_idx, "q_idx");
   {
     const dsa_status_t qs = check_query_dtype(q_dtype, q_scale, k_dtype);
@@ -315,6 +379,7 @@ size_t dsa_topk_workspace_size(int B, int T, int max_ctx, int K) {
 dsa_status_t dsa_topk(const float* scores, int64_t ld, const int32_t* cu_q,
                       const int32_t* ctx_len, int B, int T, int max_q, int max_ctx, int K,
                       int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  TraceRange tr("dsa_topk");
   DSA_PTR(scores, "scores");
   DSA_PTR(idx, "idx");
   dsa_status_t st = check_batch(cu_q, ctx_len, nullptr, false, B, T, max_q, max_ctx);
@@ -331,11 +396,12 @@ dsa_status_t dsa_topk(const float* scores, int64_t ld, const int32_t* cu_q,
   hipError_t e;
   if (dsa::topk_use_rows(T)) {
     e = dsa::launch_topk_rows(scores, ld, cu_q, ctx_len, B, T, K, idx, t_topk_counters, s);
-    return hip_status(e, "dsa_topk");
+  } else {
+    e = dsa::launch_tile_reports(scores, ld, cu_q, ctx_len, B, T, K, w, s);
+    if (e == hipSuccess) e = dsa::launch_topk_resolve(scores, ld, cu_q, ctx_len, B, T, K, w, idx,
+                                                      t_topk_counters, s);
   }
-  e = dsa::launch_tile_reports(scores, ld, cu_q, ctx_len, B, T, K, w, s);
-  if (e == hipSuccess) e = dsa::launch_topk_resolve(scores, ld, cu_q, ctx_len, B, T, K, w, idx,
-                                                    t_topk_counters, s);
+  if (e == hipSuccess) e = check_selected(idx, K, cu_q, ctx_len, B, T, s);
   return hip_status(e, "dsa_topk");
 }
 
@@ -344,6 +410,7 @@ dsa_status_t dsa_cache_append(const void* k_idx_new, int d_I, const void* k_new,
                               const int32_t* ctx_len, const int64_t* cu_ctx, int B, int T,
                               void* k_idx_cache, int k_dtype, float* k_scale_cache,
                               void* k_cache, void* v_cache, void* stream) {
+  TraceRange tr("dsa_cache_append");
   DSA_REQUIRE(B >= 1 && T >= 1, DSA_ERR_INVALID_ARG, "B and T must be >= 1 (got %d, %d)", B, T);
   DSA_REQUIRE(ctx_len != nullptr && cu_ctx != nullptr, DSA_ERR_INVALID_ARG,
               "ctx_len and cu_ctx must not be NULL");
@@ -390,6 +457,7 @@ dsa_status_t dsa_sparse_attn(const void* q, const void* k_cache, const void* v_c
                              const int32_t* ctx_len, const int64_t* cu_ctx, int B, int T,
                              int max_q, int max_ctx, void* out, float* lse, void* ws,
                              size_t ws_bytes, void* stream) {
+  TraceRange tr("dsa_sparse_attn");
   DSA_PTR(q, "q");
   DSA_PTR(k_cache, "k_cache");
   DSA_PTR(v_cache, "v_cache");
@@ -415,10 +483,14 @@ dsa_status_t dsa_sparse_attn(const void* q, const void* k_cache, const void* v_c
   DSA_REQUIRE(ws_bytes >= plan.ws_bytes, DSA_ERR_WORKSPACE,
               "workspace too small: %zu < %zu bytes", ws_bytes, plan.ws_bytes);
   if (plan.ws_bytes) DSA_PTR(ws, "ws");
-  hipError_t e = dsa::launch_sparse_attn(q, k_cache, v_cache, idx, K, idx ? 0 : window, gate,
-                                         (int)gate_stride_d, sm_scale, Hq, D, cu_q, ctx_len,
-                                         cu_ctx, B, T, out, lse, ws, plan,
-                                         static_cast<hipStream_t>(stream));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (idx && t_idx_checks)  // the caller's rows, before they are gathered with
+    e = dsa::launch_check_index_rows(idx, K, cu_q, ctx_len, B, T, false, t_idx_checks, s);
+  if (e == hipSuccess)
+    e = dsa::launch_sparse_attn(q, k_cache, v_cache, idx, K, idx ? 0 : window, gate,
+                                (int)gate_stride_d, sm_scale, Hq, D, cu_q, ctx_len, cu_ctx, B, T,
+                                out, lse, ws, plan, s);
   return hip_status(e, "dsa_sparse_attn");
 }
 
@@ -427,6 +499,7 @@ dsa_status_t dsa_swa_decode_layers(int n_layers, const void* const* q, const voi
                                    int64_t gate_stride_d, int window, float sm_scale, int Hq,
                                    int D, const int32_t* ctx_len, const int64_t* cu_ctx, int B,
                                    int max_ctx, void* const* out, void* stream) {
+  TraceRange tr("dsa_swa_decode_layers");
   DSA_REQUIRE(n_layers >= 1 && n_layers <= dsa::kMaxAttnLayers, DSA_ERR_UNSUPPORTED,
               "n_layers must be in [1, %d] (got %d)", dsa::kMaxAttnLayers, n_layers);
   DSA_REQUIRE(q && k_cache && v_cache && out, DSA_ERR_INVALID_ARG,
@@ -479,6 +552,27 @@ thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
 dsa_status_t dsa_set_topk_counters(uint32_t* counters) {
   t_topk_counters = counters;
   return DSA_OK;
+}
+
+dsa_status_t dsa_set_index_checks(uint32_t* counters) {
+  t_idx_checks = counters;
+  return DSA_OK;
+}
+
+dsa_status_t dsa_check_index_rows(const int32_t* idx, int K, const int32_t* cu_q,
+                                  const int32_t* ctx_len, int B, int T, int full,
+                                  uint32_t* counters, void* stream) {
+  TraceRange tr("dsa_check_index_rows");
+  DSA_PTR(idx, "idx");
+  DSA_PTR(counters, "counters");
+  DSA_REQUIRE(ctx_len != nullptr, DSA_ERR_INVALID_ARG, "ctx_len must not be NULL");
+  DSA_REQUIRE(B >= 1 && T >= 1, DSA_ERR_INVALID_ARG, "B and T must be >= 1 (got %d, %d)", B, T);
+  DSA_REQUIRE(cu_q != nullptr || T == B, DSA_ERR_INVALID_ARG,
+              "cu_q == NULL means one row per sequence: T (%d) must equal B (%d)", T, B);
+  DSA_REQUIRE(K >= 1, DSA_ERR_INVALID_ARG, "K must be >= 1 (got %d)", K);
+  const hipError_t e = dsa::launch_check_index_rows(idx, K, cu_q, ctx_len, B, T, full != 0,
+                                                    counters, static_cast<hipStream_t>(stream));
+  return hip_status(e, "dsa_check_index_rows");
 }
 
 dsa_status_t dsa_set_indexer_events(void* start, void* stop) {
@@ -549,6 +643,7 @@ static dsa_status_t layer_decode_impl(
                                      t_topk_counters, s)
              : dsa::launch_topk_resolve(L.scores, L.ld, nullptr, ctx_len, B, B, K, L.topk, idx,
                                         t_topk_counters, s);
+  if (e == hipSuccess) e = check_selected(idx, K, nullptr, ctx_len, B, B, s);
   if (e == hipSuccess) {
     const dsa::AttnPlan plan = dsa::attn_plan(B, K, 0, Hq, D);
     e = dsa::launch_sparse_attn(q, k_cache, v_cache, idx, K, 0, gate, (int)gate_stride_d,
@@ -565,6 +660,7 @@ dsa_status_t dsa_layer_decode(const void* q_idx, const void* w, int64_t w_ld, co
                               const int32_t* ctx_len, const int64_t* cu_ctx, int B, int max_ctx,
                               void* out, int32_t* idx_out, void* ws, size_t ws_bytes,
                               void* stream) {
+  TraceRange tr("dsa_layer_decode");
   return layer_decode_impl(q_idx, w, w_ld, k_idx, k_dtype, k_scale, H_I, d_I, q, k_cache,
                            v_cache, gate, gate_stride_d, sm_scale, Hq, D, K, ctx_len, cu_ctx, B,
                            max_ctx, out, idx_out, ws, ws_bytes, nullptr, stream,
@@ -579,6 +675,7 @@ dsa_status_t dsa_layer_decode_append(const void* q_idx, const void* w, int64_t w
                                      int max_ctx, const void* k_idx_new, const void* k_new,
                                      const void* v_new, void* out, int32_t* idx_out, void* ws,
                                      size_t ws_bytes, void* stream) {
+  TraceRange tr("dsa_layer_decode_append");
   dsa::DecodeAppend app;
   app.k_idx_new = static_cast<const uint16_t*>(k_idx_new);
   app.k_new = static_cast<const uint16_t*>(k_new);
@@ -603,6 +700,7 @@ dsa_status_t dsa_layer_decode_noalloc(const void* q_idx, const void* w, int64_t 
                                       int64_t gate_stride_d, float sm_scale, int Hq, int D, int K,
                                       const int32_t* ctx_len, const int64_t* cu_ctx, int B,
                                       int max_ctx, void* out, int32_t* idx_out, void* stream) {
+  TraceRange tr("dsa_layer_decode_noalloc");
   // the size check comes first: an oversize call is refused without
   // touching the GPU
   DSA_REQUIRE(B >= 1 && max_ctx >= 1 && K >= 1, DSA_ERR_INVALID_ARG,
@@ -643,6 +741,7 @@ dsa_status_t dsa_layer_prefill(const void* q_idx, int q_dtype, const float* q_sc
                                const int64_t* cu_ctx, int B, int T, int max_q, int max_ctx,
                                void* out, int32_t* idx_out, void* ws, size_t ws_bytes,
                                void* stream) {
+  TraceRange tr("dsa_layer_prefill");
   DSA_PTR(q_idx, "q_idx");
   DSA_PTR(w, "w");
   DSA_PTR(k_idx, "k_idx");

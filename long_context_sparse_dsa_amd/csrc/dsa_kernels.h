@@ -117,4 +117,10 @@ hipError_t launch_cache_append(const void* k_idx_new, int d_I, const void* k_new
                                void* k_idx_cache, int k_dtype, float* k_scale_cache,
                                void* k_cache, void* v_cache, hipStream_t stream);
 
+// Debug check of T index rows of K entries (counters: see dsa.h,
+// dsa_check_index_rows).  full: the rows are Top-K outputs.
+hipError_t launch_check_index_rows(const int32_t* idx, int K, const int32_t* cu_q,
+                                   const int32_t* ctx_len, int B, int T, bool full,
+                                   uint32_t* counters, hipStream_t stream);
+
 }  // namespace dsa

@@ -9,6 +9,9 @@
 // ctx_len - n_q .. ctx_len - 1, the rows in the range are queries
 // i0 .. i0 + n' - 1, which a descriptor with n' queries and context length
 // ctx_len - n_q + i0 + n' places at the same positions.
+//
+// cache_append_kernel: the new tokens' rows into the caches.
+// check_index_rows_kernel: the debug check of index rows.
 #include "dsa_kernels.h"
 #include "dsa_device.h"
 
@@ -104,6 +107,53 @@ hipError_t launch_cache_append(const void* k_idx_new, int d_I, const void* k_new
     return hipErrorInvalidValue;
   }
 #undef DSA_APPEND
+  return hipGetLastError();
+}
+
+// check_index_rows_kernel: one workgroup per index row t (K entries), p its
+// query's position.  Counts in c[0] the entries outside [0, p] other than
+// -1; with `full` (a Top-K output: K_eff = min(K, p + 1) ascending
+// positions, then -1 padding) also, in c[1], the neighbouring pairs that
+// break that order (a -1 before a position, or positions not increasing)
+// and, in c[2], the rows whose count of positions is not K_eff; c[3]
+// counts the rows checked.  Reads only idx and the batch descriptor.
+__global__ __launch_bounds__(256) void check_index_rows_kernel(const int32_t* __restrict__ idx,
+                                                               int K, const int32_t* cu_q,
+                                                               const int32_t* ctx_len, int B,
+                                                               int full, uint32_t* c) {
+  __shared__ uint32_t nvalid;
+  const int t = blockIdx.x;
+  const RowInfo ri = row_info(t, cu_q, ctx_len, B);
+  const int32_t* row = idx + (int64_t)t * K;
+  if (threadIdx.x == 0) nvalid = 0;
+  __syncthreads();
+  uint32_t bad = 0, order = 0, valid = 0;
+  for (int i = threadIdx.x; i < K; i += blockDim.x) {
+    const int32_t j = row[i];
+    bad += (j < -1 || (int64_t)j > ri.p) ? 1u : 0u;
+    valid += j >= 0 ? 1u : 0u;
+    if (full && i + 1 < K) {
+      const int32_t n = row[i + 1];
+      order += ((j < 0 && n >= 0) || (j >= 0 && n >= 0 && n <= j)) ? 1u : 0u;
+    }
+  }
+  if (bad) atomicAdd(&c[0], bad);
+  if (order) atomicAdd(&c[1], order);
+  atomicAdd(&nvalid, valid);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int64_t keff = ri.p + 1 < (int64_t)K ? ri.p + 1 : (int64_t)K;
+    if (full && (int64_t)nvalid != keff) atomicAdd(&c[2], 1u);
+    atomicAdd(&c[3], 1u);
+  }
+}
+
+hipError_t launch_check_index_rows(const int32_t* idx, int K, const int32_t* cu_q,
+                                   const int32_t* ctx_len, int B, int T, bool full,
+                                   uint32_t* counters, hipStream_t stream) {
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(check_index_rows_kernel, dim3(T), dim3(256), 0, stream, idx, K, cu_q,
+                     ctx_len, B, full ? 1 : 0, counters);
   return hipGetLastError();
 }
 

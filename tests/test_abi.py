@@ -186,3 +186,32 @@ def test_device_calls_without_a_device_report_a_hip_error(lib):
                               8, 64, 256, FAKE, FAKE, 1, n, FAKE, None, FAKE, ws_bytes, None)
     assert st == 4
     assert dsa.dsa_last_error()
+
+
+def test_index_check_validation(lib):
+    f = lib.dsa_check_index_rows
+    assert f(None, 16, None, FAKE, 1, 1, 1, FAKE, None) == 1 and "idx" in dsa.dsa_last_error()
+    assert f(FAKE, 0, None, FAKE, 1, 1, 1, FAKE, None) == 1 and "K must be" in dsa.dsa_last_error()
+    assert f(FAKE, 16, None, FAKE, 2, 3, 1, FAKE, None) == 1
+    assert f(FAKE, 16, None, None, 1, 1, 1, FAKE, None) == 1
+    assert f(FAKE, 16, None, FAKE, 1, 1, 1, FAKE_MIS, None) == 1
+    assert lib.dsa_set_index_checks(None) == 0
+
+
+def test_trace_ranges_load_on_demand():
+    """DSA_TRACE=1 opens the roctx library on the first call that would
+    enqueue work; validation and error reporting behave as without it."""
+    import subprocess
+    import sys
+    code = ("import ctypes, long_context_sparse_dsa_amd as dsa\n"
+            "lib = dsa.load()\n"
+            "F = ctypes.c_void_p(0x10000)\n"
+            "st = lib.dsa_topk(F, 100, None, F, 1, 1, 1, 100, 0, F, F, 1 << 20, None)\n"
+            "assert st == 2, st\n"
+            "assert 'K must be' in dsa.dsa_last_error()\n"
+            "print('trace ok')\n")
+    env = dict(os.environ, DSA_TRACE="1")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env,
+                       cwd=ROOT, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert "trace ok" in r.stdout

@@ -870,6 +870,88 @@ def test_layer_prefill_smallest_workspace(dsa):
         _run_prefill(dsa, w, d, torch.empty(nb - 256, dtype=torch.uint8, device=DEV))
 
 
+def test_index_checks_report_nothing_on_clean_calls(dsa):
+    """With the index-row checks on, a ragged decode layer, a sub-chunked
+    prefill layer, a batched dsa_topk and an attention call over the decode
+    layer's own rows report no violation, and every row is checked once."""
+    say("index-row checks on clean decode, prefill, topk and attention calls")
+    c = torch.zeros(4, dtype=torch.int32, device=DEV)
+    dsa.dsa_set_index_checks(c)
+    try:
+        w = wl("t", [3000, 100, 70000, 2048, 2049], [1] * 5, 16, 128, 64, 128, 2048, seed=31,
+               plant_frac=0.05)
+        d = to_dev(W.make_inputs(w))
+        L = max(w.ctx_lens)
+        idx = torch.empty(w.B, w.K, dtype=torch.int32, device=DEV)
+        ws = torch.empty(dsa.dsa_layer_decode_workspace_size(w.B, L, w.K, w.Hq, w.D),
+                         dtype=torch.uint8, device=DEV)
+        dsa.dsa_layer_decode(d["q_idx"], d["w"], d["k_idx"], d["k_scale"], d["q"], d["k_cache"],
+                             d["v_cache"], d["gate"], w.K, d["ctx_len"], d["cu_ctx"], max_ctx=L,
+                             idx_out=idx, ws=ws)
+        dsa.dsa_sparse_attn(d["q"], d["k_cache"], d["v_cache"], idx, d["ctx_len"], d["cu_ctx"],
+                            gate=d["gate"], max_ctx=L)
+        rows = 2 * w.B
+        w2 = _prefill_small()
+        d2 = W.make_inputs(w2, device=DEV)
+        L2 = max(w2.ctx_lens)
+        small = (dsa.dsa_layer_prefill_workspace_size(w2.B, 900, L2, w2.K, w2.Hq, w2.D) +
+                 dsa.dsa_layer_prefill_min_workspace_size(w2.B, L2, w2.K, w2.Hq, w2.D))
+        _run_prefill(dsa, w2, d2, torch.empty(small, dtype=torch.uint8, device=DEV))
+        rows += w2.T
+        lens, nq = [9000, 300, 50000], [5, 300, 40]
+        g = torch.Generator().manual_seed(3)
+        sc = torch.randn(sum(nq), max(lens), generator=g).to(DEV)
+        cu_q = torch.tensor(np.concatenate([[0], np.cumsum(nq)]), dtype=torch.int32, device=DEV)
+        dsa.dsa_topk(sc, 2048, torch.tensor(lens, dtype=torch.int32, device=DEV), cu_q=cu_q,
+                     max_ctx=max(lens))
+        rows += sum(nq)
+        torch.cuda.synchronize()
+    finally:
+        dsa.dsa_set_index_checks(None)
+    got = c.cpu().numpy().tolist()
+    assert got == [0, 0, 0, rows], got
+
+
+def test_index_check_counts_planted_faults(dsa):
+    """dsa_check_index_rows alone (no attention) on host-built rows with
+    planted faults: its counts equal the same counts taken on the host."""
+    say("index-row check on planted faults")
+    g = np.random.default_rng(9)
+    lens = [40, 3000, 700, 5]
+    K = 64
+    rows = []
+    for n in lens:
+        keff = min(K, n)
+        r = np.sort(g.choice(n, size=keff, replace=False)).astype(np.int32)
+        rows.append(np.concatenate([r, np.full(K - keff, -1, np.int32)]))
+    idx = np.stack(rows)
+    idx[0, 3] = 40          # past p = 39
+    idx[1, 10] = -7         # below -1
+    idx[1, 20], idx[1, 21] = idx[1, 21], idx[1, 20]   # a descending pair
+    idx[2, 0] = -1          # a -1 before positions (and one position fewer)
+    idx[3, 5] = 4           # a position in the padding (one more than K_eff = 5)
+
+    def host_counts(full):
+        bad = order = wrong = 0
+        for t, n in enumerate(lens):
+            r = idx[t]
+            bad += int(np.sum((r < -1) | (r > n - 1)))
+            if full:
+                a, b = r[:-1], r[1:]
+                order += int(np.sum(((a < 0) & (b >= 0)) | ((a >= 0) & (b >= 0) & (b <= a))))
+                wrong += int(np.sum(r >= 0) != min(K, n))
+        return [bad, order if full else 0, wrong if full else 0, len(lens)]
+
+    ctx = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    d_idx = torch.from_numpy(idx).to(DEV)
+    for full in (True, False):
+        c = dsa.dsa_check_index_rows(d_idx, ctx, full=full)
+        torch.cuda.synchronize()
+        got = c.cpu().numpy().tolist()
+        assert got == host_counts(full), (full, got, host_counts(full))
+        assert got[0] == 2
+
+
 def test_internal_workspaces_on_a_side_stream(dsa):
     """Calls on a stream that is not the current one, with the binding's own
     workspaces: while they run, the current stream allocates and overwrites

@@ -291,16 +291,18 @@ dsa_status_t dsa_set_indexer_events(void* start, void* stop);
 
 /* Diagnostic hook: on the calling thread, every later Top-K selection     */
 /* (dsa_topk, dsa_layer_decode, dsa_layer_prefill) adds, per row, 1 to one  */
-/* of the first four of five caller-owned device counters (uint32 [5],     */
-/* zeroed by the caller) naming the path that produced the row: [0] the     */
-/* union of the row's sub-tile candidate reports, certified exact; [1] the  */
-/* exact radix select over the whole score row (certification failed, or a  */
-/* key shared by too many positions); [2] the direct select of a row of at  */
-/* most 16384 positions; [3] the collection sweep over the row's scores     */
-/* used when a call has 1024 rows or more.  [4] counts the rows of [3]      */
-/* whose collection threshold came from a sample of the row (one sweep      */
-/* instead of histogram sweeps first).  Rows with at most K positions take  */
-/* none of them.  Pass NULL to stop.  Always DSA_OK.                        */
+/* of six caller-owned device counters (uint32 [6], zeroed by the caller)   */
+/* naming the path that produced the row: [0] the union of the row's        */
+/* sub-tile candidate reports, certified exact; [1] the exact radix select  */
+/* over the whole score row (a key shared by too many positions, or keys    */
+/* too many for [5]); [2] the direct select of a row of at most 16384       */
+/* positions; [3] the collection sweep over the row's scores used when a    */
+/* call has 1024 rows or more; [5] a report union whose certification       */
+/* failed, resolved by one collection sweep of the row's keys at or above   */
+/* the union's K-th best key.  [4] counts the rows of [3] whose collection  */
+/* threshold came from a sample of the row (one sweep instead of histogram  */
+/* sweeps first).  Rows with at most K positions take none of them.  Pass   */
+/* NULL to stop.  Always DSA_OK.                                            */
 dsa_status_t dsa_set_topk_counters(uint32_t* counters);
 
 /* Debug check of index rows (the Top-K output rows of the Architecture     */

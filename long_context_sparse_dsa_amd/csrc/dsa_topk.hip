@@ -333,11 +333,17 @@ __device__ __forceinline__ void union_threshold(SM& sm, const UnionRegs<NSL>& R,
 // registers.  With ntiles > 0 the set is a report union and is certified
 // against the sub-tile headers kept in sm.wu / sm.wj.  Returns false,
 // leaving `out` untouched, when the set has fewer than k candidates or the
-// certification fails.  nt: active threads.
+// certification fails.  nt: active threads.  When the set holds at least k
+// candidates, *theta (if given) receives the key of its k-th best and
+// *has_theta is set, whether or not the certification holds; when the
+// certification fails, *nbad (if given) receives the number of sub-tiles
+// that failed it.
 template <int NSL, class SM>
 __device__ __forceinline__ bool select_from_regs(SM& sm, const UnionRegs<NSL>& R,
                                                  uint32_t k, int K, int ntiles, int nt,
-                                                 int32_t* out) {
+                                                 int32_t* out, uint32_t* theta = nullptr,
+                                                 bool* has_theta = nullptr,
+                                                 uint32_t* nbad = nullptr) {
   const int tid = threadIdx.x, l = lane_id(), wv = wave_id();
   // candidate count and key range, in one block reduction; both histograms
   // are cleared meanwhile
@@ -377,6 +383,10 @@ __device__ __forceinline__ bool select_from_regs(SM& sm, const UnionRegs<NSL>& R
   uint32_t tau_u;
   int32_t tau_j;
   union_threshold(sm, R, k, mn, mx, nt, &tau_u, &tau_j);
+  if (theta) {
+    *theta = tau_u;
+    *has_theta = true;
+  }
   // certification: every partly reported sub-tile ends at or below theta
   // (checked in the same block exchange as the ranks)
   bool bad = false;
@@ -403,6 +413,19 @@ __device__ __forceinline__ bool select_from_regs(SM& sm, const UnionRegs<NSL>& R
   ordered_ranks<NSL>(sm, smask, R.qn, nt, rk, &total, bad, &any_bad, false);
   if (any_bad) {
     lds_barrier();  // the caller's exact select reuses sm.red
+    if (nbad) {  // the failing sub-tiles, counted (this path only)
+      uint32_t c = 0;
+      for (int ti = tid; ti < ntiles; ti += nt) {
+        const uint32_t wu = sm.wu[ti], wj = sm.wj[ti];
+        const int32_t wpos = (int32_t)(wj & 0x7fffffffu);
+        c += (!(wj >> 31) && !((wu < tau_u) || (wu == tau_u && wpos >= tau_j))) ? 1u : 0u;
+      }
+      c = wave_sum_u32(c);
+      if (l == 0) sm.red[wv] = c;
+      lds_barrier();
+      *nbad = wave_sum_u32(l < (nt >> 6) ? sm.red[l] : 0u);
+      lds_barrier();
+    }
     return false;
   }
   // each selected slot's position goes to its rank in LDS (the histograms
@@ -655,10 +678,99 @@ __device__ __forceinline__ void exact_select_row(SM& sm, const float* row, int64
   }
 }
 
+// Ordered collection of every key of a row at or above `lo` into cu / cj
+// (position order, the first `cap` of them; the rest are only counted):
+// rounds of 8 consecutive keys per thread, the next round's loads in
+// flight while the current one is ranked with a block prefix sum.  Stops
+// once more than `cap` keys were seen; returns the count (block-uniform).
+template <class SM>
+__device__ uint32_t collect_keys_at_least(SM& sm, const float* row, int64_t n, bool vec,
+                                          uint32_t lo, uint32_t* cu, int32_t* cj, uint32_t cap,
+                                          int nt) {
+  constexpr int PER = 8;
+  const int tid = threadIdx.x, nw = nt >> 6;
+  const int64_t step = PER * (int64_t)nt;
+  uint32_t ua[PER], ub[PER];
+  uint32_t cum = 0, par = 0;
+  auto rank = [&](const uint32_t(&u)[PER], uint32_t vm, int64_t p0) {
+    uint32_t f = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) f |= (uint32_t)(u[i] >= lo) << i;
+    f &= vm;
+    uint32_t tot;
+    uint32_t r = cum + excl_scan_pingpong(sm, (uint32_t)__popc(f), nw, par++, &tot);
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if ((f >> i) & 1u) {
+        if (r < cap) {
+          cu[r] = u[i];
+          cj[r] = (int32_t)(p0 + i);
+        }
+        ++r;
+      }
+    cum += tot;
+  };
+  uint32_t va = load_keys<PER>(row, n, PER * tid, vec, ua);
+#pragma unroll 1
+  for (int64_t b0 = 0; b0 < n && cum <= cap; b0 += 2 * step) {
+    const uint32_t vb = load_keys<PER>(row, n, b0 + step + PER * tid, vec, ub);
+    rank(ua, va, b0 + PER * tid);
+    if (b0 + step >= n || cum > cap) break;
+    va = load_keys<PER>(row, n, b0 + 2 * step + PER * tid, vec, ua);
+    rank(ub, vb, b0 + step + PER * tid);
+  }
+  lds_barrier();  // the collected keys are in LDS; sm.scan is free again
+  return cum;
+}
+
+constexpr int kRefineCap = 4096;  // keys a failed union's second chance collects
+
+// The second chance of a report union that failed its certification: every
+// key of the row at or above theta (the union's K-th best, at most the
+// row's) collected in one ordered sweep and, if they fit, the K best of
+// them selected by the register path.  Returns false if they do not fit.
+// Its register path holds 4 slots per thread (4096 keys in a block of
+// 1024 threads), so that it needs fewer registers than the union's path
+// and leaves the resolve's register allocation as it is.
+__device__ __forceinline__ bool resolve_by_collection(ResolveSmem& sm, const float* row,
+                                                      int64_t n, bool vec, uint32_t theta,
+                                                      uint32_t k, int K, int nt, int32_t* out) {
+  constexpr int NSL = 4, QN = 1;
+  __shared__ uint32_t fb_u[kRefineCap];
+  __shared__ int32_t fb_j[kRefineCap];
+  const int tid = threadIdx.x;
+  const uint32_t cap = min((uint32_t)kRefineCap, (uint32_t)(nt * NSL));
+  const uint32_t C = collect_keys_at_least(sm, row, n, vec, theta, fb_u, fb_j, cap, nt);
+  if (C > cap) return false;  // k <= C: the union's top K are among them
+  UnionRegs<NSL> R;
+  R.vmask = 0;
+  R.qn = (int)((C + 4 * nt - 1) / (4 * nt));
+#pragma unroll
+  for (int q = 0; q < QN; ++q) {
+    const int s0 = slot_of(q, tid, nt);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool v = (uint32_t)(s0 + e) < C;
+      R.u[4 * q + e] = v ? fb_u[s0 + e] : 0u;
+      R.j[4 * q + e] = v ? fb_j[s0 + e] : 0;
+      R.vmask |= (uint32_t)v << (4 * q + e);
+    }
+  }
+  return select_from_regs(sm, R, k, K, 0, nt, out);  // C >= k: always succeeds
+}
+
 // One workgroup per row.  Rows of at most kDirectMax positions are selected
 // from their scores directly; longer rows from the union of their sub-tile
 // reports, certified; anything else (a failed certification, more
 // sub-tiles than the block holds) by the exact select over the row.
+//
+// A failed certification still leaves a bound: the union is part of the
+// row, so its K-th best key theta is at most the row's K-th best, and every
+// key of the row's top K is at or above theta.  Such a row first collects
+// the keys at or above theta in one ordered sweep; when they fit (a few
+// sub-tiles that held more than 16 winners add at most S - 16 keys each)
+// the K best of them are the row's, found by the same register path.  Only
+// rows whose collection overflows take the exact select.
 //
 // The block is sized for the most slots any row may need; a row that needs
 // fewer threads lets the surplus waves exit before the first barrier (a
@@ -737,6 +849,7 @@ __global__ __launch_bounds__(kResolveSlots / NSL) void topk_resolve_kernel(
   };
   int path = -1;   // counter index of the register path taken: 0 union, 2 direct
   int ntiles = 0;  // sub-tiles to certify (union path)
+  int sub_s = 0;   // their size
   int nt = nb;     // active threads
   R.vmask = 0;
   if (n <= kDirectMax && n <= (int64_t)nb * NSL) {
@@ -771,6 +884,7 @@ __global__ __launch_bounds__(kResolveSlots / NSL) void topk_resolve_kernel(
     path = 2;
   } else {
     const int S = topk_subtile(n, K);
+    sub_s = S;
     const int nt_row = (int)((n + S - 1) >> (31 - __clz(S)));  // S: a power of two
     if (nt_row <= kResolveTiles && nt_row <= stride && nt_row * kRep <= nb * NSL) {
       nt = max(threads_for((int64_t)nt_row * kRep), eager_nt);
@@ -801,9 +915,23 @@ __global__ __launch_bounds__(kResolveSlots / NSL) void topk_resolve_kernel(
     }
   }
   bool ok = false;
+  uint32_t theta = 0, nbad = 0;
+  bool has_theta = false;
   if (path >= 0) {
-    ok = select_from_regs(sm, R, k, K, ntiles, nt, out);
+    ok = select_from_regs(sm, R, k, K, ntiles, nt, out, &theta, &has_theta, &nbad);
     if (ok && stats && tid == 0) atomicAdd(&stats[path], 1u);
+  }
+  // A report union that failed its certification bounds the row: its keys
+  // at or above theta are at most K plus the failing sub-tiles' left-out
+  // elements (S - 16 each, ties at theta aside); the second chance is tried
+  // when that bound fits its slots.
+  const bool bounded =
+      !ok && path == 0 && has_theta &&
+      (uint64_t)K + (uint64_t)nbad * (uint64_t)(sub_s - kRep) <=
+          (uint64_t)min(kRefineCap, nt * 4);
+  if (bounded) {
+    ok = resolve_by_collection(sm, row, n, vec, theta, k, K, nt, out);
+    if (ok && stats && tid == 0) atomicAdd(&stats[5], 1u);
   }
   if (!ok) {
     exact_select_row(sm, row, n, k, vec, nt, out);

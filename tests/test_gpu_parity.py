@@ -186,7 +186,7 @@ RAGGED_TOPK_LENS = [5000, 16384, 16385, 20000, 31000, 70000, 131071, 131072, 300
 
 
 def _with_counters(dsa, fn):
-    cnt = torch.zeros(5, dtype=torch.int32, device=DEV)
+    cnt = torch.zeros(6, dtype=torch.int32, device=DEV)
     dsa.dsa_set_topk_counters(cnt)
     try:
         res = fn()
@@ -214,6 +214,10 @@ def test_topk_ragged_rows_subtile_reports(dsa, kind):
 
 
 def test_topk_clustered_rows_take_the_exact_fallback(dsa):
+    """Every winner inside 3000 consecutive positions: the report unions
+    fail their certification and the keys at or above each union's K-th
+    best overflow the second chance's 4096 slots, so the rows take the
+    exact select over the whole row."""
     say("topk clustered winners: exact fallback")
     lens, K = [40000, 131072, 70001], 2048
     L = max(lens)
@@ -224,7 +228,30 @@ def test_topk_clustered_rows_take_the_exact_fallback(dsa):
     got, c = _with_counters(dsa, lambda: dsa.dsa_topk(s.to(DEV), K, ctx.to(DEV), max_ctx=L))
     want = oracle.topk(s.numpy(), K, ctx.numpy())
     assert np.array_equal(got.cpu().numpy(), want)
-    assert c[1] == len(lens)
+    assert c[1] == len(lens) and c[5] == 0
+
+
+@pytest.mark.parametrize("width", [300, 700, 1500])
+def test_topk_failed_certification_takes_one_collection_sweep(dsa, width):
+    """A few hundred winners packed together: the sub-tiles holding them
+    report only 16 each, so the union fails its certification; the keys of
+    each row at or above the union's K-th best (the packed winners plus
+    about K others) fit 4096 slots and are selected in one collection sweep.
+    Bit-exact against the oracle; every row takes that path."""
+    say(f"topk failed certification, {width} packed winners: one collection sweep")
+    lens, K = [40000, 131072, 70001, 300000], 2048
+    L = max(lens)
+    s = torch.zeros(len(lens), L)
+    for i, n in enumerate(lens):
+        g = torch.Generator().manual_seed(90 + i)
+        x = torch.randn(n, generator=g)
+        x[n // 2: n // 2 + width] += 10.0
+        s[i, :n] = x
+    ctx = torch.tensor(lens, dtype=torch.int32)
+    got, c = _with_counters(dsa, lambda: dsa.dsa_topk(s.to(DEV), K, ctx.to(DEV), max_ctx=L))
+    want = oracle.topk(s.numpy(), K, ctx.numpy())
+    assert np.array_equal(got.cpu().numpy(), want)
+    assert c[5] == len(lens) and c[1] == 0 and c[0] == 0, c
 
 
 @pytest.mark.parametrize("kind", ["normal", "ties", "relu_like", "clustered", "equal"])
@@ -525,21 +552,29 @@ def test_layer_decode_128k_full_size(dsa):
 
 
 def test_layer_decode_deterministic(dsa):
-    say("layer_decode determinism")
+    """100 reruns of the 128K decode layer, the workspace alternately zeroed
+    and poisoned with 0xFF before each: every output and index row equal to
+    the first bit for bit (races in LDS or atomics, or reads of unwritten
+    scratch, would show as differences)."""
+    say("layer_decode determinism: 100 reruns, poisoned / zeroed workspace")
     w = W.decode_128k()
     inp = W.make_inputs(w)
     d = to_dev(inp)
-    outs = []
-    for _ in range(3):
-        idx = torch.empty(1, w.K, dtype=torch.int32, device=DEV)
-        o = dsa.dsa_layer_decode(d["q_idx"], d["w"], d["k_idx"], None, d["q"], d["k_cache"],
-                                 d["v_cache"], d["gate"], w.K, d["ctx_len"], d["cu_ctx"],
-                                 max_ctx=w.ctx_lens[0], idx_out=idx)
-        outs.append((o.clone(), idx.clone()))
+    L = w.ctx_lens[0]
+    ws = torch.empty(dsa.dsa_layer_decode_workspace_size(1, L, w.K, w.Hq, w.D),
+                     dtype=torch.uint8, device=DEV)
+    n = 100
+    outs = torch.empty(n, 1, w.Hq, w.D, dtype=torch.bfloat16, device=DEV)
+    idxs = torch.empty(n, 1, w.K, dtype=torch.int32, device=DEV)
+    for r in range(n):
+        ws.fill_(255 if r % 2 else 0)
+        dsa.dsa_layer_decode(d["q_idx"], d["w"], d["k_idx"], None, d["q"], d["k_cache"],
+                             d["v_cache"], d["gate"], w.K, d["ctx_len"], d["cu_ctx"],
+                             max_ctx=L, out=outs[r], idx_out=idxs[r], ws=ws)
     torch.cuda.synchronize()
-    for o, i in outs[1:]:
-        assert torch.equal(o.view(torch.int16), outs[0][0].view(torch.int16))
-        assert torch.equal(i, outs[0][1])
+    o16 = outs.view(torch.int16)
+    assert torch.equal(o16, o16[:1].expand_as(o16))
+    assert torch.equal(idxs, idxs[:1].expand_as(idxs))
 
 
 def test_layer_decode_1m_fp8_batched_sampled(dsa):

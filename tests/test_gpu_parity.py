@@ -816,6 +816,70 @@ def test_layer_prefill_per_head_gate(dsa):
                          gate=gate)
 
 
+# --------------------------------------------------------------------------
+# Seeded random shapes: every supported indexer and attention shape, K,
+# key dtype and gate kind, ragged batches mixing rows shorter than K,
+# direct rows, sub-tile rows and lengths at the sub-tile-size boundaries
+# --------------------------------------------------------------------------
+
+_IDX_SHAPES = [(4, 64), (16, 128), (32, 128)]
+_ATT_SHAPES = [(8, 64), (64, 128)]
+_BOUNDARY_LENS = [16384, 16385, 32768, 65536, 65537, 131071, 131072]
+
+
+def _random_case(seed, prefill):
+    g = np.random.default_rng(seed)
+    H_I, d_I = _IDX_SHAPES[g.integers(len(_IDX_SHAPES))]
+    Hq, D = _ATT_SHAPES[g.integers(len(_ATT_SHAPES))]
+    K = int(g.choice([16, 64, 256, 1000, 2048, 4096]))
+    key = "fp8" if g.random() < 0.5 else "bf16"
+    q8 = prefill and key == "fp8" and d_I == 128 and g.random() < 0.5
+    B = int(g.integers(1, 5 if prefill else 7))
+    lens, nq = [], []
+    for _ in range(B):
+        kind = int(g.integers(5))
+        if kind == 0:
+            n = int(g.integers(1, K + 1))
+        elif kind == 1:
+            n = int(g.integers(K + 1, 16385)) if K < 16384 else 16384
+        elif kind == 2:
+            n = int(g.integers(16385, 70000))
+        elif kind == 3:
+            n = int(g.integers(70000, 300000 if not prefill else 140000))
+        else:
+            n = int(g.choice(_BOUNDARY_LENS))
+        lens.append(n)
+        nq.append(int(g.integers(1, min(n, 40) + 1)) if prefill else 1)
+    gate_kind = int(g.integers(2))   # 0: elementwise, 1: one value per head
+    w = wl(f"rand{seed}", lens, nq, H_I, d_I, Hq, D, K, key_dtype=key,
+           q_dtype="fp8" if q8 else "bf16", seed=seed,
+           plant_frac=0.05 if g.random() < 0.5 else 0.0)
+    return w, gate_kind
+
+
+@pytest.mark.parametrize("seed", list(range(1000, 1012)))
+def test_layer_decode_random_shapes(dsa, seed):
+    w, gate_kind = _random_case(seed, prefill=False)
+    say(f"layer_decode random seed={seed}: lens={w.ctx_lens} H_I={w.H_I} d_I={w.d_I} "
+        f"Hq={w.Hq} D={w.D} K={w.K} keys={w.key_dtype} gate={'head' if gate_kind else 'elem'}")
+    inp = W.make_inputs(w)
+    gate = W.randn_bf16((w.B, w.Hq), seed, "head_gate") if gate_kind else None
+    _layer_decode_check(dsa, w, inp, to_dev(inp), gate=gate,
+                        atol=ATOL_FP8 if w.key_dtype == "fp8" else ATOL_BF16)
+
+
+@pytest.mark.parametrize("seed", list(range(2000, 2006)))
+def test_layer_prefill_random_shapes(dsa, seed):
+    w, gate_kind = _random_case(seed, prefill=True)
+    say(f"layer_prefill random seed={seed}: lens={w.ctx_lens} nq={w.n_q} H_I={w.H_I} "
+        f"d_I={w.d_I} Hq={w.Hq} D={w.D} K={w.K} keys={w.key_dtype} queries={w.q_dtype} "
+        f"gate={'head' if gate_kind else 'elem'}")
+    inp = W.make_inputs(w)
+    gate = W.randn_bf16((w.T, w.Hq), seed, "head_gate") if gate_kind else None
+    rows = sorted(set(list(range(0, w.T, max(1, w.T // 12))) + [w.T - 1]))
+    _layer_prefill_check(dsa, w, inp, to_dev(inp), rows=rows, gate=gate)
+
+
 def _run_decode(dsa, w, d, ws):
     idx = torch.empty(w.B, w.K, dtype=torch.int32, device=DEV)
     out = dsa.dsa_layer_decode(d["q_idx"], d["w"], d["k_idx"], d["k_scale"], d["q"], d["k_cache"],

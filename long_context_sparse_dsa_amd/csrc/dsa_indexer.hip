@@ -30,6 +30,8 @@
 #include "dsa_kernels.h"
 #include "dsa_topk_tile.h"
 
+#include <cmath>
+#include <mutex>
 #include <type_traits>
 
 namespace dsa {
@@ -553,7 +555,7 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void index_prefill_kernel(
     const uint16_t* __restrict__ w, int64_t w_ld, const uint8_t* __restrict__ k_idx,
     const float* __restrict__ k_scale, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ ctx_len, const int64_t* __restrict__ cu_ctx,
-    float* __restrict__ scores, int64_t ld, int nsplit) {
+    float* __restrict__ scores, int64_t ld, int nsplit, int qtiles, int nitems) {
   static_assert(!Q8 || FP8, "fp8 query heads need fp8 keys");
   const uint16_t* __restrict__ q_idx = static_cast<const uint16_t*>(q_idx_v);
   const uint8_t* __restrict__ q8 = static_cast<const uint8_t*>(q_idx_v);
@@ -570,7 +572,16 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void index_prefill_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t lds[NBUF * PS::BUFB];
   uint8_t* const ring = lds;
 
-  const int b = blockIdx.z, qt = blockIdx.y, split = blockIdx.x;
+  // Work item of this workgroup.  Workgroups go to the 8 XCDs in turn
+  // (id % 8); XCD x takes the contiguous run of items [x n8, (x + 1) n8),
+  // ordered sequence-major, then split, then query tile, so the workgroups
+  // an XCD runs at one time mostly stream the same key range through its L2.
+  const int n8 = (nitems + 7) >> 3;
+  const int item = (int)(blockIdx.x & 7) * n8 + (int)(blockIdx.x >> 3);
+  if (item >= nitems) return;
+  const int per_b = nsplit * qtiles;
+  const int b = item / per_b, split = (item - b * per_b) / qtiles;
+  const int qt = item - b * per_b - split * qtiles;
   const int nq = cu_q[b + 1] - cu_q[b];
   const int qbase = qt * QWG;
   if (qbase >= nq) return;
@@ -784,6 +795,35 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void index_prefill_kernel(
   }
 }
 
+// Workgroups of `kernel` (block of `threads`) resident on the whole device
+// at once: CUs x workgroups per CU (from the occupancy calculator), looked
+// up once per device and kernel.
+static int prefill_slots(const void* kernel, int threads) {
+  struct Entry {
+    int dev;
+    const void* k;
+    int slots;
+  };
+  static Entry cache[16];
+  static int ncache = 0;
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < ncache; ++i)
+    if (cache[i].dev == dev && cache[i].k == kernel) return cache[i].slots;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
+      per_cu <= 0)
+    per_cu = 1;
+  const int slots = cus * per_cu;
+  if (ncache < 16) cache[ncache++] = Entry{dev, kernel, slots};
+  return slots;
+}
+
 template <int DI, int HI, bool FP8, bool Q8>
 static hipError_t launch_prefill_t(const void* q, const float* qs, const uint16_t* w, int64_t w_ld,
                                    const uint8_t* k, const float* ks, const int32_t* cu_q,
@@ -796,15 +836,40 @@ static hipError_t launch_prefill_t(const void* q, const float* qs, const uint16_
   constexpr int MB = HI == 4 ? 1 : 2, NCW = 7, NBUF = 4;
   constexpr int QWG = NCW * MB * (32 / HI);
   const int qtiles = (max_q + QWG - 1) / QWG;
-  // enough workgroups to fill the chip: split the key range when needed
+  // Enough workgroups to fill the chip: the key range of each query tile is
+  // split when the tiles alone are too few.  The workgroups run in rounds
+  // of `slots` (CUs x resident workgroups per CU) and take about equally
+  // long, so among the split counts that give 4 to 8 rounds (or, when even
+  // 4 rounds are out of reach, any count) the one that leaves the least of
+  // the last round idle is taken (e.g. 8192 queries of 16 heads: 293 query
+  // tiles, 6 splits = 1758 workgroups = 6.9 rounds of 256, where 4 splits
+  // gave 4.6 rounds).  Each split keeps at least 4096 keys, so that loading
+  // the query heads and filling the stage ring stay a small part of it.
+  auto ker = index_prefill_kernel<DI, HI, FP8, MB, NCW, NBUF, Q8>;
+  const int slots = prefill_slots(reinterpret_cast<const void*>(ker), 64 * (NCW + 1));
+  const int64_t tiles = (int64_t)qtiles * B;
   int nsplit = 1;
-  while ((int64_t)qtiles * B * nsplit < 1024 && nsplit < 64 &&
-         (int64_t)max_ctx / (nsplit * 2) >= 1024)
-    nsplit *= 2;
-  dim3 grid(nsplit, qtiles, B);
-  hipLaunchKernelGGL((index_prefill_kernel<DI, HI, FP8, MB, NCW, NBUF, Q8>), grid,
-                     dim3(64 * (NCW + 1)), 0, st, q, qs, w, w_ld, k, ks, cu_q, ctx_len, cu_ctx,
-                     scores, ld, nsplit);
+  if (tiles < 4 * (int64_t)slots) {
+    const int nmax = std::max(1, std::min(64, max_ctx / 4096));
+    const bool reach4 = tiles * nmax >= 4 * (int64_t)slots;
+    double best = 1e30;
+    for (int n = 1; n <= nmax; ++n) {
+      const int64_t wgs = tiles * n;
+      if (reach4 && wgs < 4 * (int64_t)slots) continue;
+      if (reach4 && wgs > 8 * (int64_t)slots) break;
+      const double rounds = (double)wgs / slots;
+      const double waste = std::ceil(rounds) / rounds;  // time over the ideal time
+      if (waste < best - 1e-3) {
+        best = waste;
+        nsplit = n;
+      }
+    }
+  }
+  const int64_t nitems = tiles * nsplit;
+  if (nitems > (int64_t)INT32_MAX - 8) return hipErrorInvalidValue;
+  const int grid = (int)((nitems + 7) / 8) * 8;
+  hipLaunchKernelGGL(ker, dim3(grid), dim3(64 * (NCW + 1)), 0, st, q, qs, w, w_ld, k, ks, cu_q,
+                     ctx_len, cu_ctx, scores, ld, nsplit, qtiles, (int)nitems);
   return hipGetLastError();
 }
 

@@ -174,7 +174,8 @@ dsa_status_t dsa_cache_append(const void* k_idx_new, int d_I, const void* k_new,
 /*                                                                           */
 /* For query row t and head h (all Hq heads share one K/V head and one       */
 /* index row):                                                               */
-/*   S = idx[t, :] without -1 entries   (idx != NULL), or                    */
+/*   S = the entries of idx[t, :] in [0, p_t]   (idx != NULL; -1 padding,   */
+/*       and any other entry outside that range, is skipped), or            */
 /*   S = {max(0, p_t - window + 1) .. p_t}   (idx == NULL, window >= 1)      */
 /*   o = softmax_{j in S}(c * q[t,h,:] . K[row(j),:]) @ V[row(j),:]          */
 /*   out[t,h,:] = o * sigmoid(gate[t,h,:])   (gate == NULL: out = o)         */

@@ -197,16 +197,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   };
   const int G = l >> 4, jj = l & 15;
   // K/V row of list entry lp (lp >= lo) in index mode (IM) or window mode;
-  // entries past the list, and -1 entries, are invalid and map to row 0 of
-  // the sequence.  Branch-free: staged entries past the list read -1, and
-  // the LDS index is clamped.
+  // entries past the list, and entries outside [0, p] (the -1 padding, or
+  // anything else a caller passed), are invalid and map to row 0 of the
+  // sequence, so no gather leaves the sequence's rows.  Branch-free: staged
+  // entries past the list read -1, the LDS index is clamped, and one
+  // unsigned compare tests 0 <= j <= p.
+  const uint32_t jmax = (uint32_t)min<int64_t>(ri.p, (int64_t)INT32_MAX);
   auto row_of = [&](auto im, int lp, bool* ok) {
     int32_t j;
     if constexpr (decltype(im)::value)
       j = idx_lds[min(lp - lo, kAttnMaxRows - 1)];
     else
       j = (int32_t)jw0 + lp;
-    const bool v = (lp < hi) & (j >= 0);
+    const bool v = (lp < hi) & ((uint32_t)j <= jmax);
     *ok = v;
     return v ? j : 0;
   };

@@ -334,6 +334,39 @@ def test_sparse_attn_indexed(dsa, Hq, D, K, lens, nq, gated):
     np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=1e-4, atol=1e-4)
 
 
+def test_sparse_attn_skips_entries_outside_the_visible_range(dsa):
+    """Index entries outside [0, p] (other negatives, positions past the
+    query, the int32 maximum) are skipped like the -1 padding: the output
+    equals the oracle's over the same rows with those entries set to -1, and
+    no gather leaves the sequence."""
+    say("sparse_attn out-of-range entries")
+    lens, nq, K = [3000, 5000], [3, 2], 256
+    w = wl("t", lens, nq, 4, 64, 64, 128, K, seed=23)
+    inp = W.make_inputs(w)
+    idx = _rand_idx(lens, nq, K, seed=6)
+    bad = idx.clone()
+    g = np.random.default_rng(7)
+    t = 0
+    for L, n in zip(lens, nq):
+        for i in range(n):
+            p = L - n + i
+            cols = g.choice(K, 40, replace=False)
+            vals = [p + 1, p + 1000, 2**31 - 1, -2, -100000, L, 10**9]
+            for c, v in zip(cols, vals * 6):
+                bad[t, c] = v
+            t += 1
+    clean = bad.clone()
+    clean[(bad < 0) | (bad > torch.tensor(positions(lens, nq))[:, None])] = -1
+    d = to_dev(inp)
+    out = dsa.dsa_sparse_attn(d["q"], d["k_cache"], d["v_cache"], bad.to(DEV), d["ctx_len"],
+                              d["cu_ctx"], gate=d["gate"], cu_q=d["cu_q"], max_ctx=max(lens))
+    torch.cuda.synchronize()
+    ref, _ = oracle.sparse_attn(inp["q"], inp["k_cache"], inp["v_cache"], idx=clean,
+                                gate=inp["gate"], ctx_len=inp["ctx_len"], cu_q=inp["cu_q"],
+                                cu_ctx=inp["cu_ctx"])
+    check_out(out, ref, ATOL_BF16)
+
+
 @pytest.mark.parametrize("lens,window", [([4096, 100, 129], 128), ([50000], 128), ([3], 128)])
 def test_sparse_attn_window(dsa, lens, window):
     say(f"sparse_attn window={window} lens={lens}")

@@ -638,18 +638,30 @@ static dsa_status_t layer_decode_impl(
                                           ctx_len, cu_ctx, B, max_ctx, L.scores, L.ld,
                                           rows ? nullptr : &L.topk, app, s, t_ev_start,
                                           t_ev_stop);
+  const dsa::AttnPlan plan = dsa::attn_plan(B, K, 0, Hq, D);
+  if (!rows && dsa::select_attend_fits(B, K, plan.nsplit, plan.rows_per_split, Hq, D)) {
+    // few sequences: the selection runs inside the split attention's launch
+    // (each split repeats it in its own LDS), then the combine
+    if (e == hipSuccess)
+      e = dsa::launch_select_attend(L.scores, L.ld, ctx_len, B, K, L.topk, idx, t_topk_counters,
+                                    q, k_cache, v_cache, cu_ctx, sm_scale,
+                                    static_cast<float*>(L.attn), plan.nsplit, s);
+    if (e == hipSuccess) e = check_selected(idx, K, nullptr, ctx_len, B, B, s);
+    if (e == hipSuccess)
+      e = dsa::launch_attn_combine(B, Hq, D, static_cast<const float*>(L.attn), plan.nsplit, gate,
+                                   (int)gate_stride_d, out, nullptr, s);
+    return hip_status(e, fn);
+  }
   if (e == hipSuccess)
     e = rows ? dsa::launch_topk_rows(L.scores, L.ld, nullptr, ctx_len, B, B, K, idx,
                                      t_topk_counters, s)
              : dsa::launch_topk_resolve(L.scores, L.ld, nullptr, ctx_len, B, B, K, L.topk, idx,
                                         t_topk_counters, s);
   if (e == hipSuccess) e = check_selected(idx, K, nullptr, ctx_len, B, B, s);
-  if (e == hipSuccess) {
-    const dsa::AttnPlan plan = dsa::attn_plan(B, K, 0, Hq, D);
+  if (e == hipSuccess)
     e = dsa::launch_sparse_attn(q, k_cache, v_cache, idx, K, 0, gate, (int)gate_stride_d,
                                 sm_scale, Hq, D, nullptr, ctx_len, cu_ctx, B, B, out, nullptr,
                                 L.attn, plan, s);
-  }
   return hip_status(e, fn);
 }
 

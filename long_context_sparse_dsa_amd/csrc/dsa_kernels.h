@@ -82,6 +82,25 @@ struct AttnPlan {
 };
 AttnPlan attn_plan(int T, int K, int window, int Hq, int D);
 
+// Merge of split partials (m, l, O) into the gated bf16 output (and lse).
+hipError_t launch_attn_combine(int T, int Hq, int D, const float* part, int nsplit,
+                               const void* gate, int gstride, void* out, float* lse,
+                               hipStream_t stream);
+
+// Decode (one query per sequence, few sequences, Hq = 64, D = 128, index
+// rows of 64 per split): the Top-K selection from the candidate reports and
+// the split attention in one launch; every workgroup of a sequence repeats
+// the selection in its own LDS and attends over its 64 selected rows.
+// Writes idx [B, K] (split 0 of each sequence) and the partials `part`,
+// merged afterwards by launch_attn_combine.  select_attend_fits tells
+// whether a call of B sequences and nsplit splits may take it.
+bool select_attend_fits(int B, int K, int nsplit, int rows_per_split, int Hq, int D);
+hipError_t launch_select_attend(const float* scores, int64_t ld, const int32_t* ctx_len, int B,
+                                int K, const TopkWs& w, int32_t* idx, uint32_t* stats,
+                                const void* q, const void* k_cache, const void* v_cache,
+                                const int64_t* cu_ctx, float sm_scale, float* part,
+                                int nsplit, hipStream_t stream);
+
 // Several attention layers over one batch descriptor in one launch (grid z
 // = layer): layer z reads q[z], k_cache[z], v_cache[z], gate[z] and writes
 // out[z] in place of the single-layer pointers.

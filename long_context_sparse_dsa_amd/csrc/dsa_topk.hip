@@ -26,6 +26,7 @@
 //                       position order and selects among them the same way.
 #include <algorithm>
 
+#include "dsa_attn_tile.h"
 #include "dsa_kernels.h"
 #include "dsa_topk_tile.h"
 
@@ -333,7 +334,9 @@ __device__ __forceinline__ void union_threshold(SM& sm, const UnionRegs<NSL>& R,
 // registers.  With ntiles > 0 the set is a report union and is certified
 // against the sub-tile headers kept in sm.wu / sm.wj.  Returns false,
 // leaving `out` untouched, when the set has fewer than k candidates or the
-// certification fails.  nt: active threads.  When the set holds at least k
+// certification fails.  On success the selection is also left in sm.hbuf
+// (K words, rank order) and `out` may be null.  nt: active threads.  When
+// the set holds at least k
 // candidates, *theta (if given) receives the key of its k-th best and
 // *has_theta is set, whether or not the certification holds; when the
 // certification fails, *nbad (if given) receives the number of sub-tiles
@@ -437,6 +440,7 @@ __device__ __forceinline__ bool select_from_regs(SM& sm, const UnionRegs<NSL>& R
     if (i / 4 < R.qn && (((smask >> i) & 1u) & (uint32_t)(rk[i] < k)))
       stage[rk[i]] = (uint32_t)R.j[i];
   lds_barrier();
+  if (out == nullptr) return true;  // the caller reads the selection from sm.hbuf
   if ((K & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
     for (int i = tid; i < K / 4; i += nt)
       *reinterpret_cast<u32x4*>(out + 4 * i) = *reinterpret_cast<const u32x4*>(stage + 4 * i);
@@ -554,7 +558,8 @@ __device__ __forceinline__ uint32_t load_keys16(const float* row, int64_t n, int
 // writes the selected positions in ascending order.
 template <class SM>
 __device__ __forceinline__ void exact_select_row(SM& sm, const float* row, int64_t n,
-                                                 uint32_t k, bool vec, int nt, int32_t* out) {
+                                                 uint32_t k, bool vec, int nt, int32_t* out,
+                                                 bool stage = false) {
   const int tid = threadIdx.x, l = lane_id(), wv = wave_id(), nw = nt >> 6;
   const int64_t step = 16 * (int64_t)nt;
   uint32_t u[16];
@@ -671,7 +676,10 @@ __device__ __forceinline__ void exact_select_row(SM& sm, const float* row, int64
 #pragma unroll
     for (int i = 0; i < 16; ++i)
       if ((f >> i) & 1u) {
-        if (r < k) out[r] = (int32_t)(p0 + i);
+        if (r < k) {
+          if (out) out[r] = (int32_t)(p0 + i);
+          if (stage) sm.hbuf[r] = (uint32_t)(p0 + i);  // the histograms are done with
+        }
         ++r;
       }
     cum += tot;
@@ -780,15 +788,19 @@ __device__ __forceinline__ bool resolve_by_collection(ResolveSmem& sm, const flo
 // before the row's length is known: one round trip for the common case at
 // small batch.  A row that needs another layout or more groups loads them
 // after.
-template <int NSL>
-__global__ __launch_bounds__(kResolveSlots / NSL) void topk_resolve_kernel(
-    const float* __restrict__ scores, int64_t ld, const int32_t* cu_q, const int32_t* ctx_len,
-    int B, int K, int stride, int eager_nt, int eager_q, const RepHeader* __restrict__ hdr,
-    const uint32_t* __restrict__ rep_u, const int32_t* __restrict__ rep_j, int32_t* idx,
-    uint32_t* stats) {
+//
+// ALL (phase one of the fused selection + attention kernel): every thread
+// of the block stays to the end (nt is the whole block on every path), the
+// selection is always left in sm.hbuf (K words in rank order, -1 past
+// K_eff) and idx may be null (then only sm.hbuf receives it).
+template <int NSL, bool ALL>
+__device__ __forceinline__ void resolve_row(
+    ResolveSmem& sm, int t, const float* __restrict__ scores, int64_t ld, const int32_t* cu_q,
+    const int32_t* ctx_len, int B, int K, int stride, int eager_nt, int eager_q,
+    const RepHeader* __restrict__ hdr, const uint32_t* __restrict__ rep_u,
+    const int32_t* __restrict__ rep_j, int32_t* idx, uint32_t* stats) {
   constexpr int QN = NSL / 4;
-  __shared__ ResolveSmem sm;
-  const int t = blockIdx.x, tid = threadIdx.x, nb = blockDim.x;
+  const int tid = threadIdx.x, nb = blockDim.x;
   const int64_t slot0 = (int64_t)t * stride;
   const int nslots = min(stride, kResolveTiles) * kRep;  // a row's slots in the workspace
   UnionRegs<NSL> R;
@@ -834,9 +846,13 @@ __global__ __launch_bounds__(kResolveSlots / NSL) void topk_resolve_kernel(
   if (eager_q > 0 && tid < eager_nt) load_eager(eager_q, eager_nt);
   const RowInfo ri = row_info(t, cu_q, ctx_len, B);
   const int64_t n = ri.p + 1;
-  int32_t* out = idx + (int64_t)t * K;
+  int32_t* out = idx ? idx + (int64_t)t * K : nullptr;
   if (n <= K) {
-    for (int i = tid; i < K; i += nb) out[i] = i < n ? i : -1;
+    for (int i = tid; i < K; i += nb) {
+      const int32_t v = i < n ? i : -1;
+      if (out) out[i] = v;
+      if (ALL) sm.hbuf[i] = (uint32_t)v;
+    }
     return;
   }
   const uint32_t k = (uint32_t)K;
@@ -854,7 +870,7 @@ __global__ __launch_bounds__(kResolveSlots / NSL) void topk_resolve_kernel(
   R.vmask = 0;
   if (n <= kDirectMax && n <= (int64_t)nb * NSL) {
     // ---- direct: slot s holds position s ----
-    nt = threads_for(n);
+    nt = ALL ? nb : threads_for(n);
     if (tid >= nt) return;
     R.qn = (int)((n + 4 * nt - 1) / (4 * nt));
     // every group is loaded (straight-line loads, one round trip); groups
@@ -887,7 +903,7 @@ __global__ __launch_bounds__(kResolveSlots / NSL) void topk_resolve_kernel(
     sub_s = S;
     const int nt_row = (int)((n + S - 1) >> (31 - __clz(S)));  // S: a power of two
     if (nt_row <= kResolveTiles && nt_row <= stride && nt_row * kRep <= nb * NSL) {
-      nt = max(threads_for((int64_t)nt_row * kRep), eager_nt);
+      nt = ALL ? nb : max(threads_for((int64_t)nt_row * kRep), eager_nt);
       if (tid >= nt) return;
       R.qn = (nt_row * kRep + 4 * nt - 1) / (4 * nt);
       if (nt != eager_nt || eager_q == 0)
@@ -934,9 +950,231 @@ __global__ __launch_bounds__(kResolveSlots / NSL) void topk_resolve_kernel(
     if (ok && stats && tid == 0) atomicAdd(&stats[5], 1u);
   }
   if (!ok) {
-    exact_select_row(sm, row, n, k, vec, nt, out);
+    exact_select_row(sm, row, n, k, vec, nt, out, ALL);
     if (stats && tid == 0) atomicAdd(&stats[1], 1u);
   }
+}
+
+template <int NSL>
+__global__ __launch_bounds__(kResolveSlots / NSL) void topk_resolve_kernel(
+    const float* __restrict__ scores, int64_t ld, const int32_t* cu_q, const int32_t* ctx_len,
+    int B, int K, int stride, int eager_nt, int eager_q, const RepHeader* __restrict__ hdr,
+    const uint32_t* __restrict__ rep_u, const int32_t* __restrict__ rep_j, int32_t* idx,
+    uint32_t* stats) {
+  __shared__ ResolveSmem sm;
+  resolve_row<NSL, false>(sm, blockIdx.x, scores, ld, cu_q, ctx_len, B, K, stride, eager_nt,
+                          eager_q, hdr, rep_u, rep_j, idx, stats);
+}
+
+// ---------------------------------------------------------------------------
+// Decode: selection and split attention in one launch
+// ---------------------------------------------------------------------------
+// At decode the Top-K resolve (one workgroup per row) and the split
+// attention (nsplit workgroups per row, 64 selected rows each) would be two
+// dependent launches, and the attention's first step a round trip for its
+// part of the index row.  Here each of a row's nsplit workgroups (1024
+// threads) first runs the whole selection of the row (resolve_row, ALL
+// mode: the same exact result in every workgroup; split 0 also writes the
+// row to idx) and then attends over ranks 64 s .. 64 s + 63 of it, read
+// from its own LDS.  The attention phase is laid out for 16 waves:
+//   wave w: row block rb = w & 1 (selected rows 32 rb .. + 31 of the
+//   split), head block hb = (w >> 1) & 1 (heads 32 hb .. + 31), output dim
+//   block dq = w >> 2 (dims 32 dq .. + 31);
+//   - the split's K and V rows are gathered once, two 1 KiB loads per wave,
+//     into the swizzled row tiles (RowTile);
+//   - S^T = K_rb . q_hb^T (v_mfma_f32_32x32x16_bf16, 8 k-steps) is computed
+//     alike by the four dim-block waves of (rb, hb), so no exchange comes
+//     before the softmax;
+//   - softmax over the row block (each lane holds one head: max and sum
+//     take one cross-half exchange); P^T is the B operand of O^T = V^T . P^T
+//     for the wave's 32 dims (two MFMAs, V^T through the transpose read);
+//   - the rb = 1 waves hand (m, l, O) to their rb = 0 partners through LDS,
+//     which merge them and write the split's partial (m, l, O) in the
+//     layout of the split attention kernel, merged by the combine kernel.
+// Ranks at or past K_eff (-1) are masked; an entry outside [0, p] cannot
+// come out of the selection but would be masked the same way, so no gather
+// leaves the sequence.
+constexpr int kSaThreads = 1024;
+constexpr int kSaRows = 64;  // selected rows per split
+
+__global__ __launch_bounds__(kSaThreads) void select_attend_kernel(
+    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ ctx_len, int B,
+    int K, int stride, int eager_q, const RepHeader* __restrict__ hdr,
+    const uint32_t* __restrict__ rep_u, const int32_t* __restrict__ rep_j, int32_t* idx,
+    uint32_t* stats, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, const int64_t* __restrict__ cu_ctx, float scale_log2,
+    float* __restrict__ part, int nsplit) {
+  constexpr int NSL = 16, D = 128, HQ = 64, KS = D / 16;
+  using VT = RowTile<D>;
+  __shared__ ResolveSmem sm;
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[4 * VT::kBytes];  // K rb 0, 1; V rb 0, 1
+  __shared__ float mrg[8 * 18 * 64];  // (m, l, O) of the rb = 1 waves, per (hb, dq)
+  // the query's 64 heads, chunk c of head h at 16 (c ^ (h % 16)): the B
+  // operand reads (16 heads, one chunk) hit 16 distinct 16-byte slots
+  __shared__ __attribute__((aligned(16))) uint8_t q_lds[HQ * D * 2];
+  const int t = blockIdx.y, split = blockIdx.x;
+  const int l = lane_id(), g = l >> 5, wv = wave_id();
+  // wave w loads heads 4 w .. 4 w + 3 (one 1 KiB load, lane: head 4 w + l / 16,
+  // chunk l % 16) before the selection; it lands in LDS after it
+  const int qh = 4 * wv + (l >> 4), qc = l & 15;
+  const u32x4 qv = ld16(q + ((int64_t)t * HQ + qh) * D + 8 * qc);
+  resolve_row<NSL, true>(sm, t, scores, ld, nullptr, ctx_len, B, K, stride, kSaThreads, eager_q,
+                         hdr, rep_u, rep_j, split == 0 ? idx : nullptr,
+                         split == 0 ? stats : nullptr);
+  *reinterpret_cast<u32x4*>(q_lds + qh * (2 * D) + ((qc ^ (qh & 15)) << 4)) = qv;
+  // the selection is in sm.hbuf (rank order, -1 past K_eff); split 0's
+  // stores of it to idx stay in flight
+  dma_barrier();
+
+  const int rb = wv & 1, hb = (wv >> 1) & 1, dq = wv >> 2;
+  const int64_t p = (int64_t)ctx_len[t] - 1;
+  const int64_t row0 = cu_ctx[t];
+  const uint32_t jmax = (uint32_t)min<int64_t>(p, (int64_t)INT32_MAX);
+  const int e0 = kSaRows * split;  // first rank of this split
+  auto sel = [&](int r) -> uint32_t {  // selected position of split row r, or ~0
+    const int e = e0 + r;
+    return e < K ? sm.hbuf[e] : 0xffffffffu;
+  };
+  bf16x8 qb[KS];
+  // gathers: wave w fills tile w >> 2 (0, 1: K rows of row blocks 0, 1;
+  // 2, 3: V rows), its load instructions c = 2 (w & 3) and 2 (w & 3) + 1:
+  // tile rows kRPI c + l / kNC, chunk l % kNC; invalid rows read row 0
+  {
+    const int tl = wv >> 2, trb = tl & 1;
+    const int gch = l % VT::kNC, grow = l / VT::kNC;
+    const uint16_t* base = (tl < 2 ? kc : vc) + row0 * D + 8 * gch;
+    u32x4 v[2];
+    int rr[2];
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      const int r = VT::kRPI * (2 * (wv & 3) + c2) + grow;
+      const uint32_t j = sel(32 * trb + r);
+      v[c2] = ld16(base + (int64_t)(j <= jmax ? j : 0u) * D);
+      rr[c2] = r;
+    }
+    // q heads of the wave's head block from LDS while the gathers are in
+    // flight (B operand of S^T: column = head 32 hb + l % 32, k = dims
+    // 16 s + 8 g .. + 7)
+    const int h = 32 * hb + (l & 31);
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      qb[s] = as_bf16x8(
+          *reinterpret_cast<const u32x4*>(q_lds + h * (2 * D) + (((2 * s + g) ^ (h & 15)) << 4)));
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+      *reinterpret_cast<u32x4*>(tiles + tl * VT::kBytes + VT::offset(rr[c2], 8 * gch)) = v[c2];
+  }
+  // bit r: selected row 32 rb + r is valid (lanes 32..63 repeat 0..31)
+  const uint32_t vmask = (uint32_t)__ballot(sel(32 * rb + (l & 31)) <= jmax);
+  dma_barrier();  // the tiles are complete
+
+  // S^T = K . q^T: the A operand of k-step s is tile row l % 32, dims 16 s + 8 g .. + 7
+  f32x16 sacc = {};
+  {
+    const uint8_t* kt = tiles + rb * VT::kBytes;
+    u32x4 kf[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      kf[s] = *reinterpret_cast<const u32x4*>(kt + VT::offset(l & 31, 16 * s + 8 * g));
+#pragma unroll
+    for (int s = 0; s < KS; ++s) sacc = mfma32(as_bf16x8(kf[s]), qb[s], sacc);
+  }
+  // softmax of the row block per head (exp2 domain, c > 0)
+  float mx = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int ir = 8 * (r >> 2) + 4 * g + (r & 3);
+    if (!((vmask >> ir) & 1u)) sacc[r] = -INFINITY;
+    mx = fmaxf(mx, sacc[r]);
+  }
+  const float m = xor32_max(mx) * scale_log2;
+  const float mu = (m == -INFINITY) ? 0.f : m;
+  float sv[16];
+  float psum = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    sv[r] = fexp2(fmaf(sacc[r], scale_log2, -mu));
+    psum += sv[r];
+  }
+  const float lsum = xor32_add(psum);
+  bf16x8 pb[2];
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pb[s2][e] = static_cast<__bf16>(sv[8 * s2 + e]);
+  // O^T = V^T . P^T for dims 32 dq .. + 31: k slot e of step s2 is
+  // accumulator row 16 s2 + 8 (e / 4) + 4 g + e % 4, whose two 4-row groups
+  // each come from one transpose read (lane jj of a 16-lane group addresses
+  // row k0 + jj / 4, dims n0 + 4 (jj % 4) .. + 3)
+  f32x16 o = {};
+  {
+    const uint16_t* vt16 = reinterpret_cast<const uint16_t*>(tiles + (2 + rb) * VT::kBytes);
+    const int G = l >> 4, jj = l & 15;
+    const int n0 = 32 * dq + 16 * (G & 1) + 4 * (jj & 3);
+    u32x2 av[2][2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int k0 = 16 * s2 + 4 * g + (jj >> 2);
+      av[s2][0] = lds_read_tr16(vt16 + VT::offset(k0, n0) / 2);
+      av[s2][1] = lds_read_tr16(vt16 + VT::offset(k0 + 8, n0) / 2);
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+      o = mfma32(as_bf16x8(u32x4{av[s2][0][0], av[s2][0][1], av[s2][1][0], av[s2][1][1]}), pb[s2],
+                 o);
+  }
+  // merge the two row blocks: rb = 1 hands over, rb = 0 writes the partial
+  float* ms = mrg + (hb * 4 + dq) * 18 * 64;
+  if (rb == 1) {
+    ms[l] = m;
+    ms[64 + l] = lsum;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ms[(2 + r) * 64 + l] = o[r];
+  }
+  lds_barrier();
+  if (rb == 1) return;
+  const float mo = ms[l], lo2 = ms[64 + l];
+  const float M = fmaxf(m, mo);
+  const float a = (M == -INFINITY) ? 0.f : fexp2(m - M);
+  const float bb = (M == -INFINITY) ? 0.f : fexp2(mo - M);
+  const float L = lsum * a + lo2 * bb;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) o[r] = o[r] * a + ms[(2 + r) * 64 + l] * bb;
+  float* pp = part + (((int64_t)t * nsplit + split) * HQ + 32 * hb + (l & 31)) * (D + 2);
+#pragma unroll
+  for (int r4 = 0; r4 < 4; ++r4)
+    *reinterpret_cast<f32x4*>(pp + 32 * dq + 8 * r4 + 4 * g) =
+        f32x4{o[4 * r4], o[4 * r4 + 1], o[4 * r4 + 2], o[4 * r4 + 3]};
+  if (dq == 0 && g == 0) {
+    pp[D] = M;
+    pp[D + 1] = L;
+  }
+}
+
+bool select_attend_fits(int B, int K, int nsplit, int rows_per_split, int Hq, int D) {
+  return Hq == 64 && D == 128 && rows_per_split == kSaRows && nsplit >= 2 && K <= 4096 &&
+         (int64_t)B * nsplit <= 256;
+}
+
+hipError_t launch_select_attend(const float* scores, int64_t ld, const int32_t* ctx_len, int B,
+                                int K, const TopkWs& w, int32_t* idx, uint32_t* stats,
+                                const void* q, const void* k_cache, const void* v_cache,
+                                const int64_t* cu_ctx, float sm_scale, float* part,
+                                int nsplit, hipStream_t stream) {
+  // eager report loads laid out for the whole block, as in the resolve kernel
+  int eager_q = 0;
+  if (w.max_ctx > kDirectMax) {
+    const int s = topk_subtile(w.max_ctx, K);
+    const int64_t slots =
+        std::min<int64_t>(kResolveSlots, (int64_t)((w.max_ctx + s - 1) / s) * kRep);
+    eager_q = (int)((slots + 4 * kSaThreads - 1) / (4 * kSaThreads));
+  }
+  const float scale = (sm_scale != 0.f ? sm_scale : 1.f / sqrtf(128.f)) * kLog2e;
+  hipLaunchKernelGGL(select_attend_kernel, dim3(nsplit, B), dim3(kSaThreads), 0, stream, scores,
+                     ld, ctx_len, B, K, w.stride, eager_q, w.hdr, w.rep_u, w.rep_j, idx, stats,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
+                     static_cast<const uint16_t*>(v_cache), cu_ctx, scale, part, nsplit);
+  return hipGetLastError();
 }
 
 // Exact Top-K of many rows straight from their scores (prefill: thousands

@@ -542,6 +542,27 @@ def test_layer_decode_ragged_lengths_take_the_fast_paths(dsa):
     assert c[2] == 2 and c[0] == len(lens) - 2 and c[1] == 0
 
 
+def test_layer_decode_clustered_winners_take_the_fallbacks(dsa):
+    """Winners packed into a few hundred consecutive positions break the
+    per-sub-tile certification; in the decode layer of few sequences the
+    selection runs inside every split workgroup of the attention launch, so
+    both second chances run there: a cluster of 1500 positions (its failing
+    sub-tiles leave at most 3152 keys at or above the union's threshold)
+    takes the one collection sweep, a cluster of 3500 (4688 > 4096) the
+    exact select over the row.  Index rows stay bit-exact against the
+    oracle's Top-K of the layer's own scores, outputs within tolerance."""
+    say("layer_decode clustered winners: collection sweep and exact select in the fused launch")
+    lens = [40000, 60000]
+    w = wl("t", lens, [1, 1], 16, 128, 64, 128, 2048, seed=61)
+    inp = W.make_inputs(w)
+    k = inp["k_idx"].float()
+    k[5000:6500] *= 8.0                    # sequence 0
+    k[lens[0] + 10000:lens[0] + 13500] *= 8.0  # sequence 1
+    inp["k_idx"] = k.to(torch.bfloat16)    # powers of two: exact
+    _, c = _with_counters(dsa, lambda: _layer_decode_check(dsa, w, inp, to_dev(inp)))
+    assert c[5] == 1 and c[1] == 1 and c[0] == 0, c
+
+
 def test_layer_decode_large_batch_takes_the_row_sweeps(dsa):
     """1024 sequences and more: the indexer writes plain scores and every row
     is selected by sweeps over them (no candidate reports)."""

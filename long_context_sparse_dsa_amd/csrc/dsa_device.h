@@ -127,6 +127,12 @@ __device__ __forceinline__ float xor32_max(float v) {
 // Inclusive wave scan with an associative operator op and identity id:
 // row shifts 1, 2, 4, 8 build 16-lane row scans, two row broadcasts join
 // the rows.
+// Every lane of a quad (4 aligned lanes) gets lane K of the quad.
+template <int K>
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, K * 0x55, 0xf, 0xf, false);
+}
+
 template <typename Op>
 __device__ __forceinline__ uint32_t dpp_wave_scan(uint32_t v, uint32_t id, Op op) {
   v = op(v, dpp_u32<kDppRowShr1, 0xf, 0xf>(id, v));

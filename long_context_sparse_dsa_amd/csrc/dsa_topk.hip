@@ -793,7 +793,10 @@ __device__ __forceinline__ bool resolve_by_collection(ResolveSmem& sm, const flo
 // of the block stays to the end (nt is the whole block on every path), the
 // selection is always left in sm.hbuf (K words in rank order, -1 past
 // K_eff) and idx may be null (then only sm.hbuf receives it).
-template <int NSL, bool ALL>
+// QE > 0: the report groups loaded before the row length is known are
+// exactly the first QE (a compile-time count, so no load is issued for the
+// others); QE = 0: the first eager_q, with the others reading slot 0.
+template <int NSL, bool ALL, int QE = 0>
 __device__ __forceinline__ void resolve_row(
     ResolveSmem& sm, int t, const float* __restrict__ scores, int64_t ld, const int32_t* cu_q,
     const int32_t* ctx_len, int B, int K, int stride, int eager_nt, int eager_q,
@@ -804,7 +807,12 @@ __device__ __forceinline__ void resolve_row(
   const int64_t slot0 = (int64_t)t * stride;
   const int nslots = min(stride, kResolveTiles) * kRep;  // a row's slots in the workspace
   UnionRegs<NSL> R;
-  RepHeader hq[QN];
+  // one dword of the sub-tile header per thread: the four threads of a
+  // sub-tile's slots are four consecutive lanes (4 slots each), lane l
+  // loads dword l % 4 (count, complete, worst key, worst position) and the
+  // quad shares them with DPP (a quarter of the bytes of whole headers)
+  uint32_t hw[QN];
+  const uint32_t* hdr32 = reinterpret_cast<const uint32_t*>(hdr);
   // eager report loads in the layout of nt threads: every group is loaded,
   // groups at or beyond qe from slot 0 (a cached line), so the loads are
   // straight-line code and all go out before the first wait (loads under
@@ -812,11 +820,12 @@ __device__ __forceinline__ void resolve_row(
   auto load_eager = [&](int qe, int nt) {
 #pragma unroll
     for (int q = 0; q < QN; ++q) {
+      if (QE > 0 && q >= QE) continue;
       const int sidx = slot_of(q, tid, nt);
-      const int sc = (q < qe && sidx < nslots) ? sidx : 0;
+      const int sc = ((QE > 0 || q < qe) && sidx < nslots) ? sidx : 0;
       const u32x4 a = *reinterpret_cast<const u32x4*>(rep_u + slot0 * kRep + sc);
       const u32x4 c = *reinterpret_cast<const u32x4*>(rep_j + slot0 * kRep + sc);
-      hq[q] = hdr[slot0 + sc / kRep];
+      hw[q] = hdr32[(slot0 + sc / kRep) * 4 + (tid & 3)];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         R.u[4 * q + e] = a[e];
@@ -834,7 +843,7 @@ __device__ __forceinline__ void resolve_row(
         const int sc = sidx < nslots ? sidx : 0;
         const u32x4 a = *reinterpret_cast<const u32x4*>(rep_u + slot0 * kRep + sc);
         const u32x4 c = *reinterpret_cast<const u32x4*>(rep_j + slot0 * kRep + sc);
-        hq[q] = hdr[slot0 + sc / kRep];
+        hw[q] = hdr32[(slot0 + sc / kRep) * 4 + (tid & 3)];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           R.u[4 * q + e] = a[e];
@@ -916,13 +925,18 @@ __device__ __forceinline__ void resolve_row(
           const int sidx = slot_of(q, tid, nt);
           const bool tile_ok = sidx / kRep < nt_row;
           const uint32_t sub = (uint32_t)(sidx % kRep);
-          const uint32_t cnt = hq[q].count;
+          // the sub-tile's header from its quad (every lane of the quad
+          // runs this: the group test is block-uniform)
+          const uint32_t cnt = quad_bcast<0>(hw[q]);
+          const uint32_t hcomplete = quad_bcast<1>(hw[q]);
+          const uint32_t hworst_u = quad_bcast<2>(hw[q]);
+          const uint32_t hworst_j = quad_bcast<3>(hw[q]);
           // slots sub .. sub+3 of the sub-tile are valid while below its count
           const uint32_t nv = tile_ok ? (cnt > sub ? min(cnt - sub, 4u) : 0u) : 0u;
           R.vmask |= ((1u << nv) - 1u) << (4 * q);
           if (sub == 0 && tile_ok) {
-            sm.wu[sidx / kRep] = hq[q].worst_u;
-            sm.wj[sidx / kRep] = (uint32_t)hq[q].worst_j | (hq[q].complete ? 0x80000000u : 0u);
+            sm.wu[sidx / kRep] = hworst_u;
+            sm.wj[sidx / kRep] = hworst_j | (hcomplete ? 0x80000000u : 0u);
           }
         }
       }
@@ -997,6 +1011,7 @@ __global__ __launch_bounds__(kResolveSlots / NSL) void topk_resolve_kernel(
 constexpr int kSaThreads = 1024;
 constexpr int kSaRows = 64;  // selected rows per split
 
+template <int QE>
 __global__ __launch_bounds__(kSaThreads) void select_attend_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ ctx_len, int B,
     int K, int stride, int eager_q, const RepHeader* __restrict__ hdr,
@@ -1018,9 +1033,9 @@ __global__ __launch_bounds__(kSaThreads) void select_attend_kernel(
   // chunk l % 16) before the selection; it lands in LDS after it
   const int qh = 4 * wv + (l >> 4), qc = l & 15;
   const u32x4 qv = ld16(q + ((int64_t)t * HQ + qh) * D + 8 * qc);
-  resolve_row<NSL, true>(sm, t, scores, ld, nullptr, ctx_len, B, K, stride, kSaThreads, eager_q,
-                         hdr, rep_u, rep_j, split == 0 ? idx : nullptr,
-                         split == 0 ? stats : nullptr);
+  resolve_row<NSL, true, QE>(sm, t, scores, ld, nullptr, ctx_len, B, K, stride, kSaThreads,
+                             eager_q, hdr, rep_u, rep_j, split == 0 ? idx : nullptr,
+                             split == 0 ? stats : nullptr);
   *reinterpret_cast<u32x4*>(q_lds + qh * (2 * D) + ((qc ^ (qh & 15)) << 4)) = qv;
   // the selection is in sm.hbuf (rank order, -1 past K_eff); split 0's
   // stores of it to idx stay in flight
@@ -1170,10 +1185,21 @@ hipError_t launch_select_attend(const float* scores, int64_t ld, const int32_t* 
     eager_q = (int)((slots + 4 * kSaThreads - 1) / (4 * kSaThreads));
   }
   const float scale = (sm_scale != 0.f ? sm_scale : 1.f / sqrtf(128.f)) * kLog2e;
-  hipLaunchKernelGGL(select_attend_kernel, dim3(nsplit, B), dim3(kSaThreads), 0, stream, scores,
-                     ld, ctx_len, B, K, w.stride, eager_q, w.hdr, w.rep_u, w.rep_j, idx, stats,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
-                     static_cast<const uint16_t*>(v_cache), cu_ctx, scale, part, nsplit);
+  // the groups loaded ahead are a compile-time count (no loads for the rest)
+#define DSA_SA_LAUNCH(QE_)                                                                     \
+  hipLaunchKernelGGL(select_attend_kernel<QE_>, dim3(nsplit, B), dim3(kSaThreads), 0, stream,  \
+                     scores, ld, ctx_len, B, K, w.stride, eager_q, w.hdr, w.rep_u, w.rep_j, idx, \
+                     stats, static_cast<const uint16_t*>(q),                                   \
+                     static_cast<const uint16_t*>(k_cache),                                    \
+                     static_cast<const uint16_t*>(v_cache), cu_ctx, scale, part, nsplit)
+  switch (eager_q) {
+    case 1: DSA_SA_LAUNCH(1); break;
+    case 2: DSA_SA_LAUNCH(2); break;
+    case 3: DSA_SA_LAUNCH(3); break;
+    case 4: DSA_SA_LAUNCH(4); break;
+    default: DSA_SA_LAUNCH(0); break;
+  }
+#undef DSA_SA_LAUNCH
   return hipGetLastError();
 }
 

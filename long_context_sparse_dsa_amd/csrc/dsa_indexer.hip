@@ -507,10 +507,18 @@ struct RowMap {
   }
 };
 
-// Prefill workgroup = NCW compute waves + one loader wave.
+// Prefill workgroup = NCW compute waves + one loader wave, or (SELF) NCW
+// compute waves that load the stages themselves.
 //   - the loader streams the key range in stages of KT keys into a ring of
 //     NBUF LDS buffers with direct global-to-LDS loads; its load counter
-//     tracks nothing else, so its waits are exact.  Two buffers of 128 keys
+//     tracks nothing else, so its waits are exact.  In the SELF form every
+//     compute wave issues its share of each stage's load instructions right
+//     after the stage barrier and waits for all of its memory operations
+//     (vmcnt(0)) before the next one; its score stores are kept back in a
+//     per-wave LDS stash and go out during the next stage's first two
+//     blocks, so that wait finds them long done.  (Flushing the stash right
+//     after the barrier, with every wave at once, idled the matrix pipes
+//     and made the kernel 6% slower than the loader form.)  Two buffers of 128 keys
 //     (256 with fp8 query heads, whose operands take fewer registers)
 //     measured 4-7% faster than four of 64: half the workgroup barriers per
 //     key, and the same bytes in flight;
@@ -552,8 +560,8 @@ struct PrefillShape {
 // (the quantiser's amax / 448) the epilogue folds the query scale into the
 // head weight and applies the key scale once per key after the head sum:
 // s = sigma_j * sum_h (w_h rho_h) ReLU(acc_h).
-template <int DI, int HI, bool FP8, int MB, int NCW, int NBUF, bool Q8>
-__global__ __launch_bounds__(64 * (NCW + 1)) void index_prefill_kernel(
+template <int DI, int HI, bool FP8, int MB, int NCW, int NBUF, bool Q8, bool SELF>
+__global__ __launch_bounds__(64 * (NCW + (SELF ? 0 : 1))) void index_prefill_kernel(
     const void* __restrict__ q_idx_v, const float* __restrict__ q_scale,
     const uint16_t* __restrict__ w, int64_t w_ld, const uint8_t* __restrict__ k_idx,
     const float* __restrict__ k_scale, const int32_t* __restrict__ cu_q,
@@ -572,7 +580,12 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void index_prefill_kernel(
   constexpr int NLD = FP8 ? KS / 2 : KS;     // 16-byte operand chunks per lane per key block
   static_assert(PS::NL * (NBUF - 1) <= 63, "loads in flight");
 
-  __shared__ __attribute__((aligned(16))) uint8_t lds[NBUF * PS::BUFB];
+  constexpr int NB = KT / 32;                // 32-key blocks per stage
+  constexpr int NSUM = HI == 4 ? 4 : 1;      // sums per query block per lane
+  // SELF: per wave, the sums of the blocks reduced during one stage, stored
+  // to memory during the next stage's first two blocks
+  constexpr int kStash = SELF ? NB * MB * NSUM * 64 * 4 : 0;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NBUF * PS::BUFB + NCW * kStash];
   uint8_t* const ring = lds;
 
   // Work item of this workgroup.  Workgroups go to the 8 XCDs in turn
@@ -601,7 +614,7 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void index_prefill_kernel(
   const int nst = (int)(nst_all * (split + 1) / nsplit - st_lo);
   if (nst <= 0) return;
 
-  if (wv == NCW) {
+  if (!SELF && wv == NCW) {
     // ---------------- loader ----------------
     const int lrow = l % PS::RPK, lchunk = l / PS::RPK;
     auto issue = [&](int k) {
@@ -666,7 +679,6 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void index_prefill_kernel(
       wr[m][r] = q2 < nq ? wv2 : 0.f;
     }
   }
-  constexpr int NB = KT / 32;  // 32-key blocks per stage
   // The 32-key blocks form a pipeline inside each wave: while the MFMAs of
   // one block run, the wave reduces the previous block (ReLU, head weights,
   // head sum: vector ALU work that does not depend on those MFMAs) and
@@ -675,7 +687,6 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void index_prefill_kernel(
   f32x16 acc[2][MB];
 #pragma unroll
   for (int m = 0; m < MB; ++m) acc[1][m] = f32x16{};
-  constexpr int NSUM = HI == 4 ? 4 : 1;  // sums per query block per lane
   auto reduce = [&](int p, float sgp, float (&sum)[MB][NSUM]) {
 #pragma unroll
     for (int m = 0; m < MB; ++m)
@@ -722,11 +733,58 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void index_prefill_kernel(
       }
     }
   };
+  // SELF: wave w issues load instructions c = w, w + NCW, ... of every
+  // stage (the loader's stage layout)
+  [[maybe_unused]] const int wvu = __builtin_amdgcn_readfirstlane(wv);
+  [[maybe_unused]] float* const stash =
+      reinterpret_cast<float*>(lds + NBUF * PS::BUFB + wvu * kStash);
+  [[maybe_unused]] auto issue_share = [&](int k) {
+    uint8_t* buf = ring + (k % NBUF) * PS::BUFB;
+    const int64_t kb = (st_lo + k) * KT;
+    const int lrow = l % PS::RPK, lchunk = l / PS::RPK;
+#pragma unroll
+    for (int k8 = 0; k8 < (PS::NL + NCW - 1) / NCW; ++k8) {
+      const int c = wvu + NCW * k8;  // wave-uniform
+      if (PS::NL % NCW != 0 && c >= PS::NL) break;
+      if (FP8 && c >= PS::NI)
+        lds_dma4(k_scale + row0 + min<int64_t>(kb + 64 * (c - PS::NI) + l, L - 1),
+                 buf + PS::KEYB + 256 * (c - PS::NI));
+      else
+        lds_dma16(k_idx + (row0 + min<int64_t>(kb + c * PS::RPK + lrow, L - 1)) * ROWB +
+                      16 * lchunk,
+                  buf + c * PS::STRIDE);
+    }
+  };
+  // stash slot n of a stage holds the sums reduced during its block n (those
+  // of the block before; the previous stage's last block for n = 0)
+  [[maybe_unused]] auto stash_put = [&](int n, const float (&sum)[MB][NSUM]) {
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int c4 = 0; c4 < NSUM; ++c4) stash[((n * MB + m) * NSUM + c4) * 64 + l] = sum[m][c4];
+  };
+  // stores of slot n of stage s's stash (slot 0 of stage 0 holds nothing)
+  [[maybe_unused]] auto flush = [&](int s, int n) {
+    if (s == 0 && n == 0) return;
+    float sum[MB][NSUM];
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int c4 = 0; c4 < NSUM; ++c4) sum[m][c4] = stash[((n * MB + m) * NSUM + c4) * 64 + l];
+    store((st_lo + s) * KT + 32 * (n - 1) + (l & 31), sum);
+  };
   int64_t j_prev = 0;  // key of this lane in the block awaiting its reduction
   float sg_prev = 1.f;
+  if constexpr (SELF) issue_share(0);
 #pragma unroll 1
   for (int i = 0; i < nst; ++i) {
+    // SELF: this wave's loads of stage i have landed, and its stores, issued
+    // in the first half of stage i - 1, are done
+    if constexpr (SELF) wait_vmcnt(0);
     dma_barrier();  // stage i has landed; every wave is done with stage i - 1
+    if constexpr (SELF) {
+      if (i + 1 < nst) issue_share(i + 1);  // into the buffer of stage i - 1
+    }
     const uint8_t* buf = ring + (i % NBUF) * PS::BUFB;
     const int64_t kb = (st_lo + i) * KT;
     // B operands: block n + 1's reads are issued at block n's start and land
@@ -793,7 +851,18 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void index_prefill_kernel(
       for (int m = 0; m < MB; ++m)
 #pragma unroll
         for (int c4 = 0; c4 < NSUM; ++c4) asm volatile("" : "+v"(sum[m][c4]));
-      if (i > 0 || n > 0) store(j_prev, sum);
+      if constexpr (SELF) {
+        // the previous stage's slots go out during blocks 0 and 1, each slot
+        // before this stage overwrites it
+        constexpr int HALF = NB / 2;
+        if (i > 0 && n < 2) {
+#pragma unroll
+          for (int h = 0; h < HALF; ++h) flush(i - 1, n * HALF + h);
+        }
+        stash_put(n, sum);
+      } else if (i > 0 || n > 0) {
+        store(j_prev, sum);
+      }
       j_prev = kb + R;
       sg_prev = sgn;
       if (n + 1 < NB) {
@@ -802,6 +871,9 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void index_prefill_kernel(
         sgc = sgnx;
       }
     }
+  }
+  if constexpr (SELF) {
+    for (int n = 0; n < NB; ++n) flush(nst - 1, n);
   }
   {
     float sum[MB][NSUM];
@@ -839,16 +911,18 @@ static int prefill_slots(const void* kernel, int threads) {
   return slots;
 }
 
-template <int DI, int HI, bool FP8, bool Q8>
-static hipError_t launch_prefill_t(const void* q, const float* qs, const uint16_t* w, int64_t w_ld,
+template <int DI, int HI, bool FP8, bool Q8, int NCW, bool SELF>
+static hipError_t launch_prefill_v(const void* q, const float* qs, const uint16_t* w, int64_t w_ld,
                                    const uint8_t* k, const float* ks, const int32_t* cu_q,
                                    const int32_t* ctx_len, const int64_t* cu_ctx, int B,
                                    int max_q, int max_ctx, float* scores, int64_t ld,
                                    hipStream_t st) {
-  // 7 compute waves + the loader (two waves per SIMD at this register use);
-  // two 32-row query blocks per compute wave where the registers allow it
-  // (8 queries of 4 heads fill a block)
-  constexpr int MB = HI == 4 ? 1 : 2, NCW = 7, NBUF = 2;
+  // eight waves per workgroup (two per SIMD at this register use): NCW = 7
+  // compute waves + the loader, or 8 self-loading compute waves; two 32-row
+  // query blocks per compute wave where the registers allow it (8 queries
+  // of 4 heads fill a block)
+  constexpr int MB = HI == 4 ? 1 : 2, NBUF = 2;
+  constexpr int NT = 64 * (NCW + (SELF ? 0 : 1));
   constexpr int QWG = NCW * MB * (32 / HI);
   const int qtiles = (max_q + QWG - 1) / QWG;
   // Enough workgroups to fill the chip: the key range of each query tile is
@@ -856,12 +930,12 @@ static hipError_t launch_prefill_t(const void* q, const float* qs, const uint16_
   // of `slots` (CUs x resident workgroups per CU) and take about equally
   // long, so among the split counts that give 4 to 8 rounds (or, when even
   // 4 rounds are out of reach, any count) the one that leaves the least of
-  // the last round idle is taken (e.g. 8192 queries of 16 heads: 293 query
-  // tiles, 6 splits = 1758 workgroups = 6.9 rounds of 256, where 4 splits
-  // gave 4.6 rounds).  Each split keeps at least 4096 keys, so that loading
+  // the last round idle is taken (e.g. 8192 queries of 16 heads in 28-query
+  // tiles: 293 tiles, 6 splits = 1758 workgroups = 6.9 rounds of 256, where
+  // 4 splits gave 4.6 rounds; in 32-query tiles: 256 x 4 = 4.0 rounds).  Each split keeps at least 4096 keys, so that loading
   // the query heads and filling the stage ring stay a small part of it.
-  auto ker = index_prefill_kernel<DI, HI, FP8, MB, NCW, NBUF, Q8>;
-  const int slots = prefill_slots(reinterpret_cast<const void*>(ker), 64 * (NCW + 1));
+  auto ker = index_prefill_kernel<DI, HI, FP8, MB, NCW, NBUF, Q8, SELF>;
+  const int slots = prefill_slots(reinterpret_cast<const void*>(ker), NT);
   const int64_t tiles = (int64_t)qtiles * B;
   int nsplit = 1;
   if (tiles < 4 * (int64_t)slots) {
@@ -883,9 +957,27 @@ static hipError_t launch_prefill_t(const void* q, const float* qs, const uint16_
   const int64_t nitems = tiles * nsplit;
   if (nitems > (int64_t)INT32_MAX - 8) return hipErrorInvalidValue;
   const int grid = (int)((nitems + 7) / 8) * 8;
-  hipLaunchKernelGGL(ker, dim3(grid), dim3(64 * (NCW + 1)), 0, st, q, qs, w, w_ld, k, ks, cu_q,
+  hipLaunchKernelGGL(ker, dim3(grid), dim3(NT), 0, st, q, qs, w, w_ld, k, ks, cu_q,
                      ctx_len, cu_ctx, scores, ld, nsplit, qtiles, (int)nitems);
   return hipGetLastError();
+}
+
+template <int DI, int HI, bool FP8, bool Q8>
+static hipError_t launch_prefill_t(const void* q, const float* qs, const uint16_t* w, int64_t w_ld,
+                                   const uint8_t* k, const float* ks, const int32_t* cu_q,
+                                   const int32_t* ctx_len, const int64_t* cu_ctx, int B,
+                                   int max_q, int max_ctx, float* scores, int64_t ld,
+                                   hipStream_t st) {
+  // bf16 keys: 8 compute waves that load their own stages (1% faster at
+  // 8192 queries x 139264 keys than 7 + a loader wave); fp8 keys, whose
+  // epilogue and operand conversions keep the vector ALU busy, stay with
+  // the loader wave (the self-loading form is 6% slower there)
+  if constexpr (FP8)
+    return launch_prefill_v<DI, HI, FP8, Q8, 7, false>(q, qs, w, w_ld, k, ks, cu_q, ctx_len,
+                                                       cu_ctx, B, max_q, max_ctx, scores, ld, st);
+  else
+    return launch_prefill_v<DI, HI, FP8, Q8, 8, true>(q, qs, w, w_ld, k, ks, cu_q, ctx_len,
+                                                      cu_ctx, B, max_q, max_ctx, scores, ld, st);
 }
 
 hipError_t launch_index_prefill(const void* q_idx, int q_dtype, const float* q_scale,

@@ -72,7 +72,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   constexpr int MERGE_BYTES = (RB / 2) * HB * 64 * ST_FLOATS * 4;
   constexpr int TILE_BYTES = 2 * RB * 2 * VT::kBytes;  // 2 buffers x RB row blocks x {K, V}
   constexpr int SMEM_BYTES = MERGE_BYTES > TILE_BYTES ? MERGE_BYTES : TILE_BYTES;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM_BYTES];
+  // One LDS array: the staged index entries (index mode) first, so that
+  // the step loop's reads of them take immediate offsets, then the tiles
+  // (and the merge area over them).
+  constexpr int kIdxPad = 2 * STEP;
+  constexpr int IDX_BYTES = (kAttnMaxRows + kIdxPad) * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_all[IDX_BYTES + SMEM_BYTES];
+  int32_t* const idx_lds = reinterpret_cast<int32_t*>(lds_all);
+  uint8_t* const smem = lds_all + IDX_BYTES;
 
   // Workgroups go to the 8 XCDs (each with its own L2) in turn.  With one
   // workgroup per query, query t + 1 would land on another XCD than query t,
@@ -91,26 +98,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   const int lp0 = lo + 32 * rb + (l & 31);
   // In index mode the workgroup's part of the index row (at most
   // kAttnMaxRows entries) goes to LDS first; these loads do not depend on
-  // the batch descriptor, so they share its round trip.
-  __shared__ int32_t idx_lds[kAttnMaxRows];
+  // the batch descriptor, so they share its round trip.  Each entry is
+  // checked once as it is staged: entries past the list, and entries
+  // outside [0, p] (the -1 padding, or anything else a caller passed), are
+  // staged as -1.  The array runs two steps past kAttnMaxRows (staged -1),
+  // so the step loop reads it unclamped.
+  constexpr int PT = kAttnMaxRows / 256;
+  int32_t iv[PT];
   if (idx) {
     const int nr = min(K, lo + rows_per_split) - lo;
     const int32_t* src = idx + (int64_t)t * K + lo;
-    constexpr int PT = kAttnMaxRows / 256;
-    int32_t v[PT];
 #pragma unroll
     for (int r = 0; r < PT; ++r) {
       const int e = (int)threadIdx.x + 256 * r;
-      v[r] = e < nr ? src[e] : -1;
+      iv[r] = e < nr ? src[e] : -1;
     }
-#pragma unroll
-    for (int r = 0; r < PT; ++r) idx_lds[threadIdx.x + 256 * r] = v[r];
   }
   const RowInfo ri = row_info(t, cu_q, ctx_len, B);
   const int64_t row0 = cu_ctx[ri.b];
   const int nlist = idx ? K : (int)min<int64_t>(window, ri.p + 1);
   const int64_t jw0 = ri.p - nlist + 1;  // window mode: first position
   const int hi = min(nlist, lo + rows_per_split);
+  const uint32_t jmax = (uint32_t)min<int64_t>(ri.p, (int64_t)INT32_MAX);
+  if (idx) {
+#pragma unroll
+    for (int r = 0; r < PT; ++r)
+      idx_lds[threadIdx.x + 256 * r] = (uint32_t)iv[r] <= jmax ? iv[r] : -1;
+    if ((int)threadIdx.x < kIdxPad) idx_lds[kAttnMaxRows + threadIdx.x] = -1;
+  }
 
   // q as the B operand of S^T: column = head 32 hb + l % 32, k = dims 16 s + 8 g + 0..7.
   // Heads past Hq repeat the last head; their results are never written.
@@ -141,22 +156,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     return smem + ((b * RB + r) * 2 + kind) * VT::kBytes;
   };
   const int G = l >> 4, jj = l & 15;
-  // K/V row of list entry lp (lp >= lo) in index mode (IM) or window mode;
-  // entries past the list, and entries outside [0, p] (the -1 padding, or
-  // anything else a caller passed), are invalid and map to row 0 of the
-  // sequence, so no gather leaves the sequence's rows.  Branch-free: staged
-  // entries past the list read -1, the LDS index is clamped, and one
-  // unsigned compare tests 0 <= j <= p.
-  const uint32_t jmax = (uint32_t)min<int64_t>(ri.p, (int64_t)INT32_MAX);
+  // K/V row of list entry lp (lo <= lp < lo + rows_per_split + 2 STEP) in
+  // index mode (IM) or window mode; invalid entries (past the list, or
+  // outside [0, p]) map to row 0 of the sequence, so no gather leaves the
+  // sequence's rows.  Index mode reads the staged, already checked entry
+  // (-1 if invalid); window mode tests its position with one unsigned
+  // compare (0 <= j <= p).
   auto row_of = [&](auto im, int lp, bool* ok) {
-    int32_t j;
-    if constexpr (decltype(im)::value)
-      j = idx_lds[min(lp - lo, kAttnMaxRows - 1)];
-    else
-      j = (int32_t)jw0 + lp;
-    const bool v = (lp < hi) & ((uint32_t)j <= jmax);
-    *ok = v;
-    return v ? j : 0;
+    if constexpr (decltype(im)::value) {
+      const int32_t j = idx_lds[lp - lo];
+      *ok = j >= 0;
+      return max(j, 0);
+    } else {
+      const int32_t j = (int32_t)jw0 + lp;
+      const bool v = (lp < hi) & ((uint32_t)j <= jmax);
+      *ok = v;
+      return v ? j : 0;
+    }
   };
   // gather layout: this lane's chunk and its tile rows (one per load); row
   // j of the sequence is at 32-bit element offset j * D from these bases

@@ -69,6 +69,11 @@ __global__ __launch_bounds__(64) void tile_report_kernel(const float* __restrict
 // ---------------------------------------------------------------------------
 constexpr int kBucketMax = 64;  // boundary-bucket size ranked directly by wave 0
 
+// An empty hook: nothing to issue or stage at the hook's point.
+struct NoPost {
+  __device__ void operator()() const {}
+};
+
 template <int NTILE>
 struct ResolveSmemT {
   // two 2048-bin histograms (the union select alternates between them);
@@ -340,13 +345,16 @@ __device__ __forceinline__ void union_threshold(SM& sm, const UnionRegs<NSL>& R,
 // candidates, *theta (if given) receives the key of its k-th best and
 // *has_theta is set, whether or not the certification holds; when the
 // certification fails, *nbad (if given) receives the number of sub-tiles
-// that failed it.
-template <int NSL, class SM>
+// that failed it.  On success, every thread runs stage() right before the
+// barrier that publishes the staged selection, so a caller's own LDS writes
+// placed there are published by the same barrier.
+template <int NSL, class SM, class Stage = NoPost>
 __device__ __forceinline__ bool select_from_regs(SM& sm, const UnionRegs<NSL>& R,
                                                  uint32_t k, int K, int ntiles, int nt,
                                                  int32_t* out, uint32_t* theta = nullptr,
                                                  bool* has_theta = nullptr,
-                                                 uint32_t* nbad = nullptr) {
+                                                 uint32_t* nbad = nullptr,
+                                                 Stage stage_hook = Stage()) {
   const int tid = threadIdx.x, l = lane_id(), wv = wave_id();
   // candidate count and key range, in one block reduction; both histograms
   // are cleared meanwhile
@@ -439,6 +447,7 @@ __device__ __forceinline__ bool select_from_regs(SM& sm, const UnionRegs<NSL>& R
   for (int i = 0; i < NSL; ++i)
     if (i / 4 < R.qn && (((smask >> i) & 1u) & (uint32_t)(rk[i] < k)))
       stage[rk[i]] = (uint32_t)R.j[i];
+  stage_hook();
   lds_barrier();
   if (out == nullptr) return true;  // the caller reads the selection from sm.hbuf
   if ((K & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
@@ -796,21 +805,19 @@ __device__ __forceinline__ bool resolve_by_collection(ResolveSmem& sm, const flo
 // QE > 0: the report groups loaded before the row length is known are
 // exactly the first QE (a compile-time count, so no load is issued for the
 // others); QE = 0: the first eager_q, with the others reading slot 0.
-// Nothing to issue once the row's candidates are in registers.
-struct NoPost {
-  __device__ void operator()() const {}
-};
-
 // post() runs once per thread when the row's candidates (or its scores) are
 // in registers, before the selection's first exchange: a caller's own loads
 // issued there queue behind the candidates' instead of ahead of them, and
-// are in flight during the selection.
-template <int NSL, bool ALL, int QE = 0, class Post = NoPost>
-__device__ __forceinline__ void resolve_row(
+// are in flight during the selection.  stage() runs before the barrier that
+// publishes the selection when the register path succeeds at once (the
+// usual case); returns whether it ran (block-uniform).
+template <int NSL, bool ALL, int QE = 0, class Post = NoPost, class Stage = NoPost>
+__device__ __forceinline__ bool resolve_row(
     ResolveSmem& sm, int t, const float* __restrict__ scores, int64_t ld, const int32_t* cu_q,
     const int32_t* ctx_len, int B, int K, int stride, int eager_nt, int eager_q,
     const RepHeader* __restrict__ hdr, const uint32_t* __restrict__ rep_u,
-    const int32_t* __restrict__ rep_j, int32_t* idx, uint32_t* stats, Post post = Post()) {
+    const int32_t* __restrict__ rep_j, int32_t* idx, uint32_t* stats, Post post = Post(),
+    Stage stage_hook = Stage()) {
   constexpr int QN = NSL / 4;
   const int tid = threadIdx.x, nb = blockDim.x;
   const int64_t slot0 = (int64_t)t * stride;
@@ -872,7 +879,7 @@ __device__ __forceinline__ void resolve_row(
       if (out) out[i] = v;
       if (ALL) sm.hbuf[i] = (uint32_t)v;
     }
-    return;
+    return false;
   }
   const uint32_t k = (uint32_t)K;
   const float* row = scores + (int64_t)t * ld;
@@ -890,7 +897,7 @@ __device__ __forceinline__ void resolve_row(
   if (n <= kDirectMax && n <= (int64_t)nb * NSL) {
     // ---- direct: slot s holds position s ----
     nt = ALL ? nb : threads_for(n);
-    if (tid >= nt) return;
+    if (tid >= nt) return false;
     R.qn = (int)((n + 4 * nt - 1) / (4 * nt));
     // every group is loaded (straight-line loads, one round trip); groups
     // past the row read position 0 and are invalid
@@ -923,7 +930,7 @@ __device__ __forceinline__ void resolve_row(
     const int nt_row = (int)((n + S - 1) >> (31 - __clz(S)));  // S: a power of two
     if (nt_row <= kResolveTiles && nt_row <= stride && nt_row * kRep <= nb * NSL) {
       nt = ALL ? nb : max(threads_for((int64_t)nt_row * kRep), eager_nt);
-      if (tid >= nt) return;
+      if (tid >= nt) return false;
       R.qn = (nt_row * kRep + 4 * nt - 1) / (4 * nt);
       if (nt != eager_nt || eager_q == 0)
         load_reports(0, R.qn, nt);  // another layout: load every group
@@ -959,9 +966,10 @@ __device__ __forceinline__ void resolve_row(
   uint32_t theta = 0, nbad = 0;
   bool has_theta = false;
   if (path >= 0) {
-    ok = select_from_regs(sm, R, k, K, ntiles, nt, out, &theta, &has_theta, &nbad);
+    ok = select_from_regs(sm, R, k, K, ntiles, nt, out, &theta, &has_theta, &nbad, stage_hook);
     if (ok && stats && tid == 0) atomicAdd(&stats[path], 1u);
   }
+  const bool staged = ok;
   // A report union that failed its certification bounds the row: its keys
   // at or above theta are at most K plus the failing sub-tiles' left-out
   // elements (S - 16 each, ties at theta aside); the second chance is tried
@@ -978,6 +986,7 @@ __device__ __forceinline__ void resolve_row(
     exact_select_row(sm, row, n, k, vec, nt, out, ALL);
     if (stats && tid == 0) atomicAdd(&stats[1], 1u);
   }
+  return staged;
 }
 
 template <int NSL>
@@ -1001,18 +1010,21 @@ __global__ __launch_bounds__(kResolveSlots / NSL) void topk_resolve_kernel(
 // threads) first runs the whole selection of the row (resolve_row, ALL
 // mode: the same exact result in every workgroup; split 0 also writes the
 // row to idx) and then attends over ranks 64 s .. 64 s + 63 of it, read
-// from its own LDS.  The attention phase is laid out for 16 waves:
-//   wave w: row block rb = w & 1 (selected rows 32 rb .. + 31 of the
+// from its own LDS.  All 16 waves gather; the attention math runs on 8:
+//   wave w < 8: row block rb = w & 1 (selected rows 32 rb .. + 31 of the
 //   split), head block hb = (w >> 1) & 1 (heads 32 hb .. + 31), output dim
-//   block dq = w >> 2 (dims 32 dq .. + 31);
-//   - the split's K and V rows are gathered once, two 1 KiB loads per wave,
-//     into the swizzled row tiles (RowTile);
+//   half dh = w >> 2 (dims 64 dh .. + 63).  Waves w and w + 4 share a SIMD
+//   (waves go to the SIMDs in turn) and the same (rb, hb);
+//   - the split's K and V rows are gathered once, two 1 KiB loads per wave
+//     of all 16, into the swizzled row tiles (RowTile); waves 8..15 then
+//     exit;
 //   - S^T = K_rb . q_hb^T (v_mfma_f32_32x32x16_bf16, 8 k-steps) is computed
-//     alike by the four dim-block waves of (rb, hb), so no exchange comes
-//     before the softmax;
+//     alike by the two dim-half waves of (rb, hb), so no exchange comes
+//     before the softmax (with four dim-quarter waves per (rb, hb) each
+//     SIMD's matrix pipe computed the same S four times);
 //   - softmax over the row block (each lane holds one head: max and sum
 //     take one cross-half exchange); P^T is the B operand of O^T = V^T . P^T
-//     for the wave's 32 dims (two MFMAs, V^T through the transpose read);
+//     for the wave's 64 dims (four MFMAs, V^T through the transpose read);
 //   - the rb = 1 waves hand (m, l, O) to their rb = 0 partners through LDS,
 //     which merge them and write the split's partial (m, l, O) in the
 //     layout of the split attention kernel, merged by the combine kernel.
@@ -1021,6 +1033,8 @@ __global__ __launch_bounds__(kResolveSlots / NSL) void topk_resolve_kernel(
 // leaves the sequence.
 constexpr int kSaThreads = 1024;
 constexpr int kSaRows = 64;  // selected rows per split
+constexpr int kSaDimBlocks = 2;  // 32-dim output blocks per attention wave (2 or 4)
+constexpr int kSaMathWaves = 16 / kSaDimBlocks;  // waves that run the attention math
 
 template <int QE>
 __global__ __launch_bounds__(kSaThreads) void select_attend_kernel(
@@ -1034,7 +1048,9 @@ __global__ __launch_bounds__(kSaThreads) void select_attend_kernel(
   using VT = RowTile<D>;
   __shared__ ResolveSmem sm;
   __shared__ __attribute__((aligned(16))) uint8_t tiles[4 * VT::kBytes];  // K rb 0, 1; V rb 0, 1
-  __shared__ float mrg[8 * 18 * 64];  // (m, l, O) of the rb = 1 waves, per (hb, dq)
+  constexpr int DB = kSaDimBlocks, NMW = kSaMathWaves;
+  // (m, l, O) of the rb = 1 waves, per (hb, dh)
+  __shared__ float mrg[NMW / 2 * (2 + 16 * DB) * 64];
   // the query's 64 heads, chunk c of head h at 16 (c ^ (h % 16)): the B
   // operand reads (16 heads, one chunk) hit 16 distinct 16-byte slots
   __shared__ __attribute__((aligned(16))) uint8_t q_lds[HQ * D * 2];
@@ -1044,19 +1060,27 @@ __global__ __launch_bounds__(kSaThreads) void select_attend_kernel(
   // chunk l % 16) once its report candidates are in registers, so that the
   // load is in flight during the selection without delaying the reports
   // (0.3 us less per 128K decode step than issuing it first); it goes to
-  // LDS after the selection
+  // LDS at the end of the selection, published by the barrier that
+  // publishes the selection
   const int qh = 4 * wv + (l >> 4), qc = l & 15;
   u32x4 qv;
-  resolve_row<NSL, true, QE>(sm, t, scores, ld, nullptr, ctx_len, B, K, stride, kSaThreads,
-                             eager_q, hdr, rep_u, rep_j, split == 0 ? idx : nullptr,
-                             split == 0 ? stats : nullptr,
-                             [&]() { qv = ld16(q + ((int64_t)t * HQ + qh) * D + 8 * qc); });
-  *reinterpret_cast<u32x4*>(q_lds + qh * (2 * D) + ((qc ^ (qh & 15)) << 4)) = qv;
+  auto put_q = [&]() {
+    *reinterpret_cast<u32x4*>(q_lds + qh * (2 * D) + ((qc ^ (qh & 15)) << 4)) = qv;
+  };
+  const bool q_put = resolve_row<NSL, true, QE>(
+      sm, t, scores, ld, nullptr, ctx_len, B, K, stride, kSaThreads, eager_q, hdr, rep_u, rep_j,
+      split == 0 ? idx : nullptr, split == 0 ? stats : nullptr,
+      [&]() { qv = ld16(q + ((int64_t)t * HQ + qh) * D + 8 * qc); }, put_q);
+  if (!q_put) {
+    // the selection took another path: the query heads, and the selection
+    // itself, are published here
+    put_q();
+    dma_barrier();
+  }
   // the selection is in sm.hbuf (rank order, -1 past K_eff); split 0's
   // stores of it to idx stay in flight
-  dma_barrier();
 
-  const int rb = wv & 1, hb = (wv >> 1) & 1, dq = wv >> 2;
+  const int rb = wv & 1, hb = (wv >> 1) & 1, dh = (wv >> 2) & (NMW / 4 - 1);
   const int64_t p = (int64_t)ctx_len[t] - 1;
   const int64_t row0 = cu_ctx[t];
   const uint32_t jmax = (uint32_t)min<int64_t>(p, (int64_t)INT32_MAX);
@@ -1084,12 +1108,14 @@ __global__ __launch_bounds__(kSaThreads) void select_attend_kernel(
     }
     // q heads of the wave's head block from LDS while the gathers are in
     // flight (B operand of S^T: column = head 32 hb + l % 32, k = dims
-    // 16 s + 8 g .. + 7)
+    // 16 s + 8 g .. + 7); the gather-only waves skip them
     const int h = 32 * hb + (l & 31);
+    if (wv < NMW) {
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
-      qb[s] = as_bf16x8(
-          *reinterpret_cast<const u32x4*>(q_lds + h * (2 * D) + (((2 * s + g) ^ (h & 15)) << 4)));
+      for (int s = 0; s < KS; ++s)
+        qb[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(q_lds + h * (2 * D) +
+                                                          (((2 * s + g) ^ (h & 15)) << 4)));
+    }
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2)
       *reinterpret_cast<u32x4*>(tiles + tl * VT::kBytes + VT::offset(rr[c2], 8 * gch)) = v[c2];
@@ -1097,6 +1123,7 @@ __global__ __launch_bounds__(kSaThreads) void select_attend_kernel(
   // bit r: selected row 32 rb + r is valid (lanes 32..63 repeat 0..31)
   const uint32_t vmask = (uint32_t)__ballot(sel(32 * rb + (l & 31)) <= jmax);
   dma_barrier();  // the tiles are complete
+  if (wv >= NMW) return;  // the later barrier waits for the math waves left
 
   // S^T = K . q^T: the A operand of k-step s is tile row l % 32, dims 16 s + 8 g .. + 7
   f32x16 sacc = {};
@@ -1132,34 +1159,40 @@ __global__ __launch_bounds__(kSaThreads) void select_attend_kernel(
   for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
     for (int e = 0; e < 8; ++e) pb[s2][e] = static_cast<__bf16>(sv[8 * s2 + e]);
-  // O^T = V^T . P^T for dims 32 dq .. + 31: k slot e of step s2 is
-  // accumulator row 16 s2 + 8 (e / 4) + 4 g + e % 4, whose two 4-row groups
-  // each come from one transpose read (lane jj of a 16-lane group addresses
-  // row k0 + jj / 4, dims n0 + 4 (jj % 4) .. + 3)
-  f32x16 o = {};
+  // O^T = V^T . P^T for dims 64 dh .. + 63, as two 32-dim blocks dqq: k slot
+  // e of step s2 is accumulator row 16 s2 + 8 (e / 4) + 4 g + e % 4, whose
+  // two 4-row groups each come from one transpose read (lane jj of a
+  // 16-lane group addresses row k0 + jj / 4, dims n0 + 4 (jj % 4) .. + 3)
+  f32x16 o[DB] = {};
   {
     const uint16_t* vt16 = reinterpret_cast<const uint16_t*>(tiles + (2 + rb) * VT::kBytes);
     const int G = l >> 4, jj = l & 15;
-    const int n0 = 32 * dq + 16 * (G & 1) + 4 * (jj & 3);
-    u32x2 av[2][2];
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const int k0 = 16 * s2 + 4 * g + (jj >> 2);
-      av[s2][0] = lds_read_tr16(vt16 + VT::offset(k0, n0) / 2);
-      av[s2][1] = lds_read_tr16(vt16 + VT::offset(k0 + 8, n0) / 2);
+    for (int d2 = 0; d2 < DB; ++d2) {
+      const int n0 = 32 * (DB * dh + d2) + 16 * (G & 1) + 4 * (jj & 3);
+      u32x2 av[2][2];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int k0 = 16 * s2 + 4 * g + (jj >> 2);
+        av[s2][0] = lds_read_tr16(vt16 + VT::offset(k0, n0) / 2);
+        av[s2][1] = lds_read_tr16(vt16 + VT::offset(k0 + 8, n0) / 2);
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+        o[d2] = mfma32(
+            as_bf16x8(u32x4{av[s2][0][0], av[s2][0][1], av[s2][1][0], av[s2][1][1]}), pb[s2],
+            o[d2]);
     }
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-      o = mfma32(as_bf16x8(u32x4{av[s2][0][0], av[s2][0][1], av[s2][1][0], av[s2][1][1]}), pb[s2],
-                 o);
   }
   // merge the two row blocks: rb = 1 hands over, rb = 0 writes the partial
-  float* ms = mrg + (hb * 4 + dq) * 18 * 64;
+  float* ms = mrg + (hb * (NMW / 4) + dh) * (2 + 16 * DB) * 64;
   if (rb == 1) {
     ms[l] = m;
     ms[64 + l] = lsum;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) ms[(2 + r) * 64 + l] = o[r];
+    for (int d2 = 0; d2 < DB; ++d2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ms[(2 + 16 * d2 + r) * 64 + l] = o[d2][r];
   }
   lds_barrier();
   if (rb == 1) return;
@@ -1168,14 +1201,17 @@ __global__ __launch_bounds__(kSaThreads) void select_attend_kernel(
   const float a = (M == -INFINITY) ? 0.f : fexp2(m - M);
   const float bb = (M == -INFINITY) ? 0.f : fexp2(mo - M);
   const float L = lsum * a + lo2 * bb;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) o[r] = o[r] * a + ms[(2 + r) * 64 + l] * bb;
   float* pp = part + (((int64_t)t * nsplit + split) * HQ + 32 * hb + (l & 31)) * (D + 2);
 #pragma unroll
-  for (int r4 = 0; r4 < 4; ++r4)
-    *reinterpret_cast<f32x4*>(pp + 32 * dq + 8 * r4 + 4 * g) =
-        f32x4{o[4 * r4], o[4 * r4 + 1], o[4 * r4 + 2], o[4 * r4 + 3]};
-  if (dq == 0 && g == 0) {
+  for (int d2 = 0; d2 < DB; ++d2) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[d2][r] = o[d2][r] * a + ms[(2 + 16 * d2 + r) * 64 + l] * bb;
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4)
+      *reinterpret_cast<f32x4*>(pp + 32 * (DB * dh + d2) + 8 * r4 + 4 * g) =
+          f32x4{o[d2][4 * r4], o[d2][4 * r4 + 1], o[d2][4 * r4 + 2], o[d2][4 * r4 + 3]};
+  }
+  if (dh == 0 && g == 0) {
     pp[D] = M;
     pp[D + 1] = L;
   }

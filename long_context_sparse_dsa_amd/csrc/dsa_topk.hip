@@ -204,6 +204,7 @@ __device__ __forceinline__ void ordered_ranks(SM& sm, uint32_t fmask, int qn, in
 template <int NSL, class SM>
 __device__ __forceinline__ void gather_bucket(SM& sm, const UnionRegs<NSL>& R,
                                               uint32_t lo, uint32_t wm1) {
+  if (R.qn == 0) return;  // a wave outside the selecting threads
   const int l = lane_id();
   uint32_t inb = 0;
 #pragma unroll
@@ -240,7 +241,7 @@ __device__ __forceinline__ void rank_bucket(SM& sm, uint32_t h, uint32_t need, i
   const uint32_t um = mine_ok ? sm.bu[l] : 0u;
   const int32_t jm = mine_ok ? sm.bj[l] : 0;
 #pragma unroll 1
-  for (int e = wv; e < (int)h; e += nw) {
+  for (int e = wv < nw ? wv : (int)h; e < (int)h; e += nw) {
     const uint32_t ue = sm.bu[e];
     const int32_t je = sm.bj[e];
     const uint64_t beats = __ballot(mine_ok && (um > ue || (um == ue && jm < je)));
@@ -292,7 +293,7 @@ __device__ __forceinline__ void union_threshold(SM& sm, const UnionRegs<NSL>& R,
       wave_find_digit(sm, hc, above, k);
       if (nt == 64)  // a single wave clears the next pass's histogram itself
         for (int i = tid; i < 2048; i += 64) hn[i] = 0;
-    } else {
+    } else if (tid < nt) {
       for (int i = tid - 64; i < 2048; i += nt - 64) hn[i] = 0;  // next pass's histogram
     }
     lds_barrier();
@@ -375,7 +376,7 @@ __device__ __forceinline__ bool select_from_regs(SM& sm, const UnionRegs<NSL>& R
     sm.red0[16 + wv] = mn;
     sm.red0[32 + wv] = mx;
   }
-  for (int i = tid; i < 2048; i += nt) {
+  for (int i = tid; i < 2048 && tid < nt; i += nt) {
     sm.hist()[i] = 0;
     sm.hist2()[i] = 0;
   }
@@ -401,7 +402,7 @@ __device__ __forceinline__ bool select_from_regs(SM& sm, const UnionRegs<NSL>& R
   // certification: every partly reported sub-tile ends at or below theta
   // (checked in the same block exchange as the ranks)
   bool bad = false;
-  for (int ti = tid; ti < ntiles; ti += nt) {
+  for (int ti = tid; ti < ntiles && tid < nt; ti += nt) {
     const uint32_t wu = sm.wu[ti], wj = sm.wj[ti];
     const bool complete = wj >> 31;
     const int32_t wpos = (int32_t)(wj & 0x7fffffffu);
@@ -426,7 +427,7 @@ __device__ __forceinline__ bool select_from_regs(SM& sm, const UnionRegs<NSL>& R
     lds_barrier();  // the caller's exact select reuses sm.red
     if (nbad) {  // the failing sub-tiles, counted (this path only)
       uint32_t c = 0;
-      for (int ti = tid; ti < ntiles; ti += nt) {
+      for (int ti = tid; ti < ntiles && tid < nt; ti += nt) {
         const uint32_t wu = sm.wu[ti], wj = sm.wj[ti];
         const int32_t wpos = (int32_t)(wj & 0x7fffffffu);
         c += (!(wj >> 31) && !((wu < tau_u) || (wu == tau_u && wpos >= tau_j))) ? 1u : 0u;
@@ -451,10 +452,10 @@ __device__ __forceinline__ bool select_from_regs(SM& sm, const UnionRegs<NSL>& R
   lds_barrier();
   if (out == nullptr) return true;  // the caller reads the selection from sm.hbuf
   if ((K & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
-    for (int i = tid; i < K / 4; i += nt)
+    for (int i = tid; i < K / 4 && tid < nt; i += nt)
       *reinterpret_cast<u32x4*>(out + 4 * i) = *reinterpret_cast<const u32x4*>(stage + 4 * i);
   } else {
-    for (int i = tid; i < K; i += nt) out[i] = (int32_t)stage[i];
+    for (int i = tid; i < K && tid < nt; i += nt) out[i] = (int32_t)stage[i];
   }
   return true;
 }
@@ -929,9 +930,13 @@ __device__ __forceinline__ bool resolve_row(
     sub_s = S;
     const int nt_row = (int)((n + S - 1) >> (31 - __clz(S)));  // S: a power of two
     if (nt_row <= kResolveTiles && nt_row <= stride && nt_row * kRep <= nb * NSL) {
-      nt = ALL ? nb : max(threads_for((int64_t)nt_row * kRep), eager_nt);
-      if (tid >= nt) return false;
-      R.qn = (nt_row * kRep + 4 * nt - 1) / (4 * nt);
+      // ALL: the first eager_nt threads select when the union fits them
+      // (the others stay for the caller, with no slots: they take part in
+      // the selection's barriers only); otherwise the whole block
+      nt = ALL ? (nt_row * kRep <= eager_nt * NSL ? eager_nt : nb)
+               : max(threads_for((int64_t)nt_row * kRep), eager_nt);
+      if (!ALL && tid >= nt) return false;
+      R.qn = tid < nt ? (nt_row * kRep + 4 * nt - 1) / (4 * nt) : 0;
       if (nt != eager_nt || eager_q == 0)
         load_reports(0, R.qn, nt);  // another layout: load every group
       else if (R.qn > eager_q)
@@ -974,16 +979,17 @@ __device__ __forceinline__ bool resolve_row(
   // at or above theta are at most K plus the failing sub-tiles' left-out
   // elements (S - 16 each, ties at theta aside); the second chance is tried
   // when that bound fits its slots.
+  const int nt_fb = ALL ? nb : nt;  // the fallbacks take every thread left
   const bool bounded =
       !ok && path == 0 && has_theta &&
       (uint64_t)K + (uint64_t)nbad * (uint64_t)(sub_s - kRep) <=
-          (uint64_t)min(kRefineCap, nt * 4);
+          (uint64_t)min(kRefineCap, nt_fb * 4);
   if (bounded) {
-    ok = resolve_by_collection(sm, row, n, vec, theta, k, K, nt, out);
+    ok = resolve_by_collection(sm, row, n, vec, theta, k, K, nt_fb, out);
     if (ok && stats && tid == 0) atomicAdd(&stats[5], 1u);
   }
   if (!ok) {
-    exact_select_row(sm, row, n, k, vec, nt, out, ALL);
+    exact_select_row(sm, row, n, k, vec, nt_fb, out, ALL);
     if (stats && tid == 0) atomicAdd(&stats[1], 1u);
   }
   return staged;
@@ -1043,7 +1049,7 @@ __global__ __launch_bounds__(kSaThreads) void select_attend_kernel(
     const uint32_t* __restrict__ rep_u, const int32_t* __restrict__ rep_j, int32_t* idx,
     uint32_t* stats, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int64_t* __restrict__ cu_ctx, float scale_log2,
-    float* __restrict__ part, int nsplit) {
+    float* __restrict__ part, int nsplit, int sel_nt) {
   constexpr int NSL = 16, D = 128, HQ = 64, KS = D / 16;
   using VT = RowTile<D>;
   __shared__ ResolveSmem sm;
@@ -1068,7 +1074,7 @@ __global__ __launch_bounds__(kSaThreads) void select_attend_kernel(
     *reinterpret_cast<u32x4*>(q_lds + qh * (2 * D) + ((qc ^ (qh & 15)) << 4)) = qv;
   };
   const bool q_put = resolve_row<NSL, true, QE>(
-      sm, t, scores, ld, nullptr, ctx_len, B, K, stride, kSaThreads, eager_q, hdr, rep_u, rep_j,
+      sm, t, scores, ld, nullptr, ctx_len, B, K, stride, sel_nt, eager_q, hdr, rep_u, rep_j,
       split == 0 ? idx : nullptr, split == 0 ? stats : nullptr,
       [&]() { qv = ld16(q + ((int64_t)t * HQ + qh) * D + 8 * qc); }, put_q);
   if (!q_put) {
@@ -1227,13 +1233,17 @@ hipError_t launch_select_attend(const float* scores, int64_t ld, const int32_t* 
                                 const void* q, const void* k_cache, const void* v_cache,
                                 const int64_t* cu_ctx, float sm_scale, float* part,
                                 int nsplit, hipStream_t stream) {
-  // eager report loads laid out for the whole block, as in the resolve kernel
-  int eager_q = 0;
+  // A union of up to 8192 candidates is selected by the first 512 threads
+  // (16 slots each): per-wave work (scans, exchanges, address arithmetic)
+  // is then paid by 8 waves instead of 16, and the CU's vector issue is the
+  // selection's bound.  The eager report loads are laid out for them.
+  int eager_q = 0, sel_nt = kSaThreads;
   if (w.max_ctx > kDirectMax) {
     const int s = topk_subtile(w.max_ctx, K);
     const int64_t slots =
         std::min<int64_t>(kResolveSlots, (int64_t)((w.max_ctx + s - 1) / s) * kRep);
-    eager_q = (int)((slots + 4 * kSaThreads - 1) / (4 * kSaThreads));
+    if (slots <= (int64_t)(kSaThreads / 2) * 16) sel_nt = kSaThreads / 2;
+    eager_q = (int)((slots + 4 * sel_nt - 1) / (4 * sel_nt));
   }
   const float scale = (sm_scale != 0.f ? sm_scale : 1.f / sqrtf(128.f)) * kLog2e;
   // the groups loaded ahead are a compile-time count (no loads for the rest)
@@ -1242,7 +1252,7 @@ hipError_t launch_select_attend(const float* scores, int64_t ld, const int32_t* 
                      scores, ld, ctx_len, B, K, w.stride, eager_q, w.hdr, w.rep_u, w.rep_j, idx, \
                      stats, static_cast<const uint16_t*>(q),                                   \
                      static_cast<const uint16_t*>(k_cache),                                    \
-                     static_cast<const uint16_t*>(v_cache), cu_ctx, scale, part, nsplit)
+                     static_cast<const uint16_t*>(v_cache), cu_ctx, scale, part, nsplit, sel_nt)
   switch (eager_q) {
     case 1: DSA_SA_LAUNCH(1); break;
     case 2: DSA_SA_LAUNCH(2); break;

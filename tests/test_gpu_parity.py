@@ -563,6 +563,42 @@ def test_layer_decode_clustered_winners_take_the_fallbacks(dsa):
     assert c[5] == 1 and c[1] == 1 and c[0] == 0, c
 
 
+def test_layer_decode_selection_widths_in_the_fused_launch(dsa):
+    """In the decode layer of few sequences a union of at most 8192 report
+    candidates is selected by the first 8 waves of each split workgroup (16
+    slots per thread) and a larger one by all 16: a row of 131072 positions
+    (512 sub-tiles of 256) next to a row of 100000 (782 sub-tiles of 128,
+    in the wider layout) in one launch, then the same two rows with their
+    winners clustered so that the first takes the collection sweep and the
+    second the exact select, both run by the whole block.  Index rows stay
+    bit-exact against the oracle's Top-K of the layer's own scores."""
+    say("layer_decode selection widths: 8-wave and 16-wave unions, fallbacks after the 8-wave one")
+    lens = [131072, 100000]
+    w = wl("t", lens, [1, 1], 16, 128, 64, 128, 2048, seed=67, plant_frac=0.05)
+    inp = W.make_inputs(w)
+    _, c = _with_counters(dsa, lambda: _layer_decode_check(dsa, w, inp, to_dev(inp)))
+    assert c[0] == 2 and c[1] == 0 and c[5] == 0, c
+    w = wl("t", lens, [1, 1], 16, 128, 64, 128, 2048, seed=68)
+    inp = W.make_inputs(w)
+    k = inp["k_idx"].float()
+    k[20000:21500] *= 8.0                      # sequence 0: collection sweep
+    k[lens[0] + 30000:lens[0] + 33500] *= 8.0  # sequence 1: exact select
+    inp["k_idx"] = k.to(torch.bfloat16)        # powers of two: exact
+    _, c = _with_counters(dsa, lambda: _layer_decode_check(dsa, w, inp, to_dev(inp)))
+    assert c[5] == 1 and c[1] == 1 and c[0] == 0, c
+
+
+def test_layer_decode_2m_context_full_union(dsa):
+    """One sequence of 2^21 positions (fp8 keys): 1024 sub-tiles of 2048,
+    16384 report candidates, selected by all 16 waves of each split
+    workgroup inside the attention's launch."""
+    say("layer_decode 2M context fp8: 16384-candidate union in the fused launch")
+    w = wl("t", [1 << 21], [1], 32, 128, 64, 128, 2048, key_dtype="fp8", seed=69)
+    inp = W.make_inputs(w)
+    _, c = _with_counters(dsa, lambda: _layer_decode_check(dsa, w, inp, to_dev(inp)))
+    assert c[0] == 1 and c[1] == 0 and c[5] == 0, c
+
+
 def test_layer_decode_large_batch_takes_the_row_sweeps(dsa):
     """1024 sequences and more: the indexer writes plain scores and every row
     is selected by sweeps over them (no candidate reports)."""

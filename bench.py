@@ -429,12 +429,21 @@ def bench_prefill(args, torch, dsa, W):
     return result
 
 
+_FLUSH = {}
+
+
 def flush_infinity_cache(torch, mib=512):
-    """Write a buffer twice the 256 MiB Infinity Cache, so that no layer
-    buffer stays cached from set-up or warm-up."""
-    buf = torch.empty(mib << 20, dtype=torch.uint8, device="cuda")
-    buf.fill_(1)
-    del buf
+    """Read a buffer twice the 256 MiB Infinity Cache, so that no layer
+    buffer stays cached from set-up or warm-up.  The buffer is written once,
+    on the first call; later calls only read it, so the cache is left
+    holding clean lines and the timed steps do not pay for writing a
+    flush's dirty lines back to HBM."""
+    buf = _FLUSH.get(mib)
+    if buf is None:
+        buf = torch.ones(mib << 20, dtype=torch.uint8, device="cuda")
+        _FLUSH[mib] = buf
+        torch.cuda.synchronize()
+    buf.view(torch.int64).amax()
 
 
 def measured_copy_bandwidth(torch, mib=2048, reps=5):

@@ -40,12 +40,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--workload", default="dec128k",
                     choices=["dec128k", "dec1m_b32_fp8", "prefill8k", "prefill8k_fp8",
-                             "hybrid51"],
+                             "hybrid51", "tiny"],
                     help="dec128k (default, the headline metric); the others time the "
                          "same path on the batched 1M-context fp8 decode, on the 8K "
                          "prefill chunk (bf16, or fp8 query heads and keys on the fp8 "
-                         "MFMA), and on one 5:1 SWA/DSA hybrid decode step of a ragged "
-                         "batch of 8")
+                         "MFMA), on one 5:1 SWA/DSA hybrid decode step of a ragged "
+                         "batch of 8, and on the tiny 4K-context decode parity shape")
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--rotate", type=int, default=None, help="distinct layer buffer sets")
@@ -56,7 +56,7 @@ def parse():
                          "kernel of known traffic for hardware-counter runs)")
     a = ap.parse_args()
     dflt = {"dec128k": (200, 20, 16), "dec1m_b32_fp8": (20, 3, 1), "prefill8k": (5, 1, 1),
-            "prefill8k_fp8": (5, 1, 1), "hybrid51": (50, 5, 1)}
+            "prefill8k_fp8": (5, 1, 1), "hybrid51": (50, 5, 1), "tiny": (200, 20, 1)}
     st, wu, rot = dflt[a.workload]
     a.steps = a.steps if a.steps is not None else st
     a.warmup = a.warmup if a.warmup is not None else wu
@@ -145,7 +145,8 @@ def main():
 
 def bench_decode(args, torch, dsa, W):
     dev = "cuda"
-    wl = W.decode_128k() if args.workload == "dec128k" else W.decode_1m_b32_fp8()
+    wl = {"dec128k": W.decode_128k, "dec1m_b32_fp8": W.decode_1m_b32_fp8,
+          "tiny": W.tiny_decode}[args.workload]()
     L = max(wl.ctx_lens)
     sets = [W.make_inputs(wl, device=dev, seed_offset=i) for i in range(args.rotate)]
     ws = torch.empty(dsa.dsa_layer_decode_workspace_size(wl.B, L, wl.K, wl.Hq, wl.D),
@@ -248,8 +249,10 @@ def bench_decode(args, torch, dsa, W):
         "warm_cache": {"ms_per_step": round(ms_warm, 5),
                        "tokens_per_s": round(wl.B / (ms_warm * 1e-3), 1)},
     }
-    if args.workload != "dec128k":
+    if args.workload == "dec1m_b32_fp8":
         result["metric"] = "DSA layer decode tokens/s (batched 1M-context fp8 decode)"
+    elif args.workload == "tiny":
+        result["metric"] = "DSA layer decode tokens/s (4K-context parity shape)"
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(sets[0], wl, args.cpu_seconds)
     return result

@@ -178,8 +178,9 @@ __device__ __forceinline__ void ordered_ranks(SM& sm, uint32_t fmask, int qn, in
   const bool wbad = __ballot(bad) != 0;
   if (l == 0) sm.flag[wv] = wbad ? 1u : 0u;
   lds_barrier();
+  // (a wave with no slots needs neither the exchange's prefix nor its total)
   const uint32_t x = l < qn * nw ? sm.red[l] : 0u;
-  const uint32_t xi = wave_incl_scan(x);
+  const uint32_t xi = qn > 0 ? wave_incl_scan(x) : 0u;
   const uint32_t xe = xi - x;
   *total = (uint32_t)__builtin_amdgcn_readlane((int)xi, 63);
   if (any_bad) *any_bad = __ballot(l < nw && sm.flag[l] != 0u) != 0;
@@ -368,13 +369,15 @@ __device__ __forceinline__ bool select_from_regs(SM& sm, const UnionRegs<NSL>& R
       mx = max(mx, vi ? R.u[i] : 0u);
     }
   }
-  const uint32_t cw = wave_sum_u32((uint32_t)__popc(R.vmask));
-  mn = wave_min_u32(mn);
-  mx = wave_max_u32(mx);
-  if (l == 0) {
-    sm.red0[wv] = cw;
-    sm.red0[16 + wv] = mn;
-    sm.red0[32 + wv] = mx;
+  if (wv < (nt >> 6)) {  // waves outside the selecting threads hold nothing
+    const uint32_t cw = wave_sum_u32((uint32_t)__popc(R.vmask));
+    mn = wave_min_u32(mn);
+    mx = wave_max_u32(mx);
+    if (l == 0) {
+      sm.red0[wv] = cw;
+      sm.red0[16 + wv] = mn;
+      sm.red0[32 + wv] = mx;
+    }
   }
   for (int i = tid; i < 2048 && tid < nt; i += nt) {
     sm.hist()[i] = 0;
